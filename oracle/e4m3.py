@@ -1,0 +1,107 @@
+"""FP8 E4M3 state quantise/dequantise with one amax scale per [K, block_v] tile.
+
+Pages followed:
+* modelopt ... linear_attention.config, LinearAttentionConfig: ``state.block_v``
+  gives one dynamic scale per [Dk, block_v] tile of each sequence and head.
+* modelopt ... linear_attention.decode, EncodedLinearAttentionTensor: values
+  are kept fake-decoded next to their scales; there is no compressed storage.
+  ``recurrent_decode`` names ``state_format='fp8_e4m3'`` and ``block_v=64``.
+
+The FP8 format itself is not on the pages; it follows the OCP 8-bit
+floating point specification (E4M3): sign bit, 4 exponent bits with bias 7,
+3 mantissa bits, exponent field 0 holds subnormals m * 2^-9, the single NaN
+pattern is S.1111.111, there are no infinities, the largest finite value is
+448.
+
+Readings (listed in the design doc):
+* dynamic scale s = amax / 448, so the tile's largest magnitude maps to the
+  top of the grid;
+* round to nearest, ties to even mantissa, saturating at +-448; subnormals
+  kept; a tile whose amax is 0 is left as it is; NaN propagates.
+
+Pins (tests/test_oracle_e4m3.py): the 256-code table built from the bit
+fields is checked against PyTorch's CPU ``float8_e4m3fn`` decode; every
+finite code is a fixed point of ``e4m3_round``; exact midpoints go to the
+even code; random values agree with PyTorch's CPU cast inside the finite
+range; QDQ is idempotent and maps each tile's extreme element to +-amax.
+"""
+import numpy as np
+
+E4M3_MAX = 448.0
+E4M3_BIAS = 7
+E4M3_MIN_NORMAL_EXP = -6  # 2^(1 - bias)
+
+
+def e4m3_decode_code(code):
+    """Value of one 8-bit E4M3 code (0..255) from its bit fields; NaN for S.1111.111."""
+    code = int(code)
+    sign = -1.0 if (code >> 7) & 1 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** (1 - E4M3_BIAS)
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - E4M3_BIAS)
+
+
+def e4m3_table():
+    """All 256 code values, index = code."""
+    return np.array([e4m3_decode_code(c) for c in range(256)], dtype=np.float64)
+
+
+def e4m3_round(y):
+    """Round float64 values to the E4M3 grid: nearest, ties to even, saturate at +-448.
+
+    Within the binade [2^e, 2^(e+1)) the grid spacing is 2^(e-3); below the
+    smallest normal 2^-6 the spacing stays 2^-9 (subnormals).  Dividing by a
+    power of two is exact, so ``rint`` (ties to even) on y / spacing picks the
+    nearest grid point and, on a tie, the one with an even mantissa field.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    _, ex = np.frexp(a)                    # a = m * 2^ex, m in [0.5, 1)
+    e = np.clip(ex - 1, E4M3_MIN_NORMAL_EXP, 8)
+    step = np.ldexp(1.0, e - 3)
+    r = np.rint(a / step) * step
+    r = np.minimum(r, E4M3_MAX)
+    r = np.where(np.isnan(a), np.nan, r)
+    return np.copysign(r, y)
+
+
+def tile_qdq(S, block_v=64):
+    """Quantise/dequantise S [H, K, V] with one scale per [K, block_v] tile of each head.
+
+    For each tile: amax = max |S|; if amax == 0 the tile is unchanged;
+    otherwise s = amax / 448 and each x becomes s * e4m3_round(x / s).
+    """
+    S = np.asarray(S, dtype=np.float64)
+    H, K, V = S.shape
+    if V % block_v != 0:
+        raise ValueError("block_v must divide the value head dim")
+    out = S.copy()
+    for j0 in range(0, V, block_v):
+        tile = S[:, :, j0:j0 + block_v]
+        amax = np.max(np.abs(tile), axis=(1, 2))
+        for h in range(H):
+            if amax[h] == 0.0:
+                continue
+            s = amax[h] / E4M3_MAX
+            out[h, :, j0:j0 + block_v] = s * e4m3_round(tile[h] / s)
+    return out
+
+
+def tile_scales(S, block_v=64):
+    """The per-tile scales s = amax / 448 of S [H, K, V] -> [H, V // block_v]."""
+    S = np.asarray(S, dtype=np.float64)
+    H, K, V = S.shape
+    amax = np.abs(S).reshape(H, K, V // block_v, block_v).max(axis=(1, 3))
+    return amax / E4M3_MAX
+
+
+def e4m3_spacing(y):
+    """Grid spacing of E4M3 at magnitude |y| (the size of one quantisation step there)."""
+    a = np.abs(np.asarray(y, dtype=np.float64))
+    _, ex = np.frexp(a)
+    e = np.clip(ex - 1, E4M3_MIN_NORMAL_EXP, 8)
+    return np.ldexp(1.0, e - 3)

@@ -1,0 +1,255 @@
+"""Seeded synthetic inputs for the decode workloads.
+
+This module draws random inputs and builds index tables; it holds none of
+the decode arithmetic.  Tests, the bench and the smoke run feed the same
+draws to the HIP library and to the CPU oracle.
+
+Recipe (fixed draw order, numpy ``Generator(PCG64(seed))``):
+lengths -> page table -> q -> k -> v -> gate input (a or raw_gate) ->
+beta input (b or beta_logits) -> dt_bias -> A_log -> slot choice.
+Values are drawn in float32 and cast to the I/O dtype with round-to-nearest-
+even (torch CPU ``.to(bfloat16)``); the oracle receives the cast values.
+The state pool is filled on its own device with ``torch.Generator``
+(N(0, 0.05)) from ``seed + 1``; the oracle reads back the rows it needs.
+
+Distributions: q, k, v, a, b, raw_gate, beta_logits ~ N(0, 1);
+dt_bias ~ U(-1, 1); A_log (a_log) ~ U(0, ln 16).
+"""
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+K_FIRST = "K_FIRST"
+V_FIRST = "V_FIRST"
+
+
+@dataclass
+class Workload:
+    kind: str                         # "gdn_pooled" | "kda_pooled" | "gdn_paged"
+    name: str
+    B: int
+    HK: int
+    HV: int
+    K: int
+    V: int
+    io_dtype: torch.dtype
+    out_dtype: torch.dtype
+    state_layout: str
+    num_rows: int                     # slots (pooled) or pages (paged)
+    inputs: dict = field(default_factory=dict)   # CPU tensors
+    options: dict = field(default_factory=dict)  # beta_mode, qdq, block_v, ...
+    pool_seed: int = 0
+    pool_zero: bool = False
+
+    @property
+    def T(self):
+        return self.inputs["q"].shape[0]
+
+    def pool_shape(self):
+        tail = (self.K, self.V) if self.state_layout == K_FIRST else (self.V, self.K)
+        return (self.num_rows, self.HV) + tail
+
+    def read_rows(self):
+        """Pool rows read by the call (sorted unique)."""
+        if self.kind == "gdn_paged":
+            ind = self.inputs["page_indices"].numpy()
+            ptr = self.inputs["page_indptr"].numpy()
+            lpl = self.inputs["last_page_len"].numpy()
+            rows = [int(ind[ptr[b + 1] - 2]) if lpl[b] == 1 else int(ind[ptr[b + 1] - 1])
+                    for b in range(self.B)]
+        else:
+            rows = [int(s) for s in self.inputs["state_indices"].numpy()]
+        return sorted(set(rows))
+
+    def tokens(self):
+        return self.T
+
+
+def make_pool(w, device, dtype=torch.float32):
+    """The state pool of workload ``w`` on ``device``: N(0, 0.05) or zeros."""
+    shape = w.pool_shape()
+    if w.pool_zero:
+        return torch.zeros(shape, dtype=dtype, device=device)
+    g = torch.Generator(device=device)
+    g.manual_seed(w.pool_seed)
+    pool = torch.empty(shape, dtype=dtype, device=device)
+    pool.normal_(0.0, 0.05, generator=g)
+    return pool
+
+
+def _cast(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dtype)
+
+
+def _normal(rng, shape):
+    return rng.standard_normal(shape, dtype=np.float32)
+
+
+def _uniform(rng, lo, hi, shape):
+    return rng.uniform(lo, hi, shape).astype(np.float32)
+
+
+def lengths_to_cu(lengths):
+    return torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32)
+
+
+def gdn_pooled(B, HK, HV, K, V, *, lengths=None, num_slots=None, state_layout=K_FIRST,
+               io_dtype=torch.bfloat16, out_dtype=None, seed=0, name="gdn_pooled", zero_state=False,
+               **options):
+    """Pooled GDN decode; ``lengths`` None means one token per sequence (cu_seqlens = NULL)."""
+    rng = np.random.default_rng(seed)
+    T = B if lengths is None else int(np.sum(lengths))
+    num_slots = num_slots or B
+    inp = {}
+    inp["q"] = _cast(_normal(rng, (T, HK, K)), io_dtype)
+    inp["k"] = _cast(_normal(rng, (T, HK, K)), io_dtype)
+    inp["v"] = _cast(_normal(rng, (T, HV, V)), io_dtype)
+    inp["a"] = _cast(_normal(rng, (T, HV)), io_dtype)
+    inp["b"] = _cast(_normal(rng, (T, HV)), io_dtype)
+    inp["dt_bias"] = _cast(_uniform(rng, -1, 1, (HV,)), torch.float32)
+    inp["A_log"] = _cast(_uniform(rng, 0, math.log(16), (HV,)), torch.float32)
+    inp["state_indices"] = torch.tensor(rng.permutation(num_slots)[:B], dtype=torch.int32)
+    inp["cu_seqlens"] = None if lengths is None else lengths_to_cu(lengths)
+    return Workload("gdn_pooled", name, B, HK, HV, K, V, io_dtype, out_dtype or io_dtype, state_layout,
+                    num_slots, inp, options, pool_seed=seed + 1, pool_zero=zero_state)
+
+
+def kda_pooled(B, HK, HV, K, V, *, lengths, num_slots=None, state_layout=V_FIRST,
+               io_dtype=torch.bfloat16, out_dtype=None, seed=0, name="kda_pooled", zero_state=False,
+               **options):
+    """Pooled KDA decode over varlen suffixes given by ``lengths``."""
+    rng = np.random.default_rng(seed)
+    T = int(np.sum(lengths))
+    num_slots = num_slots or B
+    inp = {}
+    inp["q"] = _cast(_normal(rng, (T, HK, K)), io_dtype)
+    inp["k"] = _cast(_normal(rng, (T, HK, K)), io_dtype)
+    inp["v"] = _cast(_normal(rng, (T, HV, V)), io_dtype)
+    inp["raw_gate"] = _cast(_normal(rng, (T, HV, K)), io_dtype)
+    inp["beta_logits"] = _cast(_normal(rng, (T, HV)), io_dtype)
+    inp["dt_bias"] = _cast(_uniform(rng, -1, 1, (HV, K)), torch.float32)
+    inp["a_log"] = _cast(_uniform(rng, 0, math.log(16), (HV,)), torch.float32)
+    inp["state_indices"] = torch.tensor(rng.permutation(num_slots)[:B], dtype=torch.int32)
+    inp["cu_seqlens"] = lengths_to_cu(lengths)
+    return Workload("kda_pooled", name, B, HK, HV, K, V, io_dtype, out_dtype or io_dtype, state_layout,
+                    num_slots, inp, options, pool_seed=seed + 1, pool_zero=zero_state)
+
+
+def build_page_table(prefix_lengths, page_size, share_frac, rng, force_shared_new_page=8):
+    """CSR page table for sequences whose decoded token follows ``prefix_lengths`` tokens.
+
+    Sequence b holds n_b = L_b + 1 tokens on ceil(n_b / page_size) pages;
+    ``last_page_len`` = n_b - page_size * (pages - 1).  A fraction
+    ``share_frac`` of the full (non-last) pages is aliased to the page with
+    the same position in another sequence whose page there is also full, as
+    shared prefixes are; last pages are never shared.  Some sequences whose
+    decoded token opens a new page get a shared previous page on purpose.
+    Page ids are compacted to 0..num_pages-1 in a random physical order.
+    Returns (page_indices int64 [nnz], page_indptr int64 [B+1],
+    last_page_len int64 [B], num_pages).
+    """
+    L = np.asarray(prefix_lengths, dtype=np.int64)
+    n = L + 1
+    P = -(-n // page_size)
+    last_len = n - page_size * (P - 1)
+    B = len(L)
+    uid = [list(range(int(s), int(s + p))) for s, p in zip(np.concatenate([[0], np.cumsum(P)[:-1]]), P)]
+    full = [(b, j) for b in range(B) for j in range(int(P[b]) - 1)]
+    n_share = int(round(share_frac * len(full)))
+    chosen = set()
+    # sequences whose decoded token opens a new page: share their previous page first
+    newpage = [b for b in range(B) if last_len[b] == 1 and P[b] >= 2]
+    rng.shuffle(newpage)
+    for b in newpage[:force_shared_new_page]:
+        chosen.add((b, int(P[b]) - 2))
+    order = rng.permutation(len(full))
+    for i in order:
+        if len(chosen) >= n_share:
+            break
+        chosen.add(full[i])
+    # targets: same page position in another sequence, page not itself aliased
+    for (b, j) in sorted(chosen):
+        cands = np.nonzero((P - 1 > j) & (np.arange(B) != b))[0]
+        cands = [c for c in cands if (int(c), j) not in chosen]
+        if not cands:
+            continue
+        src = int(cands[rng.integers(len(cands))])
+        uid[b][j] = uid[src][j]
+    used = sorted({p for pages in uid for p in pages})
+    phys = rng.permutation(len(used))
+    remap = {old: int(phys[i]) for i, old in enumerate(used)}
+    indices = np.array([remap[p] for pages in uid for p in pages], dtype=np.int64)
+    indptr = np.concatenate([[0], np.cumsum(P)]).astype(np.int64)
+    return indices, indptr, last_len.astype(np.int64), len(used)
+
+
+def gdn_paged(B, HK, HV, K, V, *, prefix_lengths=None, max_prefix=2048, page_size=16, share_frac=0.1,
+              state_layout=V_FIRST, io_dtype=torch.bfloat16, out_dtype=None, index_dtype=torch.int64,
+              seed=0, name="gdn_paged", **options):
+    """Single-token GDN decode on a CSR-paged pool with shared prefix pages."""
+    rng = np.random.default_rng(seed)
+    if prefix_lengths is None:
+        prefix_lengths = rng.integers(1, max_prefix + 1, B)
+    ind, ptr, lpl, num_pages = build_page_table(prefix_lengths, page_size, share_frac, rng)
+    inp = {}
+    inp["q"] = _cast(_normal(rng, (B, HK, K)), io_dtype)
+    inp["k"] = _cast(_normal(rng, (B, HK, K)), io_dtype)
+    inp["v"] = _cast(_normal(rng, (B, HV, V)), io_dtype)
+    inp["a"] = _cast(_normal(rng, (B, HV)), io_dtype)
+    inp["b"] = _cast(_normal(rng, (B, HV)), io_dtype)
+    inp["dt_bias"] = _cast(_uniform(rng, -1, 1, (HV,)), torch.float32)
+    inp["A_log"] = _cast(_uniform(rng, 0, math.log(16), (HV,)), torch.float32)
+    inp["page_indices"] = torch.from_numpy(ind).to(index_dtype)
+    inp["page_indptr"] = torch.from_numpy(ptr).to(index_dtype)
+    inp["last_page_len"] = torch.from_numpy(lpl).to(index_dtype)
+    inp["prefix_lengths"] = torch.from_numpy(np.asarray(prefix_lengths, dtype=np.int64))
+    opts = dict(page_size=page_size, **options)
+    return Workload("gdn_paged", name, B, HK, HV, K, V, io_dtype, out_dtype or io_dtype, state_layout,
+                    num_pages, inp, opts, pool_seed=seed + 1)
+
+
+# ------------------------------------------------------------------ named workloads
+
+def tiny_gdn(seed=1001):
+    """B=1, HK=HV=1, K=V=16, 8 tokens, fp32 everywhere, zero initial state in a 1-slot pool."""
+    return gdn_pooled(1, 1, 1, 16, 16, lengths=[8], num_slots=1, state_layout=K_FIRST,
+                      io_dtype=torch.float32, seed=seed, name="tiny_gdn_b1_k16_t8_f32", zero_state=True)
+
+
+def pooled_gdn_b64(seed=1002):
+    """B=64 single-token GDN decode, HK=16, HV=32, K=V=128, bf16 I/O, 256-slot K_FIRST pool."""
+    return gdn_pooled(64, 16, 32, 128, 128, lengths=None, num_slots=256, state_layout=K_FIRST,
+                      seed=seed, name="pooled_gdn_b64_hv32_k128")
+
+
+def pooled_kda_varlen_b128(seed=1003):
+    """B=128 KDA varlen decode, suffixes U{1..8}, HK=HV=32, K=V=128, bf16 I/O, 512-slot V_FIRST pool."""
+    rng = np.random.default_rng(seed + 500)
+    lengths = rng.integers(1, 9, 128)
+    return kda_pooled(128, 32, 32, 128, 128, lengths=lengths, num_slots=512, state_layout=V_FIRST,
+                      seed=seed, name="pooled_kda_varlen_b128_hv32_k128")
+
+
+def paged_gdn_b256(seed=1004, state_layout=V_FIRST, index_dtype=torch.int64):
+    """B=256 paged GDN decode, HK=16, HV=32, K=V=128, page_size 16, prefixes U{1..2048}, 10% shared."""
+    return gdn_paged(256, 16, 32, 128, 128, max_prefix=2048, page_size=16, share_frac=0.1,
+                     state_layout=state_layout, index_dtype=index_dtype, seed=seed,
+                     name="paged_gdn_b256_hv32_k128_ps16")
+
+
+def fp8_qdq_gdn_b512(seed=1005):
+    """B=512 GDN decode with 4-token suffixes and fp8 e4m3 tile QDQ (block_v=64), 1024-slot pool."""
+    return gdn_pooled(512, 16, 32, 128, 128, lengths=np.full(512, 4), num_slots=1024,
+                      state_layout=K_FIRST, seed=seed, name="fp8_qdq_gdn_b512_t4_hv32_k128",
+                      qdq="fp8_e4m3_tile", block_v=64)
+
+
+NAMED = {
+    "tiny_gdn": tiny_gdn,
+    "pooled_gdn_b64": pooled_gdn_b64,
+    "pooled_kda_varlen_b128": pooled_kda_varlen_b128,
+    "paged_gdn_b256": paged_gdn_b256,
+    "fp8_qdq_gdn_b512": fp8_qdq_gdn_b512,
+}

@@ -1,0 +1,109 @@
+"""Pins of the E4M3 rounding and of the per-tile quantise/dequantise.
+
+The format is fixed by the OCP 8-bit floating point specification (the
+pages only name ``fp8_e4m3``); PyTorch's CPU ``float8_e4m3fn`` is an
+independent implementation of the same format and is used as a cross-check.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import e4m3
+
+
+def test_code_table_matches_torch_decode():
+    ours = e4m3.e4m3_table()
+    theirs = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(theirs))
+    fin = ~np.isnan(ours)
+    assert np.array_equal(ours[fin], theirs[fin])
+    assert np.nanmax(ours) == 448.0
+    assert np.isnan(ours).sum() == 2            # S.1111.111 only
+    assert ours[1] == 2.0 ** -9                  # smallest subnormal
+
+
+def _positive_grid():
+    t = e4m3.e4m3_table()[:128]
+    return np.sort(t[~np.isnan(t)])
+
+
+def test_every_finite_code_is_a_fixed_point():
+    t = e4m3.e4m3_table()
+    fin = t[~np.isnan(t)]
+    assert np.array_equal(e4m3.e4m3_round(fin), fin)
+
+
+def test_midpoints_round_to_even_code_and_neighbours_to_nearest():
+    g = _positive_grid()
+    codes = {float(v): c for c, v in enumerate(e4m3.e4m3_table()[:128]) if not np.isnan(v)}
+    for lo, hi in zip(g[:-1], g[1:]):
+        mid = (lo + hi) / 2
+        want = lo if codes[float(lo)] % 2 == 0 else hi
+        assert e4m3.e4m3_round(mid) == want
+        assert e4m3.e4m3_round(-mid) == -want
+        eps = (hi - lo) * 1e-6
+        assert e4m3.e4m3_round(mid - eps) == lo
+        assert e4m3.e4m3_round(mid + eps) == hi
+
+
+def test_saturation_above_448():
+    assert e4m3.e4m3_round(463.9) == 448.0
+    assert e4m3.e4m3_round(464.0) == 448.0      # tie between 448 and (absent) 480 -> even code 448
+    assert e4m3.e4m3_round(1e6) == 448.0
+    assert e4m3.e4m3_round(-1e6) == -448.0
+    assert np.isnan(e4m3.e4m3_round(np.nan))
+
+
+def test_random_values_match_torch_cast_inside_range():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.uniform(-448, 448, 20000),
+                        rng.standard_normal(20000) * 2.0 ** rng.integers(-12, 8, 20000)])
+    x = x[np.abs(x) <= 448]
+    ours = e4m3.e4m3_round(x)
+    theirs = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(ours, theirs)
+
+
+def test_tile_qdq_extreme_maps_to_amax_and_error_is_half_step():
+    rng = np.random.default_rng(1)
+    H, K, V, bv = 2, 16, 8, 4
+    S = rng.standard_normal((H, K, V)) * 0.05
+    Q = e4m3.tile_qdq(S, bv)
+    s = e4m3.tile_scales(S, bv)
+    for h in range(H):
+        for j in range(V // bv):
+            tile, qt = S[h, :, j * bv:(j + 1) * bv], Q[h, :, j * bv:(j + 1) * bv]
+            np.testing.assert_allclose(np.max(np.abs(qt)), np.max(np.abs(tile)), rtol=1e-15)
+            step = s[h, j] * e4m3.e4m3_spacing(tile / s[h, j])
+            assert np.all(np.abs(qt - tile) <= step / 2 * (1 + 1e-12))
+            codes = qt / s[h, j]
+            assert np.allclose(e4m3.e4m3_round(codes), codes, rtol=1e-14, atol=0)
+
+
+def test_tile_qdq_idempotent_and_zero_tile_untouched():
+    rng = np.random.default_rng(2)
+    S = rng.standard_normal((3, 8, 12))
+    S[1, :, 4:8] = 0.0
+    Q = e4m3.tile_qdq(S, 4)
+    np.testing.assert_allclose(e4m3.tile_qdq(Q, 4), Q, rtol=1e-15, atol=0)
+    assert np.array_equal(Q[1, :, 4:8], np.zeros((8, 4)))
+
+
+def test_tile_groups_all_key_rows_and_block_v_value_columns():
+    rng = np.random.default_rng(3)
+    S = rng.standard_normal((1, 8, 8))
+    base = e4m3.tile_qdq(S, 4)
+    # scaling the second [K, 4] tile by a power of two scales its QDQ exactly
+    # and leaves the first tile alone; a tile spanning the wrong axis fails this
+    S2 = S.copy()
+    S2[:, :, 4:] *= 1024.0
+    Q2 = e4m3.tile_qdq(S2, 4)
+    assert np.array_equal(Q2[:, :, :4], base[:, :, :4])
+    assert np.array_equal(Q2[:, :, 4:], base[:, :, 4:] * 1024.0)
+    # one large element in a row of the first tile changes the whole first tile's
+    # resolution (amax is over all K rows) but nothing in the second tile
+    S3 = S.copy()
+    S3[0, 5, 1] = 100.0
+    Q3 = e4m3.tile_qdq(S3, 4)
+    assert np.array_equal(Q3[:, :, 4:], base[:, :, 4:])
+    assert not np.array_equal(Q3[0, 0, :4], base[0, 0, :4])
