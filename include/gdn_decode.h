@@ -1,0 +1,209 @@
+/*
+ * gdn_decode.h -- C ABI of the gated delta-rule recurrent decode library
+ * (libgdn_decode.so, HIP kernels for gfx950 / MI355X).
+ *
+ * One call advances, for every sequence b and value head h, an fp32 state
+ * S[K, V] over the sequence's suffix tokens and writes one output row per
+ * token.  Per token (decay first, then the delta write, then the readout of
+ * the updated state -- Circuit.LLM.Mixer, "Delta rule" and "Gated memory"):
+ *
+ *   q_hat = l2norm(q) * scale        k_hat = l2norm(k)
+ *   g     = -exp(A_log) * softplus(a + dt_bias)     (GDN: one per head;
+ *                                                    KDA: one per key channel)
+ *   beta  = sigmoid(b)  or  b                       (beta_mode)
+ *   S    <- exp(g) * S          (KDA: row c of S scaled by exp(g_c))
+ *   u     = beta * (v - k_hat^T S)
+ *   S    <- S + k_hat u^T
+ *   o     = q_hat^T S
+ *
+ * with l2norm(x) = x / sqrt(sum(x^2) + 1e-6), softplus(x) =
+ * max(x,0) + log1p(exp(-|x|)), value head h reading key head h / (HV/HK),
+ * and, when enabled, an fp8 e4m3 quantise/dequantise of S after every token
+ * with one amax/448 scale per [K, block_v] tile (OCP E4M3, nearest-even,
+ * saturating).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named as device pointers must be device memory (or memory the
+ *   device can access) of the HIP runtime loaded in the process; all arrays
+ *   are dense and row-major ("contiguous") in the shapes given.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *   stream).  The library allocates nothing, keeps no state between calls,
+ *   and is reentrant; the caller owns every buffer.
+ * - `state_pool` is read and written in place; only the rows named below
+ *   as written are modified, byte for byte nothing else.  `out` is fully
+ *   overwritten for every token of a non-empty suffix and must not alias an
+ *   input or the pool.  All other arrays are read only.
+ * - Return value: GDN_OK, or an error code from host-side checks made
+ *   before anything is launched (nothing is written then), or GDN_ERR_HIP
+ *   if the launch itself failed.  gdn_status_string() names the code and
+ *   gdn_last_error() gives the calling thread's last error message.
+ * - Not checked (undefined behaviour if violated; max.nn.state_space.kda_decode,
+ *   Raises, and flashinfer.gdn_paged.gated_delta_rule_decode_paged, slots,
+ *   leave these unchecked on the device too): index values inside the pool,
+ *   distinct state_indices, distinct write pages, a write page that another
+ *   sequence of the same call reads, non-decreasing cu_seqlens, and
+ *   last_page_len == 1 with fewer than two pages.
+ */
+#ifndef GDN_DECODE_H
+#define GDN_DECODE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  The mapping follows max.nn.state_space.kda_decode, Raises:
+ * a dtype grouping that binds no kernel, or ranks/extents that disagree,
+ * are reported on the host before any launch. */
+enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_INVALID = 1,      /* null required pointer, dimension <= 0, HV % HK != 0, bad enum */
+  GDN_ERR_SHAPE = 2,        /* extents disagree (e.g. T != B without cu_seqlens) */
+  GDN_ERR_UNSUPPORTED = 3,  /* valid request with no compiled kernel (head dims, block_v, gate_mode) */
+  GDN_ERR_HIP = 4           /* the HIP launch reported an error */
+};
+
+/* Element types of the I/O tensors and of the page table. */
+enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1, GDN_I32 = 2, GDN_I64 = 3 };
+
+/* Pool axis order of one (row, head) state (max.nn.state_space.kda_decode,
+ * state_layout): K_FIRST stores [K][V] (V contiguous), V_FIRST stores
+ * [V][K] (K contiguous; the [num_pages, HV, V, K] pool of
+ * flashinfer.gdn_paged.gated_delta_rule_decode_paged). */
+enum gdn_layout { GDN_K_FIRST = 0, GDN_V_FIRST = 1 };
+
+/* max.nn.state_space.kda_decode, beta_mode: apply the sigmoid or not. */
+enum gdn_beta_mode { GDN_BETA_LOGITS = 0, GDN_BETA_PROBABILITY = 1 };
+
+/* max.nn.state_space.kda_decode, gate_mode.  GDN_GATE_SAFE depends on a
+ * lower-bound constant the page does not give and returns
+ * GDN_ERR_UNSUPPORTED. */
+enum gdn_gate_mode { GDN_GATE_ORIGINAL = 0, GDN_GATE_SAFE = 1 };
+
+/* State quantise/dequantise after every token (modelopt ...
+ * linear_attention.config, LinearAttentionConfig: one dynamic scale per
+ * [Dk, block_v] tile; ... linear_attention.decode: state_format
+ * 'fp8_e4m3'). */
+enum gdn_qdq { GDN_QDQ_NONE = 0, GDN_QDQ_FP8_E4M3_TILE = 1 };
+
+/* modelopt ... linear_attention.config, LinearAttentionDecodeConfig,
+ * readout: 'working' reads o from the updated state before its rounding,
+ * 'stored' from the rounded state. */
+enum gdn_readout { GDN_READOUT_WORKING = 0, GDN_READOUT_STORED = 1 };
+
+/* Options of a call.  Fill with gdn_options_init() and change fields. */
+typedef struct gdn_options {
+  float scale;              /* query scale; 0 means 1/sqrt(K)                     (default 0) */
+  int32_t use_qk_l2norm;    /* 1: L2-normalise q and k inside the call              (default 1) */
+  int32_t io_dtype;         /* q, k, v, a, b, raw_gate, beta_logits: F32 or BF16  (default BF16) */
+  int32_t out_dtype;        /* out: F32 or BF16                                    (default BF16) */
+  int32_t state_layout;     /* gdn_layout                                   (default K_FIRST) */
+  int32_t beta_mode;        /* gdn_beta_mode                                 (default LOGITS) */
+  int32_t gate_mode;        /* gdn_gate_mode                               (default ORIGINAL) */
+  int32_t index_dtype;      /* paged table: I32 or I64                           (default I32) */
+  int32_t qdq;              /* gdn_qdq                                           (default NONE) */
+  int32_t block_v;          /* QDQ tile width over V; must divide V           (default 64) */
+  int32_t quantize_initial; /* 1: also round the state read before the first token (default 0) */
+  int32_t readout;          /* gdn_readout                                     (default WORKING) */
+} gdn_options;
+
+/* Fill `opt` with the defaults listed above.  `opt` must not be NULL. */
+void gdn_options_init(gdn_options* opt);
+
+/*
+ * gdn_decode_pooled -- GDN decode (one gate per value head) on a slot pool,
+ * varlen suffixes.  flashinfer.gdn_paged.gated_delta_rule_decode_paged,
+ * parameters q..b and scale/use_qk_l2norm (inherited from the pooled
+ * decode), generalised to several tokens per sequence the way
+ * max.nn.state_space.kda_decode, cu_seqlens, does.
+ *
+ *   q, k          [T, HK, K]   io_dtype   device
+ *   v             [T, HV, V]   io_dtype   device
+ *   a, b          [T, HV]      io_dtype   device
+ *   A_log, dt_bias[HV]         f32        device
+ *   cu_seqlens    [B+1]        i32        device; exclusive prefix offsets of
+ *                                         the suffixes in the token axis, or
+ *                                         NULL for exactly one token per
+ *                                         sequence (then T must equal B)
+ *   state_indices [B]          i32        device; pool slot of each sequence
+ *   state_pool    [num_slots, HV, K, V] (K_FIRST) or [num_slots, HV, V, K]
+ *                 (V_FIRST)    f32        device; slot state_indices[b] is
+ *                                         read and written in place if the
+ *                                         suffix of b is non-empty; an empty
+ *                                         suffix reads and writes nothing
+ *   out           [T, HV, V]   out_dtype  device
+ */
+int gdn_decode_pooled(const void* q, const void* k, const void* v, const void* a, const void* b,
+                      const float* A_log, const float* dt_bias, const int32_t* cu_seqlens,
+                      const int32_t* state_indices, float* state_pool, void* out, int32_t B,
+                      int32_t T, int32_t HK, int32_t HV, int32_t K, int32_t V, int64_t num_slots,
+                      const gdn_options* opt, void* stream);
+
+/*
+ * gdn_decode_paged -- single-token GDN decode on a CSR-paged pool
+ * (flashinfer.gdn_paged.gated_delta_rule_decode_paged).  Token b is the
+ * decoded token of sequence b and sits at position last_page_len[b] of the
+ * sequence's last page, page_indices[page_indptr[b+1]-1].  If
+ * last_page_len[b] == 1 the token opens that page: the state is read from
+ * the previous page page_indices[page_indptr[b+1]-2] and written to the
+ * last page, and the previous page (which may be shared) is left
+ * untouched.  Otherwise the last page is read and updated in place.
+ *
+ *   q, k          [B, HK, K]   io_dtype   device
+ *   v             [B, HV, V]   io_dtype   device
+ *   a, b          [B, HV]      io_dtype   device
+ *   A_log, dt_bias[HV]         f32        device
+ *   page_indices  [nnz]        index_dtype device
+ *   page_indptr   [B+1]        index_dtype device
+ *   last_page_len [B]          index_dtype device, values in [1, page_size]
+ *   state_pool    [num_pages, HV, V, K] (V_FIRST) or [num_pages, HV, K, V]
+ *                 (K_FIRST)    f32        device, updated in place
+ *   out           [B, HV, V]   out_dtype  device (the [B, 1, HV, V] output)
+ */
+int gdn_decode_paged(const void* q, const void* k, const void* v, const void* a, const void* b,
+                     const float* A_log, const float* dt_bias, const void* page_indices,
+                     const void* page_indptr, const void* last_page_len, float* state_pool,
+                     void* out, int32_t B, int32_t HK, int32_t HV, int32_t K, int32_t V,
+                     int64_t num_pages, int64_t nnz, const gdn_options* opt, void* stream);
+
+/*
+ * kda_decode_pooled -- KDA decode (one gate per value head and key channel)
+ * on a slot pool, varlen suffixes (max.nn.state_space.kda_decode).
+ *
+ *   q, k          [T, HK, K]   io_dtype   device
+ *   v             [T, HV, V]   io_dtype   device
+ *   raw_gate      [T, HV, K]   io_dtype   device; gate pre-activation before dt_bias
+ *   beta_logits   [T, HV]      io_dtype   device
+ *   a_log         [HV]         f32        device
+ *   dt_bias       [HV, K]      f32        device
+ *   cu_seqlens    [B+1]        i32        device, required
+ *   state_indices [B]          i32        device
+ *   state_pool    as for gdn_decode_pooled
+ *   out           [T, HV, V]   out_dtype  device
+ */
+int kda_decode_pooled(const void* q, const void* k, const void* v, const void* raw_gate,
+                      const void* beta_logits, const float* a_log, const float* dt_bias,
+                      const int32_t* cu_seqlens, const int32_t* state_indices, float* state_pool,
+                      void* out, int32_t B, int32_t T, int32_t HK, int32_t HV, int32_t K, int32_t V,
+                      int64_t num_slots, const gdn_options* opt, void* stream);
+
+/* Static name of a status code ("GDN_OK", ...); "unknown status" otherwise. */
+const char* gdn_status_string(int status);
+
+/* Message of the calling thread's last failed call ("" if none).  The
+ * pointer stays valid until the thread's next call into the library. */
+const char* gdn_last_error(void);
+
+/* Head dims with a compiled kernel: writes up to `cap` (K, VB) pairs as
+ * 2*n ints into `pairs` (NULL allowed) and returns the number of pairs
+ * available.  A key head dim K is supported with any value head dim V that
+ * is a multiple of its VB; fp8 tile QDQ needs block_v == VB. */
+int gdn_supported_head_dims(int32_t* pairs, int cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_DECODE_H */

@@ -22,7 +22,8 @@ h // (HV / HK), i.e. consecutive value heads share a key head.
 rows the call reads).  Each function returns ``(out, written)``:
 ``out`` [T, HV, V] float64 (rows of sequences not in ``seqs`` are NaN) and
 ``written`` a dict {row id: new tile in pool layout, float64}.  Rows not in
-``written`` are not modified by the call.
+``written`` are not modified by the call.  ``trace`` (a dict, optional)
+receives per sequence the per-token record of ``recurrence.run_suffix``.
 """
 import numpy as np
 
@@ -47,20 +48,22 @@ def _key_head_map(HK, HV):
 
 
 def _run_one(tile, state_layout, q, k, v, alpha, beta, hk_of_h, scale, use_qk_l2norm,
-             qdq_fn, quantize_initial, readout):
+             qdq_fn, quantize_initial, readout, trace=None):
     """Run one sequence's suffix.  q, k [T, HK, K]; v [T, HV, V]; alpha [T, HV] or [T, HV, K]."""
     S0 = paging.to_logical(tile, state_layout)
     q_hat, k_hat = act.prepare_qk(q, k, scale=scale, use_qk_l2norm=use_qk_l2norm)
     q_hat = q_hat[:, hk_of_h, :]
     k_hat = k_hat[:, hk_of_h, :]
     o, S = run_suffix(S0, q_hat, k_hat, np.asarray(v, dtype=np.float64), alpha, beta,
-                      state_qdq=qdq_fn, quantize_initial=quantize_initial, readout_mode=readout)
+                      state_qdq=qdq_fn, quantize_initial=quantize_initial, readout_mode=readout,
+                      trace=trace)
     return o, paging.from_logical(S, state_layout)
 
 
 def gdn_decode_pooled(q, k, v, a, b, A_log, dt_bias, cu_seqlens, state_indices, pool, *,
                       scale=None, use_qk_l2norm=True, beta_mode="logits", state_layout="K_FIRST",
-                      qdq=None, block_v=64, quantize_initial=False, readout="working", seqs=None):
+                      qdq=None, block_v=64, quantize_initial=False, readout="working", seqs=None,
+                      trace=None):
     """GDN (scalar gate per value head) decode on a slot pool, varlen suffixes.
 
     q, k [T, HK, K]; v [T, HV, V]; a, b [T, HV]; A_log, dt_bias [HV];
@@ -82,7 +85,8 @@ def gdn_decode_pooled(q, k, v, a, b, A_log, dt_bias, cu_seqlens, state_indices, 
         alpha = np.exp(act.gdn_log_gate(A_log, a[t0:t1], dt_bias))
         beta = act.beta_from(b[t0:t1], beta_mode)
         o, tile = _run_one(pool[r], state_layout, q[t0:t1], k[t0:t1], v[t0:t1], alpha, beta,
-                           hk_of_h, scale, use_qk_l2norm, qdq_fn, quantize_initial, readout)
+                           hk_of_h, scale, use_qk_l2norm, qdq_fn, quantize_initial, readout,
+                           None if trace is None else trace.setdefault(bi, []))
         out[t0:t1] = o
         written[w] = tile
     return out, written
@@ -91,7 +95,7 @@ def gdn_decode_pooled(q, k, v, a, b, A_log, dt_bias, cu_seqlens, state_indices, 
 def kda_decode_pooled(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_indices,
                       pool, *, scale=None, use_qk_l2norm=True, beta_mode="logits",
                       state_layout="K_FIRST", qdq=None, block_v=64, quantize_initial=False,
-                      readout="working", seqs=None):
+                      readout="working", seqs=None, trace=None):
     """KDA (per-key-channel gate) decode on a slot pool, varlen suffixes.
 
     q, k [T, HK, K]; v [T, HV, V]; raw_gate [T, HV, K]; beta_logits [T, HV];
@@ -112,7 +116,8 @@ def kda_decode_pooled(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens
         alpha = np.exp(act.kda_log_gate(a_log, raw_gate[t0:t1], dt_bias))
         beta = act.beta_from(beta_logits[t0:t1], beta_mode)
         o, tile = _run_one(pool[r], state_layout, q[t0:t1], k[t0:t1], v[t0:t1], alpha, beta,
-                           hk_of_h, scale, use_qk_l2norm, qdq_fn, quantize_initial, readout)
+                           hk_of_h, scale, use_qk_l2norm, qdq_fn, quantize_initial, readout,
+                           None if trace is None else trace.setdefault(bi, []))
         out[t0:t1] = o
         written[w] = tile
     return out, written
@@ -121,7 +126,7 @@ def kda_decode_pooled(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens
 def gdn_decode_paged(q, k, v, a, b, A_log, dt_bias, page_indices, page_indptr, last_page_len,
                      pool, *, scale=None, use_qk_l2norm=True, beta_mode="logits",
                      state_layout="V_FIRST", qdq=None, block_v=64, quantize_initial=False,
-                     readout="working", seqs=None):
+                     readout="working", seqs=None, trace=None):
     """Single-token GDN decode on a CSR-paged pool (token b belongs to sequence b).
 
     q, k [B, HK, K]; v [B, HV, V]; a, b [B, HV]; returns out [B, HV, V]
@@ -139,7 +144,8 @@ def gdn_decode_paged(q, k, v, a, b, A_log, dt_bias, page_indices, page_indptr, l
         alpha = np.exp(act.gdn_log_gate(A_log, a[sl], dt_bias))
         beta = act.beta_from(b[sl], beta_mode)
         o, tile = _run_one(pool[r], state_layout, q[sl], k[sl], v[sl], alpha, beta, hk_of_h,
-                           scale, use_qk_l2norm, qdq_fn, quantize_initial, readout)
+                           scale, use_qk_l2norm, qdq_fn, quantize_initial, readout,
+                           None if trace is None else trace.setdefault(bi, []))
         out[bi] = o[0]
         written[w] = tile
     return out, written

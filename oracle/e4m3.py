@@ -18,6 +18,11 @@ Readings (listed in DESIGN.md):
   top of the grid;
 * round to nearest, ties to even mantissa, saturating at +-448; subnormals
   kept; a tile whose amax is 0 is left as it is; NaN propagates.
+* the pages do not fix the precision in which the code of each element is
+  chosen; it is taken in float32, as the GPU kernel takes it:
+  y = f32(f32(x) * f32(448 / amax)), code = E4M3(y), value =
+  f32(code * f32(amax / 448)).  ``precision='float64'`` gives the same
+  rule in float64 throughout (x / s with s = amax / 448).
 
 Pins (tests/test_oracle_e4m3.py): the 256-code table built from the bit
 fields is checked against PyTorch's CPU ``float8_e4m3fn`` decode; every
@@ -69,11 +74,13 @@ def e4m3_round(y):
     return np.copysign(r, y)
 
 
-def tile_qdq(S, block_v=64):
+def tile_qdq(S, block_v=64, precision="float32"):
     """Quantise/dequantise S [H, K, V] with one scale per [K, block_v] tile of each head.
 
     For each tile: amax = max |S|; if amax == 0 the tile is unchanged;
-    otherwise s = amax / 448 and each x becomes s * e4m3_round(x / s).
+    otherwise each element x becomes s * E4M3(x / s) with s = amax / 448,
+    the division and the product evaluated in ``precision`` (see the module
+    docstring for the float32 reading).
     """
     S = np.asarray(S, dtype=np.float64)
     H, K, V = S.shape
@@ -81,13 +88,27 @@ def tile_qdq(S, block_v=64):
         raise ValueError("block_v must divide the value head dim")
     out = S.copy()
     for j0 in range(0, V, block_v):
-        tile = S[:, :, j0:j0 + block_v]
-        amax = np.max(np.abs(tile), axis=(1, 2))
         for h in range(H):
-            if amax[h] == 0.0:
-                continue
-            s = amax[h] / E4M3_MAX
-            out[h, :, j0:j0 + block_v] = s * e4m3_round(tile[h] / s)
+            tile = S[h, :, j0:j0 + block_v]
+            if precision == "float64":
+                amax = np.max(np.abs(tile))
+                if amax == 0.0:
+                    continue
+                s = amax / E4M3_MAX
+                out[h, :, j0:j0 + block_v] = s * e4m3_round(tile / s)
+            elif precision == "float32":
+                x = tile.astype(np.float32)
+                amax = np.max(np.abs(x))
+                if amax == 0.0:
+                    out[h, :, j0:j0 + block_v] = x
+                    continue
+                inv = np.float32(np.float32(E4M3_MAX) / amax)
+                sc = np.float32(amax / np.float32(E4M3_MAX))
+                y = (x * inv).astype(np.float32)
+                code = e4m3_round(y.astype(np.float64)).astype(np.float32)
+                out[h, :, j0:j0 + block_v] = (code * sc).astype(np.float32)
+            else:
+                raise ValueError(f"unknown precision {precision!r}")
     return out
 
 

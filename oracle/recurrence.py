@@ -74,12 +74,15 @@ def gated_delta_step(S, q_hat, k_hat, v, alpha, beta, state_qdq=None, readout_mo
 
 
 def run_suffix(S0, q_hat, k_hat, v, alpha, beta, state_qdq=None, quantize_initial=False,
-               readout_mode="working"):
+               readout_mode="working", trace=None):
     """Left fold of the step over the T tokens of one suffix (scanMixer shape).
 
     S0 [H, K, V]; q_hat/k_hat [T, H, K]; v [T, H, V]; alpha [T, H] or
     [T, H, K]; beta [T, H].  Returns (o [T, H, V], S_T).  With T = 0 the
     state is returned untouched and no initial quantisation happens.
+    If ``trace`` is a list, one dict per token is appended with the state
+    entering the token and the token's q_hat, k_hat, alpha, beta and the
+    state leaving it (instrumentation for tests; no effect on the result).
     """
     T = q_hat.shape[0]
     S = np.array(S0, dtype=np.float64, copy=True)
@@ -89,6 +92,9 @@ def run_suffix(S0, q_hat, k_hat, v, alpha, beta, state_qdq=None, quantize_initia
     if state_qdq is not None and quantize_initial:
         S = state_qdq(S)
     for t in range(T):
+        S_in = S
         outs[t], S = gated_delta_step(S, q_hat[t], k_hat[t], v[t], alpha[t], beta[t],
                                       state_qdq=state_qdq, readout_mode=readout_mode)
+        if trace is not None:
+            trace.append(dict(S_in=S_in, q_hat=q_hat[t], k_hat=k_hat[t], alpha=alpha[t], beta=beta[t], S_out=S))
     return outs, S

@@ -1,0 +1,16 @@
+"""MI355X-native gated delta-rule (GDN / KDA) recurrent-state decode.
+
+The compute lives in ``libgdn_decode.so`` (hand-written HIP kernels for
+gfx950 behind the C ABI of ``include/gdn_decode.h``); this package is its
+thin Python binding plus the seeded workload generators used by the tests
+and the bench.  PyTorch only provides device memory and streams.
+"""
+from ._binding import (  # noqa: F401
+    GdnError,
+    LIB_PATH,
+    gdn_decode_paged,
+    gdn_decode_pooled,
+    kda_decode_pooled,
+    load_library,
+    supported_head_dims,
+)

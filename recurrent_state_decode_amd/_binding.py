@@ -1,0 +1,278 @@
+"""ctypes binding of libgdn_decode.so (C ABI in include/gdn_decode.h).
+
+Argument marshalling only: shapes and dtypes are read off the tensors,
+``out`` is allocated when not given, and the call is enqueued on the
+current torch stream of the tensors' device.  Every step of the decode runs
+in the library's HIP kernels; there is no fallback.  If the library is not
+built, every call raises.
+"""
+import ctypes
+import os
+import threading
+
+import torch
+
+from . import build as _build
+
+LIB_PATH = _build.LIB
+
+GDN_OK, GDN_ERR_INVALID, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = range(5)
+GDN_F32, GDN_BF16, GDN_I32, GDN_I64 = range(4)
+_LAYOUT = {"K_FIRST": 0, "V_FIRST": 1}
+_BETA = {"logits": 0, "probability": 1}
+_GATE = {"original": 0, "safe": 1}
+_QDQ = {None: 0, "none": 0, "fp8_e4m3_tile": 1}
+_READOUT = {"working": 0, "stored": 1}
+_IO = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
+_IDX = {torch.int32: GDN_I32, torch.int64: GDN_I64}
+
+
+class GdnOptions(ctypes.Structure):
+    _fields_ = [
+        ("scale", ctypes.c_float),
+        ("use_qk_l2norm", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("state_layout", ctypes.c_int32),
+        ("beta_mode", ctypes.c_int32),
+        ("gate_mode", ctypes.c_int32),
+        ("index_dtype", ctypes.c_int32),
+        ("qdq", ctypes.c_int32),
+        ("block_v", ctypes.c_int32),
+        ("quantize_initial", ctypes.c_int32),
+        ("readout", ctypes.c_int32),
+    ]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status, name, message):
+        super().__init__(f"{name} ({status}): {message}")
+        self.status = status
+        self.name = name
+        self.message = message
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_OPT = ctypes.POINTER(GdnOptions)
+
+_SIGNATURES = {
+    "gdn_options_init": (None, [_OPT]),
+    "gdn_decode_pooled": (ctypes.c_int, [_P] * 11 + [_I32] * 6 + [_I64, _OPT, _P]),
+    "gdn_decode_paged": (ctypes.c_int, [_P] * 12 + [_I32] * 5 + [_I64, _I64, _OPT, _P]),
+    "kda_decode_pooled": (ctypes.c_int, [_P] * 11 + [_I32] * 6 + [_I64, _OPT, _P]),
+    "gdn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "gdn_last_error": (ctypes.c_char_p, []),
+    "gdn_supported_head_dims": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int32), ctypes.c_int]),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path=None):
+    """Load (once) and return the ctypes handle of libgdn_decode.so; raise if it is not built."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+                               "or `python recurrent_state_decode_amd/build.py`")
+        lib = ctypes.CDLL(p)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def supported_head_dims():
+    lib = load_library()
+    n = lib.gdn_supported_head_dims(None, 0)
+    buf = (ctypes.c_int32 * (2 * n))()
+    lib.gdn_supported_head_dims(buf, n)
+    return [(buf[2 * i], buf[2 * i + 1]) for i in range(n)]
+
+
+def _options(**kw):
+    lib = load_library()
+    o = GdnOptions()
+    lib.gdn_options_init(ctypes.byref(o))
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dev(name, t, device, dtypes=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+
+
+def _stream_handle(device, stream):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _raise(lib, status):
+    name = lib.gdn_status_string(status).decode()
+    raise GdnError(status, name, lib.gdn_last_error().decode())
+
+
+def _common_opts(io_dtype, out_dtype, scale, use_qk_l2norm, beta_mode, state_layout, qdq, block_v,
+                 quantize_initial, readout, gate_mode="original", index_dtype=GDN_I32):
+    return _options(scale=0.0 if scale is None else float(scale), use_qk_l2norm=int(bool(use_qk_l2norm)),
+                    io_dtype=_IO[io_dtype], out_dtype=_IO[out_dtype], state_layout=_LAYOUT[state_layout],
+                    beta_mode=_BETA[beta_mode], gate_mode=_GATE[gate_mode], index_dtype=index_dtype,
+                    qdq=_QDQ[qdq], block_v=int(block_v), quantize_initial=int(bool(quantize_initial)),
+                    readout=_READOUT[readout])
+
+
+def _pool_check(state_pool, HV, K, V, state_layout):
+    tail = (HV, K, V) if state_layout == "K_FIRST" else (HV, V, K)
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != tail:
+        raise ValueError(f"state_pool shape {tuple(state_pool.shape)} does not match [rows, {tail}] for {state_layout}")
+
+
+def gdn_decode_pooled(q, k, v, a, b, A_log, dt_bias, cu_seqlens, state_indices, state_pool, out=None, *,
+                      scale=None, use_qk_l2norm=True, beta_mode="logits", state_layout="K_FIRST",
+                      out_dtype=None, qdq=None, block_v=64, quantize_initial=False, readout="working",
+                      stream=None):
+    """GDN decode on a slot pool (see gdn_decode_pooled in include/gdn_decode.h). Returns ``out`` [T, HV, V]."""
+    lib = load_library()
+    T, HK, K = q.shape
+    HV, V = v.shape[1], v.shape[2]
+    B = state_indices.numel()
+    dev = q.device
+    io = q.dtype
+    out_dtype = out_dtype or io
+    for n, t in (("q", q), ("k", k), ("v", v), ("a", a), ("b", b)):
+        _check_dev(n, t, dev, (io,))
+    _check_dev("A_log", A_log, dev, (torch.float32,))
+    _check_dev("dt_bias", dt_bias, dev, (torch.float32,))
+    _check_dev("cu_seqlens", cu_seqlens, dev, (torch.int32,))
+    _check_dev("state_indices", state_indices, dev, (torch.int32,))
+    _check_dev("state_pool", state_pool, dev, (torch.float32,))
+    if k.shape != q.shape or v.shape[0] != T or a.shape != (T, HV) or b.shape != (T, HV):
+        raise ValueError("q/k/v/a/b shapes disagree")
+    if A_log.shape != (HV,) or dt_bias.shape != (HV,):
+        raise ValueError("A_log and dt_bias must be [HV]")
+    if cu_seqlens is not None and cu_seqlens.shape != (B + 1,):
+        raise ValueError("cu_seqlens must be [B+1]")
+    _pool_check(state_pool, HV, K, V, state_layout)
+    if out is None:
+        out = torch.empty((T, HV, V), dtype=out_dtype, device=dev)
+    _check_dev("out", out, dev, (out_dtype,))
+    if out.shape != (T, HV, V):
+        raise ValueError("out must be [T, HV, V]")
+    opt = _common_opts(io, out_dtype, scale, use_qk_l2norm, beta_mode, state_layout, qdq, block_v,
+                       quantize_initial, readout)
+    st = lib.gdn_decode_pooled(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+                               _ptr(cu_seqlens), _ptr(state_indices), _ptr(state_pool), _ptr(out),
+                               B, T, HK, HV, K, V, state_pool.shape[0], ctypes.byref(opt),
+                               _stream_handle(dev, stream))
+    if st != GDN_OK:
+        _raise(lib, st)
+    return out
+
+
+def gdn_decode_paged(q, k, v, a, b, A_log, dt_bias, page_indices, page_indptr, last_page_len, state_pool,
+                     out=None, *, scale=None, use_qk_l2norm=True, beta_mode="logits", state_layout="V_FIRST",
+                     out_dtype=None, qdq=None, block_v=64, quantize_initial=False, readout="working",
+                     stream=None):
+    """Single-token GDN decode on a CSR-paged pool (see gdn_decode_paged). Returns ``out`` [B, HV, V]."""
+    lib = load_library()
+    B, HK, K = q.shape
+    HV, V = v.shape[1], v.shape[2]
+    dev = q.device
+    io = q.dtype
+    out_dtype = out_dtype or io
+    for n, t in (("q", q), ("k", k), ("v", v), ("a", a), ("b", b)):
+        _check_dev(n, t, dev, (io,))
+    _check_dev("A_log", A_log, dev, (torch.float32,))
+    _check_dev("dt_bias", dt_bias, dev, (torch.float32,))
+    idt = page_indices.dtype
+    for n, t in (("page_indices", page_indices), ("page_indptr", page_indptr), ("last_page_len", last_page_len)):
+        _check_dev(n, t, dev, (idt,))
+    if idt not in _IDX:
+        raise TypeError("page table must be int32 or int64")
+    _check_dev("state_pool", state_pool, dev, (torch.float32,))
+    if k.shape != q.shape or v.shape[0] != B or a.shape != (B, HV) or b.shape != (B, HV):
+        raise ValueError("q/k/v/a/b shapes disagree")
+    if page_indptr.shape != (B + 1,) or last_page_len.shape != (B,):
+        raise ValueError("page_indptr must be [B+1] and last_page_len [B]")
+    _pool_check(state_pool, HV, K, V, state_layout)
+    if out is None:
+        out = torch.empty((B, HV, V), dtype=out_dtype, device=dev)
+    _check_dev("out", out, dev, (out_dtype,))
+    if out.numel() != B * HV * V:
+        raise ValueError("out must hold [B, HV, V]")
+    opt = _common_opts(io, out_dtype, scale, use_qk_l2norm, beta_mode, state_layout, qdq, block_v,
+                       quantize_initial, readout, index_dtype=_IDX[idt])
+    st = lib.gdn_decode_paged(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+                              _ptr(page_indices), _ptr(page_indptr), _ptr(last_page_len), _ptr(state_pool),
+                              _ptr(out), B, HK, HV, K, V, state_pool.shape[0], page_indices.numel(),
+                              ctypes.byref(opt), _stream_handle(dev, stream))
+    if st != GDN_OK:
+        _raise(lib, st)
+    return out
+
+
+def kda_decode_pooled(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_indices, state_pool,
+                      out=None, *, scale=None, use_qk_l2norm=True, beta_mode="logits", state_layout="K_FIRST",
+                      gate_mode="original", out_dtype=None, qdq=None, block_v=64, quantize_initial=False,
+                      readout="working", stream=None):
+    """KDA decode on a slot pool (see kda_decode_pooled). Returns ``out`` [T, HV, V]."""
+    lib = load_library()
+    T, HK, K = q.shape
+    HV, V = v.shape[1], v.shape[2]
+    B = state_indices.numel()
+    dev = q.device
+    io = q.dtype
+    out_dtype = out_dtype or io
+    for n, t in (("q", q), ("k", k), ("v", v), ("raw_gate", raw_gate), ("beta_logits", beta_logits)):
+        _check_dev(n, t, dev, (io,))
+    _check_dev("a_log", a_log, dev, (torch.float32,))
+    _check_dev("dt_bias", dt_bias, dev, (torch.float32,))
+    _check_dev("cu_seqlens", cu_seqlens, dev, (torch.int32,))
+    _check_dev("state_indices", state_indices, dev, (torch.int32,))
+    _check_dev("state_pool", state_pool, dev, (torch.float32,))
+    if cu_seqlens is None:
+        raise ValueError("cu_seqlens is required for KDA decode")
+    if k.shape != q.shape or v.shape[0] != T or raw_gate.shape != (T, HV, K) or beta_logits.shape != (T, HV):
+        raise ValueError("q/k/v/raw_gate/beta_logits shapes disagree")
+    if a_log.shape != (HV,) or dt_bias.shape != (HV, K):
+        raise ValueError("a_log must be [HV] and dt_bias [HV, K]")
+    if cu_seqlens.shape != (B + 1,):
+        raise ValueError("cu_seqlens must be [B+1]")
+    _pool_check(state_pool, HV, K, V, state_layout)
+    if out is None:
+        out = torch.empty((T, HV, V), dtype=out_dtype, device=dev)
+    _check_dev("out", out, dev, (out_dtype,))
+    if out.shape != (T, HV, V):
+        raise ValueError("out must be [T, HV, V]")
+    opt = _common_opts(io, out_dtype, scale, use_qk_l2norm, beta_mode, state_layout, qdq, block_v,
+                       quantize_initial, readout, gate_mode=gate_mode)
+    st = lib.kda_decode_pooled(_ptr(q), _ptr(k), _ptr(v), _ptr(raw_gate), _ptr(beta_logits), _ptr(a_log),
+                               _ptr(dt_bias), _ptr(cu_seqlens), _ptr(state_indices), _ptr(state_pool), _ptr(out),
+                               B, T, HK, HV, K, V, state_pool.shape[0], ctypes.byref(opt),
+                               _stream_handle(dev, stream))
+    if st != GDN_OK:
+        _raise(lib, st)
+    return out

@@ -1,0 +1,257 @@
+// Host side of libgdn_decode: argument checks, kernel selection and launch
+// for the C ABI declared in include/gdn_decode.h.
+//
+// Error convention (max.nn.state_space.kda_decode, Raises): a request whose
+// types or extents bind no kernel is refused on the host before anything is
+// launched; device-side index ranges are not checked.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "gdn_decode.h"
+#include "decode_kernel.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+enum class Kind { GdnPooled, GdnPaged, KdaPooled };
+
+struct HeadCfg {
+  int K, VB;
+};
+// Key head dims with compiled kernels and the V-block each uses: V may be
+// any multiple of VB (one workgroup per V-block).
+constexpr HeadCfg kHeads[] = {{16, 16}, {128, 64}};
+
+template <int K, int VB, int NT, bool VF, bool KDA, bool QDQ, bool PAGED>
+hipError_t launch_one(const gdn::Params& p, int64_t units, hipStream_t stream) {
+  hipLaunchKernelGGL((gdn::decode_kernel<K, VB, NT, VF, KDA, QDQ, PAGED>), dim3(static_cast<uint32_t>(units)),
+                     dim3(NT), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int K, int VB, int NT, bool KDA, bool PAGED>
+hipError_t launch_layout_qdq(const gdn::Params& p, int64_t units, bool vfirst, bool qdq, hipStream_t s) {
+  if (vfirst) {
+    return qdq ? launch_one<K, VB, NT, true, KDA, true, PAGED>(p, units, s)
+               : launch_one<K, VB, NT, true, KDA, false, PAGED>(p, units, s);
+  }
+  return qdq ? launch_one<K, VB, NT, false, KDA, true, PAGED>(p, units, s)
+             : launch_one<K, VB, NT, false, KDA, false, PAGED>(p, units, s);
+}
+
+template <int K, int VB, int NT>
+hipError_t launch_kind(Kind kind, const gdn::Params& p, int64_t units, bool vfirst, bool qdq, hipStream_t s) {
+  switch (kind) {
+    case Kind::GdnPooled: return launch_layout_qdq<K, VB, NT, false, false>(p, units, vfirst, qdq, s);
+    case Kind::GdnPaged: return launch_layout_qdq<K, VB, NT, false, true>(p, units, vfirst, qdq, s);
+    case Kind::KdaPooled: return launch_layout_qdq<K, VB, NT, true, false>(p, units, vfirst, qdq, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+int vblock_for(int K) {
+  for (const auto& h : kHeads)
+    if (h.K == K) return h.VB;
+  return 0;
+}
+
+bool head_supported(int K, int V) {
+  const int vb = vblock_for(K);
+  return vb > 0 && V % vb == 0;
+}
+
+int check_options(const gdn_options* o, int K, int V, Kind kind) {
+  if (!o) return fail(GDN_ERR_INVALID, "options pointer is NULL");
+  if (o->io_dtype != GDN_F32 && o->io_dtype != GDN_BF16)
+    return fail(GDN_ERR_INVALID, "io_dtype must be GDN_F32 or GDN_BF16 (got %d)", o->io_dtype);
+  if (o->out_dtype != GDN_F32 && o->out_dtype != GDN_BF16)
+    return fail(GDN_ERR_INVALID, "out_dtype must be GDN_F32 or GDN_BF16 (got %d)", o->out_dtype);
+  if (o->state_layout != GDN_K_FIRST && o->state_layout != GDN_V_FIRST)
+    return fail(GDN_ERR_INVALID, "state_layout must be GDN_K_FIRST or GDN_V_FIRST (got %d)", o->state_layout);
+  if (o->beta_mode != GDN_BETA_LOGITS && o->beta_mode != GDN_BETA_PROBABILITY)
+    return fail(GDN_ERR_INVALID, "beta_mode must be LOGITS or PROBABILITY (got %d)", o->beta_mode);
+  if (o->gate_mode != GDN_GATE_ORIGINAL && o->gate_mode != GDN_GATE_SAFE)
+    return fail(GDN_ERR_INVALID, "gate_mode must be ORIGINAL or SAFE (got %d)", o->gate_mode);
+  if (o->gate_mode == GDN_GATE_SAFE)
+    return fail(GDN_ERR_UNSUPPORTED, "gate_mode SAFE needs a gate lower bound this library does not define");
+  if (o->qdq != GDN_QDQ_NONE && o->qdq != GDN_QDQ_FP8_E4M3_TILE)
+    return fail(GDN_ERR_INVALID, "qdq must be NONE or FP8_E4M3_TILE (got %d)", o->qdq);
+  if (o->readout != GDN_READOUT_WORKING && o->readout != GDN_READOUT_STORED)
+    return fail(GDN_ERR_INVALID, "readout must be WORKING or STORED (got %d)", o->readout);
+  if (kind == Kind::GdnPaged && o->index_dtype != GDN_I32 && o->index_dtype != GDN_I64)
+    return fail(GDN_ERR_INVALID, "index_dtype must be GDN_I32 or GDN_I64 (got %d)", o->index_dtype);
+  if (!(o->scale >= 0.0f) || std::isinf(o->scale))
+    return fail(GDN_ERR_INVALID, "scale must be finite and >= 0 (0 selects 1/sqrt(K))");
+  if (o->qdq == GDN_QDQ_FP8_E4M3_TILE) {
+    if (o->block_v <= 0 || V % o->block_v != 0)
+      return fail(GDN_ERR_INVALID, "block_v=%d must be positive and divide V=%d", o->block_v, V);
+    if (o->block_v != vblock_for(K))
+      return fail(GDN_ERR_UNSUPPORTED, "fp8 tile QDQ is compiled for block_v=%d at K=%d (got %d)", vblock_for(K), K,
+                  o->block_v);
+  }
+  return GDN_OK;
+}
+
+int check_dims(int32_t B, int32_t HK, int32_t HV, int32_t K, int32_t V) {
+  if (B <= 0 || HK <= 0 || HV <= 0 || K <= 0 || V <= 0)
+    return fail(GDN_ERR_INVALID, "dimensions must be positive (B=%d HK=%d HV=%d K=%d V=%d)", B, HK, HV, K, V);
+  if (HV % HK != 0) return fail(GDN_ERR_INVALID, "HV=%d is not a multiple of HK=%d", HV, HK);
+  if (!head_supported(K, V)) return fail(GDN_ERR_UNSUPPORTED, "no kernel for head dims K=%d V=%d", K, V);
+  return GDN_OK;
+}
+
+void fill_common(gdn::Params& p, const gdn_options* o, int32_t B, int32_t HK, int32_t HV, int32_t K, int32_t V) {
+  p.B = B;
+  p.HK = HK;
+  p.HV = HV;
+  p.V = V;
+  p.nvb = V / vblock_for(K);
+  p.gqa = HV / HK;
+  p.scale = o->scale > 0.0f ? o->scale : 1.0f / std::sqrt(static_cast<float>(K));
+  p.l2norm = o->use_qk_l2norm ? 1 : 0;
+  p.io_bf16 = o->io_dtype == GDN_BF16;
+  p.out_bf16 = o->out_dtype == GDN_BF16;
+  p.beta_prob = o->beta_mode == GDN_BETA_PROBABILITY;
+  p.idx64 = o->index_dtype == GDN_I64;
+  p.quantize_initial = (o->qdq != GDN_QDQ_NONE && o->quantize_initial) ? 1 : 0;
+  p.readout_stored = (o->qdq != GDN_QDQ_NONE && o->readout == GDN_READOUT_STORED) ? 1 : 0;
+}
+
+int run(Kind kind, const gdn::Params& p, int K, const gdn_options* o, void* stream) {
+  const int64_t units = static_cast<int64_t>(p.B) * p.HV * p.nvb;
+  if (units > 0x7fffffffLL) return fail(GDN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)units);
+  const bool vfirst = o->state_layout == GDN_V_FIRST;
+  const bool qdq = o->qdq != GDN_QDQ_NONE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = hipErrorInvalidValue;
+  switch (K) {
+    case 16: err = launch_kind<16, 16, 64>(kind, p, units, vfirst, qdq, s); break;
+    case 128: err = launch_kind<128, 64, 256>(kind, p, units, vfirst, qdq, s); break;
+    default: return fail(GDN_ERR_UNSUPPORTED, "no kernel for K=%d", K);
+  }
+  if (err != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  g_last_error.clear();
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void gdn_options_init(gdn_options* o) {
+  if (!o) return;
+  o->scale = 0.0f;
+  o->use_qk_l2norm = 1;
+  o->io_dtype = GDN_BF16;
+  o->out_dtype = GDN_BF16;
+  o->state_layout = GDN_K_FIRST;
+  o->beta_mode = GDN_BETA_LOGITS;
+  o->gate_mode = GDN_GATE_ORIGINAL;
+  o->index_dtype = GDN_I32;
+  o->qdq = GDN_QDQ_NONE;
+  o->block_v = 64;
+  o->quantize_initial = 0;
+  o->readout = GDN_READOUT_WORKING;
+}
+
+int gdn_decode_pooled(const void* q, const void* k, const void* v, const void* a, const void* b,
+                      const float* A_log, const float* dt_bias, const int32_t* cu_seqlens,
+                      const int32_t* state_indices, float* state_pool, void* out, int32_t B, int32_t T,
+                      int32_t HK, int32_t HV, int32_t K, int32_t V, int64_t num_slots, const gdn_options* opt,
+                      void* stream) {
+  if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !state_indices || !state_pool || !out)
+    return fail(GDN_ERR_INVALID, "a required pointer is NULL");
+  if (int rc = check_dims(B, HK, HV, K, V)) return rc;
+  if (T < 0 || num_slots <= 0) return fail(GDN_ERR_INVALID, "T must be >= 0 and num_slots > 0");
+  if (!cu_seqlens && T != B)
+    return fail(GDN_ERR_SHAPE, "without cu_seqlens each sequence has one token, so T (%d) must equal B (%d)", T, B);
+  if (int rc = check_options(opt, K, V, Kind::GdnPooled)) return rc;
+  gdn::Params p{};
+  p.q = q; p.k = k; p.v = v; p.gate = a; p.beta = b;
+  p.a_log = A_log; p.dt_bias = dt_bias;
+  p.cu_seqlens = cu_seqlens; p.state_indices = state_indices;
+  p.pool = state_pool; p.out = out;
+  fill_common(p, opt, B, HK, HV, K, V);
+  if (T == 0) { g_last_error.clear(); return GDN_OK; }
+  return run(Kind::GdnPooled, p, K, opt, stream);
+}
+
+int gdn_decode_paged(const void* q, const void* k, const void* v, const void* a, const void* b,
+                     const float* A_log, const float* dt_bias, const void* page_indices, const void* page_indptr,
+                     const void* last_page_len, float* state_pool, void* out, int32_t B, int32_t HK, int32_t HV,
+                     int32_t K, int32_t V, int64_t num_pages, int64_t nnz, const gdn_options* opt, void* stream) {
+  if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !page_indices || !page_indptr || !last_page_len ||
+      !state_pool || !out)
+    return fail(GDN_ERR_INVALID, "a required pointer is NULL");
+  if (int rc = check_dims(B, HK, HV, K, V)) return rc;
+  if (num_pages <= 0 || nnz <= 0) return fail(GDN_ERR_INVALID, "num_pages and nnz must be positive");
+  if (nnz < B) return fail(GDN_ERR_SHAPE, "nnz (%lld) must be at least B (%d): every sequence owns a page",
+                           (long long)nnz, B);
+  if (int rc = check_options(opt, K, V, Kind::GdnPaged)) return rc;
+  gdn::Params p{};
+  p.q = q; p.k = k; p.v = v; p.gate = a; p.beta = b;
+  p.a_log = A_log; p.dt_bias = dt_bias;
+  p.page_indices = page_indices; p.page_indptr = page_indptr; p.last_page_len = last_page_len;
+  p.pool = state_pool; p.out = out;
+  fill_common(p, opt, B, HK, HV, K, V);
+  return run(Kind::GdnPaged, p, K, opt, stream);
+}
+
+int kda_decode_pooled(const void* q, const void* k, const void* v, const void* raw_gate, const void* beta_logits,
+                      const float* a_log, const float* dt_bias, const int32_t* cu_seqlens,
+                      const int32_t* state_indices, float* state_pool, void* out, int32_t B, int32_t T, int32_t HK,
+                      int32_t HV, int32_t K, int32_t V, int64_t num_slots, const gdn_options* opt, void* stream) {
+  if (!q || !k || !v || !raw_gate || !beta_logits || !a_log || !dt_bias || !cu_seqlens || !state_indices ||
+      !state_pool || !out)
+    return fail(GDN_ERR_INVALID, "a required pointer is NULL (cu_seqlens is required for KDA)");
+  if (int rc = check_dims(B, HK, HV, K, V)) return rc;
+  if (T < 0 || num_slots <= 0) return fail(GDN_ERR_INVALID, "T must be >= 0 and num_slots > 0");
+  if (int rc = check_options(opt, K, V, Kind::KdaPooled)) return rc;
+  gdn::Params p{};
+  p.q = q; p.k = k; p.v = v; p.gate = raw_gate; p.beta = beta_logits;
+  p.a_log = a_log; p.dt_bias = dt_bias;
+  p.cu_seqlens = cu_seqlens; p.state_indices = state_indices;
+  p.pool = state_pool; p.out = out;
+  fill_common(p, opt, B, HK, HV, K, V);
+  if (T == 0) { g_last_error.clear(); return GDN_OK; }
+  return run(Kind::KdaPooled, p, K, opt, stream);
+}
+
+const char* gdn_status_string(int status) {
+  switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_INVALID: return "GDN_ERR_INVALID";
+    case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP";
+  }
+  return "unknown status";
+}
+
+const char* gdn_last_error(void) { return g_last_error.c_str(); }
+
+int gdn_supported_head_dims(int32_t* pairs, int cap) {
+  const int n = static_cast<int>(sizeof(kHeads) / sizeof(kHeads[0]));
+  for (int i = 0; i < n && i < cap && pairs; ++i) {
+    pairs[2 * i] = kHeads[i].K;
+    pairs[2 * i + 1] = kHeads[i].VB;
+  }
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,303 @@
+"""Helpers shared by the GPU parity tests, the smoke run and the bench's oracle leg.
+
+They move seeded workloads to the device, call the HIP library through its
+Python binding, run the CPU oracle on the same values (pool rows read back
+from the device before the call), and compare the two under the tolerances
+below.
+
+Tolerances (readings of the stated contract, listed in the design doc):
+* index work is exact: the rows written are exactly the call's write rows,
+  every other pool byte is bit-identical to its value before the call;
+* fp32 states: |gpu - ref| <= 2e-3 * (|ref| + rms(ref over the row's tile));
+* outputs: the oracle value is rounded to the output dtype (nearest even)
+  first; bf16 outputs must then agree to one bf16 ulp at the larger
+  magnitude plus 1e-5 * rms(ref) (an absolute floor for values near 0),
+  fp32 outputs to 2e-3 * (|ref| + rms(ref)); and the relative L2 error of
+  all outputs against the unrounded oracle must be <= 2e-3 (plus, for bf16,
+  the 2^-9 relative rounding the output dtype itself adds);
+* fp8 tile QDQ ("one quantisation step"): every rounding of the state may
+  land one E4M3 step (the grid spacing at that magnitude, in its tile's
+  scale) away from the oracle's, and an earlier difference is carried by the
+  recurrence's linear update.  So the bound E_t on |gpu - oracle| of the
+  state after token t is E_t = A(E_{t-1}) + step_t, with
+  A(E) = alpha*E + beta |k_hat| (|k_hat|^T (alpha*E)) the elementwise bound
+  of the update's action on a state difference, E_0 = 0 (one step of S_0
+  with quantize_initial), plus 1e-5 relative for float32 arithmetic.  A
+  working-readout output is bounded by its bf16 ulp + |q_hat|^T(alpha E_{t-1})
+  + |q_hat . k_hat| beta |k_hat|^T (alpha E_{t-1}); a stored-readout output by
+  its ulp + |q_hat|^T E_t.  Since a bound of this kind would also accept a
+  systematically different rounding rule, the fraction of state elements
+  that differ at all must stay below 1e-3 (exact agreement of the rounding
+  itself is tested separately with a scale of exactly 1).
+"""
+import math
+
+import numpy as np
+import torch
+
+import recurrent_state_decode_amd as rsd
+from recurrent_state_decode_amd import workloads as wl
+from oracle import decode as odec
+from oracle import e4m3
+
+STATE_RTOL = 2e-3
+OUT_REL_L2 = 2e-3
+
+
+def device_inputs(w, device="cuda"):
+    return {k: (None if v is None else v.to(device)) for k, v in w.inputs.items() if k != "prefix_lengths"}
+
+
+def host64(t):
+    return None if t is None else t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def host_int(t):
+    return None if t is None else t.detach().to("cpu").to(torch.int64).numpy()
+
+
+def gpu_call(w, pool, d, out=None, **over):
+    """Run workload ``w`` on the device pool through the binding. Returns ``out``."""
+    o = dict(w.options)
+    o.pop("page_size", None)
+    o.update(over)
+    common = dict(state_layout=w.state_layout, out_dtype=w.out_dtype, **o)
+    if w.kind == "gdn_pooled":
+        return rsd.gdn_decode_pooled(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                                     d["cu_seqlens"], d["state_indices"], pool, out, **common)
+    if w.kind == "kda_pooled":
+        return rsd.kda_decode_pooled(d["q"], d["k"], d["v"], d["raw_gate"], d["beta_logits"], d["a_log"],
+                                     d["dt_bias"], d["cu_seqlens"], d["state_indices"], pool, out, **common)
+    if w.kind == "gdn_paged":
+        return rsd.gdn_decode_paged(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                                    d["page_indices"], d["page_indptr"], d["last_page_len"], pool, out, **common)
+    raise ValueError(w.kind)
+
+
+def rows_for(w, seqs=None):
+    """(read rows, write rows) of the sequences ``seqs`` (all if None), from the host tables."""
+    inp = w.inputs
+    seqs = range(w.B) if seqs is None else seqs
+    reads, writes = [], []
+    for b in seqs:
+        if w.kind == "gdn_paged":
+            ind, ptr, lpl = host_int(inp["page_indices"]), host_int(inp["page_indptr"]), host_int(inp["last_page_len"])
+            last = int(ind[ptr[b + 1] - 1])
+            reads.append(int(ind[ptr[b + 1] - 2]) if lpl[b] == 1 else last)
+            writes.append(last)
+        else:
+            cu = host_int(inp["cu_seqlens"])
+            if cu is not None and cu[b + 1] <= cu[b]:
+                continue
+            s = int(inp["state_indices"][b])
+            reads.append(s)
+            writes.append(s)
+    return reads, writes
+
+
+def oracle_call(w, pool_rows, seqs=None, trace=None, **over):
+    """Run the CPU oracle for workload ``w`` on ``pool_rows`` {row: float64 tile}."""
+    o = dict(w.options)
+    o.pop("page_size", None)
+    o.update(over)
+    o.pop("out_dtype", None)
+    inp = w.inputs
+    common = dict(state_layout=w.state_layout, seqs=seqs, trace=trace, **o)
+    if w.kind == "gdn_pooled":
+        return odec.gdn_decode_pooled(host64(inp["q"]), host64(inp["k"]), host64(inp["v"]), host64(inp["a"]),
+                                      host64(inp["b"]), host64(inp["A_log"]), host64(inp["dt_bias"]),
+                                      host_int(inp["cu_seqlens"]), host_int(inp["state_indices"]), pool_rows,
+                                      **common)
+    if w.kind == "kda_pooled":
+        return odec.kda_decode_pooled(host64(inp["q"]), host64(inp["k"]), host64(inp["v"]),
+                                      host64(inp["raw_gate"]), host64(inp["beta_logits"]), host64(inp["a_log"]),
+                                      host64(inp["dt_bias"]), host_int(inp["cu_seqlens"]),
+                                      host_int(inp["state_indices"]), pool_rows, **common)
+    if w.kind == "gdn_paged":
+        return odec.gdn_decode_paged(host64(inp["q"]), host64(inp["k"]), host64(inp["v"]), host64(inp["a"]),
+                                     host64(inp["b"]), host64(inp["A_log"]), host64(inp["dt_bias"]),
+                                     host_int(inp["page_indices"]), host_int(inp["page_indptr"]),
+                                     host_int(inp["last_page_len"]), pool_rows, **common)
+    raise ValueError(w.kind)
+
+
+def gather_rows(pool, rows):
+    rows = sorted(set(rows))
+    if not rows:
+        return {}
+    idx = torch.tensor(rows, dtype=torch.int64, device=pool.device)
+    vals = pool.index_select(0, idx).to("cpu").to(torch.float64).numpy()
+    return {r: vals[i] for i, r in enumerate(rows)}
+
+
+def bf16_ulp(x):
+    _, ex = np.frexp(np.abs(x))
+    return np.ldexp(1.0, np.maximum(ex - 8, -133))
+
+
+def token_rows(w, seqs):
+    """Token indices (output rows) that belong to sequences ``seqs``."""
+    if w.kind == "gdn_paged":
+        return np.array(sorted(seqs), dtype=np.int64)
+    cu = host_int(w.inputs["cu_seqlens"])
+    if cu is None:
+        return np.array(sorted(seqs), dtype=np.int64)
+    return np.concatenate([np.arange(cu[b], cu[b + 1]) for b in sorted(seqs)] + [np.zeros(0, np.int64)])
+
+
+def _step_at(S, bv, mag):
+    """E4M3 grid spacing at magnitude ``mag`` in the tile scale of S [H, K, V] (0 where the tile is 0)."""
+    s = np.repeat(e4m3.tile_scales(S, bv), bv, axis=1)[:, None, :]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.where(s > 0, s * e4m3.e4m3_spacing(mag / np.where(s > 0, s, 1)), 0.0)
+
+
+def qdq_bounds(w, trace, seqs):
+    """Propagated one-step-per-rounding bounds: ({token: output bound [H, V]}, {seq: final state bound [H, K, V]})."""
+    bv = w.options.get("block_v", 64)
+    stored = w.options.get("readout", "working") == "stored"
+    qinit = bool(w.options.get("quantize_initial", False))
+    out_b, state_b = {}, {}
+    cu = host_int(w.inputs.get("cu_seqlens"))
+    for b in seqs:
+        recs = trace.get(b, [])
+        if not recs:
+            continue
+        t0 = b if (w.kind == "gdn_paged" or cu is None) else int(cu[b])
+        S0 = recs[0]["S_in"]
+        E = _step_at(S0, bv, np.abs(S0) * 1.125) if qinit else np.zeros_like(S0)
+        for i, rec in enumerate(recs):
+            al = np.asarray(rec["alpha"], dtype=np.float64)
+            al = al[:, None, None] if al.ndim == 1 else al[:, :, None]
+            aE = al * E
+            kabs = np.abs(rec["k_hat"])
+            carried = aE + rec["beta"][:, None, None] * kabs[:, :, None] * np.einsum("hk,hkv->hv", kabs, aE)[:, None, :]
+            S = rec["S_out"]
+            E_new = carried + _step_at(S, bv, (np.abs(S) + carried) * 1.125) + 1e-5 * np.abs(S)
+            if stored:
+                bound = np.einsum("hk,hkv->hv", np.abs(rec["q_hat"]), E_new)
+            else:
+                qk = np.abs(np.sum(rec["q_hat"] * rec["k_hat"], axis=-1))
+                bound = (np.einsum("hk,hkv->hv", np.abs(rec["q_hat"]), aE)
+                         + (qk * rec["beta"])[:, None] * np.einsum("hk,hkv->hv", kabs, aE))
+            out_b[t0 + i] = bound
+            E = E_new
+        state_b[b] = E
+    return out_b, state_b
+
+
+class Report:
+    """Collects worst normalised errors for printing next to the pass/fail assertions."""
+
+    def __init__(self):
+        self.items = {}
+
+    def add(self, k, v):
+        self.items[k] = max(self.items.get(k, 0.0), float(v))
+
+    def __str__(self):
+        return " ".join(f"{k}={v:.3g}" for k, v in self.items.items())
+
+
+def compare_outputs(gpu_out, ref, w, rows, report, qdq_bound=None):
+    g = gpu_out.detach().to("cpu").to(torch.float64).numpy()[rows]
+    r = ref[rows]
+    assert np.all(np.isfinite(r)), "oracle produced non-finite outputs"
+    assert np.all(np.isfinite(g)), "GPU produced non-finite outputs"
+    r_round = torch.from_numpy(r).to(w.out_dtype).to(torch.float64).numpy()
+    rms = math.sqrt(float(np.mean(r * r))) if r.size else 0.0
+    diff = np.abs(g - r_round)
+    if w.out_dtype == torch.bfloat16:
+        tol = bf16_ulp(np.maximum(np.abs(g), np.abs(r_round))) + 1e-5 * rms
+        l2_tol = OUT_REL_L2 + 2.0 ** -9
+    else:
+        tol = STATE_RTOL * (np.abs(r) + rms)
+        l2_tol = OUT_REL_L2
+    if qdq_bound is not None:
+        tol = tol + qdq_bound
+    ratio = diff / tol
+    report.add("out_max_tol_ratio", ratio.max() if ratio.size else 0)
+    bad = np.argwhere(diff > tol)
+    assert bad.size == 0, f"{len(bad)} outputs out of tolerance; first {bad[:5].tolist()} gpu={g[tuple(bad[0])]} ref={r[tuple(bad[0])]}"
+    rel = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
+    report.add("out_rel_l2", rel)
+    assert rel <= l2_tol, f"output relative L2 error {rel} > {l2_tol}"
+
+
+def compare_states(gpu_rows, ref_rows, report, qdq_bound=None, layout="K_FIRST"):
+    """fp32 states within the relative tolerance, or (QDQ) within the propagated bounds {row: [H, K, V]}."""
+    assert set(gpu_rows) == set(ref_rows)
+    flips, total = 0, 0
+    for row, ref in ref_rows.items():
+        g = gpu_rows[row]
+        assert np.all(np.isfinite(g)), f"non-finite GPU state in row {row}"
+        if qdq_bound is not None:
+            logical = ref if layout == "K_FIRST" else np.swapaxes(ref, -1, -2)
+            gl = g if layout == "K_FIRST" else np.swapaxes(g, -1, -2)
+            tol = qdq_bound[row]
+            diff = np.abs(gl - logical)
+            flips += int(np.sum(diff > 1e-5 * np.abs(logical) + 1e-30))
+            total += diff.size
+            report.add("qdq_state_bound_ratio", (diff / np.maximum(tol, 1e-300)).max())
+        else:
+            rms = np.sqrt(np.mean(ref * ref, axis=(-1, -2), keepdims=True))
+            tol = STATE_RTOL * (np.abs(ref) + rms)
+            diff = np.abs(g - ref)
+            report.add("state_max_tol_ratio", (diff / tol).max())
+            report.add("state_max_rel", (diff / (np.abs(ref) + rms)).max())
+        bad = np.argwhere(diff > tol)
+        assert bad.size == 0, f"row {row}: {len(bad)} state elements out of tolerance, first {bad[:3].tolist()}"
+    if qdq_bound is not None and total:
+        report.add("qdq_state_diff_frac", flips / total)
+        assert flips / total < 1e-3, f"{flips} of {total} QDQ state elements differ: rounding rule mismatch?"
+
+
+def check_untouched(pool_before, pool_after, write_rows, chunk_rows=256):
+    """Every row not in ``write_rows`` is bit-identical to its value before the call."""
+    n = pool_before.shape[0]
+    written = torch.zeros(n, dtype=torch.bool, device=pool_before.device)
+    if write_rows:
+        written[torch.tensor(sorted(set(write_rows)), device=pool_before.device)] = True
+    changed = torch.zeros(n, dtype=torch.bool, device=pool_before.device)
+    for r0 in range(0, n, chunk_rows):
+        r1 = min(n, r0 + chunk_rows)
+        a = pool_before[r0:r1].view(torch.int32).flatten(1)
+        b = pool_after[r0:r1].view(torch.int32).flatten(1)
+        changed[r0:r1] = (a != b).any(dim=1)
+    stray = torch.nonzero(changed & ~written).flatten().tolist()
+    assert not stray, f"rows modified that the call does not write: {stray[:10]}"
+
+
+def run_and_check(w, seqs=None, report=None, pool=None, snapshot=True, check_all_written=True, **over):
+    """Full parity check of workload ``w``: GPU call vs oracle on the sequences ``seqs``."""
+    report = report if report is not None else Report()
+    d = device_inputs(w)
+    if pool is None:
+        pool = wl.make_pool(w, "cuda")
+    all_reads, all_writes = rows_for(w)
+    reads, writes = rows_for(w, seqs)
+    before = gather_rows(pool, reads)
+    snap = pool.clone() if snapshot else None
+    out = gpu_call(w, pool, d, **over)
+    torch.cuda.synchronize()
+    trace = {} if w.options.get("qdq") else None
+    ref_out, ref_written = oracle_call(w, before, seqs=seqs, trace=trace, **over)
+    seq_list = list(range(w.B)) if seqs is None else list(seqs)
+    trows = token_rows(w, seq_list)
+    bound, state_bound = None, None
+    if trace is not None:
+        out_b, seq_b = qdq_bounds(w, trace, seq_list)
+        full = np.zeros(ref_out.shape)
+        for t, bnd in out_b.items():
+            full[t] = bnd
+        bound = full[trows]
+        _, wr = rows_for(w, [b for b in seq_list if b in seq_b])
+        state_bound = {row: seq_b[b] for row, b in zip(wr, [b for b in seq_list if b in seq_b])}
+    if len(trows):
+        compare_outputs(out, ref_out, w, trows, report, qdq_bound=bound)
+    got = gather_rows(pool, list(ref_written))
+    compare_states(got, ref_written, report, qdq_bound=state_bound, layout=w.state_layout)
+    assert sorted(ref_written) == sorted(set(writes))
+    if snap is not None:
+        check_untouched(snap, pool, all_writes)
+    return report, out, pool

@@ -1,0 +1,98 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol, and refuses bad
+arguments on the host with the documented status codes.  Nothing here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import recurrent_state_decode_amd as rsd
+from recurrent_state_decode_amd import _binding as bnd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h")]
+
+# The error-path calls below pass fake (never dereferenced) pointers.  They are
+# refused on the host before any launch; still, keep them off a machine with a GPU.
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="fake-pointer ABI checks run only without a GPU")
+
+
+def declared_functions():
+    names = []
+    for path in HEADERS:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?(?:int|void|char)\s*\*?\s*(\w+)\s*\(", text, flags=re.M):
+            names.append(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = rsd.load_library()
+    names = declared_functions()
+    assert {"gdn_decode_pooled", "gdn_decode_paged", "kda_decode_pooled", "gdn_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError):
+        bnd.load_library(str(tmp_path / "absent.so"))
+
+
+def test_options_defaults_and_status_strings():
+    o = bnd._options()
+    assert (o.scale, o.use_qk_l2norm, o.io_dtype, o.out_dtype, o.state_layout) == (0.0, 1, 1, 1, 0)
+    assert (o.beta_mode, o.gate_mode, o.index_dtype, o.qdq, o.block_v, o.quantize_initial, o.readout) == \
+        (0, 0, bnd.GDN_I32, 0, 64, 0, 0)
+    lib = rsd.load_library()
+    assert [lib.gdn_status_string(i).decode() for i in range(5)] == \
+        ["GDN_OK", "GDN_ERR_INVALID", "GDN_ERR_SHAPE", "GDN_ERR_UNSUPPORTED", "GDN_ERR_HIP"]
+    assert lib.gdn_status_string(99).decode() == "unknown status"
+    assert (128, 64) in rsd.supported_head_dims() and (16, 16) in rsd.supported_head_dims()
+
+
+FAKE = ctypes.c_void_p(0x1000)
+
+
+def _pooled(lib, B=2, T=2, HK=1, HV=2, K=128, V=128, cu=FAKE, nulls=(), **opt):
+    o = bnd._options(**opt)
+    ptrs = [None if i in nulls else FAKE for i in range(11)]
+    ptrs[7] = cu
+    return lib.gdn_decode_pooled(*ptrs, B, T, HK, HV, K, V, 4, ctypes.byref(o), None)
+
+
+@no_gpu
+def test_pooled_argument_errors():
+    lib = rsd.load_library()
+    assert _pooled(lib, nulls=(0,)) == bnd.GDN_ERR_INVALID
+    assert _pooled(lib, nulls=(9,)) == bnd.GDN_ERR_INVALID
+    assert _pooled(lib, HK=3, HV=4) == bnd.GDN_ERR_INVALID
+    assert _pooled(lib, B=0) == bnd.GDN_ERR_INVALID
+    assert _pooled(lib, K=96) == bnd.GDN_ERR_UNSUPPORTED
+    assert _pooled(lib, V=96) == bnd.GDN_ERR_UNSUPPORTED
+    assert _pooled(lib, cu=None, B=3, T=2) == bnd.GDN_ERR_SHAPE
+    assert _pooled(lib, gate_mode=1) == bnd.GDN_ERR_UNSUPPORTED
+    assert "SAFE" in lib.gdn_last_error().decode()
+    assert _pooled(lib, io_dtype=7) == bnd.GDN_ERR_INVALID
+    assert _pooled(lib, state_layout=2) == bnd.GDN_ERR_INVALID
+    assert _pooled(lib, qdq=1, block_v=48) == bnd.GDN_ERR_INVALID
+    assert _pooled(lib, qdq=1, block_v=128) == bnd.GDN_ERR_UNSUPPORTED
+    assert _pooled(lib, scale=float("inf")) == bnd.GDN_ERR_INVALID
+    # an empty call (T = 0 with cu_seqlens) launches nothing and succeeds
+    assert _pooled(lib, T=0) == bnd.GDN_OK
+
+
+@no_gpu
+def test_paged_and_kda_argument_errors():
+    lib = rsd.load_library()
+    o = bnd._options(index_dtype=5)
+    assert lib.gdn_decode_paged(*([FAKE] * 12), 2, 1, 2, 128, 128, 10, 4, ctypes.byref(o), None) == bnd.GDN_ERR_INVALID
+    o = bnd._options(index_dtype=bnd.GDN_I64)
+    assert lib.gdn_decode_paged(*([FAKE] * 12), 4, 1, 2, 128, 128, 10, 3, ctypes.byref(o), None) == bnd.GDN_ERR_SHAPE
+    ptrs = [FAKE] * 11
+    ptrs[7] = None                     # cu_seqlens is required for KDA
+    o = bnd._options()
+    assert lib.kda_decode_pooled(*ptrs, 2, 4, 1, 2, 128, 128, 4, ctypes.byref(o), None) == bnd.GDN_ERR_INVALID
+    assert "cu_seqlens" in lib.gdn_last_error().decode()

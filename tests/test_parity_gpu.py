@@ -1,0 +1,219 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle on seeded inputs.
+
+Every case also checks the index work exactly: the rows written are the
+call's write rows and every other pool byte is unchanged.
+"""
+import numpy as np
+import pytest
+import torch
+
+from recurrent_state_decode_amd import workloads as wl
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _report(name, rep):
+    print(f"[parity] {name}: {rep}", flush=True)
+
+
+# ---------------------------------------------------------------- the five workloads at full size
+
+def test_tiny_gdn_b1_k16_t8_f32():
+    w = wl.tiny_gdn()
+    rep, _, _ = P.run_and_check(w)
+    _report(w.name, rep)
+
+
+def test_pooled_gdn_b64_hv32_k128():
+    w = wl.pooled_gdn_b64()
+    rep, _, _ = P.run_and_check(w)
+    _report(w.name, rep)
+
+
+def test_pooled_kda_varlen_b128_hv32_k128():
+    w = wl.pooled_kda_varlen_b128()
+    rep, _, _ = P.run_and_check(w)
+    _report(w.name, rep)
+
+
+@pytest.mark.parametrize("layout,idx", [("V_FIRST", torch.int64), ("K_FIRST", torch.int32)])
+def test_paged_gdn_b256_hv32_k128(layout, idx):
+    w = wl.paged_gdn_b256(state_layout=layout, index_dtype=idx)
+    rep, _, _ = P.run_and_check(w)
+    _report(f"{w.name}/{layout}/{idx}", rep)
+
+
+def test_fp8_qdq_gdn_b512_t4_sampled():
+    w = wl.fp8_qdq_gdn_b512()
+    seqs = sorted(np.random.default_rng(7).choice(w.B, 48, replace=False).tolist())
+    rep, _, _ = P.run_and_check(w, seqs=seqs)
+    _report(w.name, rep)
+
+
+# ---------------------------------------------------------------- smaller cases: layouts, kinds, dtypes
+
+LENS = [0, 1, 3, 0, 8, 9, 17, 2]       # empty suffixes, T = 1, a chunk boundary at 8, several chunks
+
+
+@pytest.mark.parametrize("layout", ["K_FIRST", "V_FIRST"])
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("hk", [2, 4])
+def test_varlen_small(layout, kind, hk):
+    mk = wl.gdn_pooled if kind == "gdn" else wl.kda_pooled
+    w = mk(len(LENS), hk, 4, 128, 128, lengths=LENS, num_slots=11, state_layout=layout, seed=31)
+    rep, _, _ = P.run_and_check(w)
+    _report(f"varlen/{kind}/{layout}/hk{hk}", rep)
+
+
+@pytest.mark.parametrize("io,out", [(torch.float32, torch.float32), (torch.bfloat16, torch.float32),
+                                    (torch.float32, torch.bfloat16)])
+@pytest.mark.parametrize("layout", ["K_FIRST", "V_FIRST"])
+def test_dtype_combinations(io, out, layout):
+    w = wl.gdn_pooled(5, 1, 2, 128, 256, lengths=[2, 1, 0, 4, 1], num_slots=7, state_layout=layout,
+                      io_dtype=io, out_dtype=out, seed=32)
+    rep, _, _ = P.run_and_check(w)
+    _report(f"dtypes/{io}/{out}/{layout}", rep)
+
+
+@pytest.mark.parametrize("layout", ["K_FIRST", "V_FIRST"])
+def test_small_heads_k16_v32(layout):
+    w = wl.gdn_pooled(3, 1, 3, 16, 32, lengths=[5, 0, 12], num_slots=4, state_layout=layout,
+                      io_dtype=torch.float32, seed=33)
+    rep, _, _ = P.run_and_check(w)
+    _report(f"k16v32/{layout}", rep)
+
+
+@pytest.mark.parametrize("opts", [dict(beta_mode="probability"), dict(use_qk_l2norm=False),
+                                  dict(scale=0.37), dict(beta_mode="probability", use_qk_l2norm=False)])
+def test_activation_options(opts):
+    w = wl.gdn_pooled(4, 2, 4, 128, 128, lengths=[1, 3, 2, 1], num_slots=6, seed=34)
+    if opts.get("beta_mode") == "probability":
+        w.inputs["b"] = torch.rand(w.inputs["b"].shape, generator=torch.Generator().manual_seed(1)).to(w.io_dtype)
+    rep, _, _ = P.run_and_check(w, **opts)
+    _report(f"opts/{opts}", rep)
+
+
+@pytest.mark.parametrize("layout", ["V_FIRST", "K_FIRST"])
+@pytest.mark.parametrize("idx", [torch.int32, torch.int64])
+def test_paged_small_page_boundaries(layout, idx):
+    # page_size 4 puts many decoded tokens on both last_page_len == 1 (new page,
+    # often with a shared previous page) and last_page_len == 4 (full page in place)
+    w = wl.gdn_paged(48, 2, 4, 128, 128, max_prefix=40, page_size=4, share_frac=0.3, state_layout=layout,
+                     index_dtype=idx, seed=35)
+    lpl = w.inputs["last_page_len"].numpy()
+    assert (lpl == 1).any() and (lpl == 4).any()
+    rep, _, _ = P.run_and_check(w)
+    _report(f"paged_small/{layout}/{idx}", rep)
+
+
+# ---------------------------------------------------------------- fp8 tile QDQ variants
+
+@pytest.mark.parametrize("layout", ["K_FIRST", "V_FIRST"])
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("extra", [dict(), dict(quantize_initial=True), dict(readout="stored")])
+def test_qdq_variants(layout, kind, extra):
+    mk = wl.gdn_pooled if kind == "gdn" else wl.kda_pooled
+    w = mk(6, 2, 4, 128, 128, lengths=[4, 1, 0, 9, 2, 3], num_slots=8, state_layout=layout, seed=36,
+           qdq="fp8_e4m3_tile", block_v=64, **extra)
+    rep, _, _ = P.run_and_check(w)
+    _report(f"qdq/{kind}/{layout}/{extra}", rep)
+
+
+@pytest.mark.parametrize("layout", ["K_FIRST", "V_FIRST"])
+def test_qdq_rounding_matches_e4m3_grid_exactly(layout):
+    """alpha = 1 and beta = 0 leave the state unchanged, so the stored state is the tile QDQ of the
+    initial pool; each tile holds 448 so that its scale is exactly 1 and every code is
+    decided on the value itself: midpoints, their neighbours and random values must round
+    exactly as the OCP E4M3 nearest-even grid."""
+    from oracle import e4m3
+    B, HV, K, V = 4, 4, 128, 128
+    w = wl.gdn_pooled(B, 1, HV, K, V, lengths=[1] * B, num_slots=B, state_layout=layout, seed=37,
+                      io_dtype=torch.float32, qdq="fp8_e4m3_tile", block_v=64)
+    w.inputs["a"] = torch.full((B, HV), -float("inf"))     # softplus(-inf) = 0 -> alpha = 1
+    w.inputs["b"] = torch.zeros((B, HV))                   # beta = b = 0 (probability mode)
+    w.options["beta_mode"] = "probability"
+    grid = np.sort(e4m3.e4m3_table()[:127])
+    mids = (grid[:-1] + grid[1:]) / 2
+    vals = np.concatenate([mids, np.nextafter(mids.astype(np.float32), np.float32(0)),
+                           np.nextafter(mids.astype(np.float32), np.float32(1e9)), grid])
+    rng = np.random.default_rng(38)
+    n = B * HV * K * V
+    fill = np.concatenate([vals, -vals, rng.uniform(-448, 448, n)])[:n].astype(np.float32)
+    rng.shuffle(fill)
+    logical = fill.reshape(B, HV, K, V)
+    for h in range(HV):
+        for j in range(0, V, 64):
+            logical[:, h, 0, j] = 448.0
+    tiles = logical if layout == "K_FIRST" else np.swapaxes(logical, -1, -2)
+    pool = torch.from_numpy(np.ascontiguousarray(tiles)).cuda()
+    rep, _, pool = P.run_and_check(w, pool=pool)
+    got = pool.cpu().numpy()
+    got_logical = got if layout == "K_FIRST" else np.swapaxes(got, -1, -2)
+    assert np.array_equal(got_logical, e4m3.e4m3_round(logical.astype(np.float64)).astype(np.float32))
+    _report(f"qdq_exact/{layout}", rep)
+
+
+# ---------------------------------------------------------------- closed forms on the GPU
+
+@pytest.mark.parametrize("layout", ["K_FIRST", "V_FIRST"])
+def test_beta0_gate0_leaves_state_bit_identical(layout):
+    w = wl.gdn_pooled(3, 2, 4, 128, 128, lengths=[1, 4, 2], num_slots=5, state_layout=layout, seed=39,
+                      io_dtype=torch.float32, beta_mode="probability")
+    T = w.T
+    w.inputs["a"] = torch.full((T, 4), -float("inf"))
+    w.inputs["b"] = torch.zeros((T, 4))
+    pool = wl.make_pool(w, "cuda")
+    before = pool.clone()
+    rep, _, pool = P.run_and_check(w, pool=pool)
+    assert torch.equal(pool, before)
+    _report(f"beta0_gate0/{layout}", rep)
+
+
+@pytest.mark.parametrize("layout", ["K_FIRST", "V_FIRST"])
+def test_alpha1_beta1_signed_basis_keys_recover_values_exactly(layout):
+    K = V = 128
+    T = 40
+    w = wl.gdn_pooled(1, 1, 1, K, V, lengths=[T], num_slots=2, state_layout=layout, seed=40,
+                      io_dtype=torch.float32, out_dtype=torch.float32, beta_mode="probability",
+                      use_qk_l2norm=False, zero_state=True)
+    perm = np.random.default_rng(41).permutation(K)[:T]
+    keys = np.zeros((T, 1, K), np.float32)
+    keys[np.arange(T), 0, perm] = np.where(np.arange(T) % 2, -1.0, 1.0)
+    w.inputs["k"] = torch.from_numpy(keys)
+    w.inputs["a"] = torch.full((T, 1), -float("inf"))
+    w.inputs["b"] = torch.ones((T, 1))
+    rep, _, pool = P.run_and_check(w)
+    slot = int(w.inputs["state_indices"][0])
+    S = pool[slot, 0].cpu().numpy()
+    S = S if layout == "K_FIRST" else S.T
+    vals = w.inputs["v"][:, 0].numpy()
+    for t in range(T):
+        assert np.array_equal(keys[t, 0] @ S, vals[t])
+    _report(f"recovery/{layout}", rep)
+
+
+def test_two_calls_equal_one_call_on_gpu():
+    """A suffix split into two calls gives the same state as one call (the pool carries the state)."""
+    w = wl.gdn_pooled(2, 1, 2, 128, 128, lengths=[5, 3], num_slots=3, seed=42)
+    d = P.device_inputs(w)
+    pool1 = wl.make_pool(w, "cuda")
+    pool2 = pool1.clone()
+    out_all = P.gpu_call(w, pool1, d)
+    # first call: tokens [0,2) of seq 0 and [5,6) of seq 1; second call: the rest
+    cu = w.inputs["cu_seqlens"].numpy()
+    part1 = [np.arange(0, 2), np.arange(5, 6)]
+    part2 = [np.arange(2, 5), np.arange(6, 8)]
+    for parts in (part1, part2):
+        rows = np.concatenate(parts)
+        sub = {k: v for k, v in d.items()}
+        for k in ("q", "k", "v", "a", "b"):
+            sub[k] = d[k][torch.from_numpy(rows).cuda()].contiguous()
+        sub["cu_seqlens"] = torch.tensor([0, len(parts[0]), len(rows)], dtype=torch.int32, device="cuda")
+        w2 = wl.Workload(w.kind, w.name, w.B, w.HK, w.HV, w.K, w.V, w.io_dtype, w.out_dtype, w.state_layout,
+                         w.num_rows, w.inputs, w.options)
+        P.gpu_call(w2, pool2, sub)
+    torch.cuda.synchronize()
+    # same per-token arithmetic in both schedules: the states agree bit for bit
+    assert torch.equal(pool1, pool2)
+    assert cu[-1] == 8
