@@ -30,36 +30,65 @@ int fail(int code, const char* fmt, ...) {
 
 enum class Kind { GdnPooled, GdnPaged, KdaPooled };
 
+// Workgroup shapes: V-block width VB (one workgroup per V-block of one
+// sequence and value head) and threads per workgroup NT.  Chosen per key
+// head dim, pool layout, whether the tile is quantised, and tokens per
+// sequence (every workgroup normalises and gates its sequence's tokens, so
+// narrow V-blocks pay that work V/VB times over):
+//   K=128, V_FIRST, no QDQ, about one token per sequence (T <= 1.5 B):
+//                            VB=8,  NT=128 (4 KiB of state per workgroup)
+//   K=128, otherwise:        VB=64, NT=256 (fp8 tiles need block_v == VB)
+//   K=16:                    VB=16, NT=64
+// V must be a multiple of VB.
+struct Shape {
+  int VB, NT;
+};
+
+Shape shape_for(int K, bool vfirst, bool qdq, int64_t T, int64_t B) {
+  if (K == 128) return (vfirst && !qdq && 2 * T <= 3 * B) ? Shape{8, 128} : Shape{64, 256};
+  if (K == 16) return Shape{16, 64};
+  return Shape{0, 0};
+}
+
+// Key head dims with kernels, and the V multiple every shape of that K accepts.
 struct HeadCfg {
   int K, VB;
 };
-// Key head dims with compiled kernels and the V-block each uses: V may be
-// any multiple of VB (one workgroup per V-block).
 constexpr HeadCfg kHeads[] = {{16, 16}, {128, 64}};
 
-template <int K, int VB, int NT, bool VF, bool KDA, bool QDQ, bool PAGED>
+template <int K, int VB, int NT, bool VF, bool KDA, bool QDQ, bool PAGED, typename TIn>
 hipError_t launch_one(const gdn::Params& p, int64_t units, hipStream_t stream) {
-  hipLaunchKernelGGL((gdn::decode_kernel<K, VB, NT, VF, KDA, QDQ, PAGED>), dim3(static_cast<uint32_t>(units)),
+  hipLaunchKernelGGL((gdn::decode_kernel<K, VB, NT, VF, KDA, QDQ, PAGED, TIn>), dim3(static_cast<uint32_t>(units)),
                      dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int K, int VB, int NT, bool KDA, bool PAGED>
-hipError_t launch_layout_qdq(const gdn::Params& p, int64_t units, bool vfirst, bool qdq, hipStream_t s) {
-  if (vfirst) {
-    return qdq ? launch_one<K, VB, NT, true, KDA, true, PAGED>(p, units, s)
-               : launch_one<K, VB, NT, true, KDA, false, PAGED>(p, units, s);
+struct Sel {
+  bool vfirst, qdq, bf16;
+};
+
+template <int K, int VB, int NT, bool KDA, bool PAGED, typename TIn>
+hipError_t launch_layout_qdq(const gdn::Params& p, int64_t units, Sel sel, hipStream_t s) {
+  if (sel.vfirst) {
+    return sel.qdq ? launch_one<K, VB, NT, true, KDA, true, PAGED, TIn>(p, units, s)
+                   : launch_one<K, VB, NT, true, KDA, false, PAGED, TIn>(p, units, s);
   }
-  return qdq ? launch_one<K, VB, NT, false, KDA, true, PAGED>(p, units, s)
-             : launch_one<K, VB, NT, false, KDA, false, PAGED>(p, units, s);
+  return sel.qdq ? launch_one<K, VB, NT, false, KDA, true, PAGED, TIn>(p, units, s)
+                 : launch_one<K, VB, NT, false, KDA, false, PAGED, TIn>(p, units, s);
+}
+
+template <int K, int VB, int NT, bool KDA, bool PAGED>
+hipError_t launch_io(const gdn::Params& p, int64_t units, Sel sel, hipStream_t s) {
+  return sel.bf16 ? launch_layout_qdq<K, VB, NT, KDA, PAGED, gdn::bf16_t>(p, units, sel, s)
+                  : launch_layout_qdq<K, VB, NT, KDA, PAGED, float>(p, units, sel, s);
 }
 
 template <int K, int VB, int NT>
-hipError_t launch_kind(Kind kind, const gdn::Params& p, int64_t units, bool vfirst, bool qdq, hipStream_t s) {
+hipError_t launch_kind(Kind kind, const gdn::Params& p, int64_t units, Sel sel, hipStream_t s) {
   switch (kind) {
-    case Kind::GdnPooled: return launch_layout_qdq<K, VB, NT, false, false>(p, units, vfirst, qdq, s);
-    case Kind::GdnPaged: return launch_layout_qdq<K, VB, NT, false, true>(p, units, vfirst, qdq, s);
-    case Kind::KdaPooled: return launch_layout_qdq<K, VB, NT, true, false>(p, units, vfirst, qdq, s);
+    case Kind::GdnPooled: return launch_io<K, VB, NT, false, false>(p, units, sel, s);
+    case Kind::GdnPaged: return launch_io<K, VB, NT, false, true>(p, units, sel, s);
+    case Kind::KdaPooled: return launch_io<K, VB, NT, true, false>(p, units, sel, s);
   }
   return hipErrorInvalidValue;
 }
@@ -73,6 +102,23 @@ int vblock_for(int K) {
 bool head_supported(int K, int V) {
   const int vb = vblock_for(K);
   return vb > 0 && V % vb == 0;
+}
+
+// Small V_FIRST workgroups (K=128, no QDQ): one instantiation per kind and io type.
+template <int VB, int NT>
+hipError_t launch_small_vfirst(Kind kind, const gdn::Params& p, int64_t units, Sel sel, hipStream_t s) {
+  switch (kind) {
+    case Kind::GdnPooled:
+      return sel.bf16 ? launch_one<128, VB, NT, true, false, false, false, gdn::bf16_t>(p, units, s)
+                      : launch_one<128, VB, NT, true, false, false, false, float>(p, units, s);
+    case Kind::GdnPaged:
+      return sel.bf16 ? launch_one<128, VB, NT, true, false, false, true, gdn::bf16_t>(p, units, s)
+                      : launch_one<128, VB, NT, true, false, false, true, float>(p, units, s);
+    case Kind::KdaPooled:
+      return sel.bf16 ? launch_one<128, VB, NT, true, true, false, false, gdn::bf16_t>(p, units, s)
+                      : launch_one<128, VB, NT, true, true, false, false, float>(p, units, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 int check_options(const gdn_options* o, int K, int V, Kind kind) {
@@ -115,16 +161,18 @@ int check_dims(int32_t B, int32_t HK, int32_t HV, int32_t K, int32_t V) {
   return GDN_OK;
 }
 
-void fill_common(gdn::Params& p, const gdn_options* o, int32_t B, int32_t HK, int32_t HV, int32_t K, int32_t V) {
+void fill_common(gdn::Params& p, const gdn_options* o, int32_t B, int32_t T, int32_t HK, int32_t HV, int32_t K,
+                 int32_t V) {
   p.B = B;
   p.HK = HK;
   p.HV = HV;
   p.V = V;
-  p.nvb = V / vblock_for(K);
+  const Shape sh = shape_for(K, o->state_layout == GDN_V_FIRST, o->qdq != GDN_QDQ_NONE, T, B);
+  p.nvb = V / sh.VB;
+  p.xcd_group = 64;
   p.gqa = HV / HK;
   p.scale = o->scale > 0.0f ? o->scale : 1.0f / std::sqrt(static_cast<float>(K));
   p.l2norm = o->use_qk_l2norm ? 1 : 0;
-  p.io_bf16 = o->io_dtype == GDN_BF16;
   p.out_bf16 = o->out_dtype == GDN_BF16;
   p.beta_prob = o->beta_mode == GDN_BETA_PROBABILITY;
   p.idx64 = o->index_dtype == GDN_I64;
@@ -132,16 +180,18 @@ void fill_common(gdn::Params& p, const gdn_options* o, int32_t B, int32_t HK, in
   p.readout_stored = (o->qdq != GDN_QDQ_NONE && o->readout == GDN_READOUT_STORED) ? 1 : 0;
 }
 
-int run(Kind kind, const gdn::Params& p, int K, const gdn_options* o, void* stream) {
+int run(Kind kind, const gdn::Params& p, int K, int32_t T, const gdn_options* o, void* stream) {
   const int64_t units = static_cast<int64_t>(p.B) * p.HV * p.nvb;
   if (units > 0x7fffffffLL) return fail(GDN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)units);
-  const bool vfirst = o->state_layout == GDN_V_FIRST;
-  const bool qdq = o->qdq != GDN_QDQ_NONE;
+  const Sel sel{o->state_layout == GDN_V_FIRST, o->qdq != GDN_QDQ_NONE, o->io_dtype == GDN_BF16};
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err = hipErrorInvalidValue;
   switch (K) {
-    case 16: err = launch_kind<16, 16, 64>(kind, p, units, vfirst, qdq, s); break;
-    case 128: err = launch_kind<128, 64, 256>(kind, p, units, vfirst, qdq, s); break;
+    case 16: err = launch_kind<16, 16, 64>(kind, p, units, sel, s); break;
+    case 128:
+      err = shape_for(K, sel.vfirst, sel.qdq, T, p.B).VB == 8 ? launch_small_vfirst<8, 128>(kind, p, units, sel, s)
+                                                             : launch_kind<128, 64, 256>(kind, p, units, sel, s);
+      break;
     default: return fail(GDN_ERR_UNSUPPORTED, "no kernel for K=%d", K);
   }
   if (err != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
@@ -186,9 +236,9 @@ int gdn_decode_pooled(const void* q, const void* k, const void* v, const void* a
   p.a_log = A_log; p.dt_bias = dt_bias;
   p.cu_seqlens = cu_seqlens; p.state_indices = state_indices;
   p.pool = state_pool; p.out = out;
-  fill_common(p, opt, B, HK, HV, K, V);
+  fill_common(p, opt, B, T, HK, HV, K, V);
   if (T == 0) { g_last_error.clear(); return GDN_OK; }
-  return run(Kind::GdnPooled, p, K, opt, stream);
+  return run(Kind::GdnPooled, p, K, T, opt, stream);
 }
 
 int gdn_decode_paged(const void* q, const void* k, const void* v, const void* a, const void* b,
@@ -208,8 +258,8 @@ int gdn_decode_paged(const void* q, const void* k, const void* v, const void* a,
   p.a_log = A_log; p.dt_bias = dt_bias;
   p.page_indices = page_indices; p.page_indptr = page_indptr; p.last_page_len = last_page_len;
   p.pool = state_pool; p.out = out;
-  fill_common(p, opt, B, HK, HV, K, V);
-  return run(Kind::GdnPaged, p, K, opt, stream);
+  fill_common(p, opt, B, B, HK, HV, K, V);
+  return run(Kind::GdnPaged, p, K, B, opt, stream);
 }
 
 int kda_decode_pooled(const void* q, const void* k, const void* v, const void* raw_gate, const void* beta_logits,
@@ -227,9 +277,9 @@ int kda_decode_pooled(const void* q, const void* k, const void* v, const void* r
   p.a_log = a_log; p.dt_bias = dt_bias;
   p.cu_seqlens = cu_seqlens; p.state_indices = state_indices;
   p.pool = state_pool; p.out = out;
-  fill_common(p, opt, B, HK, HV, K, V);
+  fill_common(p, opt, B, T, HK, HV, K, V);
   if (T == 0) { g_last_error.clear(); return GDN_OK; }
-  return run(Kind::KdaPooled, p, K, opt, stream);
+  return run(Kind::KdaPooled, p, K, T, opt, stream);
 }
 
 const char* gdn_status_string(int status) {

@@ -217,3 +217,27 @@ def test_two_calls_equal_one_call_on_gpu():
     # same per-token arithmetic in both schedules: the states agree bit for bit
     assert torch.equal(pool1, pool2)
     assert cu[-1] == 8
+
+
+# ---------------------------------------------------------------- narrow V-blocks (about one token per sequence)
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("io", [torch.bfloat16, torch.float32])
+def test_single_token_vfirst_narrow_blocks(kind, io):
+    # T <= 1.5 B selects the 8-column V-blocks for V_FIRST pools; lengths mix 0, 1 and 2 tokens
+    lens = [1, 1, 2, 0, 1, 1, 2, 1]
+    if kind == "gdn":
+        w = wl.gdn_pooled(len(lens), 2, 4, 128, 128, lengths=lens, num_slots=9, state_layout="V_FIRST",
+                          io_dtype=io, seed=43)
+    else:
+        w = wl.kda_pooled(len(lens), 4, 4, 128, 128, lengths=lens, num_slots=9, state_layout="V_FIRST",
+                          io_dtype=io, seed=44)
+    assert 2 * w.T <= 3 * w.B
+    rep, _, _ = P.run_and_check(w)
+    _report(f"narrow/{kind}/{io}", rep)
+
+
+def test_single_token_vfirst_no_cu_seqlens():
+    w = wl.gdn_pooled(24, 4, 8, 128, 256, lengths=None, num_slots=30, state_layout="V_FIRST", seed=45)
+    rep, _, _ = P.run_and_check(w)
+    _report("narrow/no_cu", rep)
