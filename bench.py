@@ -63,16 +63,103 @@ def algorithmic_bytes(w):
     return state, T * per_tok
 
 
+def traffic_path(workload_name):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload_name}.txt")
+
+
 def load_traffic(workload_name):
     """Per-launch HBM bytes from a committed rocprofv3 counter summary, if it matches these sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    path = traffic_path(workload_name)
     if not os.path.exists(path):
         return None
+    rec = {}
     with open(path) as f:
-        rec = json.load(f)
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
     if rec.get("source_hash") != source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    return int(rec["bytes_per_launch"])
+
+
+def _csvs(d, suffix):
+    import glob
+    return sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+
+
+def summarize_profiles(kt_dir, fetch_dir, write_dir, commands):
+    """Turn rocprofv3 outputs into the short summaries kept under profiles/.
+
+    kt_dir: a --kernel-trace --stats run of bench.py; fetch_dir / write_dir:
+    --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of bench.py --copy-calibration.
+    The plain 1 GiB copy in those runs gives the scale of each counter.
+    """
+    import csv
+    import statistics
+
+    def load_json(d):
+        with open(d.rstrip("/") + ".json") as f:
+            return json.loads(f.read().strip().splitlines()[-1])
+
+    bench_kt = load_json(kt_dir)
+    name = bench_kt["config"]["workload"]
+    kern = "gdn::decode_kernel"
+    # kernel trace: per-dispatch durations of the decode kernel, warm-up dispatches dropped
+    trace = [r for f in _csvs(kt_dir, "kernel_trace.csv") for r in csv.DictReader(open(f))]
+    dec = sorted((r for r in trace if kern in r["Kernel_Name"]), key=lambda r: int(r["Start_Timestamp"]))
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in dec]
+    timed = durs[bench_kt["warmup"]:]
+    stats = [r for f in _csvs(kt_dir, "kernel_stats.csv") for r in csv.DictReader(open(f))]
+    lines = [f"# rocprofv3 kernel trace: {name}", "", "Command (from the repository root):", "",
+             "    " + commands["kt"], "",
+             f"bench.py line of this run: ms_per_step={bench_kt['ms_per_step']} "
+             f"(HIP events around each launch, after the cache-flush kernel), value={bench_kt['value']} tokens/s", "",
+             f"decode kernel, timed dispatches ({len(timed)}): mean {statistics.mean(timed):.1f} us, "
+             f"median {statistics.median(timed):.1f} us, min {min(timed):.1f} us, max {max(timed):.1f} us", "",
+             "| kernel | calls | average ns | min ns | max ns | % time |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        kname = r["Name"] if len(r["Name"]) < 90 else r["Name"][:87] + "..."
+        lines.append(f"| {kname} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} | "
+                     f"{float(r['Percentage']):.1f} |")
+    with open(os.path.join(ROOT, "profiles", f"kernel_trace_{name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    def counter(d, cname):
+        rows = [r for f in _csvs(d, "counter_collection.csv") for r in csv.DictReader(open(f))]
+        dec_v = [float(r["Counter_Value"]) for r in rows if kern in r["Kernel_Name"] and r["Counter_Name"] == cname]
+        big = [r for r in rows if r["Counter_Name"] == cname and "copyBuffer" in r["Kernel_Name"]]
+        big = [float(r["Counter_Value"]) for r in big if int(r["Grid_Size"]) >= 65536]
+        return statistics.median(dec_v), statistics.median(big), len(dec_v)
+
+    bench_f = load_json(fetch_dir)
+    copy_kib = bench_f["copy_calibration_bytes"] / 1024
+    f_dec, f_copy, nf = counter(fetch_dir, "FETCH_SIZE")
+    w_dec, w_copy, nw = counter(write_dir, "WRITE_SIZE")
+    f_scale, w_scale = f_copy / copy_kib, w_copy / copy_kib
+    read_b = f_dec / f_scale * 1024
+    write_b = w_dec / w_scale * 1024
+    alg = bench_kt["roofline"]["algorithmic_bytes_per_launch"]
+    tl = [f"# rocprofv3 HBM traffic counters: {name}", "",
+          "Commands (from the repository root, one counter per run):", "",
+          "    " + commands["fetch"], "    " + commands["write"], "",
+          "Each run also copies 1 GiB -> 1 GiB once per call with a plain device copy (bench.py",
+          "--copy-calibration); what the counter reads for that copy scales the decode kernel's reading.", "",
+          f"workload: {name}",
+          f"kernel: {kern}",
+          f"source_hash: {bench_kt['roofline']['source_hash']}",
+          f"decode FETCH_SIZE KiB per dispatch (median of {nf}): {f_dec:.1f}",
+          f"decode WRITE_SIZE KiB per dispatch (median of {nw}): {w_dec:.1f}",
+          f"copy FETCH_SIZE KiB for {copy_kib:.0f} KiB read: {f_copy:.1f} (scale {f_scale:.4f})",
+          f"copy WRITE_SIZE KiB for {copy_kib:.0f} KiB written: {w_copy:.1f} (scale {w_scale:.4f})",
+          f"read_bytes_per_launch: {read_b:.0f}",
+          f"write_bytes_per_launch: {write_b:.0f}",
+          f"bytes_per_launch: {read_b + write_b:.0f}",
+          f"algorithmic_bytes_per_launch: {alg}",
+          f"traffic_over_algorithmic: {(read_b + write_b) / alg:.4f}"]
+    with open(traffic_path(name), "w") as f:
+        f.write("\n".join(tl) + "\n")
+    print("\n".join(tl))
 
 
 def cpu_baseline(w, pool, budget_s):
@@ -113,7 +200,23 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ summaries from rocprofv3 output directories (no GPU needed)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run a plain 1 GiB -> 1 GiB copy 3 times (a kernel of known traffic for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
+
+    if args.summarize_profiles:
+        kt, fe, wr = args.summarize_profiles
+        cmds = {"kt": f"rocprofv3 --kernel-trace --stats -d {kt} -o kt --output-format csv -- "
+                      "python3 bench.py --steps 20 --warmup 2 --no-cpu-baseline",
+                "fetch": f"rocprofv3 --pmc FETCH_SIZE -d {fe} -o f --output-format csv -- "
+                         "python3 bench.py --steps 10 --warmup 1 --no-cpu-baseline --copy-calibration",
+                "write": f"rocprofv3 --pmc WRITE_SIZE -d {wr} -o w --output-format csv -- "
+                         "python3 bench.py --steps 10 --warmup 1 --no-cpu-baseline --copy-calibration"}
+        summarize_profiles(kt, fe, wr, cmds)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
@@ -194,6 +297,15 @@ def main():
                      "traffic": traffic, "algorithmic_bytes_per_launch": state_b + io_b,
                      "kernel": "gdn::decode_kernel", "source_hash": source_hash()},
     }
+    if args.copy_calibration:
+        n = 256 * 1024 * 1024
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            flush.fill_(0.0) if flush is not None else None
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = n * 4
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, pool, args.cpu_budget)
     print(json.dumps(res), flush=True)
