@@ -3,30 +3,33 @@
 //
 // Math per token (Circuit.LLM.Mixer, "Delta rule" and "Gated memory";
 // max.nn.state_space.kda_decode, description): decay the state, read what
-// the key retrieves, write the delta, read the updated state out.  The
-// kernel evaluates it in a fused form that needs one pass over the state
-// per token:
-//     r = k'^T S, p = q'^T S          (k' = k_hat*alpha, q' = q_hat*alpha)
-//     u = beta * (v - r)
-//     o = p + (q_hat . k_hat) * u     (= q_hat^T S_new)
-//     S = alpha*S + k_hat u^T
-// which is the same arithmetic regrouped (alpha is a scalar for GDN, applied
-// after the reduction, and a per-key-row vector for KDA).
+// the key retrieves, write the delta, read the updated state out.
+//
+// Scaled state.  Registers hold S_reg with the true state S = c * S_reg,
+// where c is one scalar per workgroup (GDN: the decay is one factor per head)
+// or one factor per key row (KDA).  A token then needs one pass over the
+// tile and one FMA per element for the write:
+//     c' = c * alpha                                 (the decay)
+//     r  = k_hat^T S = c' (k_hat^T S_reg),  p = c' (q_hat^T S_reg)
+//     u  = beta (v - r),   o = p + (q_hat . k_hat) u  (= q_hat^T S_new)
+//     S_reg += k_hat (u / c')                         (S_new = c' S_reg)
+// (for KDA the per-row c' folds into the coefficients: r = sum_i k_hat_i c'_i
+// S_reg[i,:], S_reg[i,:] += (k_hat_i / c'_i) u).  A factor below 1e-20 is
+// applied to the registers and reset to 1, so S_reg never overflows.  The
+// fp8 tile quantisation keeps the codes in S_reg and moves the tile scale
+// amax/448 into c.  The tile is multiplied out once, when it is stored.
 //
 // Layout of the state tile in registers.  Each thread owns NS memory rows of
-// 4 consecutive floats (one 128-bit load per row); consecutive lanes cover a
-// contiguous memory row, so every wave-wide load or store is fully
-// coalesced:
+// EV floats (128-bit loads); consecutive lanes cover a contiguous memory row,
+// so every wave-wide load or store is fully coalesced:
 //   K_FIRST (V contiguous): memory row = key index i, 4 value columns per
 //       thread; the K-reduction is in-thread over NS rows, then across the
-//       row groups of a wave (lane bits above log2(VB/4)), then across waves
-//       through LDS.
-//   V_FIRST (K contiguous): memory row = value index j, 4 key elements per
-//       thread; the K-reduction is 4-wide in-thread, then across the K/4
-//       lanes of the row (the low lane bits); no cross-wave step.
-// Cross-lane sums use DPP (quad permutes, row mirrors and rotates) inside a
-// 16-lane row and the gfx950 v_permlane16_swap / v_permlane32_swap across
-// rows, so no reduction goes through LDS except the cross-wave one.
+//       row groups of a wave (v_permlane32_swap / v_permlane16_swap), then
+//       across waves through LDS.
+//   V_FIRST (K contiguous): memory row = value index j, 8 key elements per
+//       thread (two float4 half a row apart; 4 for small K); the K-reduction
+//       is in-thread, then across the 16 lanes of the row with DPP (quad
+//       permutes, row mirror, row rotate); no cross-wave step.
 //
 // Latency: the per-token inputs of the first chunk are loaded before the
 // state tile and normalised while the tile is in flight.
@@ -69,8 +72,15 @@ struct Params {
   int32_t idx64;
   int32_t quantize_initial;
   int32_t readout_stored;
-  int32_t xcd_group;       // consecutive work units kept on one XCD (>= 1)
+  int32_t xcd_shift;       // log2 of the number of consecutive work units kept on one XCD
+  // n / d as (n * m) >> sh for n < 2^31 (host-computed), for d = nvb, HV, HV / HK
+  uint64_t div_nvb_m, div_hv_m, div_gqa_m;
+  int32_t div_nvb_s, div_hv_s, div_gqa_s;
 };
+
+__device__ __forceinline__ int fast_div(int n, uint64_t m, int sh) {
+  return static_cast<int>((static_cast<uint64_t>(static_cast<uint32_t>(n)) * m) >> sh);
+}
 
 constexpr float kL2Eps = 1e-6f;
 constexpr float kE4M3Max = 448.0f;
@@ -136,11 +146,21 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// Activations on the hardware transcendental units (v_exp_f32 = 2^x,
+// v_log_f32 = log2 x, v_rcp_f32): about one ulp each, far inside the
+// decode tolerance, and a few instructions instead of a library sequence.
+constexpr float kLog2E = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * kLog2E); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// max(x, 0) + log(1 + exp(-|x|))
 __device__ __forceinline__ float softplus_f(float x) {
-  return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)));
+  return fmaxf(x, 0.0f) + __builtin_amdgcn_logf(1.0f + exp_hw(-fabsf(x))) * kLn2;
 }
 
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
+__device__ __forceinline__ float sigmoid_f(float x) { return rcp_hw(1.0f + exp_hw(-x)); }
 
 // ---- cross-lane primitives (wave64)
 
@@ -149,54 +169,69 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// x + the value of the lane in the other 16-lane row of the same 32-lane half
-__device__ __forceinline__ float sum_rows16(float x) {
+struct OpAdd {
+  __device__ static float f(float a, float b) { return a + b; }
+};
+struct OpMax {
+  __device__ static float f(float a, float b) { return fmaxf(a, b); }
+};
+
+// x combined with the value of the lane in the other 16-lane row of the same 32-lane half
+template <class Op>
+__device__ __forceinline__ float with_rows16(float x) {
   const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+  return Op::f(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
 }
 
-// x + the value of the lane in the other 32-lane half
-__device__ __forceinline__ float sum_halves32(float x) {
+// x combined with the value of the lane in the other 32-lane half
+template <class Op>
+__device__ __forceinline__ float with_halves32(float x) {
   const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+  return Op::f(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
 }
 
-// Sum over the lanes that differ from this one only in lane-index bits
-// [LO, HI); every lane receives the sum.  DPP controls: quad_perm 0xB1 swaps
-// lanes 2n and 2n+1, 0x4E swaps pairs 0-1 and 2-3, row_half_mirror (0x141)
-// reverses each group of 8, row_ror:8 (0x128) and row_ror:4 (0x124) rotate a
-// 16-lane row.  Each step adds a lane set disjoint from the one gathered so
-// far, so every lane of the group is counted exactly once.
-template <int LO, int HI>
-__device__ __forceinline__ float lane_sum(float x) {
+// Reduce over the lanes that differ from this one only in lane-index bits
+// [LO, HI); every lane receives the result.  DPP controls: quad_perm 0xB1
+// swaps lanes 2n and 2n+1, 0x4E swaps pairs 0-1 and 2-3, row_half_mirror
+// (0x141) reverses each group of 8, row_ror:8 (0x128) and row_ror:4 (0x124)
+// rotate a 16-lane row.  Each step adds a lane set disjoint from the one
+// gathered so far, so every lane of the group is counted exactly once.
+template <int LO, int HI, class Op = OpAdd>
+__device__ __forceinline__ float lane_reduce(float x) {
   static_assert(0 <= LO && LO < HI && HI <= 6, "lane bits");
   constexpr bool b0 = LO <= 0 && 0 < HI, b1 = LO <= 1 && 1 < HI, b2 = LO <= 2 && 2 < HI;
   constexpr bool b3 = LO <= 3 && 3 < HI, b4 = LO <= 4 && 4 < HI, b5 = LO <= 5 && 5 < HI;
-  if constexpr (b0) x += dpp<0xB1>(x);
-  if constexpr (b1) x += dpp<0x4E>(x);
+  if constexpr (b0) x = Op::f(x, dpp<0xB1>(x));
+  if constexpr (b1) x = Op::f(x, dpp<0x4E>(x));
   if constexpr (b2) {
     static_assert((b0 && b1) || b3, "bit 2 needs bits 0-1 (mirror) or bit 3 (rotate)");
     if constexpr (b0 && b1) {
-      x += dpp<0x141>(x);                  // lanes i and 7-i: together with bits 0,1 covers the 8
-      if constexpr (b3) x += dpp<0x128>(x);
+      x = Op::f(x, dpp<0x141>(x));         // lanes i and 7-i: with bits 0,1 covers the 8
+      if constexpr (b3) x = Op::f(x, dpp<0x128>(x));
     } else {
-      x += dpp<0x128>(x);                  // i and i+8
-      x += dpp<0x124>(x);                  // then i-4: {i, i-4, i-8, i-12}
+      x = Op::f(x, dpp<0x128>(x));         // i and i+8
+      x = Op::f(x, dpp<0x124>(x));         // then i-4: {i, i-4, i-8, i-12}
     }
   } else if constexpr (b3) {
-    x += dpp<0x128>(x);
+    x = Op::f(x, dpp<0x128>(x));
   }
-  if constexpr (b4) x = sum_rows16(x);
-  if constexpr (b5) x = sum_halves32(x);
+  if constexpr (b4) x = with_rows16<Op>(x);
+  if constexpr (b5) x = with_halves32<Op>(x);
   return x;
 }
 
-template <int HI>
-__device__ __forceinline__ float lane_max(float x) {
-  // max over lane bits [0, HI): butterflies through LDS-free swizzles
-#pragma unroll
-  for (int o = 1; o < (1 << HI); o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
+// Reduce-scatter of two values across lane bit 5: lanes 0-31 get a summed
+// over the two halves, lanes 32-63 get b summed.
+__device__ __forceinline__ float rs_halves32(float a, float b) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+}
+
+// Reduce-scatter of two values across lane bit 4: 16-lane rows 0 and 2 get a
+// summed with the next row, rows 1 and 3 get b summed.
+__device__ __forceinline__ float rs_rows16(float a, float b) {
+  const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
 }
 
 // Round x0, x1 (already divided by the tile scale) to the E4M3 grid and back
@@ -208,25 +243,32 @@ __device__ __forceinline__ void e4m3_roundtrip2(float& x0, float& x1) {
   x1 = back[1];
 }
 
+constexpr float kTinyScale = 1e-20f;
+
 template <int K, int VB, int NT, bool VF>
 struct Tile {
   static constexpr int NW = NT / 64;
-  static constexpr int LR = VF ? K / 4 : VB / 4;   // lanes covering one memory row
-  static constexpr int RPW = 64 / LR;              // memory rows per wave per load step
-  static constexpr int ROWS = VF ? VB : K;         // memory rows of the tile
-  static constexpr int NS = ROWS / (NW * RPW);     // rows per thread
-  static constexpr int LB = __builtin_ctz(LR);     // lane bits inside a memory row
+  static constexpr int EV = VF ? (K >= 64 ? 8 : 4) : 4;   // floats per thread per memory row
+  static constexpr int LR = VF ? K / EV : VB / 4;         // lanes covering one memory row
+  static constexpr int RPW = 64 / LR;                     // memory rows per wave per load step
+  static constexpr int ROWS = VF ? VB : K;                // memory rows of the tile
+  static constexpr int NS = ROWS / (NW * RPW);            // rows per thread
+  static constexpr int LB = __builtin_ctz(LR);            // lane bits inside a memory row
+  static constexpr int NKEY = VF ? EV : NS;               // key indices a thread touches
+  static constexpr bool KF_RS = !VF && LB == 4 && NW > 1; // K_FIRST reduce-scatter path
   static_assert(NT % 64 == 0, "whole waves");
   static_assert(LR >= 1 && LR <= 64 && 64 % LR == 0, "row must fit a wave");
   static_assert(ROWS % (NW * RPW) == 0 && NS >= 1, "tile must split evenly");
   static_assert(!VF || NS <= LR, "V_FIRST output store uses one lane per row");
   static_assert(K % 4 == 0 && VB % 4 == 0, "128-bit rows");
+  static_assert(!VF || EV == 4 || K / 2 == 4 * LR, "two float4 half a row apart");
 };
 
 template <int K, int VB, int NT, bool VF, bool KDA, bool QDQ, bool PAGED, typename TIn>
 __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   using Cfg = Tile<K, VB, NT, VF>;
   constexpr int NW = Cfg::NW, LR = Cfg::LR, RPW = Cfg::RPW, NS = Cfg::NS, LB = Cfg::LB;
+  constexpr int EV = Cfg::EV, NKEY = Cfg::NKEY;
   constexpr int TC = kTokensPerChunk;
   constexpr int TPW = (TC + NW - 1) / NW;          // tokens per wave in a chunk
   constexpr int EPL = (K + 63) / 64;               // q/k/gate elements per lane (contiguous)
@@ -234,21 +276,19 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   constexpr int VPL = (VB + 63) / 64;              // v elements per lane
   constexpr int VL = VB / VPL;                     // lanes holding v elements
   constexpr int GPL = KDA ? EPL : 1;
-  constexpr int KX = KDA ? K : 1;                  // extent of KDA-only arrays
+  constexpr int KX = KDA ? K : 4;                  // extent of the KDA-only array
   constexpr int TX = KDA ? TC : 1;
-  constexpr int TQ = (KDA && QDQ) ? TC : 1;
-  constexpr int KQ = (KDA && QDQ) ? K : 1;
   static_assert(K % EPL == 0 && VB % VPL == 0, "input split");
 
-  __shared__ __align__(16) float s_q[TC][K];       // reduction coefficient of p (q_hat, KDA: *alpha)
-  __shared__ __align__(16) float s_k[TC][K];       // reduction coefficient of r (k_hat, KDA: *alpha)
-  __shared__ __align__(16) float s_kh[TX][KX];     // KDA: k_hat for the write
+  // Per-token values in LDS.  Key-indexed arrays are stored at lds_pos(key):
+  // V_FIRST keeps key order; K_FIRST stores each thread's NS keys together.
+  __shared__ __align__(16) float s_q[TC][K];       // q_hat
+  __shared__ __align__(16) float s_k[TC][K];       // k_hat
   __shared__ __align__(16) float s_al[TX][KX];     // KDA: alpha per key channel
-  __shared__ __align__(16) float s_qh[TQ][KQ];     // KDA + stored readout: plain q_hat
   __shared__ __align__(16) float s_v[TC][VB];      // this V-block of v
   __shared__ float s_sc[TC][4];                    // alpha (GDN), beta, q_hat . k_hat
   __shared__ __align__(16) float s_red[VF ? 1 : 2][VF ? 1 : NW][2][VB];
-  __shared__ float s_max[NW];
+  __shared__ float s_max[2][NW];
 
   const TIn* __restrict__ gq = static_cast<const TIn*>(p.q);
   const TIn* __restrict__ gk = static_cast<const TIn*>(p.k);
@@ -259,22 +299,36 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
-  const int lr = lane % LR;        // position inside a memory row (x4 floats)
+  const int lr = lane % LR;        // position inside a memory row
   const int rg = lane / LR;        // row group inside the wave
 
   // renumber workgroups: within each span of 8 * G ids, XCD x (id % 8) gets
   // units [x * G, (x + 1) * G) of that span; ids past the last full span keep
-  // their number.  A permutation of [0, gridDim.x) for every G >= 1.
+  // their number.  A permutation of [0, gridDim.x) for every G = 2^gs.
   const int bx = blockIdx.x;
-  const int G = p.xcd_group;
-  const int span = 8 * G;
-  const int nfull = (static_cast<int>(gridDim.x) / span) * span;
-  const int unit = bx < nfull ? (bx / span) * span + (bx % 8) * G + (bx / 8) % G : bx;
-  const int vb = unit % p.nvb;
-  const int h = (unit / p.nvb) % p.HV;
-  const int bs = unit / (p.nvb * p.HV);
-  const int hk = h / p.gqa;
+  const int gs = p.xcd_shift;                       // G = 1 << gs
+  const int nfull = (static_cast<int>(gridDim.x) >> (gs + 3)) << (gs + 3);
+  const int unit = bx < nfull ? (((bx >> (gs + 3)) << (gs + 3)) | ((bx & 7) << gs) | ((bx >> 3) & ((1 << gs) - 1)))
+                              : bx;
+  const int q1 = fast_div(unit, p.div_nvb_m, p.div_nvb_s);
+  const int vb = unit - q1 * p.nvb;
+  const int bs = fast_div(q1, p.div_hv_m, p.div_hv_s);
+  const int h = q1 - bs * p.HV;
+  const int hk = fast_div(h, p.div_gqa_m, p.div_gqa_s);
   const int64_t out_col0 = static_cast<int64_t>(vb) * VB;
+
+  // key index of this thread's key slot m, and the LDS position of key c
+  auto key_of = [&](int m) -> int {
+    if constexpr (VF) return (EV == 8 ? (m / 4) * (K / 2) : 0) + 4 * lr + (m % 4);
+    else return m * (NW * RPW) + w * RPW + rg;
+  };
+  auto lds_pos = [](int c) -> int {
+    if constexpr (VF) return c;
+    else return (c % (NW * RPW)) * NS + c / (NW * RPW);
+  };
+  // first LDS position of this thread's key slots (they are contiguous in
+  // both layouts, per half row for V_FIRST)
+  const int kbase = VF ? 4 * lr : (w * RPW + rg) * NS;
 
   // ---- which tokens
   int t0, t1;
@@ -337,8 +391,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
         }
         float iq = p.scale, ik = 1.0f;
         if (p.l2norm) {
-          iq = p.scale * rsqrtf(lane_sum<0, 6>(ssq) + kL2Eps);
-          ik = rsqrtf(lane_sum<0, 6>(ssk) + kL2Eps);
+          iq = p.scale * rsqrtf(lane_reduce<0, 6>(ssq) + kL2Eps);
+          ik = rsqrtf(lane_reduce<0, 6>(ssk) + kL2Eps);
         }
         float qk = 0.0f;
         if (lane < EL) {
@@ -349,27 +403,17 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
             qk = fmaf(xq[e], xk[e], qk);
           }
         }
-        qk = lane_sum<0, 6>(qk);
+        qk = lane_reduce<0, 6>(qk);
         const float beta = p.beta_prob ? xb[0] : sigmoid_f(xb[0]);
         if (lane < EL) {
-          if constexpr (KDA) {
-            const float rate = expf(p.a_log[h]);
+          const float rate = KDA ? exp_hw(p.a_log[h]) : 0.0f;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-              const int c = EPL * lane + e;
-              const float al = expf(-rate * softplus_f(xg[e] + p.dt_bias[h * K + c]));
-              s_q[tt][c] = xq[e] * al;
-              s_k[tt][c] = xk[e] * al;
-              s_kh[tt][c] = xk[e];
-              s_al[tt][c] = al;
-              if constexpr (QDQ) s_qh[tt][c] = xq[e];
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-              s_q[tt][EPL * lane + e] = xq[e];
-              s_k[tt][EPL * lane + e] = xk[e];
-            }
+          for (int e = 0; e < EPL; ++e) {
+            const int c = EPL * lane + e;
+            const int pos = lds_pos(c);
+            s_q[tt][pos] = xq[e];
+            s_k[tt][pos] = xk[e];
+            if constexpr (KDA) s_al[tt][pos] = exp_hw(-rate * softplus_f(xg[e] + p.dt_bias[h * K + c]));
           }
         }
         if (lane < VL) {
@@ -377,7 +421,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
           for (int e = 0; e < VPL; ++e) s_v[tt][VPL * lane + e] = xv[e];
         }
         if (lane == 0) {
-          if constexpr (!KDA) s_sc[tt][0] = expf(-expf(p.a_log[h]) * softplus_f(xg[0] + p.dt_bias[h]));
+          if constexpr (!KDA) s_sc[tt][0] = exp_hw(-exp_hw(p.a_log[h]) * softplus_f(xg[0] + p.dt_bias[h]));
           s_sc[tt][1] = beta;
           s_sc[tt][2] = qk;
         }
@@ -404,63 +448,105 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   const float* src = p.pool + (rrow * p.HV + h) * tile_elems;
   float* dst = p.pool + (wrow * p.HV + h) * tile_elems;
 
-  // memory offset of this thread's row s (start of its 4 floats)
   auto row_idx = [&](int s) -> int { return s * (NW * RPW) + w * RPW + rg; };
-  auto row_off = [&](int s) -> int64_t {
-    if constexpr (VF) return static_cast<int64_t>(vb * VB + row_idx(s)) * K + 4 * lr;
+  // memory offset of this thread's float4 number f (0 .. EV/4-1) in row s
+  auto row_off = [&](int s, int f) -> int64_t {
+    if constexpr (VF) return static_cast<int64_t>(vb * VB + row_idx(s)) * K + f * (K / 2) + 4 * lr;
     else return static_cast<int64_t>(row_idx(s)) * p.V + vb * VB + 4 * lr;
   };
 
-  float S[NS][4];
+  float S[NS][EV];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + row_off(s)));
-    S[s][0] = x.x;
-    S[s][1] = x.y;
-    S[s][2] = x.z;
-    S[s][3] = x.w;
-  }
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int f = 0; f < EV / 4; ++f) {
+      const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + row_off(s, f)));
+      S[s][4 * f + 0] = x.x;
+      S[s][4 * f + 1] = x.y;
+      S[s][4 * f + 2] = x.z;
+      S[s][4 * f + 3] = x.w;
+    }
 
   finish_raw(n0);                  // overlaps the tile load
 
-  int red_buf = 0;
+  // true state = scale * S: one scale (GDN) or one per key slot (KDA)
+  constexpr int NC = KDA ? NKEY : 1;
+  float cs[NC];
+#pragma unroll
+  for (int m = 0; m < NC; ++m) cs[m] = 1.0f;
+  // key slot of element (s, e)
+  auto slot = [](int s, int e) -> int { return VF ? e : s; };
+
+  int red_buf = 0, max_buf = 0;
 
   auto block_max = [&](float m) -> float {
-    m = lane_max<6>(m);
+    m = lane_reduce<0, 6, OpMax>(m);
     if constexpr (NW > 1) {
-      __syncthreads();             // previous readers of s_max are done
-      if (lane == 0) s_max[w] = m;
+      if (lane == 0) s_max[max_buf][w] = m;
       __syncthreads();
-      m = s_max[0];
+      m = s_max[max_buf][0];
 #pragma unroll
-      for (int i = 1; i < NW; ++i) m = fmaxf(m, s_max[i]);
+      for (int i = 1; i < NW; ++i) m = fmaxf(m, s_max[max_buf][i]);
+      max_buf ^= 1;
     }
     return m;
   };
 
+  // fp8 tile QDQ of the true state; the codes stay in S, the tile scale goes to cs
   auto qdq_tile = [&]() {
     float m = 0.0f;
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(S[s][e]));
-    m = block_max(m);
-    if (m > 0.0f) {
-      const float inv = kE4M3Max / m;
-      const float sc = m / kE4M3Max;
+    if constexpr (!KDA) {
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          float x0 = S[s][e] * inv, x1 = S[s][e + 1] * inv;
-          e4m3_roundtrip2(x0, x1);
-          S[s][e] = x0 * sc;
-          S[s][e + 1] = x1 * sc;
-        }
+        for (int e = 0; e < EV; ++e) m = fmaxf(m, fabsf(S[s][e]));
+      const float ms = block_max(m);       // amax of S_reg; the true amax is cs[0] * ms
+      if (ms > 0.0f) {
+        const float inv = kE4M3Max / ms;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+          for (int e = 0; e < EV; e += 2) {
+            float x0 = S[s][e] * inv, x1 = S[s][e + 1] * inv;
+            e4m3_roundtrip2(x0, x1);
+            S[s][e] = x0;
+            S[s][e + 1] = x1;
+          }
+        cs[0] = cs[0] * (ms / kE4M3Max);
+      }
+    } else {
+      float rowm[NC];
+#pragma unroll
+      for (int k2 = 0; k2 < NC; ++k2) rowm[k2] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int e = 0; e < EV; ++e) rowm[slot(s, e)] = fmaxf(rowm[slot(s, e)], fabsf(S[s][e]));
+#pragma unroll
+      for (int k2 = 0; k2 < NC; ++k2) m = fmaxf(m, cs[k2] * rowm[k2]);
+      const float mt = block_max(m);       // true amax
+      if (mt > 0.0f) {
+        const float inv = kE4M3Max / mt;
+        float f[NC];
+#pragma unroll
+        for (int k2 = 0; k2 < NC; ++k2) f[k2] = cs[k2] * inv;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+          for (int e = 0; e < EV; e += 2) {
+            float x0 = S[s][e] * f[slot(s, e)], x1 = S[s][e + 1] * f[slot(s, e + 1)];
+            e4m3_roundtrip2(x0, x1);
+            S[s][e] = x0;
+            S[s][e + 1] = x1;
+          }
+        const float sc = mt / kE4M3Max;
+#pragma unroll
+        for (int k2 = 0; k2 < NC; ++k2) cs[k2] = sc;
+      }
     }
   };
 
-  // store 4 consecutive outputs (K_FIRST) or one (V_FIRST)
+  // output stores: 4 consecutive values (K_FIRST) or one (V_FIRST)
   auto store_out4 = [&](int64_t oi, const float (&o)[4]) {
     if (p.out_bf16) {
       uint2 pk;
@@ -476,35 +562,111 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
     else static_cast<float*>(p.out)[oi] = o;
   };
 
-  // K_FIRST: wave-level partial sums over this thread's rows -> block sums via LDS.
-  // Lanes of a wave with equal lr hold the same 4 columns; they differ in lane bits >= LB.
-  auto kfirst_reduce = [&](float (&r)[4], float (&pp)[4], bool need_p) {
+  // load NKEY consecutive LDS floats starting at pos (float4 pieces)
+  auto lds_keys = [&](const float* base, float (&x)[NKEY]) {
+    if constexpr (VF) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      r[e] = lane_sum<LB, 6>(r[e]);
-      if (need_p) pp[e] = lane_sum<LB, 6>(pp[e]);
+      for (int f = 0; f < EV / 4; ++f) {
+        const float4 v = *reinterpret_cast<const float4*>(base + f * (K / 2) + kbase);
+        x[4 * f + 0] = v.x; x[4 * f + 1] = v.y; x[4 * f + 2] = v.z; x[4 * f + 3] = v.w;
+      }
+    } else if constexpr (NS % 4 == 0) {
+#pragma unroll
+      for (int f = 0; f < NS / 4; ++f) {
+        const float4 v = *reinterpret_cast<const float4*>(base + kbase + 4 * f);
+        x[4 * f + 0] = v.x; x[4 * f + 1] = v.y; x[4 * f + 2] = v.z; x[4 * f + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NKEY; ++m) x[m] = base[kbase + m];
+    }
+  };
+
+  // K_FIRST: per-thread partial sums over its rows -> block sums of r and p for its 4 columns
+  auto kfirst_reduce = [&](float (&r)[4], float (&pp)[4]) {
+    if constexpr (Cfg::KF_RS) {
+      // lanes of a wave with equal lr hold the same columns and differ in lane bits 4, 5
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = rs_halves32(r[e], pp[e]);   // lanes < 32: r_e, else p_e
+      const float y0 = rs_rows16(x[0], x[1]);                        // column par
+      const float y1 = rs_rows16(x[2], x[3]);                        // column par + 2
+      const int kind = lane >> 5;
+      const int par = (lane >> 4) & 1;
+      s_red[red_buf][w][kind][4 * lr + par] = y0;
+      s_red[red_buf][w][kind][4 * lr + par + 2] = y1;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        r[e] = lane_reduce<LB, 6>(r[e]);
+        pp[e] = lane_reduce<LB, 6>(pp[e]);
+      }
+      if constexpr (NW > 1) {
+        if (rg == 0) {
+          *reinterpret_cast<float4*>(&s_red[red_buf][w][0][4 * lr]) = make_float4(r[0], r[1], r[2], r[3]);
+          *reinterpret_cast<float4*>(&s_red[red_buf][w][1][4 * lr]) = make_float4(pp[0], pp[1], pp[2], pp[3]);
+        }
+      }
     }
     if constexpr (NW > 1) {
-      if (rg == 0) {
-        *reinterpret_cast<float4*>(&s_red[red_buf][w][0][4 * lr]) = make_float4(r[0], r[1], r[2], r[3]);
-        if (need_p)
-          *reinterpret_cast<float4*>(&s_red[red_buf][w][1][4 * lr]) = make_float4(pp[0], pp[1], pp[2], pp[3]);
-      }
       __syncthreads();
       float4 ra = *reinterpret_cast<const float4*>(&s_red[red_buf][0][0][4 * lr]);
-      float4 pa = need_p ? *reinterpret_cast<const float4*>(&s_red[red_buf][0][1][4 * lr]) : float4{};
+      float4 pa = *reinterpret_cast<const float4*>(&s_red[red_buf][0][1][4 * lr]);
 #pragma unroll
       for (int ww = 1; ww < NW; ++ww) {
         const float4 x = *reinterpret_cast<const float4*>(&s_red[red_buf][ww][0][4 * lr]);
+        const float4 y = *reinterpret_cast<const float4*>(&s_red[red_buf][ww][1][4 * lr]);
         ra.x += x.x; ra.y += x.y; ra.z += x.z; ra.w += x.w;
-        if (need_p) {
-          const float4 y = *reinterpret_cast<const float4*>(&s_red[red_buf][ww][1][4 * lr]);
-          pa.x += y.x; pa.y += y.y; pa.z += y.z; pa.w += y.w;
-        }
+        pa.x += y.x; pa.y += y.y; pa.z += y.z; pa.w += y.w;
       }
       r[0] = ra.x; r[1] = ra.y; r[2] = ra.z; r[3] = ra.w;
       pp[0] = pa.x; pp[1] = pa.y; pp[2] = pa.z; pp[3] = pa.w;
       red_buf ^= 1;
+    }
+  };
+
+  // one pass: r = kr^T S and p = qr^T S over K, complete sums for this thread's outputs
+  // (K_FIRST: its 4 columns; V_FIRST: its NS rows)
+  constexpr int NO = VF ? NS : 4;
+  auto reduce_pass = [&](const float (&kr)[NKEY], const float (&qr)[NKEY], float (&r)[NO], float (&pp)[NO]) {
+    if constexpr (!VF) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        r[e] = kr[0] * S[0][e];
+        pp[e] = qr[0] * S[0][e];
+      }
+#pragma unroll
+      for (int s = 1; s < NS; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          r[e] = fmaf(kr[s], S[s][e], r[e]);
+          pp[e] = fmaf(qr[s], S[s][e], pp[e]);
+        }
+      kfirst_reduce(r, pp);
+    } else {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        float a = kr[0] * S[s][0], b = qr[0] * S[s][0];
+#pragma unroll
+        for (int e = 1; e < EV; ++e) {
+          a = fmaf(kr[e], S[s][e], a);
+          b = fmaf(qr[e], S[s][e], b);
+        }
+        r[s] = lane_reduce<0, LB>(a);
+        pp[s] = lane_reduce<0, LB>(b);
+      }
+    }
+  };
+
+  auto store_outputs = [&](int64_t out_row, const float (&o)[NO]) {
+    if constexpr (!VF) {
+      if (w == 0 && rg == 0) store_out4(out_row + 4 * lr, o);
+    } else {
+      float my_o = o[0];
+#pragma unroll
+      for (int s = 1; s < NS; ++s)
+        if (lr == s) my_o = o[s];
+      if (lr < NS) store_out1(out_row + row_idx(lr), my_o);
     }
   };
 
@@ -525,115 +687,98 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
       const int t = c0 + tt;
       const float beta = s_sc[tt][1];
       const float qk = s_sc[tt][2];
-      const float alpha = KDA ? 1.0f : s_sc[tt][0];   // GDN alpha is applied after the reduction
       const int64_t out_row = (static_cast<int64_t>(t) * p.HV + h) * p.V + out_col0;
       const bool stored = QDQ && p.readout_stored;
 
-      if constexpr (!VF) {
-        // K_FIRST: rows are key indices, 4 value columns per thread
-        float r[4] = {0.f, 0.f, 0.f, 0.f}, pp[4] = {0.f, 0.f, 0.f, 0.f};
+      float kh[NKEY], qh[NKEY];
+      lds_keys(&s_k[tt][0], kh);
+      lds_keys(&s_q[tt][0], qh);
+
+      // decay into the scale; reduction and write coefficients
+      float kr[NKEY], qr[NKEY], kt[NKEY];
+      float cn_g = 1.0f, icn_g = 1.0f;
+      if constexpr (!KDA) {
+        float cn = cs[0] * s_sc[tt][0];
+        if (cn < kTinyScale) {                 // uniform: one scale per workgroup
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const int i = row_idx(s);
-          const float kr = s_k[tt][i], qr = s_q[tt][i];
+          for (int s = 0; s < NS; ++s)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            r[e] = fmaf(kr, S[s][e], r[e]);
-            pp[e] = fmaf(qr, S[s][e], pp[e]);
-          }
+            for (int e = 0; e < EV; ++e) S[s][e] *= cn;
+          cn = 1.0f;
         }
-        kfirst_reduce(r, pp, true);
-        float u[4], o[4];
-        const float4 v4 = *reinterpret_cast<const float4*>(&s_v[tt][4 * lr]);
-        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+        cs[0] = cn;
+        cn_g = cn;
+        icn_g = rcp_hw(cn);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          u[e] = beta * (vv[e] - alpha * r[e]);
-          o[e] = fmaf(qk, u[e], alpha * pp[e]);
-        }
-        const bool writer = (w == 0 && rg == 0);
-        if (!stored && writer) store_out4(out_row + 4 * lr, o);
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const int i = row_idx(s);
-          const float a_s = KDA ? s_al[tt][i] : alpha;
-          const float kh = KDA ? s_kh[tt][i] : s_k[tt][i];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) S[s][e] = fmaf(a_s, S[s][e], kh * u[e]);
-        }
-        if constexpr (QDQ) {
-          qdq_tile();
-          if (stored) {
-            // o = q_hat^T S after rounding
-            float ps[4] = {0.f, 0.f, 0.f, 0.f}, dummy[4];
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-              const int i = row_idx(s);
-              const float qh = KDA ? s_qh[tt][i] : s_q[tt][i];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) ps[e] = fmaf(qh, S[s][e], ps[e]);
-            }
-            kfirst_reduce(ps, dummy, false);
-            if (writer) store_out4(out_row + 4 * lr, ps);
-          }
+        for (int m = 0; m < NKEY; ++m) {
+          kr[m] = kh[m];
+          qr[m] = qh[m];
+          kt[m] = kh[m];
         }
       } else {
-        // V_FIRST: rows are value columns j, 4 key elements per thread
-        const float4 kr4 = *reinterpret_cast<const float4*>(&s_k[tt][4 * lr]);
-        const float4 qr4 = *reinterpret_cast<const float4*>(&s_q[tt][4 * lr]);
-        float r[NS], pp[NS];
+        float al[NKEY], cn[NKEY];
+        lds_keys(&s_al[tt][0], al);
+        bool tiny = false;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          r[s] = fmaf(kr4.w, S[s][3], fmaf(kr4.z, S[s][2], fmaf(kr4.y, S[s][1], kr4.x * S[s][0])));
-          pp[s] = fmaf(qr4.w, S[s][3], fmaf(qr4.z, S[s][2], fmaf(qr4.y, S[s][1], qr4.x * S[s][0])));
+        for (int m = 0; m < NKEY; ++m) {
+          cn[m] = cs[m] * al[m];
+          tiny |= cn[m] < kTinyScale;
         }
+        if (tiny) {                            // rare: apply small factors to their key rows
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          r[s] = lane_sum<0, LB>(r[s]);
-          pp[s] = lane_sum<0, LB>(pp[s]);
-        }
-        float u[NS];
-        float my_o = 0.0f;
+          for (int m = 0; m < NKEY; ++m) {
+            const float f = cn[m] < kTinyScale ? cn[m] : 1.0f;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          u[s] = beta * (s_v[tt][row_idx(s)] - alpha * r[s]);
-          const float os = fmaf(qk, u[s], alpha * pp[s]);
-          if (lr == s) my_o = os;
-        }
-        if (!stored && lr < NS) store_out1(out_row + row_idx(lr), my_o);
-        float al4[4], kh4[4];
-        if constexpr (KDA) {
-          const float4 a = *reinterpret_cast<const float4*>(&s_al[tt][4 * lr]);
-          const float4 kk = *reinterpret_cast<const float4*>(&s_kh[tt][4 * lr]);
-          al4[0] = a.x; al4[1] = a.y; al4[2] = a.z; al4[3] = a.w;
-          kh4[0] = kk.x; kh4[1] = kk.y; kh4[2] = kk.z; kh4[3] = kk.w;
-        } else {
-          al4[0] = al4[1] = al4[2] = al4[3] = alpha;
-          kh4[0] = kr4.x; kh4[1] = kr4.y; kh4[2] = kr4.z; kh4[3] = kr4.w;
-        }
+            for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) S[s][e] = fmaf(al4[e], S[s][e], kh4[e] * u[s]);
-        if constexpr (QDQ) {
-          qdq_tile();
-          if (stored) {
-            float q4[4];
-            if constexpr (KDA) {
-              const float4 qq = *reinterpret_cast<const float4*>(&s_qh[tt][4 * lr]);
-              q4[0] = qq.x; q4[1] = qq.y; q4[2] = qq.z; q4[3] = qq.w;
-            } else {
-              q4[0] = qr4.x; q4[1] = qr4.y; q4[2] = qr4.z; q4[3] = qr4.w;
-            }
-            float mo = 0.0f;
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-              float ps = fmaf(q4[3], S[s][3], fmaf(q4[2], S[s][2], fmaf(q4[1], S[s][1], q4[0] * S[s][0])));
-              ps = lane_sum<0, LB>(ps);
-              if (lr == s) mo = ps;
-            }
-            if (lr < NS) store_out1(out_row + row_idx(lr), mo);
+              for (int e = 0; e < EV; ++e)
+                if (slot(s, e) == m) S[s][e] *= f;
+            cn[m] = cn[m] < kTinyScale ? 1.0f : cn[m];
           }
+        }
+#pragma unroll
+        for (int m = 0; m < NKEY; ++m) {
+          cs[m] = cn[m];
+          kr[m] = kh[m] * cn[m];
+          qr[m] = qh[m] * cn[m];
+          kt[m] = kh[m] * rcp_hw(cn[m]);
+        }
+      }
+
+      float r[NO], pp[NO];
+      reduce_pass(kr, qr, r, pp);
+
+      float u[NO], o[NO], wv[NO];
+#pragma unroll
+      for (int j = 0; j < NO; ++j) {
+        const int col = VF ? row_idx(j) : 4 * lr + j;
+        const float rr = KDA ? r[j] : cn_g * r[j];
+        const float pj = KDA ? pp[j] : cn_g * pp[j];
+        u[j] = beta * (s_v[tt][col] - rr);
+        o[j] = fmaf(qk, u[j], pj);
+        wv[j] = KDA ? u[j] : u[j] * icn_g;
+      }
+      if (!stored) store_outputs(out_row, o);
+
+      // S_reg += kt (x) wv
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int e = 0; e < EV; ++e) {
+          if constexpr (VF) S[s][e] = fmaf(kt[e], wv[s], S[s][e]);
+          else S[s][e] = fmaf(kt[s], wv[e], S[s][e]);
+        }
+
+      if constexpr (QDQ) {
+        qdq_tile();
+        if (stored) {
+          // o = q_hat^T S after rounding
+          float q2[NKEY];
+#pragma unroll
+          for (int m = 0; m < NKEY; ++m) q2[m] = qh[m] * cs[KDA ? m : 0];
+          float ps[NO], dummy[NO];
+          reduce_pass(q2, q2, ps, dummy);
+          store_outputs(out_row, ps);
         }
       }
     }
@@ -641,7 +786,15 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
 
 #pragma unroll
   for (int s = 0; s < NS; ++s)
-    *reinterpret_cast<float4*>(dst + row_off(s)) = make_float4(S[s][0], S[s][1], S[s][2], S[s][3]);
+#pragma unroll
+    for (int f = 0; f < EV / 4; ++f) {
+      float4 x;
+      x.x = S[s][4 * f + 0] * cs[KDA ? slot(s, 4 * f + 0) : 0];
+      x.y = S[s][4 * f + 1] * cs[KDA ? slot(s, 4 * f + 1) : 0];
+      x.z = S[s][4 * f + 2] * cs[KDA ? slot(s, 4 * f + 2) : 0];
+      x.w = S[s][4 * f + 3] * cs[KDA ? slot(s, 4 * f + 3) : 0];
+      *reinterpret_cast<float4*>(dst + row_off(s, f)) = x;
+    }
 }
 
 }  // namespace gdn

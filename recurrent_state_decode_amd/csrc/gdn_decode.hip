@@ -161,6 +161,16 @@ int check_dims(int32_t B, int32_t HK, int32_t HV, int32_t K, int32_t V) {
   return GDN_OK;
 }
 
+// n / d == (n * m) >> s for every 0 <= n < 2^31, with s = 31 + ceil(log2 d)
+// and m = floor(2^s / d) + 1 (the error term n (m d - 2^s) / (d 2^s) stays
+// below 1/d).
+void fast_div_consts(uint32_t d, uint64_t& m, int32_t& s) {
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  s = 31 + l;
+  m = ((1ull << s) / d) + 1;
+}
+
 void fill_common(gdn::Params& p, const gdn_options* o, int32_t B, int32_t T, int32_t HK, int32_t HV, int32_t K,
                  int32_t V) {
   p.B = B;
@@ -169,7 +179,10 @@ void fill_common(gdn::Params& p, const gdn_options* o, int32_t B, int32_t T, int
   p.V = V;
   const Shape sh = shape_for(K, o->state_layout == GDN_V_FIRST, o->qdq != GDN_QDQ_NONE, T, B);
   p.nvb = V / sh.VB;
-  p.xcd_group = 64;
+  p.xcd_shift = 6;   // 64 consecutive work units per XCD
+  fast_div_consts(static_cast<uint32_t>(p.nvb), p.div_nvb_m, p.div_nvb_s);
+  fast_div_consts(static_cast<uint32_t>(HV), p.div_hv_m, p.div_hv_s);
+  fast_div_consts(static_cast<uint32_t>(HV / HK), p.div_gqa_m, p.div_gqa_s);
   p.gqa = HV / HK;
   p.scale = o->scale > 0.0f ? o->scale : 1.0f / std::sqrt(static_cast<float>(K));
   p.l2norm = o->use_qk_l2norm ? 1 : 0;

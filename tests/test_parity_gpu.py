@@ -214,8 +214,9 @@ def test_two_calls_equal_one_call_on_gpu():
                          w.num_rows, w.inputs, w.options)
         P.gpu_call(w2, pool2, sub)
     torch.cuda.synchronize()
-    # same per-token arithmetic in both schedules: the states agree bit for bit
-    assert torch.equal(pool1, pool2)
+    # the kernel keeps the state as scale * registers inside a call, so a split
+    # call rounds differently; the two schedules agree to float32 accuracy
+    torch.testing.assert_close(pool1, pool2, rtol=1e-5, atol=1e-6)
     assert cu[-1] == 8
 
 
