@@ -49,14 +49,19 @@ def algorithmic_bytes(w):
     import torch
     esz = 2 if w.io_dtype == torch.bfloat16 else 4
     osz = 2 if w.out_dtype == torch.bfloat16 else 4
-    if w.kind == "gdn_paged" or w.inputs.get("cu_seqlens") is None:
+    if w.kind in ("gdn_paged", "kda_paged") or w.inputs.get("cu_seqlens") is None:
         active = w.B
     else:
         active = int(np.sum(np.diff(w.inputs["cu_seqlens"].numpy()) > 0))
     state = 2 * active * w.HV * w.K * w.V * 4
+    if w.kind.endswith("paged_varlen"):
+        # one tile read per sequence; every page a suffix fills or ends on is written
+        from tests import parity as P
+        n_writes = len(P.rows_for(w)[1])
+        state = (active + n_writes) * w.HV * w.K * w.V * 4
     T = w.T
     per_tok = 2 * w.HK * w.K * esz + w.HV * w.V * esz + w.HV * w.V * osz
-    if w.kind == "kda_pooled":
+    if w.kind.startswith("kda"):
         per_tok += w.HV * w.K * esz + w.HV * esz
     else:
         per_tok += 2 * w.HV * esz
@@ -195,7 +200,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="paged_gdn_b256",
                     choices=["paged_gdn_b256", "pooled_gdn_b64", "pooled_kda_varlen_b128", "fp8_qdq_gdn_b512",
-                             "tiny_gdn"])
+                             "tiny_gdn", "paged_kda_b256", "paged_gdn_varlen_b256_t4"])
     ap.add_argument("--layout", default=None, help="override the pool layout (K_FIRST / V_FIRST)")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
@@ -231,8 +236,9 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     maker = wl.NAMED[args.workload]
-    w = maker(state_layout=args.layout) if (args.layout and args.workload == "paged_gdn_b256") else maker()
-    if args.layout and args.workload != "paged_gdn_b256":
+    paged_makers = ("paged_gdn_b256", "paged_kda_b256", "paged_gdn_varlen_b256_t4")
+    w = maker(state_layout=args.layout) if (args.layout and args.workload in paged_makers) else maker()
+    if args.layout and args.workload not in paged_makers:
         w.state_layout = args.layout
     d = P.device_inputs(w, dev)
     pool = wl.make_pool(w, dev)

@@ -107,6 +107,10 @@ typedef struct gdn_options {
   int32_t block_v;          /* QDQ tile width over V; must divide V           (default 64) */
   int32_t quantize_initial; /* 1: also round the state read before the first token (default 0) */
   int32_t readout;          /* gdn_readout                                     (default WORKING) */
+  const int64_t* slots;     /* single-token paged calls only: device [B][2] (read row, write row)
+                               from gdn_paged_decode_slots() for the same page table, or NULL to
+                               resolve the rows inside the call (default NULL).  Not checked
+                               against the table (flashinfer.gdn_paged, slots). */
 } gdn_options;
 
 /* Fill `opt` with the defaults listed above.  `opt` must not be NULL. */
@@ -188,6 +192,64 @@ int kda_decode_pooled(const void* q, const void* k, const void* v, const void* r
                       const int32_t* cu_seqlens, const int32_t* state_indices, float* state_pool,
                       void* out, int32_t B, int32_t T, int32_t HK, int32_t HV, int32_t K, int32_t V,
                       int64_t num_slots, const gdn_options* opt, void* stream);
+
+/*
+ * kda_decode_paged -- single-token KDA decode on a CSR-paged pool: the paging
+ * of gdn_decode_paged (flashinfer.gdn_paged.gated_delta_rule_decode_paged)
+ * with the per-key-channel gate and the inputs of kda_decode_pooled
+ * (max.nn.state_space.kda_decode).  q, k [B, HK, K]; v [B, HV, V];
+ * raw_gate [B, HV, K]; beta_logits [B, HV]; a_log [HV]; dt_bias [HV, K];
+ * table, pool and out as for gdn_decode_paged.
+ */
+int kda_decode_paged(const void* q, const void* k, const void* v, const void* raw_gate,
+                     const void* beta_logits, const float* a_log, const float* dt_bias,
+                     const void* page_indices, const void* page_indptr, const void* last_page_len,
+                     float* state_pool, void* out, int32_t B, int32_t HK, int32_t HV, int32_t K,
+                     int32_t V, int64_t num_pages, int64_t nnz, const gdn_options* opt, void* stream);
+
+/*
+ * gdn_decode_paged_varlen / kda_decode_paged_varlen -- several decoded tokens
+ * per sequence on a CSR-paged pool (the single-token rule of
+ * flashinfer.gdn_paged.gated_delta_rule_decode_paged, applied token by
+ * token).  cu_seqlens [B+1] (i32, device) gives each sequence's suffix in
+ * the token axis, as in max.nn.state_space.kda_decode.  The page table
+ * describes the sequences after the suffix: sequence b holds
+ * n_b = (pages_b - 1) * page_size + last_page_len[b] tokens and the suffix is
+ * its last T_b tokens; at least one token precedes the suffix.  The state is
+ * read from the page holding token n_b - T_b; after a suffix token that fills
+ * its page (position a multiple of page_size) the state is written to that
+ * page; the final state is written to the last page.  Pages that hold no
+ * suffix token are never written; pages a suffix writes must belong to that
+ * sequence alone (not checked).  q, k [T, HK, K], v [T, HV, V], out
+ * [T, HV, V]; other inputs as for the single-token calls with T rows.
+ * opt->slots must be NULL.
+ */
+int gdn_decode_paged_varlen(const void* q, const void* k, const void* v, const void* a, const void* b,
+                            const float* A_log, const float* dt_bias, const int32_t* cu_seqlens,
+                            const void* page_indices, const void* page_indptr,
+                            const void* last_page_len, int32_t page_size, float* state_pool,
+                            void* out, int32_t B, int32_t T, int32_t HK, int32_t HV, int32_t K,
+                            int32_t V, int64_t num_pages, int64_t nnz, const gdn_options* opt,
+                            void* stream);
+int kda_decode_paged_varlen(const void* q, const void* k, const void* v, const void* raw_gate,
+                            const void* beta_logits, const float* a_log, const float* dt_bias,
+                            const int32_t* cu_seqlens, const void* page_indices,
+                            const void* page_indptr, const void* last_page_len, int32_t page_size,
+                            float* state_pool, void* out, int32_t B, int32_t T, int32_t HK,
+                            int32_t HV, int32_t K, int32_t V, int64_t num_pages, int64_t nnz,
+                            const gdn_options* opt, void* stream);
+
+/*
+ * gdn_paged_decode_slots -- the (read row, write row) pair of every sequence
+ * for a single-token paged decode step, written to slots [B][2] (int64,
+ * device).  Computed once per step and passed to every layer's call through
+ * gdn_options.slots (flashinfer.gdn_paged.gated_delta_rule_decode_paged,
+ * slots).  page_indices / page_indptr / last_page_len as for gdn_decode_paged,
+ * of type index_dtype (GDN_I32 or GDN_I64).  Asynchronous on stream.
+ */
+int gdn_paged_decode_slots(const void* page_indices, const void* page_indptr,
+                           const void* last_page_len, int32_t B, int32_t index_dtype,
+                           int64_t* slots, void* stream);
 
 /* Static name of a status code ("GDN_OK", ...); "unknown status" otherwise. */
 const char* gdn_status_string(int status);

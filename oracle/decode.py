@@ -123,6 +123,89 @@ def kda_decode_pooled(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens
     return out, written
 
 
+def _paged_varlen(kind, q, k, v, gate, beta_in, A_log, dt_bias, cu_seqlens, page_indices, page_indptr,
+                  last_page_len, page_size, pool, scale, use_qk_l2norm, beta_mode, state_layout, qdq, block_v,
+                  quantize_initial, readout, seqs, trace):
+    """Several decoded tokens per sequence on a CSR-paged pool (see paging.paged_suffix_rows).
+
+    Each page that a suffix token fills receives the state after that token;
+    the last page receives the final state.  Rows are written in token order.
+    """
+    T, HK, K = q.shape
+    HV, V = v.shape[1], v.shape[2]
+    B = len(cu_seqlens) - 1
+    hk_of_h = _key_head_map(HK, HV)
+    qdq_fn = _qdq_fn(qdq, block_v)
+    out = np.full((T, HV, V), np.nan)
+    written = {}
+    for bi in (range(B) if seqs is None else seqs):
+        t0, t1 = paging.pooled_token_range(cu_seqlens, bi)
+        if t1 <= t0:
+            continue
+        r, writes = paging.paged_suffix_rows(page_indices, page_indptr, last_page_len, page_size, t1 - t0, bi)
+        if kind == "kda":
+            alpha = np.exp(act.kda_log_gate(A_log, gate[t0:t1], dt_bias))
+        else:
+            alpha = np.exp(act.gdn_log_gate(A_log, gate[t0:t1], dt_bias))
+        beta = act.beta_from(beta_in[t0:t1], beta_mode)
+        S = pool[r]
+        done = 0
+        for i, row in writes:
+            # tokens done..i: the state carries over between pieces of the suffix
+            o, S = _run_one(S, state_layout, q[t0 + done:t0 + i + 1], k[t0 + done:t0 + i + 1],
+                            v[t0 + done:t0 + i + 1], alpha[done:i + 1], beta[done:i + 1], hk_of_h, scale,
+                            use_qk_l2norm, qdq_fn, quantize_initial and done == 0, readout,
+                            None if trace is None else trace.setdefault(bi, []))
+            out[t0 + done:t0 + i + 1] = o
+            written[row] = S
+            done = i + 1
+    return out, written
+
+
+def gdn_decode_paged_varlen(q, k, v, a, b, A_log, dt_bias, cu_seqlens, page_indices, page_indptr,
+                            last_page_len, page_size, pool, *, scale=None, use_qk_l2norm=True,
+                            beta_mode="logits", state_layout="V_FIRST", qdq=None, block_v=64,
+                            quantize_initial=False, readout="working", seqs=None, trace=None):
+    """GDN decode of varlen suffixes on a CSR-paged pool; cu_seqlens [B+1] as in kda_decode."""
+    return _paged_varlen("gdn", q, k, v, a, b, A_log, dt_bias, cu_seqlens, page_indices, page_indptr,
+                         last_page_len, page_size, pool, scale, use_qk_l2norm, beta_mode, state_layout, qdq,
+                         block_v, quantize_initial, readout, seqs, trace)
+
+
+def kda_decode_paged_varlen(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, page_indices, page_indptr,
+                            last_page_len, page_size, pool, *, scale=None, use_qk_l2norm=True,
+                            beta_mode="logits", state_layout="V_FIRST", qdq=None, block_v=64,
+                            quantize_initial=False, readout="working", seqs=None, trace=None):
+    """KDA decode of varlen suffixes on a CSR-paged pool (per-key-channel gate)."""
+    return _paged_varlen("kda", q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, page_indices,
+                         page_indptr, last_page_len, page_size, pool, scale, use_qk_l2norm, beta_mode,
+                         state_layout, qdq, block_v, quantize_initial, readout, seqs, trace)
+
+
+def kda_decode_paged(q, k, v, raw_gate, beta_logits, a_log, dt_bias, page_indices, page_indptr, last_page_len,
+                     pool, *, scale=None, use_qk_l2norm=True, beta_mode="logits", state_layout="V_FIRST",
+                     qdq=None, block_v=64, quantize_initial=False, readout="working", seqs=None, trace=None):
+    """Single-token KDA decode on a CSR-paged pool: the paging of gated_delta_rule_decode_paged
+    (flashinfer.gdn_paged) with the gate of kda_decode (max.nn.state_space)."""
+    B, HK, K = q.shape
+    HV, V = v.shape[1], v.shape[2]
+    hk_of_h = _key_head_map(HK, HV)
+    qdq_fn = _qdq_fn(qdq, block_v)
+    out = np.full((B, HV, V), np.nan)
+    written = {}
+    for bi in (range(B) if seqs is None else seqs):
+        r, w = paging.paged_rows(page_indices, page_indptr, last_page_len, bi)
+        sl = slice(bi, bi + 1)
+        alpha = np.exp(act.kda_log_gate(a_log, raw_gate[sl], dt_bias))
+        beta = act.beta_from(beta_logits[sl], beta_mode)
+        o, tile = _run_one(pool[r], state_layout, q[sl], k[sl], v[sl], alpha, beta, hk_of_h,
+                           scale, use_qk_l2norm, qdq_fn, quantize_initial, readout,
+                           None if trace is None else trace.setdefault(bi, []))
+        out[bi] = o[0]
+        written[w] = tile
+    return out, written
+
+
 def gdn_decode_paged(q, k, v, a, b, A_log, dt_bias, page_indices, page_indptr, last_page_len,
                      pool, *, scale=None, use_qk_l2norm=True, beta_mode="logits",
                      state_layout="V_FIRST", qdq=None, block_v=64, quantize_initial=False,

@@ -46,6 +46,35 @@ def paged_rows(page_indices, page_indptr, last_page_len, b):
     return last, last
 
 
+def paged_suffix_rows(page_indices, page_indptr, last_page_len, page_size, n_suffix, b):
+    """Rows touched by a suffix of ``n_suffix`` tokens of sequence b on a CSR-paged pool.
+
+    Extends the single-token rule of gated_delta_rule_decode_paged
+    (flashinfer.gdn_paged, description) to several appended tokens, with the
+    same model that rule follows: the state after token m lives on the page
+    that holds token m.  The sequence holds n = (pages - 1) * page_size +
+    last_page_len tokens after the suffix, the suffix is tokens
+    n - n_suffix + 1 .. n (1-based), and at least one token precedes it
+    (flashinfer.gdn_paged, Notes).
+
+    Returns (read row, [(i, row), ...]): the state is read from the page of
+    token n - n_suffix; after suffix token i (0-based) it is written to
+    ``row`` when that token fills its page or is the last token.
+    """
+    start = int(page_indptr[b])
+    n = (int(page_indptr[b + 1]) - start - 1) * page_size + int(last_page_len[b])
+    m0 = n - n_suffix + 1
+    if m0 < 2:
+        raise ValueError("a paged suffix needs at least one token before it")
+    page_of = lambda m: int(page_indices[start + (m - 1) // page_size])
+    writes = []
+    for i in range(n_suffix):
+        m = m0 + i
+        if m % page_size == 0 or m == n:
+            writes.append((i, page_of(m)))
+    return page_of(m0 - 1), writes
+
+
 def to_logical(tile, state_layout):
     """Pool tile -> logical S[..., K, V].  K_FIRST stores (K, V); V_FIRST stores (V, K)."""
     if state_layout == "K_FIRST":

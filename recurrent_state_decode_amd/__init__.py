@@ -9,7 +9,11 @@ from ._binding import (  # noqa: F401
     GdnError,
     LIB_PATH,
     gdn_decode_paged,
+    gdn_decode_paged_varlen,
     gdn_decode_pooled,
+    gdn_paged_decode_slots,
+    kda_decode_paged,
+    kda_decode_paged_varlen,
     kda_decode_pooled,
     load_library,
     supported_head_dims,

@@ -41,6 +41,7 @@ class GdnOptions(ctypes.Structure):
         ("block_v", ctypes.c_int32),
         ("quantize_initial", ctypes.c_int32),
         ("readout", ctypes.c_int32),
+        ("slots", ctypes.c_void_p),
     ]
 
 
@@ -62,6 +63,10 @@ _SIGNATURES = {
     "gdn_decode_pooled": (ctypes.c_int, [_P] * 11 + [_I32] * 6 + [_I64, _OPT, _P]),
     "gdn_decode_paged": (ctypes.c_int, [_P] * 12 + [_I32] * 5 + [_I64, _I64, _OPT, _P]),
     "kda_decode_pooled": (ctypes.c_int, [_P] * 11 + [_I32] * 6 + [_I64, _OPT, _P]),
+    "kda_decode_paged": (ctypes.c_int, [_P] * 12 + [_I32] * 5 + [_I64, _I64, _OPT, _P]),
+    "gdn_decode_paged_varlen": (ctypes.c_int, [_P] * 11 + [_I32] + [_P] * 2 + [_I32] * 6 + [_I64, _I64, _OPT, _P]),
+    "kda_decode_paged_varlen": (ctypes.c_int, [_P] * 11 + [_I32] + [_P] * 2 + [_I32] * 6 + [_I64, _I64, _OPT, _P]),
+    "gdn_paged_decode_slots": (ctypes.c_int, [_P] * 3 + [_I32, _I32, _P, _P]),
     "gdn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "gdn_last_error": (ctypes.c_char_p, []),
     "gdn_supported_head_dims": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int32), ctypes.c_int]),
@@ -136,12 +141,12 @@ def _raise(lib, status):
 
 
 def _common_opts(io_dtype, out_dtype, scale, use_qk_l2norm, beta_mode, state_layout, qdq, block_v,
-                 quantize_initial, readout, gate_mode="original", index_dtype=GDN_I32):
+                 quantize_initial, readout, gate_mode="original", index_dtype=GDN_I32, slots=None):
     return _options(scale=0.0 if scale is None else float(scale), use_qk_l2norm=int(bool(use_qk_l2norm)),
                     io_dtype=_IO[io_dtype], out_dtype=_IO[out_dtype], state_layout=_LAYOUT[state_layout],
                     beta_mode=_BETA[beta_mode], gate_mode=_GATE[gate_mode], index_dtype=index_dtype,
                     qdq=_QDQ[qdq], block_v=int(block_v), quantize_initial=int(bool(quantize_initial)),
-                    readout=_READOUT[readout])
+                    readout=_READOUT[readout], slots=None if slots is None else slots.data_ptr())
 
 
 def _pool_check(state_pool, HV, K, V, state_layout):
@@ -192,46 +197,130 @@ def gdn_decode_pooled(q, k, v, a, b, A_log, dt_bias, cu_seqlens, state_indices, 
     return out
 
 
-def gdn_decode_paged(q, k, v, a, b, A_log, dt_bias, page_indices, page_indptr, last_page_len, state_pool,
-                     out=None, *, scale=None, use_qk_l2norm=True, beta_mode="logits", state_layout="V_FIRST",
-                     out_dtype=None, qdq=None, block_v=64, quantize_initial=False, readout="working",
-                     stream=None):
-    """Single-token GDN decode on a CSR-paged pool (see gdn_decode_paged). Returns ``out`` [B, HV, V]."""
+def _paged(kind, q, k, v, gate, beta_in, a_log, dt_bias, cu_seqlens, page_indices, page_indptr, last_page_len,
+           page_size, state_pool, out, scale, use_qk_l2norm, beta_mode, state_layout, gate_mode, out_dtype, qdq,
+           block_v, quantize_initial, readout, slots, stream):
     lib = load_library()
-    B, HK, K = q.shape
+    T, HK, K = q.shape
     HV, V = v.shape[1], v.shape[2]
+    B = page_indptr.numel() - 1
     dev = q.device
     io = q.dtype
     out_dtype = out_dtype or io
-    for n, t in (("q", q), ("k", k), ("v", v), ("a", a), ("b", b)):
+    kda = kind.startswith("kda")
+    var = kind.endswith("varlen")
+    for n, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("beta", beta_in)):
         _check_dev(n, t, dev, (io,))
-    _check_dev("A_log", A_log, dev, (torch.float32,))
+    _check_dev("A_log", a_log, dev, (torch.float32,))
     _check_dev("dt_bias", dt_bias, dev, (torch.float32,))
     idt = page_indices.dtype
-    for n, t in (("page_indices", page_indices), ("page_indptr", page_indptr), ("last_page_len", last_page_len)):
-        _check_dev(n, t, dev, (idt,))
     if idt not in _IDX:
         raise TypeError("page table must be int32 or int64")
+    for n, t in (("page_indices", page_indices), ("page_indptr", page_indptr), ("last_page_len", last_page_len)):
+        _check_dev(n, t, dev, (idt,))
     _check_dev("state_pool", state_pool, dev, (torch.float32,))
-    if k.shape != q.shape or v.shape[0] != B or a.shape != (B, HV) or b.shape != (B, HV):
-        raise ValueError("q/k/v/a/b shapes disagree")
-    if page_indptr.shape != (B + 1,) or last_page_len.shape != (B,):
-        raise ValueError("page_indptr must be [B+1] and last_page_len [B]")
+    _check_dev("slots", slots, dev, (torch.int64,))
+    if var:
+        _check_dev("cu_seqlens", cu_seqlens, dev, (torch.int32,))
+        if cu_seqlens is None or cu_seqlens.shape != (B + 1,):
+            raise ValueError("cu_seqlens must be [B+1]")
+        if slots is not None:
+            raise ValueError("slots apply to single-token paged calls only")
+    elif T != B:
+        raise ValueError("single-token paged decode: q must be [B, HK, K]")
+    gshape = (T, HV, K) if kda else (T, HV)
+    if k.shape != q.shape or v.shape[0] != T or gate.shape != gshape or beta_in.shape != (T, HV):
+        raise ValueError("q/k/v/gate/beta shapes disagree")
+    if a_log.shape != (HV,) or dt_bias.shape != ((HV, K) if kda else (HV,)):
+        raise ValueError("A_log / dt_bias shapes disagree")
+    if last_page_len.shape != (B,):
+        raise ValueError("last_page_len must be [B]")
+    if slots is not None and slots.shape != (B, 2):
+        raise ValueError("slots must be [B, 2]")
     _pool_check(state_pool, HV, K, V, state_layout)
     if out is None:
-        out = torch.empty((B, HV, V), dtype=out_dtype, device=dev)
+        out = torch.empty((T, HV, V), dtype=out_dtype, device=dev)
     _check_dev("out", out, dev, (out_dtype,))
-    if out.numel() != B * HV * V:
-        raise ValueError("out must hold [B, HV, V]")
+    if out.numel() != T * HV * V:
+        raise ValueError("out must hold [T, HV, V]")
     opt = _common_opts(io, out_dtype, scale, use_qk_l2norm, beta_mode, state_layout, qdq, block_v,
-                       quantize_initial, readout, index_dtype=_IDX[idt])
-    st = lib.gdn_decode_paged(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
-                              _ptr(page_indices), _ptr(page_indptr), _ptr(last_page_len), _ptr(state_pool),
-                              _ptr(out), B, HK, HV, K, V, state_pool.shape[0], page_indices.numel(),
-                              ctypes.byref(opt), _stream_handle(dev, stream))
+                       quantize_initial, readout, gate_mode=gate_mode, index_dtype=_IDX[idt], slots=slots)
+    common_tail = (B, HK, HV, K, V) if not var else (B, T, HK, HV, K, V)
+    ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta_in), _ptr(a_log), _ptr(dt_bias))
+    table = (_ptr(page_indices), _ptr(page_indptr), _ptr(last_page_len))
+    fn = getattr(lib, kind)
+    if var:
+        st = fn(*ptrs, _ptr(cu_seqlens), *table, int(page_size), _ptr(state_pool), _ptr(out), *common_tail,
+                state_pool.shape[0], page_indices.numel(), ctypes.byref(opt), _stream_handle(dev, stream))
+    else:
+        st = fn(*ptrs, *table, _ptr(state_pool), _ptr(out), *common_tail, state_pool.shape[0], page_indices.numel(),
+                ctypes.byref(opt), _stream_handle(dev, stream))
     if st != GDN_OK:
         _raise(lib, st)
     return out
+
+
+def gdn_decode_paged(q, k, v, a, b, A_log, dt_bias, page_indices, page_indptr, last_page_len, state_pool,
+                     out=None, *, scale=None, use_qk_l2norm=True, beta_mode="logits", state_layout="V_FIRST",
+                     out_dtype=None, qdq=None, block_v=64, quantize_initial=False, readout="working",
+                     slots=None, stream=None):
+    """Single-token GDN decode on a CSR-paged pool (see gdn_decode_paged). Returns ``out`` [B, HV, V]."""
+    return _paged("gdn_decode_paged", q, k, v, a, b, A_log, dt_bias, None, page_indices, page_indptr,
+                  last_page_len, 0, state_pool, out, scale, use_qk_l2norm, beta_mode, state_layout, "original",
+                  out_dtype, qdq, block_v, quantize_initial, readout, slots, stream)
+
+
+def kda_decode_paged(q, k, v, raw_gate, beta_logits, a_log, dt_bias, page_indices, page_indptr, last_page_len,
+                     state_pool, out=None, *, scale=None, use_qk_l2norm=True, beta_mode="logits",
+                     state_layout="V_FIRST", gate_mode="original", out_dtype=None, qdq=None, block_v=64,
+                     quantize_initial=False, readout="working", slots=None, stream=None):
+    """Single-token KDA decode on a CSR-paged pool (see kda_decode_paged). Returns ``out`` [B, HV, V]."""
+    return _paged("kda_decode_paged", q, k, v, raw_gate, beta_logits, a_log, dt_bias, None, page_indices,
+                  page_indptr, last_page_len, 0, state_pool, out, scale, use_qk_l2norm, beta_mode, state_layout,
+                  gate_mode, out_dtype, qdq, block_v, quantize_initial, readout, slots, stream)
+
+
+def gdn_decode_paged_varlen(q, k, v, a, b, A_log, dt_bias, cu_seqlens, page_indices, page_indptr, last_page_len,
+                            page_size, state_pool, out=None, *, scale=None, use_qk_l2norm=True, beta_mode="logits",
+                            state_layout="V_FIRST", out_dtype=None, qdq=None, block_v=64, quantize_initial=False,
+                            readout="working", stream=None):
+    """GDN decode of varlen suffixes on a CSR-paged pool (see gdn_decode_paged_varlen). Returns ``out`` [T, HV, V]."""
+    return _paged("gdn_decode_paged_varlen", q, k, v, a, b, A_log, dt_bias, cu_seqlens, page_indices, page_indptr,
+                  last_page_len, page_size, state_pool, out, scale, use_qk_l2norm, beta_mode, state_layout,
+                  "original", out_dtype, qdq, block_v, quantize_initial, readout, None, stream)
+
+
+def kda_decode_paged_varlen(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, page_indices, page_indptr,
+                            last_page_len, page_size, state_pool, out=None, *, scale=None, use_qk_l2norm=True,
+                            beta_mode="logits", state_layout="V_FIRST", gate_mode="original", out_dtype=None,
+                            qdq=None, block_v=64, quantize_initial=False, readout="working", stream=None):
+    """KDA decode of varlen suffixes on a CSR-paged pool (see kda_decode_paged_varlen). Returns ``out`` [T, HV, V]."""
+    return _paged("kda_decode_paged_varlen", q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens,
+                  page_indices, page_indptr, last_page_len, page_size, state_pool, out, scale, use_qk_l2norm,
+                  beta_mode, state_layout, gate_mode, out_dtype, qdq, block_v, quantize_initial, readout, None,
+                  stream)
+
+
+def gdn_paged_decode_slots(page_indices, page_indptr, last_page_len, slots=None, stream=None):
+    """(read row, write row) per sequence for a single-token paged step, [B, 2] int64 (see gdn_paged_decode_slots)."""
+    lib = load_library()
+    B = page_indptr.numel() - 1
+    dev = page_indices.device
+    idt = page_indices.dtype
+    if idt not in _IDX:
+        raise TypeError("page table must be int32 or int64")
+    for n, t in (("page_indices", page_indices), ("page_indptr", page_indptr), ("last_page_len", last_page_len)):
+        _check_dev(n, t, dev, (idt,))
+    if slots is None:
+        slots = torch.empty((B, 2), dtype=torch.int64, device=dev)
+    _check_dev("slots", slots, dev, (torch.int64,))
+    if slots.shape != (B, 2):
+        raise ValueError("slots must be [B, 2]")
+    st = lib.gdn_paged_decode_slots(_ptr(page_indices), _ptr(page_indptr), _ptr(last_page_len), B, _IDX[idt],
+                                    _ptr(slots), _stream_handle(dev, stream))
+    if st != GDN_OK:
+        _raise(lib, st)
+    return slots
 
 
 def kda_decode_pooled(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_indices, state_pool,

@@ -60,6 +60,8 @@ struct Params {
   const void* page_indices;      // paged
   const void* page_indptr;
   const void* last_page_len;
+  const int64_t* slots;          // paged, single token: precomputed (read, write) rows, or null
+  int32_t page_size;             // paged suffixes of several tokens
   float* pool;
   void* out;
   int32_t B, HK, HV, V;
@@ -81,6 +83,14 @@ struct Params {
 __device__ __forceinline__ int fast_div(int n, uint64_t m, int sh) {
   return static_cast<int>((static_cast<uint64_t>(static_cast<uint32_t>(n)) * m) >> sh);
 }
+
+// How a work unit finds its tokens and pool rows.
+enum Addr : int {
+  kPooled = 0,      // state_indices[b]; tokens from cu_seqlens (or one per sequence)
+  kPaged1 = 1,      // one token per sequence, CSR page table, copy-on-new-page
+  kPagedVar = 2,    // cu_seqlens suffixes on a CSR page table: every page a suffix
+                    // token fills gets the state after that token
+};
 
 constexpr float kL2Eps = 1e-6f;
 constexpr float kE4M3Max = 448.0f;
@@ -264,7 +274,7 @@ struct Tile {
   static_assert(!VF || EV == 4 || K / 2 == 4 * LR, "two float4 half a row apart");
 };
 
-template <int K, int VB, int NT, bool VF, bool KDA, bool QDQ, bool PAGED, typename TIn>
+template <int K, int VB, int NT, bool VF, bool KDA, bool QDQ, int ADDR, typename TIn>
 __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   using Cfg = Tile<K, VB, NT, VF>;
   constexpr int NW = Cfg::NW, LR = Cfg::LR, RPW = Cfg::RPW, NS = Cfg::NS, LB = Cfg::LB;
@@ -332,7 +342,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
 
   // ---- which tokens
   int t0, t1;
-  if constexpr (PAGED) {
+  if constexpr (ADDR == kPaged1) {
     t0 = bs;
     t1 = bs + 1;
   } else {
@@ -434,12 +444,30 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
 
   // ---- which pool rows
   int64_t rrow, wrow;
-  if constexpr (PAGED) {
+  int64_t pg_start = 0, pos0 = 0, pos_last = 0;   // kPagedVar: first table entry, token positions
+  if constexpr (ADDR == kPaged1) {
+    if (p.slots) {
+      rrow = p.slots[2 * bs];
+      wrow = p.slots[2 * bs + 1];
+    } else {
+      const int64_t end = load_index(p.page_indptr, bs + 1, p.idx64);
+      const int64_t last = load_index(p.page_indices, end - 1, p.idx64);
+      const int64_t lpl = load_index(p.last_page_len, bs, p.idx64);
+      wrow = last;
+      rrow = (lpl == 1) ? load_index(p.page_indices, end - 2, p.idx64) : last;
+    }
+  } else if constexpr (ADDR == kPagedVar) {
+    // the sequence holds n tokens after the suffix; the suffix is positions
+    // pos0 .. n (1-based); the state before it lives on the page of pos0 - 1
+    pg_start = load_index(p.page_indptr, bs, p.idx64);
     const int64_t end = load_index(p.page_indptr, bs + 1, p.idx64);
-    const int64_t last = load_index(p.page_indices, end - 1, p.idx64);
     const int64_t lpl = load_index(p.last_page_len, bs, p.idx64);
-    wrow = last;
-    rrow = (lpl == 1) ? load_index(p.page_indices, end - 2, p.idx64) : last;
+    pos_last = (end - pg_start - 1) * p.page_size + lpl;
+    pos0 = pos_last - (t1 - t0) + 1;
+    // (clamped so that a table that breaks the one-prior-token precondition
+    // still addresses its own pages)
+    rrow = load_index(p.page_indices, pg_start + max(pos0 - 2, static_cast<int64_t>(0)) / p.page_size, p.idx64);
+    wrow = load_index(p.page_indices, end - 1, p.idx64);
   } else {
     rrow = wrow = p.state_indices[bs];
   }
@@ -670,6 +698,21 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
     }
   };
 
+  // write the true state (scale * registers) to a pool row
+  auto store_tile = [&](float* row_base) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int f = 0; f < EV / 4; ++f) {
+        float4 x;
+        x.x = S[s][4 * f + 0] * cs[KDA ? slot(s, 4 * f + 0) : 0];
+        x.y = S[s][4 * f + 1] * cs[KDA ? slot(s, 4 * f + 1) : 0];
+        x.z = S[s][4 * f + 2] * cs[KDA ? slot(s, 4 * f + 2) : 0];
+        x.w = S[s][4 * f + 3] * cs[KDA ? slot(s, 4 * f + 3) : 0];
+        *reinterpret_cast<float4*>(row_base + row_off(s, f)) = x;
+      }
+  };
+
   if constexpr (QDQ) {
     if (p.quantize_initial) qdq_tile();
   }
@@ -781,20 +824,34 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
           store_outputs(out_row, ps);
         }
       }
+      if constexpr (ADDR == kPagedVar) {
+        // a token that fills its page leaves the state there (the last token's
+        // page is written after the loop)
+        const int64_t pos = pos0 + (t - t0);
+        if (pos > 0 && pos % p.page_size == 0 && pos != pos_last) {
+          const int64_t row = load_index(p.page_indices, pg_start + (pos - 1) / p.page_size, p.idx64);
+          store_tile(p.pool + (row * p.HV + h) * tile_elems);
+        }
+      }
     }
   }
 
-#pragma unroll
-  for (int s = 0; s < NS; ++s)
-#pragma unroll
-    for (int f = 0; f < EV / 4; ++f) {
-      float4 x;
-      x.x = S[s][4 * f + 0] * cs[KDA ? slot(s, 4 * f + 0) : 0];
-      x.y = S[s][4 * f + 1] * cs[KDA ? slot(s, 4 * f + 1) : 0];
-      x.z = S[s][4 * f + 2] * cs[KDA ? slot(s, 4 * f + 2) : 0];
-      x.w = S[s][4 * f + 3] * cs[KDA ? slot(s, 4 * f + 3) : 0];
-      *reinterpret_cast<float4*>(dst + row_off(s, f)) = x;
-    }
+  store_tile(dst);
+}
+
+// (read row, write row) of every sequence for one decoded token on a CSR
+// page table (flashinfer.gdn_paged.gated_delta_rule_decode_paged, slots):
+// computed once per decode step and shared by every layer's call.
+__global__ __launch_bounds__(256) void paged_slots_kernel(const void* page_indices, const void* page_indptr,
+                                                          const void* last_page_len, int32_t B, int32_t idx64,
+                                                          int64_t* slots) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= B) return;
+  const int64_t end = load_index(page_indptr, b + 1, idx64);
+  const int64_t last = load_index(page_indices, end - 1, idx64);
+  const int64_t lpl = load_index(last_page_len, b, idx64);
+  slots[2 * b] = (lpl == 1) ? load_index(page_indices, end - 2, idx64) : last;
+  slots[2 * b + 1] = last;
 }
 
 }  // namespace gdn

@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <type_traits>
 
 #include "gdn_decode.h"
 #include "decode_kernel.hpp"
@@ -28,7 +29,7 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-enum class Kind { GdnPooled, GdnPaged, KdaPooled };
+enum class Kind { GdnPooled, GdnPaged, KdaPooled, KdaPaged, GdnPagedVar, KdaPagedVar };
 
 // Workgroup shapes: V-block width VB (one workgroup per V-block of one
 // sequence and value head) and threads per workgroup NT.  Chosen per key
@@ -56,9 +57,9 @@ struct HeadCfg {
 };
 constexpr HeadCfg kHeads[] = {{16, 16}, {128, 64}};
 
-template <int K, int VB, int NT, bool VF, bool KDA, bool QDQ, bool PAGED, typename TIn>
+template <int K, int VB, int NT, bool VF, bool KDA, bool QDQ, int ADDR, typename TIn>
 hipError_t launch_one(const gdn::Params& p, int64_t units, hipStream_t stream) {
-  hipLaunchKernelGGL((gdn::decode_kernel<K, VB, NT, VF, KDA, QDQ, PAGED, TIn>), dim3(static_cast<uint32_t>(units)),
+  hipLaunchKernelGGL((gdn::decode_kernel<K, VB, NT, VF, KDA, QDQ, ADDR, TIn>), dim3(static_cast<uint32_t>(units)),
                      dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
@@ -67,28 +68,31 @@ struct Sel {
   bool vfirst, qdq, bf16;
 };
 
-template <int K, int VB, int NT, bool KDA, bool PAGED, typename TIn>
+template <int K, int VB, int NT, bool KDA, int ADDR, typename TIn>
 hipError_t launch_layout_qdq(const gdn::Params& p, int64_t units, Sel sel, hipStream_t s) {
   if (sel.vfirst) {
-    return sel.qdq ? launch_one<K, VB, NT, true, KDA, true, PAGED, TIn>(p, units, s)
-                   : launch_one<K, VB, NT, true, KDA, false, PAGED, TIn>(p, units, s);
+    return sel.qdq ? launch_one<K, VB, NT, true, KDA, true, ADDR, TIn>(p, units, s)
+                   : launch_one<K, VB, NT, true, KDA, false, ADDR, TIn>(p, units, s);
   }
-  return sel.qdq ? launch_one<K, VB, NT, false, KDA, true, PAGED, TIn>(p, units, s)
-                 : launch_one<K, VB, NT, false, KDA, false, PAGED, TIn>(p, units, s);
+  return sel.qdq ? launch_one<K, VB, NT, false, KDA, true, ADDR, TIn>(p, units, s)
+                 : launch_one<K, VB, NT, false, KDA, false, ADDR, TIn>(p, units, s);
 }
 
-template <int K, int VB, int NT, bool KDA, bool PAGED>
+template <int K, int VB, int NT, bool KDA, int ADDR>
 hipError_t launch_io(const gdn::Params& p, int64_t units, Sel sel, hipStream_t s) {
-  return sel.bf16 ? launch_layout_qdq<K, VB, NT, KDA, PAGED, gdn::bf16_t>(p, units, sel, s)
-                  : launch_layout_qdq<K, VB, NT, KDA, PAGED, float>(p, units, sel, s);
+  return sel.bf16 ? launch_layout_qdq<K, VB, NT, KDA, ADDR, gdn::bf16_t>(p, units, sel, s)
+                  : launch_layout_qdq<K, VB, NT, KDA, ADDR, float>(p, units, sel, s);
 }
 
 template <int K, int VB, int NT>
 hipError_t launch_kind(Kind kind, const gdn::Params& p, int64_t units, Sel sel, hipStream_t s) {
   switch (kind) {
-    case Kind::GdnPooled: return launch_io<K, VB, NT, false, false>(p, units, sel, s);
-    case Kind::GdnPaged: return launch_io<K, VB, NT, false, true>(p, units, sel, s);
-    case Kind::KdaPooled: return launch_io<K, VB, NT, true, false>(p, units, sel, s);
+    case Kind::GdnPooled: return launch_io<K, VB, NT, false, gdn::kPooled>(p, units, sel, s);
+    case Kind::GdnPaged: return launch_io<K, VB, NT, false, gdn::kPaged1>(p, units, sel, s);
+    case Kind::KdaPooled: return launch_io<K, VB, NT, true, gdn::kPooled>(p, units, sel, s);
+    case Kind::KdaPaged: return launch_io<K, VB, NT, true, gdn::kPaged1>(p, units, sel, s);
+    case Kind::GdnPagedVar: return launch_io<K, VB, NT, false, gdn::kPagedVar>(p, units, sel, s);
+    case Kind::KdaPagedVar: return launch_io<K, VB, NT, true, gdn::kPagedVar>(p, units, sel, s);
   }
   return hipErrorInvalidValue;
 }
@@ -107,16 +111,24 @@ bool head_supported(int K, int V) {
 // Small V_FIRST workgroups (K=128, no QDQ): one instantiation per kind and io type.
 template <int VB, int NT>
 hipError_t launch_small_vfirst(Kind kind, const gdn::Params& p, int64_t units, Sel sel, hipStream_t s) {
+  auto go = [&](auto kda, auto addr) -> hipError_t {
+    constexpr bool KDA = decltype(kda)::value;
+    constexpr int ADDR = decltype(addr)::value;
+    return sel.bf16 ? launch_one<128, VB, NT, true, KDA, false, ADDR, gdn::bf16_t>(p, units, s)
+                    : launch_one<128, VB, NT, true, KDA, false, ADDR, float>(p, units, s);
+  };
+  using F = std::false_type;
+  using Tr = std::true_type;
+  using Pool = std::integral_constant<int, gdn::kPooled>;
+  using Pg1 = std::integral_constant<int, gdn::kPaged1>;
+  using PgV = std::integral_constant<int, gdn::kPagedVar>;
   switch (kind) {
-    case Kind::GdnPooled:
-      return sel.bf16 ? launch_one<128, VB, NT, true, false, false, false, gdn::bf16_t>(p, units, s)
-                      : launch_one<128, VB, NT, true, false, false, false, float>(p, units, s);
-    case Kind::GdnPaged:
-      return sel.bf16 ? launch_one<128, VB, NT, true, false, false, true, gdn::bf16_t>(p, units, s)
-                      : launch_one<128, VB, NT, true, false, false, true, float>(p, units, s);
-    case Kind::KdaPooled:
-      return sel.bf16 ? launch_one<128, VB, NT, true, true, false, false, gdn::bf16_t>(p, units, s)
-                      : launch_one<128, VB, NT, true, true, false, false, float>(p, units, s);
+    case Kind::GdnPooled: return go(F{}, Pool{});
+    case Kind::GdnPaged: return go(F{}, Pg1{});
+    case Kind::KdaPooled: return go(Tr{}, Pool{});
+    case Kind::KdaPaged: return go(Tr{}, Pg1{});
+    case Kind::GdnPagedVar: return go(F{}, PgV{});
+    case Kind::KdaPagedVar: return go(Tr{}, PgV{});
   }
   return hipErrorInvalidValue;
 }
@@ -139,7 +151,9 @@ int check_options(const gdn_options* o, int K, int V, Kind kind) {
     return fail(GDN_ERR_INVALID, "qdq must be NONE or FP8_E4M3_TILE (got %d)", o->qdq);
   if (o->readout != GDN_READOUT_WORKING && o->readout != GDN_READOUT_STORED)
     return fail(GDN_ERR_INVALID, "readout must be WORKING or STORED (got %d)", o->readout);
-  if (kind == Kind::GdnPaged && o->index_dtype != GDN_I32 && o->index_dtype != GDN_I64)
+  const bool paged = kind == Kind::GdnPaged || kind == Kind::KdaPaged || kind == Kind::GdnPagedVar ||
+                     kind == Kind::KdaPagedVar;
+  if (paged && o->index_dtype != GDN_I32 && o->index_dtype != GDN_I64)
     return fail(GDN_ERR_INVALID, "index_dtype must be GDN_I32 or GDN_I64 (got %d)", o->index_dtype);
   if (!(o->scale >= 0.0f) || std::isinf(o->scale))
     return fail(GDN_ERR_INVALID, "scale must be finite and >= 0 (0 selects 1/sqrt(K))");
@@ -191,6 +205,7 @@ void fill_common(gdn::Params& p, const gdn_options* o, int32_t B, int32_t T, int
   p.idx64 = o->index_dtype == GDN_I64;
   p.quantize_initial = (o->qdq != GDN_QDQ_NONE && o->quantize_initial) ? 1 : 0;
   p.readout_stored = (o->qdq != GDN_QDQ_NONE && o->readout == GDN_READOUT_STORED) ? 1 : 0;
+  p.slots = o->slots;
 }
 
 int run(Kind kind, const gdn::Params& p, int K, int32_t T, const gdn_options* o, void* stream) {
@@ -230,6 +245,7 @@ void gdn_options_init(gdn_options* o) {
   o->block_v = 64;
   o->quantize_initial = 0;
   o->readout = GDN_READOUT_WORKING;
+  o->slots = nullptr;
 }
 
 int gdn_decode_pooled(const void* q, const void* k, const void* v, const void* a, const void* b,
@@ -244,6 +260,7 @@ int gdn_decode_pooled(const void* q, const void* k, const void* v, const void* a
   if (!cu_seqlens && T != B)
     return fail(GDN_ERR_SHAPE, "without cu_seqlens each sequence has one token, so T (%d) must equal B (%d)", T, B);
   if (int rc = check_options(opt, K, V, Kind::GdnPooled)) return rc;
+  if (opt->slots) return fail(GDN_ERR_INVALID, "slots apply to paged calls only");
   gdn::Params p{};
   p.q = q; p.k = k; p.v = v; p.gate = a; p.beta = b;
   p.a_log = A_log; p.dt_bias = dt_bias;
@@ -254,25 +271,94 @@ int gdn_decode_pooled(const void* q, const void* k, const void* v, const void* a
   return run(Kind::GdnPooled, p, K, T, opt, stream);
 }
 
-int gdn_decode_paged(const void* q, const void* k, const void* v, const void* a, const void* b,
-                     const float* A_log, const float* dt_bias, const void* page_indices, const void* page_indptr,
-                     const void* last_page_len, float* state_pool, void* out, int32_t B, int32_t HK, int32_t HV,
-                     int32_t K, int32_t V, int64_t num_pages, int64_t nnz, const gdn_options* opt, void* stream) {
-  if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !page_indices || !page_indptr || !last_page_len ||
-      !state_pool || !out)
+}  // extern "C"
+
+namespace {
+
+// Shared body of the paged entry points.  T == B and cu_seqlens == NULL for
+// one token per sequence (P3 semantics), else varlen suffixes with page_size.
+int paged_call(Kind kind, const void* q, const void* k, const void* v, const void* gate, const void* beta,
+               const float* a_log, const float* dt_bias, const int32_t* cu_seqlens, const void* page_indices,
+               const void* page_indptr, const void* last_page_len, int32_t page_size, float* state_pool, void* out,
+               int32_t B, int32_t T, int32_t HK, int32_t HV, int32_t K, int32_t V, int64_t num_pages, int64_t nnz,
+               const gdn_options* opt, void* stream) {
+  const bool var = kind == Kind::GdnPagedVar || kind == Kind::KdaPagedVar;
+  if (!q || !k || !v || !gate || !beta || !a_log || !dt_bias || !page_indices || !page_indptr || !last_page_len ||
+      !state_pool || !out || (var && !cu_seqlens))
     return fail(GDN_ERR_INVALID, "a required pointer is NULL");
   if (int rc = check_dims(B, HK, HV, K, V)) return rc;
   if (num_pages <= 0 || nnz <= 0) return fail(GDN_ERR_INVALID, "num_pages and nnz must be positive");
   if (nnz < B) return fail(GDN_ERR_SHAPE, "nnz (%lld) must be at least B (%d): every sequence owns a page",
                            (long long)nnz, B);
-  if (int rc = check_options(opt, K, V, Kind::GdnPaged)) return rc;
+  if (var && page_size <= 0) return fail(GDN_ERR_INVALID, "page_size must be positive (got %d)", page_size);
+  if (var && T < 0) return fail(GDN_ERR_INVALID, "T must be >= 0");
+  if (int rc = check_options(opt, K, V, kind)) return rc;
+  if (var && opt->slots) return fail(GDN_ERR_INVALID, "slots apply to single-token paged calls only");
   gdn::Params p{};
-  p.q = q; p.k = k; p.v = v; p.gate = a; p.beta = b;
-  p.a_log = A_log; p.dt_bias = dt_bias;
+  p.q = q; p.k = k; p.v = v; p.gate = gate; p.beta = beta;
+  p.a_log = a_log; p.dt_bias = dt_bias;
+  p.cu_seqlens = cu_seqlens;
   p.page_indices = page_indices; p.page_indptr = page_indptr; p.last_page_len = last_page_len;
+  p.page_size = page_size;
   p.pool = state_pool; p.out = out;
-  fill_common(p, opt, B, B, HK, HV, K, V);
-  return run(Kind::GdnPaged, p, K, B, opt, stream);
+  fill_common(p, opt, B, T, HK, HV, K, V);
+  if (T == 0) { g_last_error.clear(); return GDN_OK; }
+  return run(kind, p, K, T, opt, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_decode_paged(const void* q, const void* k, const void* v, const void* a, const void* b,
+                     const float* A_log, const float* dt_bias, const void* page_indices, const void* page_indptr,
+                     const void* last_page_len, float* state_pool, void* out, int32_t B, int32_t HK, int32_t HV,
+                     int32_t K, int32_t V, int64_t num_pages, int64_t nnz, const gdn_options* opt, void* stream) {
+  return paged_call(Kind::GdnPaged, q, k, v, a, b, A_log, dt_bias, nullptr, page_indices, page_indptr,
+                    last_page_len, 0, state_pool, out, B, B, HK, HV, K, V, num_pages, nnz, opt, stream);
+}
+
+int kda_decode_paged(const void* q, const void* k, const void* v, const void* raw_gate, const void* beta_logits,
+                     const float* a_log, const float* dt_bias, const void* page_indices, const void* page_indptr,
+                     const void* last_page_len, float* state_pool, void* out, int32_t B, int32_t HK, int32_t HV,
+                     int32_t K, int32_t V, int64_t num_pages, int64_t nnz, const gdn_options* opt, void* stream) {
+  return paged_call(Kind::KdaPaged, q, k, v, raw_gate, beta_logits, a_log, dt_bias, nullptr, page_indices,
+                    page_indptr, last_page_len, 0, state_pool, out, B, B, HK, HV, K, V, num_pages, nnz, opt, stream);
+}
+
+int gdn_decode_paged_varlen(const void* q, const void* k, const void* v, const void* a, const void* b,
+                            const float* A_log, const float* dt_bias, const int32_t* cu_seqlens,
+                            const void* page_indices, const void* page_indptr, const void* last_page_len,
+                            int32_t page_size, float* state_pool, void* out, int32_t B, int32_t T, int32_t HK,
+                            int32_t HV, int32_t K, int32_t V, int64_t num_pages, int64_t nnz,
+                            const gdn_options* opt, void* stream) {
+  return paged_call(Kind::GdnPagedVar, q, k, v, a, b, A_log, dt_bias, cu_seqlens, page_indices, page_indptr,
+                    last_page_len, page_size, state_pool, out, B, T, HK, HV, K, V, num_pages, nnz, opt, stream);
+}
+
+int kda_decode_paged_varlen(const void* q, const void* k, const void* v, const void* raw_gate,
+                            const void* beta_logits, const float* a_log, const float* dt_bias,
+                            const int32_t* cu_seqlens, const void* page_indices, const void* page_indptr,
+                            const void* last_page_len, int32_t page_size, float* state_pool, void* out, int32_t B,
+                            int32_t T, int32_t HK, int32_t HV, int32_t K, int32_t V, int64_t num_pages,
+                            int64_t nnz, const gdn_options* opt, void* stream) {
+  return paged_call(Kind::KdaPagedVar, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, page_indices,
+                    page_indptr, last_page_len, page_size, state_pool, out, B, T, HK, HV, K, V, num_pages, nnz, opt,
+                    stream);
+}
+
+int gdn_paged_decode_slots(const void* page_indices, const void* page_indptr, const void* last_page_len, int32_t B,
+                           int32_t index_dtype, int64_t* slots, void* stream) {
+  if (!page_indices || !page_indptr || !last_page_len || !slots) return fail(GDN_ERR_INVALID, "a required pointer is NULL");
+  if (B <= 0) return fail(GDN_ERR_INVALID, "B must be positive (got %d)", B);
+  if (index_dtype != GDN_I32 && index_dtype != GDN_I64)
+    return fail(GDN_ERR_INVALID, "index_dtype must be GDN_I32 or GDN_I64 (got %d)", index_dtype);
+  hipLaunchKernelGGL(gdn::paged_slots_kernel, dim3((B + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     page_indices, page_indptr, last_page_len, B, index_dtype == GDN_I64 ? 1 : 0, slots);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  g_last_error.clear();
+  return GDN_OK;
 }
 
 int kda_decode_pooled(const void* q, const void* k, const void* v, const void* raw_gate, const void* beta_logits,
@@ -285,6 +371,7 @@ int kda_decode_pooled(const void* q, const void* k, const void* v, const void* r
   if (int rc = check_dims(B, HK, HV, K, V)) return rc;
   if (T < 0 || num_slots <= 0) return fail(GDN_ERR_INVALID, "T must be >= 0 and num_slots > 0");
   if (int rc = check_options(opt, K, V, Kind::KdaPooled)) return rc;
+  if (opt->slots) return fail(GDN_ERR_INVALID, "slots apply to paged calls only");
   gdn::Params p{};
   p.q = q; p.k = k; p.v = v; p.gate = raw_gate; p.beta = beta_logits;
   p.a_log = a_log; p.dt_bias = dt_bias;

@@ -52,8 +52,8 @@ class Workload:
         return (self.num_rows, self.HV) + tail
 
     def read_rows(self):
-        """Pool rows read by the call (sorted unique)."""
-        if self.kind == "gdn_paged":
+        """Pool rows read by the call (sorted unique), single-token paged or pooled."""
+        if self.kind in ("gdn_paged", "kda_paged"):
             ind = self.inputs["page_indices"].numpy()
             ptr = self.inputs["page_indptr"].numpy()
             lpl = self.inputs["last_page_len"].numpy()
@@ -137,41 +137,45 @@ def kda_pooled(B, HK, HV, K, V, *, lengths, num_slots=None, state_layout=V_FIRST
                     num_slots, inp, options, pool_seed=seed + 1, pool_zero=zero_state)
 
 
-def build_page_table(prefix_lengths, page_size, share_frac, rng, force_shared_new_page=8):
-    """CSR page table for sequences whose decoded token follows ``prefix_lengths`` tokens.
+def build_page_table(prefix_lengths, page_size, share_frac, rng, force_shared_new_page=8, new_tokens=None):
+    """CSR page table for sequences that append ``new_tokens`` (default 1) to ``prefix_lengths`` tokens.
 
-    Sequence b holds n_b = L_b + 1 tokens on ceil(n_b / page_size) pages;
+    Sequence b holds n_b = L_b + new_b tokens on ceil(n_b / page_size) pages;
     ``last_page_len`` = n_b - page_size * (pages - 1).  A fraction
-    ``share_frac`` of the full (non-last) pages is aliased to the page with
-    the same position in another sequence whose page there is also full, as
-    shared prefixes are; last pages are never shared.  Some sequences whose
-    decoded token opens a new page get a shared previous page on purpose.
-    Page ids are compacted to 0..num_pages-1 in a random physical order.
+    ``share_frac`` of the pages that lie entirely inside the prefix is
+    aliased to the page with the same position in another sequence whose
+    page there also lies inside its prefix, as shared prefixes are; pages
+    that hold new tokens are never shared, so no call writes a shared page.
+    Some sequences whose state is read from a full page (the prefix ends on a
+    page boundary) get a shared page there on purpose.  Page ids are
+    compacted to 0..num_pages-1 in a random physical order.
     Returns (page_indices int64 [nnz], page_indptr int64 [B+1],
     last_page_len int64 [B], num_pages).
     """
     L = np.asarray(prefix_lengths, dtype=np.int64)
-    n = L + 1
+    new = np.ones_like(L) if new_tokens is None else np.asarray(new_tokens, dtype=np.int64)
+    n = L + new
     P = -(-n // page_size)
     last_len = n - page_size * (P - 1)
+    full_prefix = L // page_size              # pages 0 .. full_prefix-1 hold prefix tokens only
     B = len(L)
     uid = [list(range(int(s), int(s + p))) for s, p in zip(np.concatenate([[0], np.cumsum(P)[:-1]]), P)]
-    full = [(b, j) for b in range(B) for j in range(int(P[b]) - 1)]
+    full = [(b, j) for b in range(B) for j in range(int(full_prefix[b]))]
     n_share = int(round(share_frac * len(full)))
     chosen = set()
-    # sequences whose decoded token opens a new page: share their previous page first
-    newpage = [b for b in range(B) if last_len[b] == 1 and P[b] >= 2]
-    rng.shuffle(newpage)
-    for b in newpage[:force_shared_new_page]:
-        chosen.add((b, int(P[b]) - 2))
+    # sequences whose state is read from a full page: share that page first
+    boundary = [b for b in range(B) if L[b] % page_size == 0 and L[b] >= page_size]
+    rng.shuffle(boundary)
+    for b in boundary[:force_shared_new_page]:
+        chosen.add((b, int(full_prefix[b]) - 1))
     order = rng.permutation(len(full))
     for i in order:
         if len(chosen) >= n_share:
             break
         chosen.add(full[i])
-    # targets: same page position in another sequence, page not itself aliased
+    # targets: same page position in another sequence, inside its prefix and not itself aliased
     for (b, j) in sorted(chosen):
-        cands = np.nonzero((P - 1 > j) & (np.arange(B) != b))[0]
+        cands = np.nonzero((full_prefix > j) & (np.arange(B) != b))[0]
         cands = [c for c in cands if (int(c), j) not in chosen]
         if not cands:
             continue
@@ -185,29 +189,51 @@ def build_page_table(prefix_lengths, page_size, share_frac, rng, force_shared_ne
     return indices, indptr, last_len.astype(np.int64), len(used)
 
 
-def gdn_paged(B, HK, HV, K, V, *, prefix_lengths=None, max_prefix=2048, page_size=16, share_frac=0.1,
-              state_layout=V_FIRST, io_dtype=torch.bfloat16, out_dtype=None, index_dtype=torch.int64,
-              seed=0, name="gdn_paged", **options):
-    """Single-token GDN decode on a CSR-paged pool with shared prefix pages."""
+def paged(kind, B, HK, HV, K, V, *, prefix_lengths=None, max_prefix=2048, page_size=16, share_frac=0.1,
+          suffix_lengths=None, state_layout=V_FIRST, io_dtype=torch.bfloat16, out_dtype=None,
+          index_dtype=torch.int64, seed=0, name=None, **options):
+    """GDN ("gdn") or KDA ("kda") decode on a CSR-paged pool with shared prefix pages.
+
+    ``suffix_lengths`` None: one decoded token per sequence (token b belongs to
+    sequence b); otherwise each sequence appends that many tokens and the
+    inputs hold them in cu_seqlens order.
+    """
     rng = np.random.default_rng(seed)
     if prefix_lengths is None:
         prefix_lengths = rng.integers(1, max_prefix + 1, B)
-    ind, ptr, lpl, num_pages = build_page_table(prefix_lengths, page_size, share_frac, rng)
+    ind, ptr, lpl, num_pages = build_page_table(prefix_lengths, page_size, share_frac, rng,
+                                                new_tokens=suffix_lengths)
+    T = B if suffix_lengths is None else int(np.sum(suffix_lengths))
     inp = {}
-    inp["q"] = _cast(_normal(rng, (B, HK, K)), io_dtype)
-    inp["k"] = _cast(_normal(rng, (B, HK, K)), io_dtype)
-    inp["v"] = _cast(_normal(rng, (B, HV, V)), io_dtype)
-    inp["a"] = _cast(_normal(rng, (B, HV)), io_dtype)
-    inp["b"] = _cast(_normal(rng, (B, HV)), io_dtype)
-    inp["dt_bias"] = _cast(_uniform(rng, -1, 1, (HV,)), torch.float32)
-    inp["A_log"] = _cast(_uniform(rng, 0, math.log(16), (HV,)), torch.float32)
+    inp["q"] = _cast(_normal(rng, (T, HK, K)), io_dtype)
+    inp["k"] = _cast(_normal(rng, (T, HK, K)), io_dtype)
+    inp["v"] = _cast(_normal(rng, (T, HV, V)), io_dtype)
+    if kind == "kda":
+        inp["raw_gate"] = _cast(_normal(rng, (T, HV, K)), io_dtype)
+        inp["beta_logits"] = _cast(_normal(rng, (T, HV)), io_dtype)
+        inp["dt_bias"] = _cast(_uniform(rng, -1, 1, (HV, K)), torch.float32)
+        inp["a_log"] = _cast(_uniform(rng, 0, math.log(16), (HV,)), torch.float32)
+    else:
+        inp["a"] = _cast(_normal(rng, (T, HV)), io_dtype)
+        inp["b"] = _cast(_normal(rng, (T, HV)), io_dtype)
+        inp["dt_bias"] = _cast(_uniform(rng, -1, 1, (HV,)), torch.float32)
+        inp["A_log"] = _cast(_uniform(rng, 0, math.log(16), (HV,)), torch.float32)
     inp["page_indices"] = torch.from_numpy(ind).to(index_dtype)
     inp["page_indptr"] = torch.from_numpy(ptr).to(index_dtype)
     inp["last_page_len"] = torch.from_numpy(lpl).to(index_dtype)
     inp["prefix_lengths"] = torch.from_numpy(np.asarray(prefix_lengths, dtype=np.int64))
+    if suffix_lengths is not None:
+        inp["cu_seqlens"] = lengths_to_cu(suffix_lengths)
     opts = dict(page_size=page_size, **options)
-    return Workload("gdn_paged", name, B, HK, HV, K, V, io_dtype, out_dtype or io_dtype, state_layout,
+    wkind = ("kda" if kind == "kda" else "gdn") + ("_paged" if suffix_lengths is None else "_paged_varlen")
+    return Workload(wkind, name or wkind, B, HK, HV, K, V, io_dtype, out_dtype or io_dtype, state_layout,
                     num_pages, inp, opts, pool_seed=seed + 1)
+
+
+def gdn_paged(B, HK, HV, K, V, **kw):
+    """Single-token GDN decode on a CSR-paged pool with shared prefix pages."""
+    kw.setdefault("name", "gdn_paged")
+    return paged("gdn", B, HK, HV, K, V, **kw)
 
 
 # ------------------------------------------------------------------ named workloads
@@ -246,10 +272,25 @@ def fp8_qdq_gdn_b512(seed=1005):
                       qdq="fp8_e4m3_tile", block_v=64)
 
 
+def paged_kda_b256(seed=1006, state_layout=V_FIRST, index_dtype=torch.int64):
+    """The paged B=256 workload with KDA gating: HK=HV=32, raw_gate [B, 32, 128], dt_bias [32, 128]."""
+    return paged("kda", 256, 32, 32, 128, 128, max_prefix=2048, page_size=16, share_frac=0.1,
+                 state_layout=state_layout, index_dtype=index_dtype, seed=seed, name="paged_kda_b256_hv32_k128_ps16")
+
+
+def paged_gdn_varlen_b256_t4(seed=1007, state_layout=V_FIRST, index_dtype=torch.int64):
+    """The paged B=256 workload decoding 4 tokens per sequence (pages filled mid-suffix are written)."""
+    return paged("gdn", 256, 16, 32, 128, 128, max_prefix=2048, page_size=16, share_frac=0.1,
+                 suffix_lengths=np.full(256, 4), state_layout=state_layout, index_dtype=index_dtype, seed=seed,
+                 name="paged_gdn_varlen_b256_t4_hv32_k128_ps16")
+
+
 NAMED = {
     "tiny_gdn": tiny_gdn,
     "pooled_gdn_b64": pooled_gdn_b64,
     "pooled_kda_varlen_b128": pooled_kda_varlen_b128,
     "paged_gdn_b256": paged_gdn_b256,
     "fp8_qdq_gdn_b512": fp8_qdq_gdn_b512,
+    "paged_kda_b256": paged_kda_b256,
+    "paged_gdn_varlen_b256_t4": paged_gdn_varlen_b256_t4,
 }

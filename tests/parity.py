@@ -39,6 +39,7 @@ import recurrent_state_decode_amd as rsd
 from recurrent_state_decode_amd import workloads as wl
 from oracle import decode as odec
 from oracle import e4m3
+from oracle import paging as opaging
 
 STATE_RTOL = 2e-3
 OUT_REL_L2 = 2e-3
@@ -56,22 +57,52 @@ def host_int(t):
     return None if t is None else t.detach().to("cpu").to(torch.int64).numpy()
 
 
-def gpu_call(w, pool, d, out=None, **over):
-    """Run workload ``w`` on the device pool through the binding. Returns ``out``."""
+def _opts(w, over, drop=()):
     o = dict(w.options)
     o.pop("page_size", None)
     o.update(over)
-    common = dict(state_layout=w.state_layout, out_dtype=w.out_dtype, **o)
+    for k in drop:
+        o.pop(k, None)
+    return o
+
+
+def gpu_call(w, pool, d, out=None, **over):
+    """Run workload ``w`` on the device pool through the binding. Returns ``out``."""
+    common = dict(state_layout=w.state_layout, out_dtype=w.out_dtype, **_opts(w, over))
+    ps = w.options.get("page_size")
     if w.kind == "gdn_pooled":
         return rsd.gdn_decode_pooled(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
                                      d["cu_seqlens"], d["state_indices"], pool, out, **common)
     if w.kind == "kda_pooled":
         return rsd.kda_decode_pooled(d["q"], d["k"], d["v"], d["raw_gate"], d["beta_logits"], d["a_log"],
                                      d["dt_bias"], d["cu_seqlens"], d["state_indices"], pool, out, **common)
+    table = (d["page_indices"], d["page_indptr"], d["last_page_len"])
     if w.kind == "gdn_paged":
-        return rsd.gdn_decode_paged(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
-                                    d["page_indices"], d["page_indptr"], d["last_page_len"], pool, out, **common)
+        return rsd.gdn_decode_paged(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"], *table,
+                                    pool, out, **common)
+    if w.kind == "kda_paged":
+        return rsd.kda_decode_paged(d["q"], d["k"], d["v"], d["raw_gate"], d["beta_logits"], d["a_log"],
+                                    d["dt_bias"], *table, pool, out, **common)
+    if w.kind == "gdn_paged_varlen":
+        return rsd.gdn_decode_paged_varlen(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                                           d["cu_seqlens"], *table, ps, pool, out, **common)
+    if w.kind == "kda_paged_varlen":
+        return rsd.kda_decode_paged_varlen(d["q"], d["k"], d["v"], d["raw_gate"], d["beta_logits"], d["a_log"],
+                                           d["dt_bias"], d["cu_seqlens"], *table, ps, pool, out, **common)
     raise ValueError(w.kind)
+
+
+def written_rows(w, b):
+    """[(token index inside the suffix, pool row)] the call writes for sequence b (none if its suffix is empty)."""
+    inp = w.inputs
+    cu = host_int(inp.get("cu_seqlens"))
+    if cu is not None and cu[b + 1] <= cu[b]:
+        return []
+    nb = 1 if cu is None or w.kind in ("gdn_paged", "kda_paged") else int(cu[b + 1] - cu[b])
+    if w.kind.endswith("paged_varlen"):
+        return opaging.paged_suffix_rows(host_int(inp["page_indices"]), host_int(inp["page_indptr"]),
+                                         host_int(inp["last_page_len"]), w.options["page_size"], nb, b)[1]
+    return [(nb - 1, rows_for(w, [b])[1][0])]
 
 
 def rows_for(w, seqs=None):
@@ -79,16 +110,22 @@ def rows_for(w, seqs=None):
     inp = w.inputs
     seqs = range(w.B) if seqs is None else seqs
     reads, writes = [], []
+    cu = host_int(inp.get("cu_seqlens"))
     for b in seqs:
-        if w.kind == "gdn_paged":
+        if cu is not None and cu[b + 1] <= cu[b]:
+            continue
+        if w.kind in ("gdn_paged", "kda_paged"):
             ind, ptr, lpl = host_int(inp["page_indices"]), host_int(inp["page_indptr"]), host_int(inp["last_page_len"])
             last = int(ind[ptr[b + 1] - 1])
             reads.append(int(ind[ptr[b + 1] - 2]) if lpl[b] == 1 else last)
             writes.append(last)
+        elif w.kind in ("gdn_paged_varlen", "kda_paged_varlen"):
+            r, wr = opaging.paged_suffix_rows(host_int(inp["page_indices"]), host_int(inp["page_indptr"]),
+                                              host_int(inp["last_page_len"]), w.options["page_size"],
+                                              int(cu[b + 1] - cu[b]), b)
+            reads.append(r)
+            writes.extend(row for _, row in wr)
         else:
-            cu = host_int(inp["cu_seqlens"])
-            if cu is not None and cu[b + 1] <= cu[b]:
-                continue
             s = int(inp["state_indices"][b])
             reads.append(s)
             writes.append(s)
@@ -97,27 +134,25 @@ def rows_for(w, seqs=None):
 
 def oracle_call(w, pool_rows, seqs=None, trace=None, **over):
     """Run the CPU oracle for workload ``w`` on ``pool_rows`` {row: float64 tile}."""
-    o = dict(w.options)
-    o.pop("page_size", None)
-    o.update(over)
-    o.pop("out_dtype", None)
+    o = _opts(w, over, drop=("out_dtype", "slots"))
     inp = w.inputs
     common = dict(state_layout=w.state_layout, seqs=seqs, trace=trace, **o)
-    if w.kind == "gdn_pooled":
-        return odec.gdn_decode_pooled(host64(inp["q"]), host64(inp["k"]), host64(inp["v"]), host64(inp["a"]),
-                                      host64(inp["b"]), host64(inp["A_log"]), host64(inp["dt_bias"]),
-                                      host_int(inp["cu_seqlens"]), host_int(inp["state_indices"]), pool_rows,
-                                      **common)
-    if w.kind == "kda_pooled":
-        return odec.kda_decode_pooled(host64(inp["q"]), host64(inp["k"]), host64(inp["v"]),
-                                      host64(inp["raw_gate"]), host64(inp["beta_logits"]), host64(inp["a_log"]),
-                                      host64(inp["dt_bias"]), host_int(inp["cu_seqlens"]),
-                                      host_int(inp["state_indices"]), pool_rows, **common)
-    if w.kind == "gdn_paged":
-        return odec.gdn_decode_paged(host64(inp["q"]), host64(inp["k"]), host64(inp["v"]), host64(inp["a"]),
-                                     host64(inp["b"]), host64(inp["A_log"]), host64(inp["dt_bias"]),
-                                     host_int(inp["page_indices"]), host_int(inp["page_indptr"]),
-                                     host_int(inp["last_page_len"]), pool_rows, **common)
+    kda = w.kind.startswith("kda")
+    gate = host64(inp["raw_gate"] if kda else inp["a"])
+    beta = host64(inp["beta_logits"] if kda else inp["b"])
+    alog = host64(inp["a_log"] if kda else inp["A_log"])
+    qkv = (host64(inp["q"]), host64(inp["k"]), host64(inp["v"]), gate, beta, alog, host64(inp["dt_bias"]))
+    cu = host_int(inp.get("cu_seqlens"))
+    if w.kind in ("gdn_pooled", "kda_pooled"):
+        fn = odec.kda_decode_pooled if kda else odec.gdn_decode_pooled
+        return fn(*qkv, cu, host_int(inp["state_indices"]), pool_rows, **common)
+    table = (host_int(inp["page_indices"]), host_int(inp["page_indptr"]), host_int(inp["last_page_len"]))
+    if w.kind in ("gdn_paged", "kda_paged"):
+        fn = odec.kda_decode_paged if kda else odec.gdn_decode_paged
+        return fn(*qkv, *table, pool_rows, **common)
+    if w.kind in ("gdn_paged_varlen", "kda_paged_varlen"):
+        fn = odec.kda_decode_paged_varlen if kda else odec.gdn_decode_paged_varlen
+        return fn(*qkv, cu, *table, w.options["page_size"], pool_rows, **common)
     raise ValueError(w.kind)
 
 
@@ -137,7 +172,7 @@ def bf16_ulp(x):
 
 def token_rows(w, seqs):
     """Token indices (output rows) that belong to sequences ``seqs``."""
-    if w.kind == "gdn_paged":
+    if w.kind in ("gdn_paged", "kda_paged"):
         return np.array(sorted(seqs), dtype=np.int64)
     cu = host_int(w.inputs["cu_seqlens"])
     if cu is None:
@@ -153,7 +188,8 @@ def _step_at(S, bv, mag):
 
 
 def qdq_bounds(w, trace, seqs):
-    """Propagated one-step-per-rounding bounds: ({token: output bound [H, V]}, {seq: final state bound [H, K, V]})."""
+    """Propagated one-step-per-rounding bounds: ({token: output bound [H, V]},
+    {seq: [state bound [H, K, V] after each of its tokens]})."""
     bv = w.options.get("block_v", 64)
     stored = w.options.get("readout", "working") == "stored"
     qinit = bool(w.options.get("quantize_initial", False))
@@ -163,7 +199,7 @@ def qdq_bounds(w, trace, seqs):
         recs = trace.get(b, [])
         if not recs:
             continue
-        t0 = b if (w.kind == "gdn_paged" or cu is None) else int(cu[b])
+        t0 = b if (w.kind in ("gdn_paged", "kda_paged") or cu is None) else int(cu[b])
         S0 = recs[0]["S_in"]
         E = _step_at(S0, bv, np.abs(S0) * 1.125) if qinit else np.zeros_like(S0)
         for i, rec in enumerate(recs):
@@ -182,7 +218,7 @@ def qdq_bounds(w, trace, seqs):
                          + (qk * rec["beta"])[:, None] * np.einsum("hk,hkv->hv", kabs, aE))
             out_b[t0 + i] = bound
             E = E_new
-        state_b[b] = E
+            state_b.setdefault(b, []).append(E)
     return out_b, state_b
 
 
@@ -291,8 +327,7 @@ def run_and_check(w, seqs=None, report=None, pool=None, snapshot=True, check_all
         for t, bnd in out_b.items():
             full[t] = bnd
         bound = full[trows]
-        _, wr = rows_for(w, [b for b in seq_list if b in seq_b])
-        state_bound = {row: seq_b[b] for row, b in zip(wr, [b for b in seq_list if b in seq_b])}
+        state_bound = {row: seq_b[b][i] for b in seq_list if b in seq_b for i, row in written_rows(w, b)}
     if len(trows):
         compare_outputs(out, ref_out, w, trows, report, qdq_bound=bound)
     got = gather_rows(pool, list(ref_written))

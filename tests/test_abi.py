@@ -96,3 +96,28 @@ def test_paged_and_kda_argument_errors():
     o = bnd._options()
     assert lib.kda_decode_pooled(*ptrs, 2, 4, 1, 2, 128, 128, 4, ctypes.byref(o), None) == bnd.GDN_ERR_INVALID
     assert "cu_seqlens" in lib.gdn_last_error().decode()
+
+
+@no_gpu
+def test_new_paged_entry_points_argument_errors():
+    lib = rsd.load_library()
+    o = bnd._options(index_dtype=bnd.GDN_I64)
+    # varlen paged: page_size must be positive, cu_seqlens is required
+    args = [FAKE] * 11
+    assert lib.gdn_decode_paged_varlen(*args, 0, FAKE, FAKE, 2, 4, 1, 2, 128, 128, 10, 4, ctypes.byref(o), None) \
+        == bnd.GDN_ERR_INVALID
+    args[7] = None
+    assert lib.kda_decode_paged_varlen(*args, 16, FAKE, FAKE, 2, 4, 1, 2, 128, 128, 10, 4, ctypes.byref(o), None) \
+        == bnd.GDN_ERR_INVALID
+    # slots belong to single-token paged calls
+    o2 = bnd._options(index_dtype=bnd.GDN_I64, slots=0x2000)
+    assert lib.gdn_decode_paged_varlen(*([FAKE] * 11), 16, FAKE, FAKE, 2, 4, 1, 2, 128, 128, 10, 4,
+                                       ctypes.byref(o2), None) == bnd.GDN_ERR_INVALID
+    ptrs = [FAKE] * 11
+    assert lib.gdn_decode_pooled(*ptrs, 2, 2, 1, 2, 128, 128, 4, ctypes.byref(o2), None) == bnd.GDN_ERR_INVALID
+    assert "slots" in lib.gdn_last_error().decode()
+    # the slot pass checks its index type and pointers
+    assert lib.gdn_paged_decode_slots(FAKE, FAKE, FAKE, 4, 9, FAKE, None) == bnd.GDN_ERR_INVALID
+    assert lib.gdn_paged_decode_slots(FAKE, FAKE, None, 4, bnd.GDN_I32, FAKE, None) == bnd.GDN_ERR_INVALID
+    assert lib.kda_decode_paged(*([FAKE] * 12), 2, 2, 3, 128, 128, 10, 4, ctypes.byref(o), None) \
+        == bnd.GDN_ERR_INVALID   # HV % HK != 0

@@ -118,3 +118,62 @@ def test_pooled_rows_and_token_ranges():
     assert paging.pooled_token_range(cu, 1) == (3, 3)
     assert paging.pooled_token_range(None, 5) == (5, 6)
     assert paging.pooled_rows([9, 4], 1) == (4, 4)
+
+
+@pytest.mark.parametrize("page_size", [1, 2, 4, 16])
+def test_single_token_suffix_rows_equal_the_new_page_rule(page_size):
+    """paged_suffix_rows (page of token m) with one token == paged_rows (last_page_len == 1 rule)."""
+    rng = np.random.default_rng(60 + page_size)
+    lengths = list(range(2, 3 * page_size + 4)) + list(rng.integers(2, 300, 40))
+    ids, indptr, last_len = _table(lengths, page_size, rng)
+    for b in range(len(lengths)):
+        r, writes = paging.paged_suffix_rows(ids, indptr, last_len, page_size, 1, b)
+        assert (r, writes[0][1]) == paging.paged_rows(ids, indptr, last_len, b) and len(writes) == 1
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("page_size", [1, 3, 4])
+def test_paged_suffix_equals_chain_of_single_token_calls(kind, page_size):
+    """One call decoding several tokens per sequence == one single-token paged call per token,
+    with the table grown by one token each time; every page written along the way matches."""
+    rng = np.random.default_rng(70 + page_size)
+    HK, HV, K, V = 1, 2, 4, 3
+    prefix = [3, 1, 7, 4]                     # tokens before the suffix
+    suffix = [5, 1, 6, 0]                     # tokens decoded by the call
+    B = len(prefix)
+    T = sum(suffix)
+    cu = np.concatenate([[0], np.cumsum(suffix)])
+    q, k = rng.standard_normal((T, HK, K)), rng.standard_normal((T, HK, K))
+    v = rng.standard_normal((T, HV, V))
+    gate = rng.standard_normal((T, HV, K)) if kind == "kda" else rng.standard_normal((T, HV))
+    bl = rng.standard_normal((T, HV))
+    A_log = rng.uniform(0, np.log(16), HV)
+    dt = rng.uniform(-1, 1, (HV, K)) if kind == "kda" else rng.uniform(-1, 1, HV)
+    # page ids for the final lengths; every page a sequence will ever use is distinct
+    lengths = [p + s for p, s in zip(prefix, suffix)]
+    ids, indptr, last_len = _table(lengths, page_size, rng)
+    pool = {int(i): rng.standard_normal((HV, V, K)) * 0.1 for i in ids}
+    start_pool = {r: x.copy() for r, x in pool.items()}
+    multi = odec.kda_decode_paged_varlen if kind == "kda" else odec.gdn_decode_paged_varlen
+    out_m, wr_m = multi(q, k, v, gate, bl, A_log, dt, cu, ids, indptr, last_len, page_size, start_pool)
+    # chain: grow each sequence one token at a time with the single-token rule
+    single = odec.kda_decode_paged if kind == "kda" else odec.gdn_decode_paged
+    chain = {r: x.copy() for r, x in pool.items()}
+    out_c = np.full_like(out_m, np.nan)
+    for b in range(B):
+        for i in range(suffix[b]):
+            t = cu[b] + i
+            n = prefix[b] + i + 1
+            pages = -(-n // page_size)
+            sub_ids = ids[indptr[b]:indptr[b] + pages]
+            o, w = single(q[t:t + 1], k[t:t + 1], v[t:t + 1], gate[t:t + 1], bl[t:t + 1], A_log, dt, sub_ids,
+                          np.array([0, pages]), np.array([n - page_size * (pages - 1)]), chain)
+            out_c[t] = o[0]
+            (row, tile), = w.items()
+            chain[row] = tile
+    np.testing.assert_allclose(out_m, out_c, rtol=1e-13, atol=1e-14)
+    for row, tile in wr_m.items():
+        np.testing.assert_allclose(tile, chain[row], rtol=1e-13, atol=1e-14)
+    # rows the chain changed are exactly the rows the multi-token call wrote
+    changed = {r for r in chain if not np.array_equal(chain[r], pool[r])}
+    assert changed == set(wr_m)

@@ -242,3 +242,60 @@ def test_single_token_vfirst_no_cu_seqlens():
     w = wl.gdn_pooled(24, 4, 8, 128, 256, lengths=None, num_slots=30, state_layout="V_FIRST", seed=45)
     rep, _, _ = P.run_and_check(w)
     _report("narrow/no_cu", rep)
+
+
+# ---------------------------------------------------------------- paged KDA, paged suffixes, precomputed slots
+
+@pytest.mark.parametrize("layout", ["V_FIRST", "K_FIRST"])
+def test_paged_kda_b256(layout):
+    w = wl.paged_kda_b256(state_layout=layout)
+    rep, _, _ = P.run_and_check(w)
+    _report(f"{w.name}/{layout}", rep)
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("layout", ["V_FIRST", "K_FIRST"])
+@pytest.mark.parametrize("idx", [torch.int32, torch.int64])
+def test_paged_varlen_small(kind, layout, idx):
+    # page_size 4 and suffixes of 0..9 tokens: suffixes that fill 0, 1 and 2 pages, start on a
+    # page boundary (state read from a full, possibly shared page) and cross the 8-token chunks
+    suffix = np.array([0, 1, 2, 3, 4, 5, 8, 9, 7, 1, 4, 0, 6, 2, 9, 3])
+    w = wl.paged(kind, len(suffix), 2, 4, 128, 128, max_prefix=30, page_size=4, share_frac=0.3,
+                 suffix_lengths=suffix, state_layout=layout, index_dtype=idx, seed=46)
+    rep, _, _ = P.run_and_check(w)
+    _report(f"paged_varlen/{kind}/{layout}/{idx}", rep)
+
+
+@pytest.mark.parametrize("layout", ["V_FIRST", "K_FIRST"])
+def test_paged_varlen_qdq(layout):
+    suffix = np.array([3, 5, 1, 0, 8, 4])
+    w = wl.paged("gdn", len(suffix), 2, 4, 128, 128, max_prefix=30, page_size=4, share_frac=0.3,
+                 suffix_lengths=suffix, state_layout=layout, seed=47, qdq="fp8_e4m3_tile", block_v=64)
+    rep, _, _ = P.run_and_check(w)
+    _report(f"paged_varlen_qdq/{layout}", rep)
+
+
+def test_paged_varlen_b256_t4():
+    w = wl.paged_gdn_varlen_b256_t4()
+    rep, _, _ = P.run_and_check(w)
+    _report(w.name, rep)
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("idx", [torch.int32, torch.int64])
+def test_precomputed_slots_match_table_and_inline_resolution(kind, idx):
+    import recurrent_state_decode_amd as rsd
+    w = wl.paged(kind, 48, 2, 4, 128, 128, max_prefix=40, page_size=4, share_frac=0.3, index_dtype=idx, seed=48)
+    d = P.device_inputs(w)
+    slots = rsd.gdn_paged_decode_slots(d["page_indices"], d["page_indptr"], d["last_page_len"])
+    torch.cuda.synchronize()
+    reads, writes = P.rows_for(w)
+    assert slots[:, 0].cpu().tolist() == reads and slots[:, 1].cpu().tolist() == writes
+    pool_a = wl.make_pool(w, "cuda")
+    pool_b = pool_a.clone()
+    out_a = P.gpu_call(w, pool_a, d)
+    out_b = P.gpu_call(w, pool_b, d, slots=slots)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b) and torch.equal(pool_a, pool_b)
+    rep, _, _ = P.run_and_check(w, slots=slots)
+    _report(f"slots/{kind}/{idx}", rep)

@@ -72,3 +72,34 @@ def test_paged_b256_table_shape_and_sharing():
     counts = np.bincount(ind, minlength=w.num_rows)
     assert np.sum((lpl == 1) & (counts[reads] > 1)) >= 1
     assert w.pool_shape() == (w.num_rows, 32, 128, 128)
+
+
+def test_paged_varlen_tables_never_share_pages_that_a_suffix_writes():
+    from oracle import paging as opaging
+    for seed in range(4):
+        suffix = np.random.default_rng(seed).integers(0, 10, 30)
+        w = wl.paged("gdn", 30, 2, 4, 16, 16, max_prefix=60, page_size=4, share_frac=0.3,
+                     suffix_lengths=suffix, seed=seed)
+        ind, ptr, lpl = (w.inputs[k].numpy() for k in ("page_indices", "page_indptr", "last_page_len"))
+        cu = w.inputs["cu_seqlens"].numpy()
+        counts = np.bincount(ind, minlength=w.num_rows)
+        writes, reads = [], []
+        for b in range(w.B):
+            nb = int(cu[b + 1] - cu[b])
+            if nb == 0:
+                continue
+            r, wr = opaging.paged_suffix_rows(ind, ptr, lpl, 4, nb, b)
+            reads.append(r)
+            writes.extend(row for _, row in wr)
+        assert len(writes) == len(set(writes))              # each written page once
+        assert all(counts[r] == 1 for r in writes)           # written pages are never shared
+        assert not (set(writes) & set(reads)) or all(      # a sequence may update its own read page
+            reads.count(r) == 1 for r in set(writes) & set(reads))
+        assert w.T == int(suffix.sum()) and w.inputs["q"].shape[0] == w.T
+
+
+def test_paged_kda_workload_shapes():
+    w = wl.paged_kda_b256()
+    assert w.kind == "kda_paged" and w.inputs["raw_gate"].shape == (256, 32, 128)
+    assert w.inputs["dt_bias"].shape == (32, 128) and w.inputs["a_log"].shape == (32,)
+    _check_paged_invariants(w, 16)
