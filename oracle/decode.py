@@ -3,7 +3,8 @@
 Each one resolves the rows a sequence reads and writes (``paging``), turns
 raw inputs into q_hat, k_hat, alpha = exp(g), beta (``activations``), and
 folds the step over the sequence's suffix tokens (``recurrence``), with the
-optional tile quantise/dequantise (``e4m3``).  Everything is float64.
+optional state quantise/dequantise (``e4m3`` tiles or the ``hadamard``
+int8_hadamard32 codec).  Everything is float64.
 
 Pages followed:
 * max.nn.state_space.kda_decode (signature, Parameters, Returns);
@@ -29,6 +30,7 @@ import numpy as np
 
 from . import activations as act
 from . import e4m3
+from . import hadamard
 from . import paging
 from .recurrence import run_suffix
 
@@ -38,6 +40,9 @@ def _qdq_fn(qdq, block_v):
         return None
     if qdq == "fp8_e4m3_tile":
         return lambda S: e4m3.tile_qdq(S, block_v)
+    if qdq == "int8_hadamard32":
+        # block_v is only the execution tile width for this codec
+        return hadamard.int8_hadamard32_qdq
     raise ValueError(f"unknown qdq {qdq!r}")
 
 

@@ -1,0 +1,98 @@
+"""The int8_hadamard32 state codec: value-basis Hadamard rotation + int8 per (key channel, 32 values).
+
+Pages followed:
+* modelopt ... linear_attention.config, LinearAttentionConfig: decode's
+  int8_hadamard32 codec fixes the scales to one key channel and 32 values
+  (instead of one per [Dk, block_v] tile); ``state.block_v`` stays the
+  execution tile width.  LinearAttentionDecodeConfig: ``state_codec`` is
+  'tile' or 'int8_hadamard32'.
+* modelopt ... linear_attention.decode, LinearAttentionCarry: the carry has a
+  ``value_basis`` and ``reconstruct`` returns the original value basis unless
+  told otherwise -- the codec works in a rotated value basis and the state is
+  handed back in the original one.
+
+Readings (listed in the design doc; the pages give no formulas):
+* the rotation is the 32-point Walsh-Hadamard transform in Sylvester order,
+  normalised to be orthonormal (H / sqrt(32), H the +-1 matrix), applied to
+  each group of 32 consecutive value columns of every key row:
+  y = x H / sqrt(32); it is its own inverse;
+* int8 is symmetric: scale s = amax(|y| over the 32 values) / 127, code =
+  round-to-nearest-even(y / s) clamped to [-127, 127]; amax = 0 leaves the
+  group unchanged;
+* the state returned is (s * code) H / sqrt(32) (the original basis).
+
+Written with z = x H the 1/sqrt(32) factors cancel: y / s = 127 z / amax|z|
+and (s * code) H / sqrt(32) = (code H) * amax|z| / (127 * 32).  The code
+below uses that form, so that values whose rotation is exactly on the code
+grid (ties included) are decided exactly.  With ``precision='float32'``
+every operation is rounded to float32 -- z by radix-2 butterflies (a + b,
+a - b) over strides 1, 2, 4, 8, 16, inv = f32(127 / amax|z|), code =
+rint(f32(z * inv)), result = f32(code H) * f32(f32(amax|z| / 127) / 32) --
+so that both sides decide each code in float32; ``'float64'`` is the same
+rule in float64.
+
+Pins (tests/test_oracle_hadamard.py): H / sqrt(32) is orthonormal and
+symmetric, the butterfly transform equals the matrix product, the folded
+form equals the definition with explicit normalisation, code points
+round-trip exactly, values on the half-code grid round to even exactly, the
+error is within half a step per rotated coordinate, groups and key rows are
+independent, and a single spike is spread over all 32 coordinates and
+reconstructed exactly.
+"""
+import numpy as np
+
+GROUP = 32
+INT8_MAX = 127.0
+
+
+def hadamard_matrix(n=GROUP):
+    """Sylvester Hadamard matrix of order n (entries +-1): H_2n = [[H, H], [H, -H]]."""
+    H = np.array([[1.0]])
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def fwht_butterflies(x, dtype=np.float64):
+    """Unnormalised Walsh-Hadamard transform along the last axis (length 32) as radix-2 butterflies."""
+    y = np.array(x, dtype=dtype, copy=True)
+    n = y.shape[-1]
+    h = 1
+    while h < n:
+        y = y.reshape(y.shape[:-1] + (n // (2 * h), 2, h))
+        a = y[..., 0, :].copy()
+        b = y[..., 1, :].copy()
+        y[..., 0, :] = a + b
+        y[..., 1, :] = a - b
+        y = y.reshape(y.shape[:-3] + (n,))
+        h *= 2
+    return y
+
+
+def int8_hadamard32_qdq(S, precision="float32"):
+    """Quantise/dequantise S [H, K, V] with the int8_hadamard32 codec (V a multiple of 32)."""
+    S = np.asarray(S, dtype=np.float64)
+    Hh, K, V = S.shape
+    if V % GROUP != 0:
+        raise ValueError("the value head dim must be a multiple of 32")
+    x = S.reshape(Hh, K, V // GROUP, GROUP)
+    if precision == "float64":
+        z = x @ hadamard_matrix()
+        amax = np.max(np.abs(z), axis=-1, keepdims=True)
+        safe = np.where(amax > 0, amax, 1.0)
+        code = np.clip(np.rint(z * INT8_MAX / safe), -INT8_MAX, INT8_MAX)
+        xq = (code @ hadamard_matrix()) * (safe / INT8_MAX / GROUP)
+        out = np.where(amax > 0, xq, x)
+        return out.reshape(Hh, K, V)
+    if precision == "float32":
+        f = np.float32
+        z = fwht_butterflies(x.astype(f), dtype=f)
+        amax = np.max(np.abs(z), axis=-1, keepdims=True)
+        safe = np.where(amax > 0, amax, f(1.0)).astype(f)
+        inv = (f(INT8_MAX) / safe).astype(f)
+        c = ((safe / f(INT8_MAX)).astype(f) / f(GROUP)).astype(f)
+        code = np.clip(np.rint((z * inv).astype(f)), -INT8_MAX, INT8_MAX).astype(f)
+        xq = (fwht_butterflies(code, dtype=f) * c).astype(f)
+        out = np.where(amax > 0, xq, x.astype(f))
+        return out.reshape(Hh, K, V).astype(np.float64)
+    raise ValueError(f"unknown precision {precision!r}")

@@ -1,17 +1,23 @@
 """Plant plausible mistakes in the oracle (on the CPU) and check that the pins catch each one.
 
-Each mutation replaces one piece of ``oracle.recurrence`` or
-``oracle.activations`` with a wrong variant; the pin tests of
-tests/test_oracle_recurrence.py and tests/test_oracle_activations.py are
-then run against the mutated oracle and at least one of them must fail.
+Each mutation replaces one piece of ``oracle.recurrence``,
+``oracle.activations`` or ``oracle.hadamard`` with a wrong variant; the pin
+tests of tests/test_oracle_recurrence.py, tests/test_oracle_activations.py
+and tests/test_oracle_hadamard.py are then run against the mutated oracle
+and at least one of them must fail.
 """
 import numpy as np
 import pytest
 
 import oracle.activations as act
+import oracle.hadamard as had
 import oracle.recurrence as rec
 import tests.test_oracle_activations as pins_act
+import tests.test_oracle_hadamard as pins_had
 import tests.test_oracle_recurrence as pins
+
+_true_hadamard = had.hadamard_matrix
+_true_qdq = had.int8_hadamard32_qdq
 
 
 def _order_write_then_decay(S, q_hat, k_hat, v, alpha, beta, state_qdq=None, readout_mode="working"):
@@ -63,7 +69,53 @@ def _sigmoid_wrong_sign(x):
     return 1.0 / (1.0 + np.exp(np.asarray(x, dtype=np.float64)))
 
 
+def _hadamard_one_sign(n=32):
+    H = _true_hadamard(n).copy()
+    H[3, 7] = -H[3, 7]
+    return H
+
+
+def _butterfly_swapped(x, dtype=np.float64):
+    y = np.array(x, dtype=dtype, copy=True)
+    n = y.shape[-1]
+    h = 1
+    while h < n:
+        y = y.reshape(y.shape[:-1] + (n // (2 * h), 2, h))
+        a, b = y[..., 0, :].copy(), y[..., 1, :].copy()
+        y[..., 0, :], y[..., 1, :] = a - b, a + b
+        y = y.reshape(y.shape[:-3] + (n,))
+        h *= 2
+    return y
+
+
+def _qdq_round_half_away(S, precision="float32"):
+    S = np.asarray(S, dtype=np.float64)
+    Hh, K, V = S.shape
+    x = S.reshape(Hh, K, V // 32, 32)
+    z = x @ _true_hadamard()
+    amax = np.max(np.abs(z), axis=-1, keepdims=True)
+    safe = np.where(amax > 0, amax, 1.0)
+    t = z * 127 / safe
+    code = np.sign(t) * np.floor(np.abs(t) + 0.5)
+    out = np.where(amax > 0, (code @ _true_hadamard()) * (safe / 127 / 32), x)
+    return out.reshape(Hh, K, V)
+
+
+def _qdq_no_back_rotation(S, precision="float32"):
+    S = np.asarray(S, dtype=np.float64)
+    Hh, K, V = S.shape
+    y = S.reshape(Hh, K, V // 32, 32) @ (_true_hadamard() / np.sqrt(32))
+    s = np.max(np.abs(y), axis=-1, keepdims=True) / 127
+    s = np.where(s > 0, s, 1.0)
+    return (s * np.rint(y / s)).reshape(Hh, K, V)
+
+
 MUTATIONS = {
+    "hadamard_entry_sign": [(had, "hadamard_matrix", _hadamard_one_sign)],
+    "butterfly_swapped": [(had, "fwht_butterflies", _butterfly_swapped)],
+    "int8_max_128": [(had, "INT8_MAX", 128.0)],
+    "codec_round_half_away": [(had, "int8_hadamard32_qdq", _qdq_round_half_away)],
+    "codec_no_back_rotation": [(had, "int8_hadamard32_qdq", _qdq_no_back_rotation)],
     "no_decay": [(rec, "decay", _no_decay)],
     "decay_after_write": [(rec, "gated_delta_step", _order_write_then_decay),
                           (pins, "gated_delta_step", _order_write_then_decay)],
@@ -92,6 +144,13 @@ PIN_TESTS = [
     pins_act.test_softplus_special_values_and_math_library,
     pins_act.test_sigmoid_special_values_and_math_library,
     pins_act.test_gate_formula_against_math_library,
+    pins_had.test_hadamard_is_orthonormal_symmetric_and_butterflies_equal_the_matrix,
+    pins_had.test_folded_form_equals_the_normalised_definition,
+    lambda: pins_had.test_half_code_grid_rounds_to_even_exactly("float64"),
+    lambda: pins_had.test_half_code_grid_rounds_to_even_exactly("float32"),
+    lambda: pins_had.test_code_points_round_trip("float32"),
+    lambda: pins_had.test_error_within_half_step_per_rotated_coordinate("float64"),
+    pins_had.test_a_spike_spreads_over_the_group_and_comes_back_exactly,
 ]
 
 
