@@ -200,7 +200,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="paged_gdn_b256",
                     choices=["paged_gdn_b256", "pooled_gdn_b64", "pooled_kda_varlen_b128", "fp8_qdq_gdn_b512",
-                             "tiny_gdn", "paged_kda_b256", "paged_gdn_varlen_b256_t4"])
+                             "tiny_gdn", "paged_kda_b256", "paged_gdn_varlen_b256_t4", "int8h32_gdn_b512"])
     ap.add_argument("--layout", default=None, help="override the pool layout (K_FIRST / V_FIRST)")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")

@@ -18,9 +18,9 @@
  *
  * with l2norm(x) = x / sqrt(sum(x^2) + 1e-6), softplus(x) =
  * max(x,0) + log1p(exp(-|x|)), value head h reading key head h / (HV/HK),
- * and, when enabled, an fp8 e4m3 quantise/dequantise of S after every token
- * with one amax/448 scale per [K, block_v] tile (OCP E4M3, nearest-even,
- * saturating).
+ * and, when enabled, a quantise/dequantise of S after every token: fp8
+ * e4m3 with one amax/448 scale per [K, block_v] tile (OCP E4M3,
+ * nearest-even, saturating), or the int8_hadamard32 codec (enum gdn_qdq).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -82,11 +82,25 @@ enum gdn_beta_mode { GDN_BETA_LOGITS = 0, GDN_BETA_PROBABILITY = 1 };
  * GDN_ERR_UNSUPPORTED. */
 enum gdn_gate_mode { GDN_GATE_ORIGINAL = 0, GDN_GATE_SAFE = 1 };
 
-/* State quantise/dequantise after every token (modelopt ...
- * linear_attention.config, LinearAttentionConfig: one dynamic scale per
- * [Dk, block_v] tile; ... linear_attention.decode: state_format
- * 'fp8_e4m3'). */
-enum gdn_qdq { GDN_QDQ_NONE = 0, GDN_QDQ_FP8_E4M3_TILE = 1 };
+/* State quantise/dequantise after every token.  The pool stays fp32; the
+ * state written back is the dequantised value.
+ *
+ * GDN_QDQ_FP8_E4M3_TILE (modelopt ... linear_attention.config,
+ * LinearAttentionConfig: one dynamic scale per [Dk, block_v] tile;
+ * ... linear_attention.decode: state_format 'fp8_e4m3'): OCP E4M3,
+ * scale = amax / 448 per tile, nearest even, saturating.
+ *
+ * GDN_QDQ_INT8_HADAMARD32 (LinearAttentionDecodeConfig, state_codec
+ * 'int8_hadamard32': one scale per key channel and 32 values;
+ * LinearAttentionCarry, value_basis / reconstruct: the codec works in a
+ * rotated value basis and the state is returned in the original one):
+ * every group of 32 consecutive value columns of a key row is rotated by
+ * the orthonormal 32-point Walsh-Hadamard matrix H/sqrt(32) (Sylvester
+ * order), rounded to int8 codes in [-127, 127] with scale amax/127 of the
+ * group (nearest even), dequantised and rotated back.  block_v stays the
+ * execution tile width and does not change the result; it must be a
+ * multiple of 32.  K = 128 only. */
+enum gdn_qdq { GDN_QDQ_NONE = 0, GDN_QDQ_FP8_E4M3_TILE = 1, GDN_QDQ_INT8_HADAMARD32 = 2 };
 
 /* modelopt ... linear_attention.config, LinearAttentionDecodeConfig,
  * readout: 'working' reads o from the updated state before its rounding,
@@ -261,7 +275,8 @@ const char* gdn_last_error(void);
 /* Head dims with a compiled kernel: writes up to `cap` (K, VB) pairs as
  * 2*n ints into `pairs` (NULL allowed) and returns the number of pairs
  * available.  A key head dim K is supported with any value head dim V that
- * is a multiple of its VB; fp8 tile QDQ needs block_v == VB. */
+ * is a multiple of its VB; fp8 tile QDQ needs block_v == VB; the
+ * int8_hadamard32 codec needs VB >= 32. */
 int gdn_supported_head_dims(int32_t* pairs, int cap);
 
 #ifdef __cplusplus

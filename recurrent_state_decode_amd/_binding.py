@@ -21,7 +21,7 @@ GDN_F32, GDN_BF16, GDN_I32, GDN_I64 = range(4)
 _LAYOUT = {"K_FIRST": 0, "V_FIRST": 1}
 _BETA = {"logits": 0, "probability": 1}
 _GATE = {"original": 0, "safe": 1}
-_QDQ = {None: 0, "none": 0, "fp8_e4m3_tile": 1}
+_QDQ = {None: 0, "none": 0, "fp8_e4m3_tile": 1, "int8_hadamard32": 2}
 _READOUT = {"working": 0, "stored": 1}
 _IO = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
 _IDX = {torch.int32: GDN_I32, torch.int64: GDN_I64}

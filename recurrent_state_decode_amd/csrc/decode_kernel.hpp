@@ -17,7 +17,11 @@
 // S_reg[i,:], S_reg[i,:] += (k_hat_i / c'_i) u).  A factor below 1e-20 is
 // applied to the registers and reset to 1, so S_reg never overflows.  The
 // fp8 tile quantisation keeps the codes in S_reg and moves the tile scale
-// amax/448 into c.  The tile is multiplied out once, when it is stored.
+// amax/448 into c.  The int8_hadamard32 codec acts on each (key row, 32
+// values) group of S_reg: it commutes with the row's scale c (the codes do
+// not depend on it), so c is left alone and the group is replaced by its
+// dequantised value in S_reg units.  The tile is multiplied out once, when
+// it is stored.
 //
 // Layout of the state tile in registers.  Each thread owns NS memory rows of
 // EV floats (128-bit loads); consecutive lanes cover a contiguous memory row,
@@ -90,6 +94,13 @@ enum Addr : int {
   kPaged1 = 1,      // one token per sequence, CSR page table, copy-on-new-page
   kPagedVar = 2,    // cu_seqlens suffixes on a CSR page table: every page a suffix
                     // token fills gets the state after that token
+};
+
+// State quantise/dequantise after every token.
+enum Qdq : int {
+  kQdqNone = 0,
+  kQdqTile = 1,     // fp8 e4m3, one amax/448 scale per [K, VB] tile
+  kQdqHad = 2,      // int8 codes of the 32-point Hadamard rotation, one scale per (key row, 32 values)
 };
 
 constexpr float kL2Eps = 1e-6f;
@@ -253,6 +264,50 @@ __device__ __forceinline__ void e4m3_roundtrip2(float& x0, float& x1) {
   x1 = back[1];
 }
 
+// ---- int8_hadamard32 codec (modelopt ... linear_attention.config,
+// LinearAttentionDecodeConfig, state_codec; ... linear_attention.decode,
+// LinearAttentionCarry, value_basis / reconstruct)
+//
+// A 32-value group sits in 8 consecutive lanes x 4 registers, value index
+// 4 * (lane % 8) + j.  wht32 is the unnormalised Walsh-Hadamard transform
+// (Sylvester order) of the group, in place: the two register bits by
+// in-thread butterflies, lane bits 0, 1, 2 by a partner lane (quad_perm
+// 0xB1 = xor 1, 0x4E = xor 2; xor 4 as row_half_mirror (xor 7) after the
+// quad reversal 0x1B (xor 3)).  A butterfly leaves a + b at the lower index
+// and a - b at the upper one; sg = -1 on lanes at the upper index gives
+// both as fma(sg, own, partner).
+__device__ __forceinline__ void wht32(float (&x)[4], float sg1, float sg2, float sg4) {
+  const float a0 = x[0] + x[1], a1 = x[0] - x[1], a2 = x[2] + x[3], a3 = x[2] - x[3];
+  x[0] = a0 + a2;
+  x[1] = a1 + a3;
+  x[2] = a0 - a2;
+  x[3] = a1 - a3;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] = fmaf(sg1, x[j], dpp<0xB1>(x[j]));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] = fmaf(sg2, x[j], dpp<0x4E>(x[j]));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] = fmaf(sg4, x[j], dpp<0x141>(dpp<0x1B>(x[j])));
+}
+
+// Codec of one group: with z = x H (H the +-1 Hadamard matrix) the rotated
+// values are y = c z / sqrt(32), so the codes rint(127 y / amax|y|) =
+// rint(127 z / amax|z|), and the dequantised group rotated back is
+// c * (codes H) * amax|z| / (127 * 32).  codes H is exact (integers below
+// 2^12).  An all-zero group stays zero.
+__device__ __forceinline__ void had_codec_group(float (&x)[4], float sg1, float sg2, float sg4) {
+  wht32(x, sg1, sg2, sg4);
+  float m = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+  m = lane_reduce<0, 3, OpMax>(m);
+  const float inv = m > 0.0f ? 127.0f / m : 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] = __builtin_amdgcn_fmed3f(__builtin_rintf(x[j] * inv), -127.0f, 127.0f);
+  wht32(x, sg1, sg2, sg4);
+  const float c = (m / 127.0f) * 0.03125f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] *= c;
+}
+
 constexpr float kTinyScale = 1e-20f;
 
 template <int K, int VB, int NT, bool VF>
@@ -274,7 +329,7 @@ struct Tile {
   static_assert(!VF || EV == 4 || K / 2 == 4 * LR, "two float4 half a row apart");
 };
 
-template <int K, int VB, int NT, bool VF, bool KDA, bool QDQ, int ADDR, typename TIn>
+template <int K, int VB, int NT, bool VF, bool KDA, int QDQ, int ADDR, typename TIn>
 __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   using Cfg = Tile<K, VB, NT, VF>;
   constexpr int NW = Cfg::NW, LR = Cfg::LR, RPW = Cfg::RPW, NS = Cfg::NS, LB = Cfg::LB;
@@ -299,6 +354,12 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   __shared__ float s_sc[TC][4];                    // alpha (GDN), beta, q_hat . k_hat
   __shared__ __align__(16) float s_red[VF ? 1 : 2][VF ? 1 : NW][2][VB];
   __shared__ float s_max[2][NW];
+  // V_FIRST int8_hadamard32: the tile passes through LDS to put each key
+  // row's values in lanes (row stride K + 1: conflict-free both ways)
+  constexpr bool HAD_LDS = VF && QDQ == kQdqHad;
+  __shared__ float s_t[HAD_LDS ? VB * (K + 1) : 1];
+  static_assert(QDQ != kQdqHad || (VF ? (K == 128 && VB == 64 && NT == 256) : (LR == 16 && EV == 4)),
+                "int8_hadamard32 codec shapes");
 
   const TIn* __restrict__ gq = static_cast<const TIn*>(p.q);
   const TIn* __restrict__ gk = static_cast<const TIn*>(p.k);
@@ -574,6 +635,47 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
     }
   };
 
+  // int8_hadamard32 codec of every (key row, 32 values) group of S_reg
+  auto had_codec = [&]() {
+    const float sg1 = (lane & 1) ? -1.0f : 1.0f;
+    const float sg2 = (lane & 2) ? -1.0f : 1.0f;
+    const float sg4 = (lane & 4) ? -1.0f : 1.0f;
+    if constexpr (!VF) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) had_codec_group(S[s], sg1, sg2, sg4);
+    } else {
+      // key rows in K_FIRST arrangement: row s * 16 + w * 4 + rg, values 4 * lr + j
+      constexpr int LD = K + 1;
+      constexpr int KR = K / 16;
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int e = 0; e < EV; ++e) s_t[row_idx(s) * LD + key_of(e)] = S[s][e];
+      __syncthreads();
+      float X[KR][4];
+#pragma unroll
+      for (int s = 0; s < KR; ++s)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) X[s][j] = s_t[(4 * lr + j) * LD + s * 16 + w * 4 + rg];
+#pragma unroll
+      for (int s = 0; s < KR; ++s) had_codec_group(X[s], sg1, sg2, sg4);
+#pragma unroll
+      for (int s = 0; s < KR; ++s)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s_t[(4 * lr + j) * LD + s * 16 + w * 4 + rg] = X[s][j];
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int e = 0; e < EV; ++e) S[s][e] = s_t[row_idx(s) * LD + key_of(e)];
+      __syncthreads();             // s_t is free for the next token
+    }
+  };
+  auto quantize = [&]() {
+    if constexpr (QDQ == kQdqTile) qdq_tile();
+    else if constexpr (QDQ == kQdqHad) had_codec();
+  };
+
   // output stores: 4 consecutive values (K_FIRST) or one (V_FIRST)
   auto store_out4 = [&](int64_t oi, const float (&o)[4]) {
     if (p.out_bf16) {
@@ -713,8 +815,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
       }
   };
 
-  if constexpr (QDQ) {
-    if (p.quantize_initial) qdq_tile();
+  if constexpr (QDQ != kQdqNone) {
+    if (p.quantize_initial) quantize();
   }
 
   for (int c0 = t0; c0 < t1; c0 += TC) {
@@ -731,7 +833,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
       const float beta = s_sc[tt][1];
       const float qk = s_sc[tt][2];
       const int64_t out_row = (static_cast<int64_t>(t) * p.HV + h) * p.V + out_col0;
-      const bool stored = QDQ && p.readout_stored;
+      const bool stored = QDQ != kQdqNone && p.readout_stored;
 
       float kh[NKEY], qh[NKEY];
       lds_keys(&s_k[tt][0], kh);
@@ -812,8 +914,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
           else S[s][e] = fmaf(kt[s], wv[e], S[s][e]);
         }
 
-      if constexpr (QDQ) {
-        qdq_tile();
+      if constexpr (QDQ != kQdqNone) {
+        quantize();
         if (stored) {
           // o = q_hat^T S after rounding
           float q2[NKEY];

@@ -38,7 +38,8 @@ enum class Kind { GdnPooled, GdnPaged, KdaPooled, KdaPaged, GdnPagedVar, KdaPage
 // narrow V-blocks pay that work V/VB times over):
 //   K=128, V_FIRST, no QDQ, about one token per sequence (T <= 1.5 B):
 //                            VB=8,  NT=128 (4 KiB of state per workgroup)
-//   K=128, otherwise:        VB=64, NT=256 (fp8 tiles need block_v == VB)
+//   K=128, otherwise:        VB=64, NT=256 (fp8 tiles need block_v == VB; the
+//                            int8_hadamard32 codec is compiled for this shape)
 //   K=16:                    VB=16, NT=64
 // V must be a multiple of VB.
 struct Shape {
@@ -57,7 +58,7 @@ struct HeadCfg {
 };
 constexpr HeadCfg kHeads[] = {{16, 16}, {128, 64}};
 
-template <int K, int VB, int NT, bool VF, bool KDA, bool QDQ, int ADDR, typename TIn>
+template <int K, int VB, int NT, bool VF, bool KDA, int QDQ, int ADDR, typename TIn>
 hipError_t launch_one(const gdn::Params& p, int64_t units, hipStream_t stream) {
   hipLaunchKernelGGL((gdn::decode_kernel<K, VB, NT, VF, KDA, QDQ, ADDR, TIn>), dim3(static_cast<uint32_t>(units)),
                      dim3(NT), 0, stream, p);
@@ -65,17 +66,29 @@ hipError_t launch_one(const gdn::Params& p, int64_t units, hipStream_t stream) {
 }
 
 struct Sel {
-  bool vfirst, qdq, bf16;
+  bool vfirst;
+  int qdq;          // gdn::Qdq
+  bool bf16;
 };
+
+// The int8_hadamard32 codec is compiled for the K=128, VB=64 shape only.
+template <int K, int VB, int NT>
+constexpr bool kHadShape = K == 128 && VB == 64 && NT == 256;
+
+template <int K, int VB, int NT, bool VF, bool KDA, int ADDR, typename TIn>
+hipError_t launch_qdq(const gdn::Params& p, int64_t units, int qdq, hipStream_t s) {
+  if (qdq == gdn::kQdqTile) return launch_one<K, VB, NT, VF, KDA, gdn::kQdqTile, ADDR, TIn>(p, units, s);
+  if (qdq == gdn::kQdqHad) {
+    if constexpr (kHadShape<K, VB, NT>) return launch_one<K, VB, NT, VF, KDA, gdn::kQdqHad, ADDR, TIn>(p, units, s);
+    return hipErrorInvalidValue;
+  }
+  return launch_one<K, VB, NT, VF, KDA, gdn::kQdqNone, ADDR, TIn>(p, units, s);
+}
 
 template <int K, int VB, int NT, bool KDA, int ADDR, typename TIn>
 hipError_t launch_layout_qdq(const gdn::Params& p, int64_t units, Sel sel, hipStream_t s) {
-  if (sel.vfirst) {
-    return sel.qdq ? launch_one<K, VB, NT, true, KDA, true, ADDR, TIn>(p, units, s)
-                   : launch_one<K, VB, NT, true, KDA, false, ADDR, TIn>(p, units, s);
-  }
-  return sel.qdq ? launch_one<K, VB, NT, false, KDA, true, ADDR, TIn>(p, units, s)
-                 : launch_one<K, VB, NT, false, KDA, false, ADDR, TIn>(p, units, s);
+  return sel.vfirst ? launch_qdq<K, VB, NT, true, KDA, ADDR, TIn>(p, units, sel.qdq, s)
+                    : launch_qdq<K, VB, NT, false, KDA, ADDR, TIn>(p, units, sel.qdq, s);
 }
 
 template <int K, int VB, int NT, bool KDA, int ADDR>
@@ -114,8 +127,8 @@ hipError_t launch_small_vfirst(Kind kind, const gdn::Params& p, int64_t units, S
   auto go = [&](auto kda, auto addr) -> hipError_t {
     constexpr bool KDA = decltype(kda)::value;
     constexpr int ADDR = decltype(addr)::value;
-    return sel.bf16 ? launch_one<128, VB, NT, true, KDA, false, ADDR, gdn::bf16_t>(p, units, s)
-                    : launch_one<128, VB, NT, true, KDA, false, ADDR, float>(p, units, s);
+    return sel.bf16 ? launch_one<128, VB, NT, true, KDA, gdn::kQdqNone, ADDR, gdn::bf16_t>(p, units, s)
+                    : launch_one<128, VB, NT, true, KDA, gdn::kQdqNone, ADDR, float>(p, units, s);
   };
   using F = std::false_type;
   using Tr = std::true_type;
@@ -147,8 +160,8 @@ int check_options(const gdn_options* o, int K, int V, Kind kind) {
     return fail(GDN_ERR_INVALID, "gate_mode must be ORIGINAL or SAFE (got %d)", o->gate_mode);
   if (o->gate_mode == GDN_GATE_SAFE)
     return fail(GDN_ERR_UNSUPPORTED, "gate_mode SAFE needs a gate lower bound this library does not define");
-  if (o->qdq != GDN_QDQ_NONE && o->qdq != GDN_QDQ_FP8_E4M3_TILE)
-    return fail(GDN_ERR_INVALID, "qdq must be NONE or FP8_E4M3_TILE (got %d)", o->qdq);
+  if (o->qdq != GDN_QDQ_NONE && o->qdq != GDN_QDQ_FP8_E4M3_TILE && o->qdq != GDN_QDQ_INT8_HADAMARD32)
+    return fail(GDN_ERR_INVALID, "qdq must be NONE, FP8_E4M3_TILE or INT8_HADAMARD32 (got %d)", o->qdq);
   if (o->readout != GDN_READOUT_WORKING && o->readout != GDN_READOUT_STORED)
     return fail(GDN_ERR_INVALID, "readout must be WORKING or STORED (got %d)", o->readout);
   const bool paged = kind == Kind::GdnPaged || kind == Kind::KdaPaged || kind == Kind::GdnPagedVar ||
@@ -163,6 +176,14 @@ int check_options(const gdn_options* o, int K, int V, Kind kind) {
     if (o->block_v != vblock_for(K))
       return fail(GDN_ERR_UNSUPPORTED, "fp8 tile QDQ is compiled for block_v=%d at K=%d (got %d)", vblock_for(K), K,
                   o->block_v);
+  }
+  if (o->qdq == GDN_QDQ_INT8_HADAMARD32) {
+    // block_v is the execution tile width: any multiple of 32 that divides V
+    // gives the same result, since no 32-value group crosses a tile
+    if (o->block_v <= 0 || V % o->block_v != 0 || o->block_v % 32 != 0)
+      return fail(GDN_ERR_INVALID, "block_v=%d must be a positive multiple of 32 dividing V=%d for int8_hadamard32",
+                  o->block_v, V);
+    if (K != 128) return fail(GDN_ERR_UNSUPPORTED, "the int8_hadamard32 codec is compiled for K=128 (got K=%d)", K);
   }
   return GDN_OK;
 }
@@ -211,13 +232,16 @@ void fill_common(gdn::Params& p, const gdn_options* o, int32_t B, int32_t T, int
 int run(Kind kind, const gdn::Params& p, int K, int32_t T, const gdn_options* o, void* stream) {
   const int64_t units = static_cast<int64_t>(p.B) * p.HV * p.nvb;
   if (units > 0x7fffffffLL) return fail(GDN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)units);
-  const Sel sel{o->state_layout == GDN_V_FIRST, o->qdq != GDN_QDQ_NONE, o->io_dtype == GDN_BF16};
+  const int qdq = o->qdq == GDN_QDQ_FP8_E4M3_TILE ? gdn::kQdqTile
+                  : o->qdq == GDN_QDQ_INT8_HADAMARD32 ? gdn::kQdqHad : gdn::kQdqNone;
+  const Sel sel{o->state_layout == GDN_V_FIRST, qdq, o->io_dtype == GDN_BF16};
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err = hipErrorInvalidValue;
   switch (K) {
     case 16: err = launch_kind<16, 16, 64>(kind, p, units, sel, s); break;
     case 128:
-      err = shape_for(K, sel.vfirst, sel.qdq, T, p.B).VB == 8 ? launch_small_vfirst<8, 128>(kind, p, units, sel, s)
+      err = shape_for(K, sel.vfirst, sel.qdq != gdn::kQdqNone, T, p.B).VB == 8
+                ? launch_small_vfirst<8, 128>(kind, p, units, sel, s)
                                                              : launch_kind<128, 64, 256>(kind, p, units, sel, s);
       break;
     default: return fail(GDN_ERR_UNSUPPORTED, "no kernel for K=%d", K);

@@ -272,6 +272,13 @@ def fp8_qdq_gdn_b512(seed=1005):
                       qdq="fp8_e4m3_tile", block_v=64)
 
 
+def int8h32_gdn_b512(seed=1008):
+    """The B=512, 4-token pooled GDN workload with the int8_hadamard32 state codec instead of fp8 tiles."""
+    return gdn_pooled(512, 16, 32, 128, 128, lengths=np.full(512, 4), num_slots=1024,
+                      state_layout=K_FIRST, seed=seed, name="int8h32_gdn_b512_t4_hv32_k128",
+                      qdq="int8_hadamard32", block_v=64)
+
+
 def paged_kda_b256(seed=1006, state_layout=V_FIRST, index_dtype=torch.int64):
     """The paged B=256 workload with KDA gating: HK=HV=32, raw_gate [B, 32, 128], dt_bias [32, 128]."""
     return paged("kda", 256, 32, 32, 128, 128, max_prefix=2048, page_size=16, share_frac=0.1,
@@ -293,4 +300,5 @@ NAMED = {
     "fp8_qdq_gdn_b512": fp8_qdq_gdn_b512,
     "paged_kda_b256": paged_kda_b256,
     "paged_gdn_varlen_b256_t4": paged_gdn_varlen_b256_t4,
+    "int8h32_gdn_b512": int8h32_gdn_b512,
 }

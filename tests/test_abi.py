@@ -79,6 +79,12 @@ def test_pooled_argument_errors():
     assert _pooled(lib, state_layout=2) == bnd.GDN_ERR_INVALID
     assert _pooled(lib, qdq=1, block_v=48) == bnd.GDN_ERR_INVALID
     assert _pooled(lib, qdq=1, block_v=128) == bnd.GDN_ERR_UNSUPPORTED
+    assert _pooled(lib, qdq=3) == bnd.GDN_ERR_INVALID
+    assert _pooled(lib, qdq=2, block_v=48) == bnd.GDN_ERR_INVALID       # not a multiple of 32
+    assert _pooled(lib, qdq=2, block_v=96) == bnd.GDN_ERR_INVALID       # does not divide V
+    assert _pooled(lib, qdq=2, K=16, V=32, block_v=32) == bnd.GDN_ERR_UNSUPPORTED
+    assert "K=128" in lib.gdn_last_error().decode()
+    assert _pooled(lib, qdq=2, block_v=128, T=0) == bnd.GDN_OK          # any multiple of 32 dividing V
     assert _pooled(lib, scale=float("inf")) == bnd.GDN_ERR_INVALID
     # an empty call (T = 0 with cu_seqlens) launches nothing and succeeds
     assert _pooled(lib, T=0) == bnd.GDN_OK

@@ -299,3 +299,84 @@ def test_precomputed_slots_match_table_and_inline_resolution(kind, idx):
     assert torch.equal(out_a, out_b) and torch.equal(pool_a, pool_b)
     rep, _, _ = P.run_and_check(w, slots=slots)
     _report(f"slots/{kind}/{idx}", rep)
+
+
+# ---------------------------------------------------------------- int8_hadamard32 state codec
+
+@pytest.mark.parametrize("layout", ["K_FIRST", "V_FIRST"])
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("extra", [dict(), dict(quantize_initial=True), dict(readout="stored")])
+def test_codec_variants(layout, kind, extra):
+    mk = wl.gdn_pooled if kind == "gdn" else wl.kda_pooled
+    w = mk(6, 2, 4, 128, 128, lengths=[4, 1, 0, 9, 2, 3], num_slots=8, state_layout=layout, seed=50,
+           qdq="int8_hadamard32", block_v=64, **extra)
+    rep, _, _ = P.run_and_check(w)
+    _report(f"codec/{kind}/{layout}/{extra}", rep)
+
+
+def _half_code_grid_pool(B, HV, K, V, rng):
+    """Logical states whose rotated groups are z = (n + f) 2^k with amax|z| = 127 2^k (k per group),
+    ties included, one all-zero group per head; returns (x, expected codec result), both exact."""
+    from oracle import hadamard as ohad
+    Hm = ohad.hadamard_matrix()
+    G = V // 32
+    n = rng.integers(-126, 127, (B, HV, K, G, 32)).astype(np.float64)
+    f = rng.choice([0.0, 0.5, -0.5, 0.25, 0.75], n.shape)
+    k = rng.integers(-12, 3, (B, HV, K, G, 1)).astype(np.float64)
+    z = (n + f) * 2.0 ** k
+    pos = rng.integers(0, 32, (B, HV, K, G))
+    sign = rng.choice([-1.0, 1.0], (B, HV, K, G))
+    np.put_along_axis(z, pos[..., None], (sign * 127)[..., None] * 2.0 ** k, axis=-1)
+    z[:, :, 5, 1, :] = 0.0
+    x = (z @ Hm) / 32
+    code = np.rint(z * 2.0 ** -k)
+    expect = (code @ Hm) * 2.0 ** (k - 5)
+    return x.reshape(B, HV, K, V), expect.reshape(B, HV, K, V)
+
+
+@pytest.mark.parametrize("layout", ["K_FIRST", "V_FIRST"])
+def test_codec_decisions_exact_on_the_half_code_grid(layout):
+    """alpha = 1 and beta = 0 leave the state unchanged, so the stored state is the codec of the
+    initial pool.  Its rotated groups sit on the half-code grid with power-of-two scales, where every
+    float32 step of the codec is exact: the GPU result must equal (rint_even(z / 2^k) H) 2^k / 32
+    bit for bit, ties to even included."""
+    B, HV, K, V = 4, 4, 128, 128
+    w = wl.gdn_pooled(B, 1, HV, K, V, lengths=[1] * B, num_slots=B, state_layout=layout, seed=51,
+                      io_dtype=torch.float32, qdq="int8_hadamard32", block_v=64)
+    w.inputs["a"] = torch.full((B, HV), -float("inf"))     # softplus(-inf) = 0 -> alpha = 1
+    w.inputs["b"] = torch.zeros((B, HV))                   # beta = b = 0 (probability mode)
+    w.options["beta_mode"] = "probability"
+    x, expect = _half_code_grid_pool(B, HV, K, V, np.random.default_rng(52))
+    assert np.array_equal(x.astype(np.float32).astype(np.float64), x)
+    tiles = x if layout == "K_FIRST" else np.swapaxes(x, -1, -2)
+    pool = torch.from_numpy(np.ascontiguousarray(tiles).astype(np.float32)).cuda()
+    rep, _, pool = P.run_and_check(w, pool=pool)
+    got = pool.cpu().numpy().astype(np.float64)
+    got_logical = got if layout == "K_FIRST" else np.swapaxes(got, -1, -2)
+    assert np.array_equal(got_logical, expect)
+    _report(f"codec_exact/{layout}", rep)
+
+
+@pytest.mark.parametrize("layout", ["V_FIRST", "K_FIRST"])
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_codec_paged_varlen(layout, kind):
+    suffix = np.array([3, 5, 1, 0, 8, 4])
+    w = wl.paged(kind, len(suffix), 2, 4, 128, 128, max_prefix=30, page_size=4, share_frac=0.3,
+                 suffix_lengths=suffix, state_layout=layout, seed=53, qdq="int8_hadamard32", block_v=64)
+    rep, _, _ = P.run_and_check(w)
+    _report(f"codec_paged_varlen/{kind}/{layout}", rep)
+
+
+@pytest.mark.parametrize("layout", ["V_FIRST", "K_FIRST"])
+def test_codec_paged_single_token(layout):
+    w = wl.paged("gdn", 40, 2, 4, 128, 128, max_prefix=30, page_size=4, share_frac=0.3,
+                 state_layout=layout, seed=54, qdq="int8_hadamard32", block_v=128)
+    rep, _, _ = P.run_and_check(w)
+    _report(f"codec_paged/{layout}", rep)
+
+
+def test_codec_gdn_b512_t4_sampled():
+    w = wl.int8h32_gdn_b512()
+    seqs = sorted(np.random.default_rng(8).choice(w.B, 48, replace=False).tolist())
+    rep, _, _ = P.run_and_check(w, seqs=seqs)
+    _report(w.name, rep)
