@@ -17,11 +17,11 @@
 // S_reg[i,:], S_reg[i,:] += (k_hat_i / c'_i) u).  A factor below 1e-20 is
 // applied to the registers and reset to 1, so S_reg never overflows.  The
 // fp8 tile quantisation keeps the codes in S_reg and moves the tile scale
-// amax/448 into c.  The int8_hadamard32 codec acts on each (key row, 32
-// values) group of S_reg: it commutes with the row's scale c (the codes do
-// not depend on it), so c is left alone and the group is replaced by its
-// dequantised value in S_reg units.  The tile is multiplied out once, when
-// it is stored.
+// amax/448 into c.  With the int8_hadamard32 codec the registers carry the
+// state rotated along V (each 32-value group times the Hadamard matrix) from
+// load to store, and each token rounds the rotated groups; the codes do not
+// depend on c, so c is left alone.  The tile is multiplied out (and rotated
+// back) once, when it is stored.
 //
 // Layout of the state tile in registers.  Each thread owns NS memory rows of
 // EV floats (128-bit loads); consecutive lanes cover a contiguous memory row,
@@ -33,7 +33,9 @@
 //   V_FIRST (K contiguous): memory row = value index j, 8 key elements per
 //       thread (two float4 half a row apart; 4 for small K); the K-reduction
 //       is in-thread, then across the 16 lanes of the row with DPP (quad
-//       permutes, row mirror, row rotate); no cross-wave step.
+//       permutes, row mirror, row rotate); no cross-wave step.  With the
+//       int8_hadamard32 codec a V_FIRST tile is transposed through LDS into
+//       the K_FIRST arrangement at load and back at store.
 //
 // Latency: the per-token inputs of the first chunk are loaded before the
 // state tile and normalised while the tile is in flight.
@@ -185,16 +187,29 @@ __device__ __forceinline__ float sigmoid_f(float x) { return rcp_hw(1.0f + exp_h
 
 // ---- cross-lane primitives (wave64)
 
+// Every control used here (quad_perm, row_mirror, row_half_mirror,
+// row_ror) reads a lane of the same row, so no lane is out of bounds and
+// bound_ctrl only tells the compiler that no old value needs keeping: the
+// move can then fold into the consuming add or max as its DPP operand.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
+
+// x with its sign flipped where sm has the sign bit (a lane-dependent +-x
+// that, unlike a multiply, cannot be contracted into an fma)
+__device__ __forceinline__ float flip_sign(float x, uint32_t sm) { return __uint_as_float(__float_as_uint(x) ^ sm); }
 
 struct OpAdd {
   __device__ static float f(float a, float b) { return a + b; }
 };
-struct OpMax {
-  __device__ static float f(float a, float b) { return fmaxf(a, b); }
+// Maximum of non-negative floats (amax reductions) as an unsigned compare
+// of their bit patterns: same order, no NaN canonicalisation, and the DPP
+// operand folds into v_max_u32.
+struct OpMaxNonNeg {
+  __device__ static float f(float a, float b) {
+    return __uint_as_float(max(__float_as_uint(a), __float_as_uint(b)));
+  }
 };
 
 // x combined with the value of the lane in the other 16-lane row of the same 32-lane half
@@ -274,41 +289,64 @@ __device__ __forceinline__ void e4m3_roundtrip2(float& x0, float& x1) {
 // in-thread butterflies, lane bits 0, 1, 2 by a partner lane (quad_perm
 // 0xB1 = xor 1, 0x4E = xor 2; xor 4 as row_half_mirror (xor 7) after the
 // quad reversal 0x1B (xor 3)).  A butterfly leaves a + b at the lower index
-// and a - b at the upper one; sg = -1 on lanes at the upper index gives
-// both as fma(sg, own, partner).
-__device__ __forceinline__ void wht32(float (&x)[4], float sg1, float sg2, float sg4) {
-  const float a0 = x[0] + x[1], a1 = x[0] - x[1], a2 = x[2] + x[3], a3 = x[2] - x[3];
-  x[0] = a0 + a2;
-  x[1] = a1 + a3;
-  x[2] = a0 - a2;
-  x[3] = a1 - a3;
+// and a - b at the upper one; flipping the own value's sign on lanes at the
+// upper index (sign masks sm1, sm2, sm4) gives both as partner + (+-own).
+// NR independent groups (rows) go through each stage together, so that a
+// lane move's result is not needed by the very next instruction.
+template <int NR>
+__device__ __forceinline__ void wht32(float (&x)[NR][4], uint32_t sm1, uint32_t sm2, uint32_t sm4) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) x[j] = fmaf(sg1, x[j], dpp<0xB1>(x[j]));
+  for (int r = 0; r < NR; ++r) {
+    const float a0 = x[r][0] + x[r][1], a1 = x[r][0] - x[r][1], a2 = x[r][2] + x[r][3], a3 = x[r][2] - x[r][3];
+    x[r][0] = a0 + a2;
+    x[r][1] = a1 + a3;
+    x[r][2] = a0 - a2;
+    x[r][3] = a1 - a3;
+  }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) x[j] = fmaf(sg2, x[j], dpp<0x4E>(x[j]));
+  for (int r = 0; r < NR; ++r)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) x[j] = fmaf(sg4, x[j], dpp<0x141>(dpp<0x1B>(x[j])));
+    for (int j = 0; j < 4; ++j) x[r][j] = dpp<0xB1>(x[r][j]) + flip_sign(x[r][j], sm1);
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[r][j] = dpp<0x4E>(x[r][j]) + flip_sign(x[r][j], sm2);
+  float t[NR][4];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t[r][j] = dpp<0x1B>(x[r][j]);
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[r][j] = dpp<0x141>(t[r][j]) + flip_sign(x[r][j], sm4);
 }
 
-// Codec of one group: with z = x H (H the +-1 Hadamard matrix) the rotated
-// values are y = c z / sqrt(32), so the codes rint(127 y / amax|y|) =
-// rint(127 z / amax|z|), and the dequantised group rotated back is
-// c * (codes H) * amax|z| / (127 * 32).  codes H is exact (integers below
-// 2^12).  An all-zero group stays zero.
-__device__ __forceinline__ void had_codec_group(float (&x)[4], float sg1, float sg2, float sg4) {
-  wht32(x, sg1, sg2, sg4);
-  float m = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
-  m = lane_reduce<0, 3, OpMax>(m);
-  const float inv = m > 0.0f ? 127.0f / m : 0.0f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) x[j] = __builtin_amdgcn_fmed3f(__builtin_rintf(x[j] * inv), -127.0f, 127.0f);
-  wht32(x, sg1, sg2, sg4);
-  const float c = (m / 127.0f) * 0.03125f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) x[j] *= c;
+// The same transform with one value per lane: the group is lane bits 0-4
+// (each 32-lane half is its own group).  Lane bit 3 pairs lanes i and i ^ 8
+// as row_mirror (xor 15) after row_half_mirror (xor 7); lane bit 4 uses
+// v_permlane16_swap, which hands every lane the values of the lower and the
+// upper 16-lane row of its pair.
+__device__ __forceinline__ float wht32_lanes(float x, int lane) {
+  const uint32_t ul = static_cast<uint32_t>(lane);
+  x = dpp<0xB1>(x) + flip_sign(x, (ul & 1u) << 31);
+  x = dpp<0x4E>(x) + flip_sign(x, (ul & 2u) << 30);
+  x = dpp<0x141>(dpp<0x1B>(x)) + flip_sign(x, (ul & 4u) << 29);
+  x = dpp<0x140>(dpp<0x141>(x)) + flip_sign(x, (ul & 8u) << 28);
+  const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(pr[0]) + flip_sign(__uint_as_float(pr[1]), (ul & 16u) << 27);
+}
+
+// 127 / m for m > 0: hardware reciprocal (about 1 ulp) and one residual
+// correction, q + (127 - q m) / m (exact for m = 127 * 2^k)
+__device__ __forceinline__ float div127_by(float m) {
+  const float r = __builtin_amdgcn_rcpf(m);
+  const float q = 127.0f * r;
+  return fmaf(fmaf(-q, m, 127.0f), r, q);
 }
 
 constexpr float kTinyScale = 1e-20f;
+constexpr float kTinyAmax = 0x1p-100f;
 
 template <int K, int VB, int NT, bool VF>
 struct Tile {
@@ -331,7 +369,12 @@ struct Tile {
 
 template <int K, int VB, int NT, bool VF, bool KDA, int QDQ, int ADDR, typename TIn>
 __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
-  using Cfg = Tile<K, VB, NT, VF>;
+  // Register arrangement: V_FIRST rows (value columns) for a V_FIRST pool,
+  // except with the int8_hadamard32 codec, which needs each key row's values
+  // in lanes; the pool layout VF itself only shapes the tile's load and store.
+  constexpr bool HAD = QDQ == kQdqHad;
+  constexpr bool AV = VF && !HAD;
+  using Cfg = Tile<K, VB, NT, AV>;
   constexpr int NW = Cfg::NW, LR = Cfg::LR, RPW = Cfg::RPW, NS = Cfg::NS, LB = Cfg::LB;
   constexpr int EV = Cfg::EV, NKEY = Cfg::NKEY;
   constexpr int TC = kTokensPerChunk;
@@ -352,14 +395,16 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   __shared__ __align__(16) float s_al[TX][KX];     // KDA: alpha per key channel
   __shared__ __align__(16) float s_v[TC][VB];      // this V-block of v
   __shared__ float s_sc[TC][4];                    // alpha (GDN), beta, q_hat . k_hat
-  __shared__ __align__(16) float s_red[VF ? 1 : 2][VF ? 1 : NW][2][VB];
+  __shared__ __align__(16) float s_red[AV ? 1 : 2][AV ? 1 : NW][2][VB];
   __shared__ float s_max[2][NW];
-  // V_FIRST int8_hadamard32: the tile passes through LDS to put each key
-  // row's values in lanes (row stride K + 1: conflict-free both ways)
-  constexpr bool HAD_LDS = VF && QDQ == kQdqHad;
-  __shared__ float s_t[HAD_LDS ? VB * (K + 1) : 1];
-  static_assert(QDQ != kQdqHad || (VF ? (K == 128 && VB == 64 && NT == 256) : (LR == 16 && EV == 4)),
-                "int8_hadamard32 codec shapes");
+  // V_FIRST pool with the codec: the tile passes through LDS between the
+  // pool's [V][K] rows and the [K][V] register arrangement (row stride K + 1
+  // keeps both directions free of bank conflicts)
+  constexpr bool TRANS = VF && HAD;
+  constexpr int LD = K + 1;
+  __shared__ float s_t[TRANS ? VB * LD : 1];
+  static_assert(!HAD || (K == 128 && VB == 64 && NT == 256 && LR == 16 && EV == 4 && NS == K / 16 && VPL == 1),
+                "int8_hadamard32 codec shape");
 
   const TIn* __restrict__ gq = static_cast<const TIn*>(p.q);
   const TIn* __restrict__ gk = static_cast<const TIn*>(p.k);
@@ -390,16 +435,16 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
 
   // key index of this thread's key slot m, and the LDS position of key c
   auto key_of = [&](int m) -> int {
-    if constexpr (VF) return (EV == 8 ? (m / 4) * (K / 2) : 0) + 4 * lr + (m % 4);
+    if constexpr (AV) return (EV == 8 ? (m / 4) * (K / 2) : 0) + 4 * lr + (m % 4);
     else return m * (NW * RPW) + w * RPW + rg;
   };
   auto lds_pos = [](int c) -> int {
-    if constexpr (VF) return c;
+    if constexpr (AV) return c;
     else return (c % (NW * RPW)) * NS + c / (NW * RPW);
   };
   // first LDS position of this thread's key slots (they are contiguous in
   // both layouts, per half row for V_FIRST)
-  const int kbase = VF ? 4 * lr : (w * RPW + rg) * NS;
+  const int kbase = AV ? 4 * lr : (w * RPW + rg) * NS;
 
   // ---- which tokens
   int t0, t1;
@@ -487,6 +532,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
             if constexpr (KDA) s_al[tt][pos] = exp_hw(-rate * softplus_f(xg[e] + p.dt_bias[h * K + c]));
           }
         }
+        if constexpr (HAD) xv[0] = wht32_lanes(xv[0], lane);   // v in the rotated basis (VPL == 1)
         if (lane < VL) {
 #pragma unroll
           for (int e = 0; e < VPL; ++e) s_v[tt][VPL * lane + e] = xv[e];
@@ -539,24 +585,68 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
 
   auto row_idx = [&](int s) -> int { return s * (NW * RPW) + w * RPW + rg; };
   // memory offset of this thread's float4 number f (0 .. EV/4-1) in row s
+  // (pool layout == register arrangement)
   auto row_off = [&](int s, int f) -> int64_t {
-    if constexpr (VF) return static_cast<int64_t>(vb * VB + row_idx(s)) * K + f * (K / 2) + 4 * lr;
+    if constexpr (AV) return static_cast<int64_t>(vb * VB + row_idx(s)) * K + f * (K / 2) + 4 * lr;
     else return static_cast<int64_t>(row_idx(s)) * p.V + vb * VB + 4 * lr;
   };
+  // TRANS: the [V][K] rows of the pool are read and written with the
+  // V_FIRST geometry (value rows s * 16 + w * 4 + rg, key float4s at
+  // f * K / 2 + 4 * lr) and staged in s_t as [value][key]
+  auto trans_off = [&](int s, int f) -> int64_t {
+    return static_cast<int64_t>(vb * VB + s * 16 + w * 4 + rg) * K + f * (K / 2) + 4 * lr;
+  };
+  auto trans_lds = [&](int s, int f) -> int { return (s * 16 + w * 4 + rg) * LD + f * (K / 2) + 4 * lr; };
+  auto kf_lds = [&](int s, int j) -> int { return (4 * lr + j) * LD + row_idx(s); };
 
   float S[NS][EV];
+  if constexpr (!TRANS) {
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
-    for (int f = 0; f < EV / 4; ++f) {
-      const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + row_off(s, f)));
-      S[s][4 * f + 0] = x.x;
-      S[s][4 * f + 1] = x.y;
-      S[s][4 * f + 2] = x.z;
-      S[s][4 * f + 3] = x.w;
-    }
+      for (int f = 0; f < EV / 4; ++f) {
+        const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + row_off(s, f)));
+        S[s][4 * f + 0] = x.x;
+        S[s][4 * f + 1] = x.y;
+        S[s][4 * f + 2] = x.z;
+        S[s][4 * f + 3] = x.w;
+      }
+    finish_raw(n0);                // overlaps the tile load
+  } else {
+    f32x4 L[VB / 16][2];
+#pragma unroll
+    for (int s = 0; s < VB / 16; ++s)
+#pragma unroll
+      for (int f = 0; f < 2; ++f) L[s][f] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + trans_off(s, f)));
+    finish_raw(n0);                // overlaps the tile load
+#pragma unroll
+    for (int s = 0; s < VB / 16; ++s)
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int a = trans_lds(s, f);
+        s_t[a + 0] = L[s][f].x;
+        s_t[a + 1] = L[s][f].y;
+        s_t[a + 2] = L[s][f].z;
+        s_t[a + 3] = L[s][f].w;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[s][j] = s_t[kf_lds(s, j)];
+  }
 
-  finish_raw(n0);                  // overlaps the tile load
+  // int8_hadamard32: the registers carry R = S H (H the +-1 Hadamard matrix
+  // of each 32-value group, H H = 32 I) for the whole suffix.  The rotation
+  // acts on the value axis, so it commutes with the decay, the scale and
+  // every K-reduction: with v staged as v H, the token's r, p, u and o all
+  // come out rotated (u H = beta (v H - k^T R)), the write is R += k (u H),
+  // and only o is rotated back (o = (o H) H / 32) for the output.  The codec
+  // then rounds R directly.
+  const uint32_t sg1 = (static_cast<uint32_t>(lane) & 1u) << 31;   // sign masks of the butterflies
+  const uint32_t sg2 = (static_cast<uint32_t>(lane) & 2u) << 30;
+  const uint32_t sg4 = (static_cast<uint32_t>(lane) & 4u) << 29;
+  if constexpr (HAD) wht32(S, sg1, sg2, sg4);
 
   // true state = scale * S: one scale (GDN) or one per key slot (KDA)
   constexpr int NC = KDA ? NKEY : 1;
@@ -564,12 +654,12 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
 #pragma unroll
   for (int m = 0; m < NC; ++m) cs[m] = 1.0f;
   // key slot of element (s, e)
-  auto slot = [](int s, int e) -> int { return VF ? e : s; };
+  auto slot = [](int s, int e) -> int { return AV ? e : s; };
 
   int red_buf = 0, max_buf = 0;
 
   auto block_max = [&](float m) -> float {
-    m = lane_reduce<0, 6, OpMax>(m);
+    m = lane_reduce<0, 6, OpMaxNonNeg>(m);
     if constexpr (NW > 1) {
       if (lane == 0) s_max[max_buf][w] = m;
       __syncthreads();
@@ -591,7 +681,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
         for (int e = 0; e < EV; ++e) m = fmaxf(m, fabsf(S[s][e]));
       const float ms = block_max(m);       // amax of S_reg; the true amax is cs[0] * ms
       if (ms > 0.0f) {
-        const float inv = kE4M3Max / ms;
+        const float msf = fmaxf(ms, kTinyAmax);   // 448 / amax stays finite
+        const float inv = kE4M3Max / msf;
 #pragma unroll
         for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -601,7 +692,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
             S[s][e] = x0;
             S[s][e + 1] = x1;
           }
-        cs[0] = cs[0] * (ms / kE4M3Max);
+        cs[0] = cs[0] * (msf / kE4M3Max);
       }
     } else {
       float rowm[NC];
@@ -615,7 +706,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
       for (int k2 = 0; k2 < NC; ++k2) m = fmaxf(m, cs[k2] * rowm[k2]);
       const float mt = block_max(m);       // true amax
       if (mt > 0.0f) {
-        const float inv = kE4M3Max / mt;
+        const float mtf = fmaxf(mt, kTinyAmax);   // 448 / amax stays finite
+        const float inv = kE4M3Max / mtf;
         float f[NC];
 #pragma unroll
         for (int k2 = 0; k2 < NC; ++k2) f[k2] = cs[k2] * inv;
@@ -628,52 +720,46 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
             S[s][e] = x0;
             S[s][e + 1] = x1;
           }
-        const float sc = mt / kE4M3Max;
+        const float sc = mtf / kE4M3Max;
 #pragma unroll
         for (int k2 = 0; k2 < NC; ++k2) cs[k2] = sc;
       }
     }
   };
 
-  // int8_hadamard32 codec of every (key row, 32 values) group of S_reg
-  auto had_codec = [&]() {
-    const float sg1 = (lane & 1) ? -1.0f : 1.0f;
-    const float sg2 = (lane & 2) ? -1.0f : 1.0f;
-    const float sg4 = (lane & 4) ? -1.0f : 1.0f;
-    if constexpr (!VF) {
+  // int8_hadamard32 codec of every (key row, 32 values) group, on R: the
+  // codes rint(127 R / amax|R|) equal rint(127 y / amax|y|) for the
+  // orthonormal rotation y = c R / sqrt(32), and the dequantised group is
+  // codes * amax|R| / 127 (still rotated; c untouched)
+  auto had_quant = [&]() {
+    // amax of each row's group (8 lanes), one reduction step for all rows at
+    // a time so that the steps of different rows interleave
+    float m[NS];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) had_codec_group(S[s], sg1, sg2, sg4);
-    } else {
-      // key rows in K_FIRST arrangement: row s * 16 + w * 4 + rg, values 4 * lr + j
-      constexpr int LD = K + 1;
-      constexpr int KR = K / 16;
+    for (int s = 0; s < NS; ++s)
+      m[s] = OpMaxNonNeg::f(OpMaxNonNeg::f(fabsf(S[s][0]), fabsf(S[s][1])),
+                            OpMaxNonNeg::f(fabsf(S[s][2]), fabsf(S[s][3])));
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
+    for (int s = 0; s < NS; ++s) m[s] = OpMaxNonNeg::f(m[s], dpp<0xB1>(m[s]));
 #pragma unroll
-        for (int e = 0; e < EV; ++e) s_t[row_idx(s) * LD + key_of(e)] = S[s][e];
-      __syncthreads();
-      float X[KR][4];
+    for (int s = 0; s < NS; ++s) m[s] = OpMaxNonNeg::f(m[s], dpp<0x4E>(m[s]));
 #pragma unroll
-      for (int s = 0; s < KR; ++s)
+    for (int s = 0; s < NS; ++s) m[s] = OpMaxNonNeg::f(m[s], dpp<0x141>(m[s]));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) X[s][j] = s_t[(4 * lr + j) * LD + s * 16 + w * 4 + rg];
+    for (int s = 0; s < NS; ++s) {
+      // (an amax below 2^-100, zero included, is raised to 2^-100: the codes
+      // of such a group only get coarser, and 127 / m stays finite)
+      const float mf = OpMaxNonNeg::f(m[s], kTinyAmax);
+      const float inv = div127_by(mf);
+      const float c = mf * (1.0f / 127.0f);
+      // |R inv| <= 127 (1 + 2^-22) rounds to at most 127: no clamp needed
 #pragma unroll
-      for (int s = 0; s < KR; ++s) had_codec_group(X[s], sg1, sg2, sg4);
-#pragma unroll
-      for (int s = 0; s < KR; ++s)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s_t[(4 * lr + j) * LD + s * 16 + w * 4 + rg] = X[s][j];
-      __syncthreads();
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int e = 0; e < EV; ++e) S[s][e] = s_t[row_idx(s) * LD + key_of(e)];
-      __syncthreads();             // s_t is free for the next token
+      for (int j = 0; j < 4; ++j) S[s][j] = __builtin_rintf(S[s][j] * inv) * c;
     }
   };
   auto quantize = [&]() {
     if constexpr (QDQ == kQdqTile) qdq_tile();
-    else if constexpr (QDQ == kQdqHad) had_codec();
+    else if constexpr (QDQ == kQdqHad) had_quant();
   };
 
   // output stores: 4 consecutive values (K_FIRST) or one (V_FIRST)
@@ -694,7 +780,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
 
   // load NKEY consecutive LDS floats starting at pos (float4 pieces)
   auto lds_keys = [&](const float* base, float (&x)[NKEY]) {
-    if constexpr (VF) {
+    if constexpr (AV) {
 #pragma unroll
       for (int f = 0; f < EV / 4; ++f) {
         const float4 v = *reinterpret_cast<const float4*>(base + f * (K / 2) + kbase);
@@ -757,9 +843,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
 
   // one pass: r = kr^T S and p = qr^T S over K, complete sums for this thread's outputs
   // (K_FIRST: its 4 columns; V_FIRST: its NS rows)
-  constexpr int NO = VF ? NS : 4;
+  constexpr int NO = AV ? NS : 4;
   auto reduce_pass = [&](const float (&kr)[NKEY], const float (&qr)[NKEY], float (&r)[NO], float (&pp)[NO]) {
-    if constexpr (!VF) {
+    if constexpr (!AV) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         r[e] = kr[0] * S[0][e];
@@ -789,7 +875,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   };
 
   auto store_outputs = [&](int64_t out_row, const float (&o)[NO]) {
-    if constexpr (!VF) {
+    if constexpr (!AV) {
       if (w == 0 && rg == 0) store_out4(out_row + 4 * lr, o);
     } else {
       float my_o = o[0];
@@ -802,17 +888,53 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
 
   // write the true state (scale * registers) to a pool row
   auto store_tile = [&](float* row_base) {
+    if constexpr (!HAD) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+      for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int f = 0; f < EV / 4; ++f) {
-        float4 x;
-        x.x = S[s][4 * f + 0] * cs[KDA ? slot(s, 4 * f + 0) : 0];
-        x.y = S[s][4 * f + 1] * cs[KDA ? slot(s, 4 * f + 1) : 0];
-        x.z = S[s][4 * f + 2] * cs[KDA ? slot(s, 4 * f + 2) : 0];
-        x.w = S[s][4 * f + 3] * cs[KDA ? slot(s, 4 * f + 3) : 0];
-        *reinterpret_cast<float4*>(row_base + row_off(s, f)) = x;
+        for (int f = 0; f < EV / 4; ++f) {
+          float4 x;
+          x.x = S[s][4 * f + 0] * cs[KDA ? slot(s, 4 * f + 0) : 0];
+          x.y = S[s][4 * f + 1] * cs[KDA ? slot(s, 4 * f + 1) : 0];
+          x.z = S[s][4 * f + 2] * cs[KDA ? slot(s, 4 * f + 2) : 0];
+          x.w = S[s][4 * f + 3] * cs[KDA ? slot(s, 4 * f + 3) : 0];
+          *reinterpret_cast<float4*>(row_base + row_off(s, f)) = x;
+        }
+    } else {
+      // back to the original value basis: S = c R H / 32
+      float X[NS][4];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) X[s][j] = S[s][j];
+      wht32(X, sg1, sg2, sg4);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const float sc = cs[KDA ? s : 0] * 0.03125f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) X[s][j] *= sc;
       }
+      if constexpr (!TRANS) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+          *reinterpret_cast<float4*>(row_base + row_off(s, 0)) = make_float4(X[s][0], X[s][1], X[s][2], X[s][3]);
+      } else {
+        __syncthreads();           // earlier readers of s_t are done
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) s_t[kf_lds(s, j)] = X[s][j];
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < VB / 16; ++s)
+#pragma unroll
+          for (int f = 0; f < 2; ++f) {
+            const int a = trans_lds(s, f);
+            *reinterpret_cast<float4*>(row_base + trans_off(s, f)) =
+                make_float4(s_t[a + 0], s_t[a + 1], s_t[a + 2], s_t[a + 3]);
+          }
+      }
+    }
   };
 
   if constexpr (QDQ != kQdqNone) {
@@ -896,21 +1018,31 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
       float u[NO], o[NO], wv[NO];
 #pragma unroll
       for (int j = 0; j < NO; ++j) {
-        const int col = VF ? row_idx(j) : 4 * lr + j;
+        const int col = AV ? row_idx(j) : 4 * lr + j;
         const float rr = KDA ? r[j] : cn_g * r[j];
         const float pj = KDA ? pp[j] : cn_g * pp[j];
         u[j] = beta * (s_v[tt][col] - rr);
         o[j] = fmaf(qk, u[j], pj);
         wv[j] = KDA ? u[j] : u[j] * icn_g;
       }
-      if (!stored) store_outputs(out_row, o);
+      if constexpr (!HAD) {
+        if (!stored) store_outputs(out_row, o);
+      } else if (!stored) {        // o back to the original value basis
+        float ow[1][NO];
+#pragma unroll
+        for (int j = 0; j < NO; ++j) ow[0][j] = o[j];
+        wht32(ow, sg1, sg2, sg4);
+#pragma unroll
+        for (int j = 0; j < NO; ++j) o[j] = ow[0][j] * 0.03125f;
+        store_outputs(out_row, o);
+      }
 
       // S_reg += kt (x) wv
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int e = 0; e < EV; ++e) {
-          if constexpr (VF) S[s][e] = fmaf(kt[e], wv[s], S[s][e]);
+          if constexpr (AV) S[s][e] = fmaf(kt[e], wv[s], S[s][e]);
           else S[s][e] = fmaf(kt[s], wv[e], S[s][e]);
         }
 
@@ -923,6 +1055,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
           for (int m = 0; m < NKEY; ++m) q2[m] = qh[m] * cs[KDA ? m : 0];
           float ps[NO], dummy[NO];
           reduce_pass(q2, q2, ps, dummy);
+          if constexpr (HAD) {
+            float pw[1][NO];
+#pragma unroll
+            for (int j = 0; j < NO; ++j) pw[0][j] = ps[j];
+            wht32(pw, sg1, sg2, sg4);
+#pragma unroll
+            for (int j = 0; j < NO; ++j) ps[j] = pw[0][j] * 0.03125f;
+          }
           store_outputs(out_row, ps);
         }
       }
