@@ -202,6 +202,8 @@ def main():
                     choices=["paged_gdn_b256", "pooled_gdn_b64", "pooled_kda_varlen_b128", "fp8_qdq_gdn_b512",
                              "tiny_gdn", "paged_kda_b256", "paged_gdn_varlen_b256_t4", "int8h32_gdn_b512"])
     ap.add_argument("--layout", default=None, help="override the pool layout (K_FIRST / V_FIRST)")
+    ap.add_argument("--qdq", default=None, choices=["none", "fp8_e4m3_tile", "int8_hadamard32"],
+                    help="override the workload's state quantisation (the workload name gets a +qdq suffix)")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -214,12 +216,15 @@ def main():
 
     if args.summarize_profiles:
         kt, fe, wr = args.summarize_profiles
+        sel = "" if args.workload == "paged_gdn_b256" else f" --workload {args.workload}"
+        sel += f" --layout {args.layout}" if args.layout else ""
+        sel += f" --qdq {args.qdq}" if args.qdq else ""
         cmds = {"kt": f"rocprofv3 --kernel-trace --stats -d {kt} -o kt --output-format csv -- "
-                      "python3 bench.py --steps 20 --warmup 2 --no-cpu-baseline",
+                      f"python3 bench.py{sel} --steps 20 --warmup 2 --no-cpu-baseline",
                 "fetch": f"rocprofv3 --pmc FETCH_SIZE -d {fe} -o f --output-format csv -- "
-                         "python3 bench.py --steps 10 --warmup 1 --no-cpu-baseline --copy-calibration",
+                         f"python3 bench.py{sel} --steps 10 --warmup 1 --no-cpu-baseline --copy-calibration",
                 "write": f"rocprofv3 --pmc WRITE_SIZE -d {wr} -o w --output-format csv -- "
-                         "python3 bench.py --steps 10 --warmup 1 --no-cpu-baseline --copy-calibration"}
+                         f"python3 bench.py{sel} --steps 10 --warmup 1 --no-cpu-baseline --copy-calibration"}
         summarize_profiles(kt, fe, wr, cmds)
         return
 
@@ -240,6 +245,13 @@ def main():
     w = maker(state_layout=args.layout) if (args.layout and args.workload in paged_makers) else maker()
     if args.layout and args.workload not in paged_makers:
         w.state_layout = args.layout
+    if args.qdq is not None and args.qdq != w.options.get("qdq", "none"):
+        if args.qdq == "none":
+            w.options.pop("qdq", None)
+        else:
+            w.options["qdq"] = args.qdq
+            w.options.setdefault("block_v", 64)
+        w.name = f"{w.name}+{args.qdq}"
     d = P.device_inputs(w, dev)
     pool = wl.make_pool(w, dev)
     out = torch.empty((w.T, w.HV, w.V), dtype=w.out_dtype, device=dev)
