@@ -36,8 +36,8 @@ METRIC = "tokens/s & state-pool HBM GB/s (% peak), GDN decode B=256,HV=32,K=V=12
 def source_hash():
     """Hash of the sources the kernels are built from (ties a profile to a kernel version)."""
     h = hashlib.sha256()
-    for rel in ("recurrent_state_decode_amd/csrc/decode_kernel.hpp", "recurrent_state_decode_amd/csrc/gdn_decode.hip",
-                "include/gdn_decode.h"):
+    for rel in ("recurrent_state_decode_amd/csrc/decode_kernel.hpp", "recurrent_state_decode_amd/csrc/prefill_kernel.hpp",
+                "recurrent_state_decode_amd/csrc/gdn_decode.hip", "include/gdn_decode.h"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -66,6 +66,10 @@ def algorithmic_bytes(w):
     else:
         per_tok += 2 * w.HV * esz
     return state, T * per_tok
+
+
+def kernel_name(w):
+    return "gdn::prefill_kernel" if w.chunked else "gdn::decode_kernel"
 
 
 def traffic_path(workload_name):
@@ -109,7 +113,7 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir, commands):
 
     bench_kt = load_json(kt_dir)
     name = bench_kt["config"]["workload"]
-    kern = "gdn::decode_kernel"
+    kern = bench_kt["roofline"]["kernel"]
     # kernel trace: per-dispatch durations of the decode kernel, warm-up dispatches dropped
     trace = [r for f in _csvs(kt_dir, "kernel_trace.csv") for r in csv.DictReader(open(f))]
     dec = sorted((r for r in trace if kern in r["Kernel_Name"]), key=lambda r: int(r["Start_Timestamp"]))
@@ -200,10 +204,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="paged_gdn_b256",
                     choices=["paged_gdn_b256", "pooled_gdn_b64", "pooled_kda_varlen_b128", "fp8_qdq_gdn_b512",
-                             "tiny_gdn", "paged_kda_b256", "paged_gdn_varlen_b256_t4", "int8h32_gdn_b512"])
+                             "tiny_gdn", "paged_kda_b256", "paged_gdn_varlen_b256_t4", "int8h32_gdn_b512",
+                             "paged_gdn_prefill_b16_t1024"])
     ap.add_argument("--layout", default=None, help="override the pool layout (K_FIRST / V_FIRST)")
     ap.add_argument("--qdq", default=None, choices=["none", "fp8_e4m3_tile", "int8_hadamard32"],
                     help="override the workload's state quantisation (the workload name gets a +qdq suffix)")
+    ap.add_argument("--token-path", action="store_true",
+                    help="run a chunked-prefill workload through the token-by-token paged call instead")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -219,6 +226,7 @@ def main():
         sel = "" if args.workload == "paged_gdn_b256" else f" --workload {args.workload}"
         sel += f" --layout {args.layout}" if args.layout else ""
         sel += f" --qdq {args.qdq}" if args.qdq else ""
+        sel += " --token-path" if args.token_path else ""
         cmds = {"kt": f"rocprofv3 --kernel-trace --stats -d {kt} -o kt --output-format csv -- "
                       f"python3 bench.py{sel} --steps 20 --warmup 2 --no-cpu-baseline",
                 "fetch": f"rocprofv3 --pmc FETCH_SIZE -d {fe} -o f --output-format csv -- "
@@ -241,10 +249,13 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     maker = wl.NAMED[args.workload]
-    paged_makers = ("paged_gdn_b256", "paged_kda_b256", "paged_gdn_varlen_b256_t4")
+    paged_makers = ("paged_gdn_b256", "paged_kda_b256", "paged_gdn_varlen_b256_t4", "paged_gdn_prefill_b16_t1024")
     w = maker(state_layout=args.layout) if (args.layout and args.workload in paged_makers) else maker()
     if args.layout and args.workload not in paged_makers:
         w.state_layout = args.layout
+    if args.token_path and w.chunked:
+        w.chunked = False
+        w.name = f"{w.name}+token_path"
     if args.qdq is not None and args.qdq != w.options.get("qdq", "none"):
         if args.qdq == "none":
             w.options.pop("qdq", None)
@@ -313,7 +324,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": state_b + io_b,
-                     "kernel": "gdn::decode_kernel", "source_hash": source_hash()},
+                     "kernel": kernel_name(w), "source_hash": source_hash()},
     }
     if args.copy_calibration:
         n = 256 * 1024 * 1024

@@ -254,6 +254,29 @@ int kda_decode_paged_varlen(const void* q, const void* k, const void* v, const v
                             const gdn_options* opt, void* stream);
 
 /*
+ * gdn_prefill_paged -- chunked GDN prefill on a CSR-paged pool: the same
+ * arguments and the same result as gdn_decode_paged_varlen (flashinfer names
+ * the paged chunked prefill chunk_gated_delta_rule_paged; the chunked form
+ * follows the step names of modelopt ... linear_attention.config,
+ * LinearAttentionConfig, with the exact solve of LinearAttentionSolveConfig,
+ * and Circuit.LLM.Mixer, "Chunked additive linear": chunked equals
+ * sequential).  The suffix is processed in chunks of 16 tokens aligned to
+ * absolute positions, each as dense products on the matrix cores, so long
+ * suffixes (prompts) run chunk-parallel instead of token by token; results
+ * agree with the token-by-token call to float32 rounding, not bit for bit.
+ * Requirements (else GDN_ERR_UNSUPPORTED): K = 128, V a multiple of 128,
+ * page_size a multiple of 16, opt->qdq == GDN_QDQ_NONE.  opt->slots must be
+ * NULL.  The chunk's identity padding (positions of a chunk outside the
+ * suffix) reads and writes nothing.
+ */
+int gdn_prefill_paged(const void* q, const void* k, const void* v, const void* a, const void* b,
+                      const float* A_log, const float* dt_bias, const int32_t* cu_seqlens,
+                      const void* page_indices, const void* page_indptr, const void* last_page_len,
+                      int32_t page_size, float* state_pool, void* out, int32_t B, int32_t T, int32_t HK,
+                      int32_t HV, int32_t K, int32_t V, int64_t num_pages, int64_t nnz,
+                      const gdn_options* opt, void* stream);
+
+/*
  * gdn_paged_decode_slots -- the (read row, write row) pair of every sequence
  * for a single-token paged decode step, written to slots [B][2] (int64,
  * device).  Computed once per step and passed to every layer's call through

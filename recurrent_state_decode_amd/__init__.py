@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     gdn_decode_paged_varlen,
     gdn_decode_pooled,
     gdn_paged_decode_slots,
+    gdn_prefill_paged,
     kda_decode_paged,
     kda_decode_paged_varlen,
     kda_decode_pooled,

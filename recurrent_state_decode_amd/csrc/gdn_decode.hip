@@ -14,6 +14,7 @@
 
 #include "gdn_decode.h"
 #include "decode_kernel.hpp"
+#include "prefill_kernel.hpp"
 
 namespace {
 
@@ -379,6 +380,60 @@ int gdn_paged_decode_slots(const void* page_indices, const void* page_indptr, co
     return fail(GDN_ERR_INVALID, "index_dtype must be GDN_I32 or GDN_I64 (got %d)", index_dtype);
   hipLaunchKernelGGL(gdn::paged_slots_kernel, dim3((B + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
                      page_indices, page_indptr, last_page_len, B, index_dtype == GDN_I64 ? 1 : 0, slots);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  g_last_error.clear();
+  return GDN_OK;
+}
+
+int gdn_prefill_paged(const void* q, const void* k, const void* v, const void* a, const void* b, const float* A_log,
+                      const float* dt_bias, const int32_t* cu_seqlens, const void* page_indices,
+                      const void* page_indptr, const void* last_page_len, int32_t page_size, float* state_pool,
+                      void* out, int32_t B, int32_t T, int32_t HK, int32_t HV, int32_t K, int32_t V,
+                      int64_t num_pages, int64_t nnz, const gdn_options* opt, void* stream) {
+  if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !cu_seqlens || !page_indices || !page_indptr ||
+      !last_page_len || !state_pool || !out)
+    return fail(GDN_ERR_INVALID, "a required pointer is NULL");
+  if (int rc = check_dims(B, HK, HV, K, V)) return rc;
+  if (K != 128 || V % 128 != 0)
+    return fail(GDN_ERR_UNSUPPORTED, "the chunked prefill is compiled for K=128 and V a multiple of 128 (K=%d V=%d)", K,
+                V);
+  if (num_pages <= 0 || nnz <= 0) return fail(GDN_ERR_INVALID, "num_pages and nnz must be positive");
+  if (nnz < B) return fail(GDN_ERR_SHAPE, "nnz (%lld) must be at least B (%d): every sequence owns a page",
+                           (long long)nnz, B);
+  if (page_size <= 0) return fail(GDN_ERR_INVALID, "page_size must be positive (got %d)", page_size);
+  if (page_size % gdn::kChunk != 0)
+    return fail(GDN_ERR_UNSUPPORTED, "the chunked prefill needs a page size that is a multiple of %d (got %d)",
+                gdn::kChunk, page_size);
+  if (T < 0) return fail(GDN_ERR_INVALID, "T must be >= 0");
+  if (int rc = check_options(opt, K, V, Kind::GdnPagedVar)) return rc;
+  if (opt->slots) return fail(GDN_ERR_INVALID, "slots apply to single-token paged calls only");
+  if (opt->qdq != GDN_QDQ_NONE) return fail(GDN_ERR_UNSUPPORTED, "the chunked prefill has no state quantisation");
+  if (T == 0) { g_last_error.clear(); return GDN_OK; }
+  gdn::PrefillParams p{};
+  p.q = q; p.k = k; p.v = v; p.gate = a; p.beta = b;
+  p.a_log = A_log; p.dt_bias = dt_bias;
+  p.cu_seqlens = cu_seqlens;
+  p.page_indices = page_indices; p.page_indptr = page_indptr; p.last_page_len = last_page_len;
+  p.page_size = page_size;
+  p.pool = state_pool; p.out = out;
+  p.B = B; p.HK = HK; p.HV = HV; p.V = V;
+  p.nvb = V / 128;
+  p.gqa = HV / HK;
+  p.scale = opt->scale > 0.0f ? opt->scale : 1.0f / std::sqrt(static_cast<float>(K));
+  p.l2norm = opt->use_qk_l2norm ? 1 : 0;
+  p.out_bf16 = opt->out_dtype == GDN_BF16;
+  p.beta_prob = opt->beta_mode == GDN_BETA_PROBABILITY;
+  p.idx64 = opt->index_dtype == GDN_I64;
+  const int64_t units = static_cast<int64_t>(B) * HV * p.nvb;
+  if (units > 0x7fffffffLL) return fail(GDN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)units);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool vf = opt->state_layout == GDN_V_FIRST, bf = opt->io_dtype == GDN_BF16;
+  const dim3 grid(static_cast<uint32_t>(units)), block(256);
+  if (vf && bf) hipLaunchKernelGGL((gdn::prefill_kernel<true, gdn::bf16_t>), grid, block, 0, s, p);
+  else if (vf) hipLaunchKernelGGL((gdn::prefill_kernel<true, float>), grid, block, 0, s, p);
+  else if (bf) hipLaunchKernelGGL((gdn::prefill_kernel<false, gdn::bf16_t>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((gdn::prefill_kernel<false, float>), grid, block, 0, s, p);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   g_last_error.clear();

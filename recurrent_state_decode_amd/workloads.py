@@ -42,6 +42,7 @@ class Workload:
     options: dict = field(default_factory=dict)  # beta_mode, qdq, block_v, ...
     pool_seed: int = 0
     pool_zero: bool = False
+    chunked: bool = False             # paged suffixes through the chunked prefill entry point
 
     @property
     def T(self):
@@ -191,7 +192,7 @@ def build_page_table(prefix_lengths, page_size, share_frac, rng, force_shared_ne
 
 def paged(kind, B, HK, HV, K, V, *, prefix_lengths=None, max_prefix=2048, page_size=16, share_frac=0.1,
           suffix_lengths=None, state_layout=V_FIRST, io_dtype=torch.bfloat16, out_dtype=None,
-          index_dtype=torch.int64, seed=0, name=None, **options):
+          index_dtype=torch.int64, seed=0, name=None, chunked=False, **options):
     """GDN ("gdn") or KDA ("kda") decode on a CSR-paged pool with shared prefix pages.
 
     ``suffix_lengths`` None: one decoded token per sequence (token b belongs to
@@ -226,8 +227,10 @@ def paged(kind, B, HK, HV, K, V, *, prefix_lengths=None, max_prefix=2048, page_s
         inp["cu_seqlens"] = lengths_to_cu(suffix_lengths)
     opts = dict(page_size=page_size, **options)
     wkind = ("kda" if kind == "kda" else "gdn") + ("_paged" if suffix_lengths is None else "_paged_varlen")
+    if chunked and wkind != "gdn_paged_varlen":
+        raise ValueError("the chunked prefill takes GDN suffixes on a paged pool")
     return Workload(wkind, name or wkind, B, HK, HV, K, V, io_dtype, out_dtype or io_dtype, state_layout,
-                    num_pages, inp, opts, pool_seed=seed + 1)
+                    num_pages, inp, opts, pool_seed=seed + 1, chunked=chunked)
 
 
 def gdn_paged(B, HK, HV, K, V, **kw):
@@ -272,6 +275,13 @@ def fp8_qdq_gdn_b512(seed=1005):
                       qdq="fp8_e4m3_tile", block_v=64)
 
 
+def paged_gdn_prefill_b16_t1024(seed=1009, state_layout=V_FIRST, index_dtype=torch.int64):
+    """Chunked prefill on the paged pool: 16 sequences each append 1024 tokens after a prefix U{1..2048}."""
+    return paged("gdn", 16, 16, 32, 128, 128, max_prefix=2048, page_size=16, share_frac=0.1,
+                 suffix_lengths=np.full(16, 1024), state_layout=state_layout, index_dtype=index_dtype, seed=seed,
+                 name="paged_gdn_prefill_b16_t1024_hv32_k128_ps16", chunked=True)
+
+
 def int8h32_gdn_b512(seed=1008):
     """The B=512, 4-token pooled GDN workload with the int8_hadamard32 state codec instead of fp8 tiles."""
     return gdn_pooled(512, 16, 32, 128, 128, lengths=np.full(512, 4), num_slots=1024,
@@ -301,4 +311,5 @@ NAMED = {
     "paged_kda_b256": paged_kda_b256,
     "paged_gdn_varlen_b256_t4": paged_gdn_varlen_b256_t4,
     "int8h32_gdn_b512": int8h32_gdn_b512,
+    "paged_gdn_prefill_b16_t1024": paged_gdn_prefill_b16_t1024,
 }

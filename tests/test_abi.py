@@ -127,3 +127,26 @@ def test_new_paged_entry_points_argument_errors():
     assert lib.gdn_paged_decode_slots(FAKE, FAKE, None, 4, bnd.GDN_I32, FAKE, None) == bnd.GDN_ERR_INVALID
     assert lib.kda_decode_paged(*([FAKE] * 12), 2, 2, 3, 128, 128, 10, 4, ctypes.byref(o), None) \
         == bnd.GDN_ERR_INVALID   # HV % HK != 0
+
+
+@no_gpu
+def test_prefill_argument_errors():
+    lib = rsd.load_library()
+    o = bnd._options(index_dtype=bnd.GDN_I64)
+    args = [FAKE] * 11
+
+    def call(page_size=16, B=2, T=4, HK=1, HV=2, K=128, V=128, opt=o, a=args):
+        return lib.gdn_prefill_paged(*a, page_size, FAKE, FAKE, B, T, HK, HV, K, V, 10, 4, ctypes.byref(opt), None)
+
+    assert call(T=0) == bnd.GDN_OK                        # nothing to do: no launch
+    assert call(page_size=0) == bnd.GDN_ERR_INVALID
+    assert call(page_size=8) == bnd.GDN_ERR_UNSUPPORTED   # chunks of 16 must end on page ends
+    assert "multiple of 16" in lib.gdn_last_error().decode()
+    assert call(K=16, V=16) == bnd.GDN_ERR_UNSUPPORTED
+    assert call(V=64) == bnd.GDN_ERR_UNSUPPORTED
+    assert call(opt=bnd._options(index_dtype=bnd.GDN_I64, qdq=1)) == bnd.GDN_ERR_UNSUPPORTED
+    assert call(opt=bnd._options(index_dtype=bnd.GDN_I64, slots=0x2000)) == bnd.GDN_ERR_INVALID
+    nul = list(args)
+    nul[7] = None                                          # cu_seqlens is required
+    assert call(a=nul) == bnd.GDN_ERR_INVALID
+    assert call(HK=3, HV=4) == bnd.GDN_ERR_INVALID

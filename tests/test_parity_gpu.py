@@ -380,3 +380,54 @@ def test_codec_gdn_b512_t4_sampled():
     seqs = sorted(np.random.default_rng(8).choice(w.B, 48, replace=False).tolist())
     rep, _, _ = P.run_and_check(w, seqs=seqs)
     _report(w.name, rep)
+
+
+# ---------------------------------------------------------------- chunked prefill on the paged pool
+
+@pytest.mark.parametrize("layout,idx,page_size", [("V_FIRST", torch.int64, 16), ("K_FIRST", torch.int32, 16),
+                                                  ("V_FIRST", torch.int32, 32), ("K_FIRST", torch.int64, 64)])
+def test_prefill_small(layout, idx, page_size):
+    """Suffixes of 0..70 tokens after prefixes that end on and off page and chunk boundaries."""
+    suffix = np.array([1, 5, 16, 17, 0, 40, 33, 70, 2, 31, 15, 64])
+    prefix = np.array([15, 16, 1, 31, 7, 32, 48, 5, 63, 64, 100, 17])
+    w = wl.paged("gdn", len(suffix), 2, 4, 128, 128, prefix_lengths=prefix, page_size=page_size, share_frac=0.3,
+                 suffix_lengths=suffix, state_layout=layout, index_dtype=idx, seed=60, chunked=True)
+    rep, _, _ = P.run_and_check(w)
+    _report(f"prefill_small/{layout}/{idx}/ps{page_size}", rep)
+
+
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+def test_prefill_options(io):
+    """fp32 I/O and outputs, probability beta, no L2 norm with an explicit scale, V = 256, GQA 4."""
+    suffix = np.array([9, 40, 23])
+    w = wl.paged("gdn", 3, 2, 8, 128, 256, max_prefix=50, page_size=16, share_frac=0.0, suffix_lengths=suffix,
+                 state_layout="V_FIRST", io_dtype=io, out_dtype=torch.float32, seed=61, chunked=True,
+                 beta_mode="probability", use_qk_l2norm=False, scale=0.05)
+    w.inputs["b"] = torch.rand(w.inputs["b"].shape).to(io)
+    for key in ("q", "k"):
+        w.inputs[key] = (w.inputs[key].float() / 8).to(io)
+    rep, _, _ = P.run_and_check(w)
+    _report(f"prefill_options/{io}", rep)
+
+
+def test_prefill_equals_token_path():
+    """The chunked call and the token-by-token call agree on outputs and every written page."""
+    import recurrent_state_decode_amd as rsd
+    suffix = np.array([3, 64, 29, 100, 16, 1])
+    w = wl.paged("gdn", len(suffix), 2, 4, 128, 128, max_prefix=90, page_size=16, share_frac=0.2,
+                 suffix_lengths=suffix, state_layout="V_FIRST", out_dtype=torch.float32, seed=62, chunked=True)
+    d = P.device_inputs(w)
+    pool_a = wl.make_pool(w, "cuda")
+    pool_b = pool_a.clone()
+    out_a = P.gpu_call(w, pool_a, d)
+    w.chunked = False
+    out_b = P.gpu_call(w, pool_b, d)
+    torch.cuda.synchronize()
+    torch.testing.assert_close(out_a, out_b, rtol=1e-4, atol=1e-5)
+    torch.testing.assert_close(pool_a, pool_b, rtol=1e-4, atol=1e-6)
+
+
+def test_prefill_b16_t1024_sampled():
+    w = wl.paged_gdn_prefill_b16_t1024()
+    rep, _, _ = P.run_and_check(w, seqs=[0, 7, 15])
+    _report(w.name, rep)
