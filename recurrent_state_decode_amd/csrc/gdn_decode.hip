@@ -429,11 +429,12 @@ int gdn_prefill_paged(const void* q, const void* k, const void* v, const void* a
   if (units > 0x7fffffffLL) return fail(GDN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)units);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool vf = opt->state_layout == GDN_V_FIRST, bf = opt->io_dtype == GDN_BF16;
-  const dim3 grid(static_cast<uint32_t>(units)), block(256);
-  if (vf && bf) hipLaunchKernelGGL((gdn::prefill_kernel<true, gdn::bf16_t>), grid, block, 0, s, p);
-  else if (vf) hipLaunchKernelGGL((gdn::prefill_kernel<true, float>), grid, block, 0, s, p);
-  else if (bf) hipLaunchKernelGGL((gdn::prefill_kernel<false, gdn::bf16_t>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((gdn::prefill_kernel<false, float>), grid, block, 0, s, p);
+  constexpr int VT = 2;             // two 16-column value tiles per wave: 4 waves per workgroup
+  const dim3 grid(static_cast<uint32_t>(units)), block(gdn::kPrefillThreads<VT>);
+  if (vf && bf) hipLaunchKernelGGL((gdn::prefill_kernel<VT, true, gdn::bf16_t>), grid, block, 0, s, p);
+  else if (vf) hipLaunchKernelGGL((gdn::prefill_kernel<VT, true, float>), grid, block, 0, s, p);
+  else if (bf) hipLaunchKernelGGL((gdn::prefill_kernel<VT, false, gdn::bf16_t>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((gdn::prefill_kernel<VT, false, float>), grid, block, 0, s, p);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   g_last_error.clear();

@@ -10,8 +10,8 @@
 //     G_t  = sum_{s<=t} g_s                       (g = log alpha, so G <= 0)
 //     A'   = strict_lower( beta_t exp(G_t - G_s) k_t . k_s )
 //     T    = (I + A')^-1                          (forward substitution)
-//     W    = T diag(beta exp(G)) K,   U~ = T diag(beta) V
-//     U    = U~ - W S0
+//     U    = T diag(beta) (V - diag(exp G) K S0)
+//          (= U~ - W S0 with U~ = T diag(beta) V, W = T diag(beta exp G) K)
 //     O    = diag(exp G) Q S0 + P U,  P = lower( exp(G_t - G_s) q_t . k_s )
 //     S_C  = exp(G_C) S0 + sum_s exp(G_C - G_s) k_s u_s^T
 // Every exponent is <= 0.  Chunks are aligned to absolute token positions
@@ -21,14 +21,17 @@
 // g = 0): their rows of A', W, U~ and U are zero and T is the identity on
 // them, so they change nothing.
 //
-// One workgroup per (sequence, value head, 128-column V-block), 4 waves; wave
-// w owns value columns [32 w, 32 w + 32) of the block and keeps S[:, those]
-// (128 x 32) as 16 MFMA accumulator tiles for the whole suffix.  The
+// One workgroup per (sequence, value head, 128-column V-block), 8 / VT waves;
+// wave w owns value columns [16 VT w, 16 VT (w + 1)) of the block and keeps
+// S[:, those] (128 x 16 VT) as 8 VT MFMA accumulator tiles for the whole
+// suffix.  The
 // products that involve S use the accumulator registers directly as the B
 // operand of v_mfma_f32_16x16x4_f32: a lane holds S rows 4 g + r of a tile
 // (g = lane / 16), so the k-step r pairs B = element r with A = the matching
-// column 16 ct + 4 g + r of the left factor.  The K-side quantities (A', P,
-// T, W) are computed once per workgroup and shared through LDS.
+// column 16 ct + 4 g + r of the left factor.  K S0 and Q S0 do not depend on
+// the solve and are formed while waves 0 and 1 build A' and P; every wave
+// then solves for T itself (16 lanes, forward substitution), so the solve
+// needs no workgroup barrier.  A chunk's inputs are loaded one chunk ahead.
 //
 // MFMA 16x16x4 f32 lane layout (checked on the device): A[i][k] from lane
 // i + 16 k, B[k][j] from lane j + 16 k, D[4 (l / 16) + r][l % 16] in lane l,
@@ -67,20 +70,24 @@ __device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <bool VF, typename TIn>
-__global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
-  constexpr int K = 128, C = kChunk, NW = 4;
+// VT value tiles (16 columns each) per wave, 8 / VT waves per workgroup.
+template <int VT>
+constexpr int kPrefillThreads = 512 / VT;
+
+template <int VT, bool VF, typename TIn>
+__global__ __launch_bounds__(kPrefillThreads<VT>) __attribute__((amdgpu_waves_per_eu(8 / (2 * VT), 8 / (2 * VT))))
+void prefill_kernel(const PrefillParams p) {
+  constexpr int K = 128, C = kChunk, NW = 8 / VT, SPW = C / NW;
   constexpr int LDK = K + 4;       // padded LDS rows
   constexpr int LDC = C + 1;
 
   __shared__ __align__(16) float s_q[C][LDK];   // q_hat (scaled)
   __shared__ __align__(16) float s_k[C][LDK];   // k_hat
   __shared__ __align__(16) float s_v[C][LDK];   // v of this V-block
-  __shared__ __align__(16) float s_w[C][LDK];   // W
   __shared__ float s_a[C][LDC];                 // A' (strict lower)
   __shared__ float s_p[C][LDC];                 // P (lower, diagonal included)
-  __shared__ float s_t[C][LDC];                 // T = (I + A')^-1
-  __shared__ float s_g[C], s_b[C], s_G[C];
+  __shared__ float s_t[NW][C][LDC];             // T = (I + A')^-1, one copy per wave
+  __shared__ float s_g[C], s_b[C];
 
   const TIn* __restrict__ gq = static_cast<const TIn*>(p.q);
   const TIn* __restrict__ gk = static_cast<const TIn*>(p.k);
@@ -108,84 +115,52 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
   // the sequence holds pos_last tokens after the suffix; the suffix is
   // positions pos0 .. pos_last (1-based); the state before it lives on the
   // page of position pos0 - 1
+  // (token positions of one sequence fit in 32 bits; table offsets may not)
   const int64_t pg_start = load_index(p.page_indptr, bs, p.idx64);
   const int64_t pg_end = load_index(p.page_indptr, bs + 1, p.idx64);
-  const int64_t lpl = load_index(p.last_page_len, bs, p.idx64);
-  const int64_t pos_last = (pg_end - pg_start - 1) * p.page_size + lpl;
-  const int64_t pos0 = pos_last - (t1 - t0) + 1;
-  const int64_t rrow =
-      load_index(p.page_indices, pg_start + max(pos0 - 2, static_cast<int64_t>(0)) / p.page_size, p.idx64);
+  const int lpl = static_cast<int>(load_index(p.last_page_len, bs, p.idx64));
+  const int pos_last = static_cast<int>(pg_end - pg_start - 1) * p.page_size + lpl;
+  const int pos0 = pos_last - (t1 - t0) + 1;
+  const int64_t rrow = load_index(p.page_indices, pg_start + max(pos0 - 2, 0) / p.page_size, p.idx64);
   const int64_t wrow = load_index(p.page_indices, pg_end - 1, p.idx64);
 
   const int64_t tile_elems = static_cast<int64_t>(K) * p.V;
-  const int vcol = vb * 128 + 32 * w;   // first value column of this wave
+  const int vcol = vb * 128 + 16 * VT * w;   // first value column of this wave
 
-  // S[ct][vt] element r = S[16 ct + 4 g4 + r][vcol + 16 vt + n16]
-  f32x4 S[8][2];
-  auto state_off = [&](int ct, int vt, int r) -> int64_t {
-    const int64_t ch = 16 * ct + 4 * g4 + r;
-    const int64_t v = vcol + 16 * vt + n16;
-    return VF ? v * K + ch : ch * p.V + v;
-  };
-  {
-    const float* src = p.pool + (rrow * p.HV + h) * tile_elems;
+  // ---- raw inputs of one chunk's slots 4 w .. 4 w + 3 (issued a chunk ahead)
+  Raw<TIn, 2> rq[SPW], rk[SPW], rv[SPW];
+  Raw<TIn, 1> ra[SPW], rb[SPW];
+  auto load_chunk = [&](int cpos) {
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-      for (int vt = 0; vt < 2; ++vt) {
-        if constexpr (VF) {
-          S[ct][vt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + state_off(ct, vt, 0)));
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) S[ct][vt][r] = __builtin_nontemporal_load(src + state_off(ct, vt, r));
-        }
-      }
-  }
-  auto store_state = [&](int64_t row) {
-    float* dst = p.pool + (row * p.HV + h) * tile_elems;
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-      for (int vt = 0; vt < 2; ++vt) {
-        if constexpr (VF) {
-          *reinterpret_cast<f32x4*>(dst + state_off(ct, vt, 0)) = S[ct][vt];
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) dst[state_off(ct, vt, r)] = S[ct][vt][r];
-        }
-      }
-  };
-
-  const float rate = exp_hw(p.a_log[h]);
-  const float dtb = p.dt_bias[h];
-  const int64_t jfirst = (pos0 - 1) / C;
-  const int64_t jlast = (pos_last - 1) / C;
-
-  for (int64_t j = jfirst; j <= jlast; ++j) {
-    const int64_t cpos = j * C + 1;          // position of slot 0
-
-    // ---- stage the chunk's inputs: wave w normalises slots 4 w .. 4 w + 3
-#pragma unroll
-    for (int i = 0; i < C / NW; ++i) {
-      const int slot = w * (C / NW) + i;
-      const int64_t pos = cpos + slot;
-      float xq[2] = {0.0f, 0.0f}, xk[2] = {0.0f, 0.0f}, xv[2] = {0.0f, 0.0f};
-      float gt = 0.0f, bt = 0.0f;
+    for (int i = 0; i < SPW; ++i) {
+      const int pos = cpos + w * SPW + i;
       if (pos >= pos0 && pos <= pos_last) {  // uniform per wave
         const int64_t t = t0 + (pos - pos0);
-        Raw<TIn, 2> rq, rk, rv;
-        Raw<TIn, 1> ra, rb;
-        load_raw_n<2>(gq, (t * p.HK + hk) * K + 2 * lane, rq);
-        load_raw_n<2>(gk, (t * p.HK + hk) * K + 2 * lane, rk);
-        load_raw_n<2>(gv, (t * p.HV + h) * p.V + vb * 128 + 2 * lane, rv);
-        load_raw_n<1>(gg, t * p.HV + h, ra);
-        load_raw_n<1>(gb, t * p.HV + h, rb);
-        decode_raw(rq, xq);
-        decode_raw(rk, xk);
-        decode_raw(rv, xv);
+        load_raw_n<2>(gq, (t * p.HK + hk) * K + 2 * lane, rq[i]);
+        load_raw_n<2>(gk, (t * p.HK + hk) * K + 2 * lane, rk[i]);
+        load_raw_n<2>(gv, (t * p.HV + h) * p.V + vb * 128 + 2 * lane, rv[i]);
+        load_raw_n<1>(gg, t * p.HV + h, ra[i]);
+        load_raw_n<1>(gb, t * p.HV + h, rb[i]);
+      }
+    }
+  };
+  const float rate = exp_hw(p.a_log[h]);
+  const float dtb = p.dt_bias[h];
+  // normalise, gate and stage the slots in LDS (positions outside the suffix: identity tokens)
+  auto stage_chunk = [&](int cpos) {
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      const int slot = w * SPW + i;
+      const int pos = cpos + slot;
+      float xq[2] = {0.0f, 0.0f}, xk[2] = {0.0f, 0.0f}, xv[2] = {0.0f, 0.0f};
+      float gt = 0.0f, bt = 0.0f;
+      if (pos >= pos0 && pos <= pos_last) {
+        decode_raw(rq[i], xq);
+        decode_raw(rk[i], xk);
+        decode_raw(rv[i], xv);
         float xa[1], xb[1];
-        decode_raw(ra, xa);
-        decode_raw(rb, xb);
+        decode_raw(ra[i], xa);
+        decode_raw(rb[i], xb);
         float iq = p.scale, ik = 1.0f;
         if (p.l2norm) {
           iq = p.scale * rsqrtf(lane_reduce<0, 6>(fmaf(xq[0], xq[0], xq[1] * xq[1])) + kL2Eps);
@@ -206,19 +181,81 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
         s_b[slot] = bt;
       }
     }
+  };
+
+  const int jfirst = (pos0 - 1) / C;
+  const int jlast = (pos_last - 1) / C;
+  // page ends met by the chunk loop: the first one at or after the end of
+  // chunk jfirst, then one every page_size / C chunks
+  const int cpp = p.page_size / C;
+  int to_page_end = (cpp - 1) - jfirst % cpp;   // chunks until one ends a page
+  int64_t page_slot = pg_start + jfirst / cpp;  // table entry of that page
+  load_chunk(jfirst * C + 1);      // in flight while the state tile loads
+
+  // S[ct][vt] element r = S[16 ct + 4 g4 + r][vcol + 16 vt + n16]
+  f32x4 S[8][VT];
+  // offset of element r of tile (ct, vt) inside one (row, head) state: a
+  // per-lane base plus a uniform part (32-bit: a state holds K V < 2^31 floats)
+  const int lane_base = VF ? (vcol + n16) * K + 4 * g4 : 4 * g4 * p.V + vcol + n16;
+  auto state_off = [&](int ct, int vt, int r) -> int {
+    return VF ? lane_base + 16 * vt * K + 16 * ct + r : lane_base + (16 * ct + r) * p.V + 16 * vt;
+  };
+  {
+    const float* src = p.pool + (rrow * p.HV + h) * tile_elems;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) {
+        if constexpr (VF) {
+          S[ct][vt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + state_off(ct, vt, 0)));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            // uniform row pointer + 32-bit lane offset (K_FIRST: one key row per element)
+            const float* rowp = src + static_cast<uint32_t>((16 * ct + r) * p.V + 16 * vt);
+            S[ct][vt][r] = __builtin_nontemporal_load(rowp + static_cast<uint32_t>(lane_base));
+          }
+        }
+      }
+  }
+  auto store_state = [&](int64_t row) {
+    float* dst = p.pool + (row * p.HV + h) * tile_elems;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) {
+        if constexpr (VF) {
+          *reinterpret_cast<f32x4*>(dst + state_off(ct, vt, 0)) = S[ct][vt];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float* rowp = dst + static_cast<uint32_t>((16 * ct + r) * p.V + 16 * vt);
+            rowp[static_cast<uint32_t>(lane_base)] = S[ct][vt][r];
+          }
+        }
+      }
+  };
+
+  for (int j = jfirst; j <= jlast; ++j) {
+    const int cpos = j * C + 1;              // position of slot 0
+    stage_chunk(cpos);
+    if (j < jlast) load_chunk(cpos + C);     // next chunk's inputs, in flight during this chunk
     __syncthreads();
 
-    // ---- gate prefix, key interaction (wave 0) and output score (wave 1)
+    // ---- gate prefix (every wave): inclusive scan of g over the 16 lanes of
+    //      each row (row_shr:n with bound_ctrl, so the first n lanes add 0)
+    float Gc = s_g[n16];                      // becomes G of column s = n16
+    Gc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(Gc), 0x111, 0xF, 0xF, true));
+    Gc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(Gc), 0x112, 0xF, 0xF, true));
+    Gc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(Gc), 0x114, 0xF, 0xF, true));
+    Gc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(Gc), 0x118, 0xF, 0xF, true));
+    float Gr[4];                              // G of rows t = 4 g4 + r
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Gr[r] = __shfl(Gc, 4 * g4 + r);
+    const float GC = __shfl(Gc, C - 1);       // G of the last slot
+
+    // ---- key interaction A' (wave 0) and output score P (wave 1), 16 x 16 over K
     if (w < 2) {
-      float G = 0.0f;                         // G of column s = n16
-      float Gr[4] = {0.0f, 0.0f, 0.0f, 0.0f}; // G of rows t = 4 g4 + r
-#pragma unroll
-      for (int s = 0; s < C; ++s) {
-        G += (s <= n16) ? s_g[s] : 0.0f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Gr[r] += (s <= 4 * g4 + r) ? s_g[s] : 0.0f;
-      }
-      if (w == 0 && lane < C) s_G[lane] = G;
       const float(*left)[LDK] = (w == 0) ? s_k : s_q;
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -226,15 +263,39 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 4 * g4 + r, s = n16;
-        const float d = exp_hw(fminf(Gr[r] - G, 0.0f));
+        const float d = exp_hw(fminf(Gr[r] - Gc, 0.0f));
         if (w == 0) s_a[t][s] = (s < t) ? s_b[t] * d * acc[r] : 0.0f;
         else s_p[t][s] = (s <= t) ? d * acc[r] : 0.0f;
       }
     }
-    __syncthreads();
 
-    // ---- exact solve T = (I + A')^-1 by forward substitution, column n16 per lane
-    if (w == 0 && lane < C) {
+    // ---- KS = K S0 and QS = Q S0 for this wave's columns (A operands: row n16,
+    //      columns 16 ct + 4 g4 + r; B: the state accumulators)
+    f32x4 KS[VT], O[VT];
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt) {
+      KS[vt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      O[vt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      const float4 kv = *reinterpret_cast<const float4*>(&s_k[n16][16 * ct + 4 * g4]);
+      const float4 qv = *reinterpret_cast<const float4*>(&s_q[n16][16 * ct + 4 * g4]);
+      const float kr[4] = {kv.x, kv.y, kv.z, kv.w};
+      const float qr[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          KS[vt] = mfma_16x16x4(kr[r], S[ct][vt][r], KS[vt]);
+          O[vt] = mfma_16x16x4(qr[r], S[ct][vt][r], O[vt]);
+        }
+    }
+    __syncthreads();                          // A' and P visible
+
+    // ---- exact solve T = (I + A')^-1 by forward substitution (every wave its
+    //      own copy: lane n16 < 16 computes column n16)
+    if (lane < C) {
       float x[C];
 #pragma unroll
       for (int t = 0; t < C; ++t) {
@@ -242,80 +303,48 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
 #pragma unroll
         for (int s = 0; s < t; ++s) acc = fmaf(-s_a[t][s], x[s], acc);
         x[t] = acc;
-        s_t[t][lane] = acc;
+        s_t[w][t][lane] = acc;
       }
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // T is read by the other lanes of this wave
+    __builtin_amdgcn_wave_barrier();
 
-    // ---- W = T diag(beta exp G) K (two column tiles per wave) and U~ = T diag(beta) V
-    f32x4 U[2];
-    {
-      float tb[4], tbe[4];          // A operands: T[t = n16][s = 4 st + g4] * beta_s (* exp G_s)
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int s = 4 * st + g4;
-        tb[st] = s_t[n16][s] * s_b[s];
-        tbe[st] = tb[st] * exp_hw(s_G[s]);
-      }
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int ct = 2 * w + cc;
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int st = 0; st < 4; ++st) acc = mfma_16x16x4(tbe[st], s_k[4 * st + g4][16 * ct + n16], acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s_w[4 * g4 + r][16 * ct + n16] = acc[r];
-      }
-#pragma unroll
-      for (int vt = 0; vt < 2; ++vt) {
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int st = 0; st < 4; ++st) acc = mfma_16x16x4(tb[st], s_v[4 * st + g4][32 * w + 16 * vt + n16], acc);
-        U[vt] = acc;
-      }
-    }
-    __syncthreads();
-
-    // ---- U = U~ - W S0 and O1 = Q S0 (A operands: row n16, columns 16 ct + 4 g4 + r)
-    f32x4 O[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-      const float4 wv = *reinterpret_cast<const float4*>(&s_w[n16][16 * ct + 4 * g4]);
-      const float4 qv = *reinterpret_cast<const float4*>(&s_q[n16][16 * ct + 4 * g4]);
-      const float wr[4] = {-wv.x, -wv.y, -wv.z, -wv.w};
-      const float qr[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-      for (int vt = 0; vt < 2; ++vt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          U[vt] = mfma_16x16x4(wr[r], S[ct][vt][r], U[vt]);
-          O[vt] = mfma_16x16x4(qr[r], S[ct][vt][r], O[vt]);
-        }
-    }
-
-    // ---- O = diag(exp G) O1 + P U   (B = U rows s = 4 g4 + r)
+    // ---- U = T diag(beta) (V - diag(exp G) K S0): R in accumulator layout
+    //      (rows s = 4 g4 + r) is the B operand; A = T[n16][4 g4 + r] beta
     float eG[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) eG[r] = exp_hw(s_G[4 * g4 + r]);
+    for (int r = 0; r < 4; ++r) eG[r] = exp_hw(Gr[r]);
+    f32x4 U[VT];
 #pragma unroll
-    for (int vt = 0; vt < 2; ++vt)
+    for (int vt = 0; vt < VT; ++vt) {
+      f32x4 R;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) R[r] = s_v[4 * g4 + r][16 * VT * w + 16 * vt + n16] - eG[r] * KS[vt][r];
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc = mfma_16x16x4(s_t[w][n16][4 * g4 + r] * s_b[4 * g4 + r], R[r], acc);
+      U[vt] = acc;
+    }
+
+    // ---- O = diag(exp G) Q S0 + P U   (B = U rows s = 4 g4 + r)
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) O[vt][r] *= eG[r];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float pa = s_p[n16][4 * g4 + r];
 #pragma unroll
-      for (int vt = 0; vt < 2; ++vt) O[vt] = mfma_16x16x4(pa, U[vt][r], O[vt]);
+      for (int vt = 0; vt < VT; ++vt) O[vt] = mfma_16x16x4(pa, U[vt][r], O[vt]);
     }
-    // outputs of the suffix tokens among rows t = 4 g4 + r
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t pos = cpos + 4 * g4 + r;
+      const int pos = cpos + 4 * g4 + r;
       if (pos >= pos0 && pos <= pos_last) {
         const int64_t t = t0 + (pos - pos0);
         const int64_t oi = (t * p.HV + h) * p.V + vcol + n16;
 #pragma unroll
-        for (int vt = 0; vt < 2; ++vt) {
+        for (int vt = 0; vt < VT; ++vt) {
           if (p.out_bf16) static_cast<uint16_t*>(p.out)[oi + 16 * vt] = to_bf16_bits(O[vt][r]);
           else static_cast<float*>(p.out)[oi + 16 * vt] = O[vt][r];
         }
@@ -323,18 +352,17 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     }
 
     // ---- S_C = exp(G_C) S0 + sum_s exp(G_C - G_s) k_s u_s^T
-    const float GC = s_G[C - 1];
     const float eC = exp_hw(GC);
     float dk[4];                    // exp(G_C - G_s) for s = 4 g4 + r
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dk[r] = exp_hw(fminf(GC - s_G[4 * g4 + r], 0.0f));
+    for (int r = 0; r < 4; ++r) dk[r] = exp_hw(fminf(GC - Gr[r], 0.0f));
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       float ka[4];                  // A[ch = 16 ct + n16][s = 4 g4 + r]
 #pragma unroll
       for (int r = 0; r < 4; ++r) ka[r] = dk[r] * s_k[4 * g4 + r][16 * ct + n16];
 #pragma unroll
-      for (int vt = 0; vt < 2; ++vt) {
+      for (int vt = 0; vt < VT; ++vt) {
         f32x4 acc = S[ct][vt] * eC;
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc = mfma_16x16x4(ka[r], U[vt][r], acc);
@@ -343,9 +371,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     }
 
     // ---- a page that ends inside the suffix gets the state after its last token
-    const int64_t pend = cpos + C - 1;
-    if (pend % p.page_size == 0 && pend < pos_last)
-      store_state(load_index(p.page_indices, pg_start + (pend - 1) / p.page_size, p.idx64));
+    if (to_page_end == 0) {
+      if (cpos + C - 1 < pos_last) store_state(load_index(p.page_indices, page_slot, p.idx64));
+      to_page_end = cpp;
+      ++page_slot;
+    }
+    --to_page_end;
     __syncthreads();                // LDS is rewritten by the next chunk
   }
 

@@ -411,7 +411,8 @@ def test_prefill_options(io):
 
 
 def test_prefill_equals_token_path():
-    """The chunked call and the token-by-token call agree on outputs and every written page."""
+    """The chunked call and the token-by-token call agree on outputs and every written page to float32
+    rounding of two different summation orders: 2e-5 of |x| + rms (a hundredth of the oracle tolerance)."""
     import recurrent_state_decode_amd as rsd
     suffix = np.array([3, 64, 29, 100, 16, 1])
     w = wl.paged("gdn", len(suffix), 2, 4, 128, 128, max_prefix=90, page_size=16, share_frac=0.2,
@@ -423,8 +424,11 @@ def test_prefill_equals_token_path():
     w.chunked = False
     out_b = P.gpu_call(w, pool_b, d)
     torch.cuda.synchronize()
-    torch.testing.assert_close(out_a, out_b, rtol=1e-4, atol=1e-5)
-    torch.testing.assert_close(pool_a, pool_b, rtol=1e-4, atol=1e-6)
+    for a, b in ((out_a, out_b), (pool_a, pool_b)):
+        a, b = a.double(), b.double()
+        rms = b.pow(2).mean().sqrt()
+        err = ((a - b).abs() / (b.abs() + rms)).max().item()
+        assert err <= 2e-5, f"chunked vs token-by-token: {err}"
 
 
 def test_prefill_b16_t1024_sampled():
