@@ -68,6 +68,31 @@ def algorithmic_bytes(w):
     return state, T * per_tok
 
 
+PEAK_FP32_MFMA_TFLOPS = 157.3
+
+
+def chunked_flops(w):
+    """Algorithmic FLOPs of the chunked prefill's WY form: per chunk of 16 aligned positions, value head
+    and 128 value columns, 2 x (k.k^T and q.k^T: 2 x 16 x 16 x K; K S0, Q S0 and the state update:
+    3 x 16 x K x 128; T (V - ...) and P U: 2 x 16 x 16 x 128) multiply-adds; the 16 x 16 solve is
+    negligible."""
+    import numpy as np
+    cu = w.inputs["cu_seqlens"].numpy()
+    lpl = w.inputs["last_page_len"].numpy()
+    ptr = w.inputs["page_indptr"].numpy()
+    ps = w.options["page_size"]
+    chunks = 0
+    for b in range(w.B):
+        n = int(cu[b + 1] - cu[b])
+        if n <= 0:
+            continue
+        pos_last = int(ptr[b + 1] - ptr[b] - 1) * ps + int(lpl[b])
+        pos0 = pos_last - n + 1
+        chunks += (pos_last - 1) // 16 - (pos0 - 1) // 16 + 1
+    per = 2 * (2 * 16 * 16 * w.K + 3 * 16 * w.K * 128 + 2 * 16 * 16 * 128)
+    return chunks * w.HV * (w.V // 128) * per
+
+
 def kernel_name(w):
     return "gdn::prefill_kernel" if w.chunked else "gdn::decode_kernel"
 
@@ -124,7 +149,7 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir, commands):
              "    " + commands["kt"], "",
              f"bench.py line of this run: ms_per_step={bench_kt['ms_per_step']} "
              f"(HIP events around each launch, after the cache-flush kernel), value={bench_kt['value']} tokens/s", "",
-             f"decode kernel, timed dispatches ({len(timed)}): mean {statistics.mean(timed):.1f} us, "
+             f"{kern}, timed dispatches ({len(timed)}): mean {statistics.mean(timed):.1f} us, "
              f"median {statistics.median(timed):.1f} us, min {min(timed):.1f} us, max {max(timed):.1f} us", "",
              "| kernel | calls | average ns | min ns | max ns | % time |", "|---|---|---|---|---|---|"]
     for r in stats:
@@ -326,6 +351,12 @@ def main():
                      "traffic": traffic, "algorithmic_bytes_per_launch": state_b + io_b,
                      "kernel": kernel_name(w), "source_hash": source_hash()},
     }
+    if w.chunked:
+        fl = chunked_flops(w)
+        tf = fl / (mean_ms * 1e-3) / 1e12
+        res["roofline_mfma_fp32"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32_MFMA_TFLOPS, 4),
+                                     "algorithmic_flops_per_launch": fl}
     if args.copy_calibration:
         n = 256 * 1024 * 1024
         src = torch.ones(n, dtype=torch.float32, device=dev)
