@@ -230,7 +230,7 @@ def main():
     ap.add_argument("--workload", default="paged_gdn_b256",
                     choices=["paged_gdn_b256", "pooled_gdn_b64", "pooled_kda_varlen_b128", "fp8_qdq_gdn_b512",
                              "tiny_gdn", "paged_kda_b256", "paged_gdn_varlen_b256_t4", "int8h32_gdn_b512",
-                             "paged_gdn_prefill_b16_t1024"])
+                             "paged_gdn_prefill_b16_t1024", "paged_kda_prefill_b16_t1024"])
     ap.add_argument("--layout", default=None, help="override the pool layout (K_FIRST / V_FIRST)")
     ap.add_argument("--qdq", default=None, choices=["none", "fp8_e4m3_tile", "int8_hadamard32"],
                     help="override the workload's state quantisation (the workload name gets a +qdq suffix)")
@@ -274,7 +274,8 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     maker = wl.NAMED[args.workload]
-    paged_makers = ("paged_gdn_b256", "paged_kda_b256", "paged_gdn_varlen_b256_t4", "paged_gdn_prefill_b16_t1024")
+    paged_makers = ("paged_gdn_b256", "paged_kda_b256", "paged_gdn_varlen_b256_t4", "paged_gdn_prefill_b16_t1024",
+                    "paged_kda_prefill_b16_t1024")
     w = maker(state_layout=args.layout) if (args.layout and args.workload in paged_makers) else maker()
     if args.layout and args.workload not in paged_makers:
         w.state_layout = args.layout

@@ -267,7 +267,9 @@ int kda_decode_paged_varlen(const void* q, const void* k, const void* v, const v
  * Requirements (else GDN_ERR_UNSUPPORTED): K = 128, V a multiple of 128,
  * page_size a multiple of 16, opt->qdq == GDN_QDQ_NONE.  opt->slots must be
  * NULL.  The chunk's identity padding (positions of a chunk outside the
- * suffix) reads and writes nothing.
+ * suffix) reads and writes nothing.  kda_prefill_paged is the same for the
+ * per-key-channel gate, with kda_decode_paged_varlen's arguments (raw_gate
+ * [T, HV, K], beta_logits [T, HV], a_log [HV], dt_bias [HV, K]).
  */
 int gdn_prefill_paged(const void* q, const void* k, const void* v, const void* a, const void* b,
                       const float* A_log, const float* dt_bias, const int32_t* cu_seqlens,
@@ -275,6 +277,12 @@ int gdn_prefill_paged(const void* q, const void* k, const void* v, const void* a
                       int32_t page_size, float* state_pool, void* out, int32_t B, int32_t T, int32_t HK,
                       int32_t HV, int32_t K, int32_t V, int64_t num_pages, int64_t nnz,
                       const gdn_options* opt, void* stream);
+int kda_prefill_paged(const void* q, const void* k, const void* v, const void* raw_gate,
+                      const void* beta_logits, const float* a_log, const float* dt_bias,
+                      const int32_t* cu_seqlens, const void* page_indices, const void* page_indptr,
+                      const void* last_page_len, int32_t page_size, float* state_pool, void* out,
+                      int32_t B, int32_t T, int32_t HK, int32_t HV, int32_t K, int32_t V,
+                      int64_t num_pages, int64_t nnz, const gdn_options* opt, void* stream);
 
 /*
  * gdn_paged_decode_slots -- the (read row, write row) pair of every sequence

@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     kda_decode_paged,
     kda_decode_paged_varlen,
     kda_decode_pooled,
+    kda_prefill_paged,
     load_library,
     supported_head_dims,
 )

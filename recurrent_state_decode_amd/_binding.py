@@ -67,6 +67,7 @@ _SIGNATURES = {
     "gdn_decode_paged_varlen": (ctypes.c_int, [_P] * 11 + [_I32] + [_P] * 2 + [_I32] * 6 + [_I64, _I64, _OPT, _P]),
     "kda_decode_paged_varlen": (ctypes.c_int, [_P] * 11 + [_I32] + [_P] * 2 + [_I32] * 6 + [_I64, _I64, _OPT, _P]),
     "gdn_prefill_paged": (ctypes.c_int, [_P] * 11 + [_I32] + [_P] * 2 + [_I32] * 6 + [_I64, _I64, _OPT, _P]),
+    "kda_prefill_paged": (ctypes.c_int, [_P] * 11 + [_I32] + [_P] * 2 + [_I32] * 6 + [_I64, _I64, _OPT, _P]),
     "gdn_paged_decode_slots": (ctypes.c_int, [_P] * 3 + [_I32, _I32, _P, _P]),
     "gdn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "gdn_last_error": (ctypes.c_char_p, []),
@@ -209,7 +210,7 @@ def _paged(kind, q, k, v, gate, beta_in, a_log, dt_bias, cu_seqlens, page_indice
     io = q.dtype
     out_dtype = out_dtype or io
     kda = kind.startswith("kda")
-    var = kind.endswith("varlen") or kind == "gdn_prefill_paged"
+    var = kind.endswith("varlen") or kind.endswith("prefill_paged")
     for n, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("beta", beta_in)):
         _check_dev(n, t, dev, (io,))
     _check_dev("A_log", a_log, dev, (torch.float32,))
@@ -309,6 +310,15 @@ def gdn_prefill_paged(q, k, v, a, b, A_log, dt_bias, cu_seqlens, page_indices, p
     return _paged("gdn_prefill_paged", q, k, v, a, b, A_log, dt_bias, cu_seqlens, page_indices, page_indptr,
                   last_page_len, page_size, state_pool, out, scale, use_qk_l2norm, beta_mode, state_layout,
                   "original", out_dtype, None, 64, False, "working", None, stream)
+
+
+def kda_prefill_paged(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, page_indices, page_indptr,
+                      last_page_len, page_size, state_pool, out=None, *, scale=None, use_qk_l2norm=True,
+                      beta_mode="logits", state_layout="V_FIRST", gate_mode="original", out_dtype=None, stream=None):
+    """Chunked KDA prefill on a CSR-paged pool (see kda_prefill_paged): the result of kda_decode_paged_varlen."""
+    return _paged("kda_prefill_paged", q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, page_indices,
+                  page_indptr, last_page_len, page_size, state_pool, out, scale, use_qk_l2norm, beta_mode,
+                  state_layout, gate_mode, out_dtype, None, 64, False, "working", None, stream)
 
 
 def gdn_paged_decode_slots(page_indices, page_indptr, last_page_len, slots=None, stream=None):

@@ -386,12 +386,17 @@ int gdn_paged_decode_slots(const void* page_indices, const void* page_indptr, co
   return GDN_OK;
 }
 
-int gdn_prefill_paged(const void* q, const void* k, const void* v, const void* a, const void* b, const float* A_log,
-                      const float* dt_bias, const int32_t* cu_seqlens, const void* page_indices,
-                      const void* page_indptr, const void* last_page_len, int32_t page_size, float* state_pool,
-                      void* out, int32_t B, int32_t T, int32_t HK, int32_t HV, int32_t K, int32_t V,
-                      int64_t num_pages, int64_t nnz, const gdn_options* opt, void* stream) {
-  if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !cu_seqlens || !page_indices || !page_indptr ||
+}  // extern "C"
+
+namespace {
+
+// Shared body of the chunked prefill entry points (GDN / KDA).
+int prefill_call(bool kda, const void* q, const void* k, const void* v, const void* gate, const void* beta,
+                 const float* a_log, const float* dt_bias, const int32_t* cu_seqlens, const void* page_indices,
+                 const void* page_indptr, const void* last_page_len, int32_t page_size, float* state_pool,
+                 void* out, int32_t B, int32_t T, int32_t HK, int32_t HV, int32_t K, int32_t V, int64_t num_pages,
+                 int64_t nnz, const gdn_options* opt, void* stream) {
+  if (!q || !k || !v || !gate || !beta || !a_log || !dt_bias || !cu_seqlens || !page_indices || !page_indptr ||
       !last_page_len || !state_pool || !out)
     return fail(GDN_ERR_INVALID, "a required pointer is NULL");
   if (int rc = check_dims(B, HK, HV, K, V)) return rc;
@@ -406,13 +411,13 @@ int gdn_prefill_paged(const void* q, const void* k, const void* v, const void* a
     return fail(GDN_ERR_UNSUPPORTED, "the chunked prefill needs a page size that is a multiple of %d (got %d)",
                 gdn::kChunk, page_size);
   if (T < 0) return fail(GDN_ERR_INVALID, "T must be >= 0");
-  if (int rc = check_options(opt, K, V, Kind::GdnPagedVar)) return rc;
+  if (int rc = check_options(opt, K, V, kda ? Kind::KdaPagedVar : Kind::GdnPagedVar)) return rc;
   if (opt->slots) return fail(GDN_ERR_INVALID, "slots apply to single-token paged calls only");
   if (opt->qdq != GDN_QDQ_NONE) return fail(GDN_ERR_UNSUPPORTED, "the chunked prefill has no state quantisation");
   if (T == 0) { g_last_error.clear(); return GDN_OK; }
   gdn::PrefillParams p{};
-  p.q = q; p.k = k; p.v = v; p.gate = a; p.beta = b;
-  p.a_log = A_log; p.dt_bias = dt_bias;
+  p.q = q; p.k = k; p.v = v; p.gate = gate; p.beta = beta;
+  p.a_log = a_log; p.dt_bias = dt_bias;
   p.cu_seqlens = cu_seqlens;
   p.page_indices = page_indices; p.page_indptr = page_indptr; p.last_page_len = last_page_len;
   p.page_size = page_size;
@@ -428,17 +433,51 @@ int gdn_prefill_paged(const void* q, const void* k, const void* v, const void* a
   const int64_t units = static_cast<int64_t>(B) * HV * p.nvb;
   if (units > 0x7fffffffLL) return fail(GDN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)units);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool vf = opt->state_layout == GDN_V_FIRST, bf = opt->io_dtype == GDN_BF16;
   constexpr int VT = 2;             // two 16-column value tiles per wave: 4 waves per workgroup
   const dim3 grid(static_cast<uint32_t>(units)), block(gdn::kPrefillThreads<VT>);
-  if (vf && bf) hipLaunchKernelGGL((gdn::prefill_kernel<VT, true, gdn::bf16_t>), grid, block, 0, s, p);
-  else if (vf) hipLaunchKernelGGL((gdn::prefill_kernel<VT, true, float>), grid, block, 0, s, p);
-  else if (bf) hipLaunchKernelGGL((gdn::prefill_kernel<VT, false, gdn::bf16_t>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((gdn::prefill_kernel<VT, false, float>), grid, block, 0, s, p);
+  auto go = [&](auto kda_c, auto vf_c, auto io_c) {
+    constexpr bool KDA = decltype(kda_c)::value, VF = decltype(vf_c)::value;
+    using TIn = typename decltype(io_c)::type;
+    hipLaunchKernelGGL((gdn::prefill_kernel<VT, KDA, VF, TIn>), grid, block, 0, s, p);
+  };
+  using F = std::false_type;
+  using Tr = std::true_type;
+  using Bf = std::common_type<gdn::bf16_t>;
+  using Fl = std::common_type<float>;
+  const bool vf = opt->state_layout == GDN_V_FIRST, bf = opt->io_dtype == GDN_BF16;
+  if (kda) {
+    if (vf) bf ? go(Tr{}, Tr{}, Bf{}) : go(Tr{}, Tr{}, Fl{});
+    else bf ? go(Tr{}, F{}, Bf{}) : go(Tr{}, F{}, Fl{});
+  } else {
+    if (vf) bf ? go(F{}, Tr{}, Bf{}) : go(F{}, Tr{}, Fl{});
+    else bf ? go(F{}, F{}, Bf{}) : go(F{}, F{}, Fl{});
+  }
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   g_last_error.clear();
   return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_prefill_paged(const void* q, const void* k, const void* v, const void* a, const void* b, const float* A_log,
+                      const float* dt_bias, const int32_t* cu_seqlens, const void* page_indices,
+                      const void* page_indptr, const void* last_page_len, int32_t page_size, float* state_pool,
+                      void* out, int32_t B, int32_t T, int32_t HK, int32_t HV, int32_t K, int32_t V,
+                      int64_t num_pages, int64_t nnz, const gdn_options* opt, void* stream) {
+  return prefill_call(false, q, k, v, a, b, A_log, dt_bias, cu_seqlens, page_indices, page_indptr, last_page_len,
+                      page_size, state_pool, out, B, T, HK, HV, K, V, num_pages, nnz, opt, stream);
+}
+
+int kda_prefill_paged(const void* q, const void* k, const void* v, const void* raw_gate, const void* beta_logits,
+                      const float* a_log, const float* dt_bias, const int32_t* cu_seqlens, const void* page_indices,
+                      const void* page_indptr, const void* last_page_len, int32_t page_size, float* state_pool,
+                      void* out, int32_t B, int32_t T, int32_t HK, int32_t HV, int32_t K, int32_t V,
+                      int64_t num_pages, int64_t nnz, const gdn_options* opt, void* stream) {
+  return prefill_call(true, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, page_indices, page_indptr,
+                      last_page_len, page_size, state_pool, out, B, T, HK, HV, K, V, num_pages, nnz, opt, stream);
 }
 
 int kda_decode_pooled(const void* q, const void* k, const void* v, const void* raw_gate, const void* beta_logits,

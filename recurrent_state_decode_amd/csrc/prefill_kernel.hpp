@@ -14,6 +14,13 @@
 //          (= U~ - W S0 with U~ = T diag(beta) V, W = T diag(beta exp G) K)
 //     O    = diag(exp G) Q S0 + P U,  P = lower( exp(G_t - G_s) q_t . k_s )
 //     S_C  = exp(G_C) S0 + sum_s exp(G_C - G_s) k_s u_s^T
+// KDA (max.nn.state_space.kda_decode: one gate per key channel): G is a
+// vector per token, exp(G) acts on key channels (the rows of S), so K S0
+// and Q S0 use the gated rows k_t exp(G_t), q_t exp(G_t), the update uses
+// exp(G_C - G_s) k_s and scales row c of S0 by exp(G_C,c), and A' / P need
+// sum_c x_tc k_sc exp(G_tc - G_sc), which is formed on the VALU pair by pair
+// (one thread per (t, s)) since splitting exp(G_t - G_s) into two factors can
+// overflow one of them.
 // Every exponent is <= 0.  Chunks are aligned to absolute token positions
 // (16 j + 1 .. 16 j + 16), so with a page size that is a multiple of 16 every
 // page end is a chunk end and its state is S_C of that chunk.  Positions of a
@@ -46,10 +53,10 @@ struct PrefillParams {
   const void* q;
   const void* k;
   const void* v;
-  const void* gate;        // a [T, HV]
-  const void* beta;        // b [T, HV]
+  const void* gate;        // GDN: a [T, HV]; KDA: raw_gate [T, HV, K]
+  const void* beta;        // b / beta_logits [T, HV]
   const float* a_log;      // [HV]
-  const float* dt_bias;    // [HV]
+  const float* dt_bias;    // GDN: [HV]; KDA: [HV, K]
   const int32_t* cu_seqlens;
   const void* page_indices;
   const void* page_indptr;
@@ -74,10 +81,11 @@ __device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c) {
 template <int VT>
 constexpr int kPrefillThreads = 512 / VT;
 
-template <int VT, bool VF, typename TIn>
+template <int VT, bool KDA, bool VF, typename TIn>
 __global__ __launch_bounds__(kPrefillThreads<VT>) __attribute__((amdgpu_waves_per_eu(8 / (2 * VT), 8 / (2 * VT))))
 void prefill_kernel(const PrefillParams p) {
   constexpr int K = 128, C = kChunk, NW = 8 / VT, SPW = C / NW;
+  static_assert(!KDA || NW * 64 == C * C, "KDA: one thread per (t, s) pair of the chunk");
   constexpr int LDK = K + 4;       // padded LDS rows
   constexpr int LDC = C + 1;
 
@@ -88,6 +96,11 @@ void prefill_kernel(const PrefillParams p) {
   __shared__ float s_p[C][LDC];                 // P (lower, diagonal included)
   __shared__ float s_t[NW][C][LDC];             // T = (I + A')^-1, one copy per wave
   __shared__ float s_g[C], s_b[C];
+  // KDA: per-channel gates.  s_G holds g, then G (in place); s_kg / s_qg =
+  // k / q times exp(G); s_kd = exp(G_C - G) k; s_eC = exp(G_C) per channel
+  constexpr int KC = KDA ? C : 1, KK = KDA ? LDK : 1;
+  __shared__ __align__(16) float s_G[KC][KK], s_kg[KC][KK], s_qg[KC][KK], s_kd[KC][KK];
+  __shared__ __align__(16) float s_eC[KDA ? K : 1];
 
   const TIn* __restrict__ gq = static_cast<const TIn*>(p.q);
   const TIn* __restrict__ gk = static_cast<const TIn*>(p.k);
@@ -128,8 +141,10 @@ void prefill_kernel(const PrefillParams p) {
   const int vcol = vb * 128 + 16 * VT * w;   // first value column of this wave
 
   // ---- raw inputs of one chunk's slots 4 w .. 4 w + 3 (issued a chunk ahead)
+  constexpr int GPL = KDA ? 2 : 1;  // gate elements per lane
   Raw<TIn, 2> rq[SPW], rk[SPW], rv[SPW];
-  Raw<TIn, 1> ra[SPW], rb[SPW];
+  Raw<TIn, GPL> ra[SPW];
+  Raw<TIn, 1> rb[SPW];
   auto load_chunk = [&](int cpos) {
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
@@ -139,13 +154,16 @@ void prefill_kernel(const PrefillParams p) {
         load_raw_n<2>(gq, (t * p.HK + hk) * K + 2 * lane, rq[i]);
         load_raw_n<2>(gk, (t * p.HK + hk) * K + 2 * lane, rk[i]);
         load_raw_n<2>(gv, (t * p.HV + h) * p.V + vb * 128 + 2 * lane, rv[i]);
-        load_raw_n<1>(gg, t * p.HV + h, ra[i]);
+        if constexpr (KDA) load_raw_n<2>(gg, (t * p.HV + h) * K + 2 * lane, ra[i]);
+        else load_raw_n<1>(gg, t * p.HV + h, ra[i]);
         load_raw_n<1>(gb, t * p.HV + h, rb[i]);
       }
     }
   };
   const float rate = exp_hw(p.a_log[h]);
-  const float dtb = p.dt_bias[h];
+  float dtb[GPL];
+#pragma unroll
+  for (int e = 0; e < GPL; ++e) dtb[e] = KDA ? p.dt_bias[h * K + 2 * lane + e] : p.dt_bias[h];
   // normalise, gate and stage the slots in LDS (positions outside the suffix: identity tokens)
   auto stage_chunk = [&](int cpos) {
 #pragma unroll
@@ -153,12 +171,12 @@ void prefill_kernel(const PrefillParams p) {
       const int slot = w * SPW + i;
       const int pos = cpos + slot;
       float xq[2] = {0.0f, 0.0f}, xk[2] = {0.0f, 0.0f}, xv[2] = {0.0f, 0.0f};
-      float gt = 0.0f, bt = 0.0f;
+      float gt[GPL] = {}, bt = 0.0f;
       if (pos >= pos0 && pos <= pos_last) {
         decode_raw(rq[i], xq);
         decode_raw(rk[i], xk);
         decode_raw(rv[i], xv);
-        float xa[1], xb[1];
+        float xa[GPL], xb[1];
         decode_raw(ra[i], xa);
         decode_raw(rb[i], xb);
         float iq = p.scale, ik = 1.0f;
@@ -170,14 +188,16 @@ void prefill_kernel(const PrefillParams p) {
         xq[1] *= iq;
         xk[0] *= ik;
         xk[1] *= ik;
-        gt = -rate * softplus_f(xa[0] + dtb);
+#pragma unroll
+        for (int e = 0; e < GPL; ++e) gt[e] = -rate * softplus_f(xa[e] + dtb[e]);
         bt = p.beta_prob ? xb[0] : sigmoid_f(xb[0]);
       }
       *reinterpret_cast<float2*>(&s_q[slot][2 * lane]) = make_float2(xq[0], xq[1]);
       *reinterpret_cast<float2*>(&s_k[slot][2 * lane]) = make_float2(xk[0], xk[1]);
       *reinterpret_cast<float2*>(&s_v[slot][2 * lane]) = make_float2(xv[0], xv[1]);
+      if constexpr (KDA) *reinterpret_cast<float2*>(&s_G[slot][2 * lane]) = make_float2(gt[0], gt[1]);
       if (lane == 0) {
-        s_g[slot] = gt;
+        if constexpr (!KDA) s_g[slot] = gt[0];
         s_b[slot] = bt;
       }
     }
@@ -242,9 +262,30 @@ void prefill_kernel(const PrefillParams p) {
     if (j < jlast) load_chunk(cpos + C);     // next chunk's inputs, in flight during this chunk
     __syncthreads();
 
-    // ---- gate prefix (every wave): inclusive scan of g over the 16 lanes of
-    //      each row (row_shr:n with bound_ctrl, so the first n lanes add 0)
-    float Gc = s_g[n16];                      // becomes G of column s = n16
+    if constexpr (KDA) {
+      // ---- per-channel gate prefix and the gated keys / queries (one thread
+      //      per channel); every exponent is <= 0 since g <= 0
+      if (tid < K) {
+        const int c = tid;
+        float G = 0.0f;
+#pragma unroll
+        for (int t = 0; t < C; ++t) {
+          G += s_G[t][c];
+          s_G[t][c] = G;
+          const float e = exp_hw(G);
+          s_kg[t][c] = s_k[t][c] * e;
+          s_qg[t][c] = s_q[t][c] * e;
+        }
+#pragma unroll
+        for (int t = 0; t < C; ++t) s_kd[t][c] = exp_hw(fminf(G - s_G[t][c], 0.0f)) * s_k[t][c];
+        s_eC[c] = exp_hw(G);
+      }
+      __syncthreads();
+    }
+
+    // ---- gate prefix (GDN, every wave): inclusive scan of g over the 16 lanes
+    //      of each row (row_shr:n with bound_ctrl, so the first n lanes add 0)
+    float Gc = KDA ? 0.0f : s_g[n16];         // becomes G of column s = n16
     Gc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(Gc), 0x111, 0xF, 0xF, true));
     Gc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(Gc), 0x112, 0xF, 0xF, true));
     Gc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(Gc), 0x114, 0xF, 0xF, true));
@@ -254,8 +295,29 @@ void prefill_kernel(const PrefillParams p) {
     for (int r = 0; r < 4; ++r) Gr[r] = __shfl(Gc, 4 * g4 + r);
     const float GC = __shfl(Gc, C - 1);       // G of the last slot
 
-    // ---- key interaction A' (wave 0) and output score P (wave 1), 16 x 16 over K
-    if (w < 2) {
+    // ---- key interaction A' and output score P, 16 x 16 over K
+    if constexpr (KDA) {
+      // per-channel decay: sum_c x_tc k_sc exp(G_tc - G_sc) does not factor into
+      // one product without overflow risk; one thread per (t, s) on the VALU
+      const int t = tid >> 4, s = tid & 15;
+      float a = 0.0f, pq = 0.0f;
+      if (s <= t) {
+#pragma unroll 4
+        for (int c = 0; c < K; c += 4) {
+          const float4 kt = *reinterpret_cast<const float4*>(&s_k[t][c]);
+          const float4 qt = *reinterpret_cast<const float4*>(&s_q[t][c]);
+          const float4 Gt = *reinterpret_cast<const float4*>(&s_G[t][c]);
+          const float4 ks = *reinterpret_cast<const float4*>(&s_k[s][c]);
+          const float4 Gs = *reinterpret_cast<const float4*>(&s_G[s][c]);
+          const float e0 = exp_hw(fminf(Gt.x - Gs.x, 0.0f)) * ks.x, e1 = exp_hw(fminf(Gt.y - Gs.y, 0.0f)) * ks.y;
+          const float e2 = exp_hw(fminf(Gt.z - Gs.z, 0.0f)) * ks.z, e3 = exp_hw(fminf(Gt.w - Gs.w, 0.0f)) * ks.w;
+          a = fmaf(kt.x, e0, fmaf(kt.y, e1, fmaf(kt.z, e2, fmaf(kt.w, e3, a))));
+          pq = fmaf(qt.x, e0, fmaf(qt.y, e1, fmaf(qt.z, e2, fmaf(qt.w, e3, pq))));
+        }
+      }
+      s_a[t][s] = (s < t) ? s_b[t] * a : 0.0f;
+      s_p[t][s] = (s <= t) ? pq : 0.0f;
+    } else if (w < 2) {
       const float(*left)[LDK] = (w == 0) ? s_k : s_q;
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -279,8 +341,9 @@ void prefill_kernel(const PrefillParams p) {
     }
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
-      const float4 kv = *reinterpret_cast<const float4*>(&s_k[n16][16 * ct + 4 * g4]);
-      const float4 qv = *reinterpret_cast<const float4*>(&s_q[n16][16 * ct + 4 * g4]);
+      // (KDA: the per-channel exp(G_t) is folded into the gated rows)
+      const float4 kv = *reinterpret_cast<const float4*>(KDA ? &s_kg[n16][16 * ct + 4 * g4] : &s_k[n16][16 * ct + 4 * g4]);
+      const float4 qv = *reinterpret_cast<const float4*>(KDA ? &s_qg[n16][16 * ct + 4 * g4] : &s_q[n16][16 * ct + 4 * g4]);
       const float kr[4] = {kv.x, kv.y, kv.z, kv.w};
       const float qr[4] = {qv.x, qv.y, qv.z, qv.w};
 #pragma unroll
@@ -311,9 +374,9 @@ void prefill_kernel(const PrefillParams p) {
 
     // ---- U = T diag(beta) (V - diag(exp G) K S0): R in accumulator layout
     //      (rows s = 4 g4 + r) is the B operand; A = T[n16][4 g4 + r] beta
-    float eG[4];
+    float eG[4];                    // GDN: exp(G_t) of rows t = 4 g4 + r (KDA: folded, 1)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) eG[r] = exp_hw(Gr[r]);
+    for (int r = 0; r < 4; ++r) eG[r] = KDA ? 1.0f : exp_hw(Gr[r]);
     f32x4 U[VT];
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt) {
@@ -330,7 +393,7 @@ void prefill_kernel(const PrefillParams p) {
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) O[vt][r] *= eG[r];
+      for (int r = 0; r < 4; ++r) O[vt][r] *= eG[r];   // (KDA: times 1)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float pa = s_p[n16][4 * g4 + r];
@@ -360,10 +423,12 @@ void prefill_kernel(const PrefillParams p) {
     for (int ct = 0; ct < 8; ++ct) {
       float ka[4];                  // A[ch = 16 ct + n16][s = 4 g4 + r]
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ka[r] = dk[r] * s_k[4 * g4 + r][16 * ct + n16];
+      for (int r = 0; r < 4; ++r) ka[r] = KDA ? s_kd[4 * g4 + r][16 * ct + n16] : dk[r] * s_k[4 * g4 + r][16 * ct + n16];
+      f32x4 dec = {eC, eC, eC, eC};   // decay of rows 16 ct + 4 g4 + r (KDA: per channel)
+      if constexpr (KDA) dec = *reinterpret_cast<const f32x4*>(&s_eC[16 * ct + 4 * g4]);
 #pragma unroll
       for (int vt = 0; vt < VT; ++vt) {
-        f32x4 acc = S[ct][vt] * eC;
+        f32x4 acc = S[ct][vt] * dec;
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc = mfma_16x16x4(ka[r], U[vt][r], acc);
         S[ct][vt] = acc;

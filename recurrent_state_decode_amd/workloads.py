@@ -227,8 +227,8 @@ def paged(kind, B, HK, HV, K, V, *, prefix_lengths=None, max_prefix=2048, page_s
         inp["cu_seqlens"] = lengths_to_cu(suffix_lengths)
     opts = dict(page_size=page_size, **options)
     wkind = ("kda" if kind == "kda" else "gdn") + ("_paged" if suffix_lengths is None else "_paged_varlen")
-    if chunked and wkind != "gdn_paged_varlen":
-        raise ValueError("the chunked prefill takes GDN suffixes on a paged pool")
+    if chunked and not wkind.endswith("_paged_varlen"):
+        raise ValueError("the chunked prefill takes suffixes on a paged pool")
     return Workload(wkind, name or wkind, B, HK, HV, K, V, io_dtype, out_dtype or io_dtype, state_layout,
                     num_pages, inp, opts, pool_seed=seed + 1, chunked=chunked)
 
@@ -282,6 +282,13 @@ def paged_gdn_prefill_b16_t1024(seed=1009, state_layout=V_FIRST, index_dtype=tor
                  name="paged_gdn_prefill_b16_t1024_hv32_k128_ps16", chunked=True)
 
 
+def paged_kda_prefill_b16_t1024(seed=1010, state_layout=V_FIRST, index_dtype=torch.int64):
+    """The chunked-prefill shape with KDA gating: 16 sequences x 1024 tokens, HK=HV=32, K=V=128, page 16."""
+    return paged("kda", 16, 32, 32, 128, 128, max_prefix=2048, page_size=16, share_frac=0.1,
+                 suffix_lengths=np.full(16, 1024), state_layout=state_layout, index_dtype=index_dtype, seed=seed,
+                 name="paged_kda_prefill_b16_t1024_hv32_k128_ps16", chunked=True)
+
+
 def int8h32_gdn_b512(seed=1008):
     """The B=512, 4-token pooled GDN workload with the int8_hadamard32 state codec instead of fp8 tiles."""
     return gdn_pooled(512, 16, 32, 128, 128, lengths=np.full(512, 4), num_slots=1024,
@@ -312,4 +319,5 @@ NAMED = {
     "paged_gdn_varlen_b256_t4": paged_gdn_varlen_b256_t4,
     "int8h32_gdn_b512": int8h32_gdn_b512,
     "paged_gdn_prefill_b16_t1024": paged_gdn_prefill_b16_t1024,
+    "paged_kda_prefill_b16_t1024": paged_kda_prefill_b16_t1024,
 }

@@ -100,6 +100,11 @@ def gpu_call(w, pool, d, out=None, **over):
     if w.kind == "gdn_paged_varlen":
         return rsd.gdn_decode_paged_varlen(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
                                            d["cu_seqlens"], *table, ps, pool, out, **common)
+    if w.kind == "kda_paged_varlen" and w.chunked:
+        o = {k2: v2 for k2, v2 in common.items() if k2 in ("scale", "use_qk_l2norm", "beta_mode", "state_layout",
+                                                            "out_dtype", "gate_mode")}
+        return rsd.kda_prefill_paged(d["q"], d["k"], d["v"], d["raw_gate"], d["beta_logits"], d["a_log"],
+                                     d["dt_bias"], d["cu_seqlens"], *table, ps, pool, out, **o)
     if w.kind == "kda_paged_varlen":
         return rsd.kda_decode_paged_varlen(d["q"], d["k"], d["v"], d["raw_gate"], d["beta_logits"], d["a_log"],
                                            d["dt_bias"], d["cu_seqlens"], *table, ps, pool, out, **common)

@@ -150,3 +150,8 @@ def test_prefill_argument_errors():
     nul[7] = None                                          # cu_seqlens is required
     assert call(a=nul) == bnd.GDN_ERR_INVALID
     assert call(HK=3, HV=4) == bnd.GDN_ERR_INVALID
+    kcall = lambda **kw: lib.kda_prefill_paged(*args, kw.get("page_size", 16), FAKE, FAKE, 2, 4, 1, 2, 128,
+                                               kw.get("V", 128), 10, 4, ctypes.byref(kw.get("opt", o)), None)
+    assert kcall(page_size=24) == bnd.GDN_ERR_UNSUPPORTED
+    assert kcall(V=64) == bnd.GDN_ERR_UNSUPPORTED
+    assert kcall(opt=bnd._options(index_dtype=bnd.GDN_I64, gate_mode=1)) == bnd.GDN_ERR_UNSUPPORTED

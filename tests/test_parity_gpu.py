@@ -384,16 +384,17 @@ def test_codec_gdn_b512_t4_sampled():
 
 # ---------------------------------------------------------------- chunked prefill on the paged pool
 
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
 @pytest.mark.parametrize("layout,idx,page_size", [("V_FIRST", torch.int64, 16), ("K_FIRST", torch.int32, 16),
                                                   ("V_FIRST", torch.int32, 32), ("K_FIRST", torch.int64, 64)])
-def test_prefill_small(layout, idx, page_size):
+def test_prefill_small(layout, idx, page_size, kind):
     """Suffixes of 0..70 tokens after prefixes that end on and off page and chunk boundaries."""
     suffix = np.array([1, 5, 16, 17, 0, 40, 33, 70, 2, 31, 15, 64])
     prefix = np.array([15, 16, 1, 31, 7, 32, 48, 5, 63, 64, 100, 17])
-    w = wl.paged("gdn", len(suffix), 2, 4, 128, 128, prefix_lengths=prefix, page_size=page_size, share_frac=0.3,
+    w = wl.paged(kind, len(suffix), 2, 4, 128, 128, prefix_lengths=prefix, page_size=page_size, share_frac=0.3,
                  suffix_lengths=suffix, state_layout=layout, index_dtype=idx, seed=60, chunked=True)
     rep, _, _ = P.run_and_check(w)
-    _report(f"prefill_small/{layout}/{idx}/ps{page_size}", rep)
+    _report(f"prefill_small/{kind}/{layout}/{idx}/ps{page_size}", rep)
 
 
 @pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
@@ -410,12 +411,13 @@ def test_prefill_options(io):
     _report(f"prefill_options/{io}", rep)
 
 
-def test_prefill_equals_token_path():
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_prefill_equals_token_path(kind):
     """The chunked call and the token-by-token call agree on outputs and every written page to float32
     rounding of two different summation orders: 2e-5 of |x| + rms (a hundredth of the oracle tolerance)."""
     import recurrent_state_decode_amd as rsd
     suffix = np.array([3, 64, 29, 100, 16, 1])
-    w = wl.paged("gdn", len(suffix), 2, 4, 128, 128, max_prefix=90, page_size=16, share_frac=0.2,
+    w = wl.paged(kind, len(suffix), 2, 4, 128, 128, max_prefix=90, page_size=16, share_frac=0.2,
                  suffix_lengths=suffix, state_layout="V_FIRST", out_dtype=torch.float32, seed=62, chunked=True)
     d = P.device_inputs(w)
     pool_a = wl.make_pool(w, "cuda")
@@ -435,3 +437,20 @@ def test_prefill_b16_t1024_sampled():
     w = wl.paged_gdn_prefill_b16_t1024()
     rep, _, _ = P.run_and_check(w, seqs=[0, 7, 15])
     _report(w.name, rep)
+
+
+def test_kda_prefill_b16_t1024_sampled():
+    w = wl.paged_kda_prefill_b16_t1024()
+    rep, _, _ = P.run_and_check(w, seqs=[3, 12])
+    _report(w.name, rep)
+
+
+def test_kda_prefill_strong_decay():
+    """Per-channel gates down to exp(-60) per token: pairwise decays underflow to 0 without overflow."""
+    suffix = np.array([40, 23])
+    w = wl.paged("kda", 2, 2, 2, 128, 128, max_prefix=40, page_size=16, share_frac=0.0, suffix_lengths=suffix,
+                 state_layout="V_FIRST", io_dtype=torch.float32, out_dtype=torch.float32, seed=63, chunked=True)
+    w.inputs["raw_gate"] = (w.inputs["raw_gate"] * 4).to(torch.float32)
+    w.inputs["a_log"] = torch.full_like(w.inputs["a_log"], float(np.log(16.0)))
+    rep, _, _ = P.run_and_check(w)
+    _report("kda_prefill_strong_decay", rep)
