@@ -33,11 +33,15 @@ PEAK_HBM_GBPS = 8000.0
 METRIC = "tokens/s & state-pool HBM GB/s (% peak), GDN decode B=256,HV=32,K=V=128"
 
 
-def source_hash():
-    """Hash of the sources the kernels are built from (ties a profile to a kernel version)."""
+def source_hash(chunked=False):
+    """Hash of the sources a kernel is built from (ties a profile to a kernel version): the decode
+    kernel's header, the host launch code and the C header; the chunked prefill adds its own header."""
     h = hashlib.sha256()
-    for rel in ("recurrent_state_decode_amd/csrc/decode_kernel.hpp", "recurrent_state_decode_amd/csrc/prefill_kernel.hpp",
-                "recurrent_state_decode_amd/csrc/gdn_decode.hip", "include/gdn_decode.h"):
+    files = ["recurrent_state_decode_amd/csrc/decode_kernel.hpp"]
+    if chunked:
+        files.append("recurrent_state_decode_amd/csrc/prefill_kernel.hpp")
+    files += ["recurrent_state_decode_amd/csrc/gdn_decode.hip", "include/gdn_decode.h"]
+    for rel in files:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -101,7 +105,7 @@ def traffic_path(workload_name):
     return os.path.join(ROOT, "profiles", f"traffic_{workload_name}.txt")
 
 
-def load_traffic(workload_name):
+def load_traffic(workload_name, chunked=False):
     """Per-launch HBM bytes from a committed rocprofv3 counter summary, if it matches these sources."""
     path = traffic_path(workload_name)
     if not os.path.exists(path):
@@ -112,7 +116,7 @@ def load_traffic(workload_name):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 rec[k.strip()] = v.strip()
-    if rec.get("source_hash") != source_hash():
+    if rec.get("source_hash") != source_hash(chunked):
         return None
     return int(rec["bytes_per_launch"])
 
@@ -325,7 +329,7 @@ def main():
     tokens = w.T
     state_b, io_b = algorithmic_bytes(w)
     achieved = (state_b + io_b) / (mean_ms * 1e-3) / 1e9
-    traffic = load_traffic(w.name)
+    traffic = load_traffic(w.name, w.chunked)
     res = {
         "metric": METRIC,
         "value": round(tokens / (mean_ms * 1e-3), 1),
@@ -350,7 +354,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": state_b + io_b,
-                     "kernel": kernel_name(w), "source_hash": source_hash()},
+                     "kernel": kernel_name(w), "source_hash": source_hash(w.chunked)},
     }
     if w.chunked:
         fl = chunked_flops(w)
