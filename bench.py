@@ -207,13 +207,15 @@ def cpu_baseline(w, pool, budget_s):
     from tests import parity as P
 
     seqs_all = list(range(w.B))
-    reads, _ = P.rows_for(w)
-    # pool rows are read back before timing; only the oracle arithmetic is timed
+    # pool rows are read back before timing; only the oracle arithmetic is timed.
+    # Sequences are taken in order, in batches of 8; a small workload is passed
+    # over again until the time budget is spent.
     with threadpool_limits(limits=1):
-        done, t_used, toks = 0, 0.0, 0
+        done, t_used, toks, passes = 0, 0.0, 0, 0
         batch = 8
-        while done < len(seqs_all) and t_used < budget_s:
-            seqs = seqs_all[done:done + batch]
+        while t_used < budget_s:
+            start = done % len(seqs_all)
+            seqs = seqs_all[start:start + batch]
             r, _ = P.rows_for(w, seqs)
             rows = P.gather_rows(pool, r)
             t0 = time.perf_counter()
@@ -221,9 +223,14 @@ def cpu_baseline(w, pool, budget_s):
             t_used += time.perf_counter() - t0
             toks += len(P.token_rows(w, seqs))
             done += len(seqs)
+            if done % len(seqs_all) == 0:
+                passes += 1
+    if passes:
+        sample = f"{done} sequences ({toks} tokens): {done / len(seqs_all):.1f} passes over all {w.B} sequences"
+    else:
+        sample = f"first {done} of {w.B} sequences ({toks} tokens)"
     return {"value": toks / t_used, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {done} of {w.B} sequences ({toks} tokens) of {w.name}, float64 NumPy, one thread",
-            "seconds": round(t_used, 3)}
+            "sample": f"{sample} of {w.name}, float64 NumPy, one thread", "seconds": round(t_used, 3)}
 
 
 def main():
