@@ -97,6 +97,42 @@ def chunked_flops(w):
     return chunks * w.HV * (w.V // 128) * per
 
 
+def gpu_clocks():
+    """Current shader / memory clocks as rocm-smi reports them (None where it is unavailable)."""
+    import re
+    import subprocess
+    try:
+        txt = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
+    except Exception:
+        return None
+    out = {}
+    for key in ("sclk", "mclk", "fclk"):
+        m = re.search(key + r"[^(\n]*\((\d+)\s*Mhz\)", txt, re.IGNORECASE)
+        if m:
+            out[key + "_mhz"] = int(m.group(1))
+    return out or None
+
+
+def copy_bandwidth(torch, dev, flush):
+    """Best of three plain 1 GiB -> 1 GiB device copies, in GB/s (read + write bytes)."""
+    n = 256 * 1024 * 1024
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    best = None
+    for _ in range(3):
+        if flush is not None:
+            flush.fill_(0.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    return 2 * n * 4 / (best * 1e-3) / 1e9
+
+
 def kernel_name(w):
     return "gdn::prefill_kernel" if w.chunked else "gdn::decode_kernel"
 
@@ -363,6 +399,13 @@ def main():
                      "traffic": traffic, "algorithmic_bytes_per_launch": state_b + io_b,
                      "kernel": kernel_name(w), "source_hash": source_hash(w.chunked)},
     }
+    try:
+        cbw = copy_bandwidth(torch, dev, flush)
+        res["device_copy_gbps"] = round(cbw, 1)        # torch's 1 GiB device-to-device copy, best of 3
+        res["frac_of_device_copy"] = round(achieved / cbw, 4)
+    except RuntimeError:
+        pass
+    res["gpu_clocks_after_run"] = gpu_clocks()
     if w.chunked:
         fl = chunked_flops(w)
         tf = fl / (mean_ms * 1e-3) / 1e12
