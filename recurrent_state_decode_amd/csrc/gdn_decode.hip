@@ -423,7 +423,8 @@ int prefill_call(bool kda, const void* q, const void* k, const void* v, const vo
   p.page_size = page_size;
   p.pool = state_pool; p.out = out;
   p.B = B; p.HK = HK; p.HV = HV; p.V = V;
-  p.nvb = V / 128;
+  constexpr int VT = 2, NW = 4;     // two 16-column value tiles per wave, 4 waves: 128 columns per workgroup
+  p.nvb = V / gdn::kPrefillVBlk<VT, NW>;
   p.gqa = HV / HK;
   p.scale = opt->scale > 0.0f ? opt->scale : 1.0f / std::sqrt(static_cast<float>(K));
   p.l2norm = opt->use_qk_l2norm ? 1 : 0;
@@ -433,12 +434,11 @@ int prefill_call(bool kda, const void* q, const void* k, const void* v, const vo
   const int64_t units = static_cast<int64_t>(B) * HV * p.nvb;
   if (units > 0x7fffffffLL) return fail(GDN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)units);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  constexpr int VT = 2;             // two 16-column value tiles per wave: 4 waves per workgroup
-  const dim3 grid(static_cast<uint32_t>(units)), block(gdn::kPrefillThreads<VT>);
+  const dim3 grid(static_cast<uint32_t>(units)), block(NW * 64);
   auto go = [&](auto kda_c, auto vf_c, auto io_c) {
     constexpr bool KDA = decltype(kda_c)::value, VF = decltype(vf_c)::value;
     using TIn = typename decltype(io_c)::type;
-    hipLaunchKernelGGL((gdn::prefill_kernel<VT, KDA, VF, TIn>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((gdn::prefill_kernel<VT, NW, KDA, VF, TIn>), grid, block, 0, s, p);
   };
   using F = std::false_type;
   using Tr = std::true_type;

@@ -65,7 +65,7 @@ struct PrefillParams {
   float* pool;
   void* out;
   int32_t B, HK, HV, V;
-  int32_t nvb;             // V / 128
+  int32_t nvb;             // V / VBLK
   int32_t gqa;
   float scale;
   int32_t l2norm, out_bf16, beta_prob, idx64;
@@ -77,15 +77,19 @@ __device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// VT value tiles (16 columns each) per wave, 8 / VT waves per workgroup.
-template <int VT>
-constexpr int kPrefillThreads = 512 / VT;
+// VT value tiles (16 columns each) per wave, NW waves per workgroup: a
+// workgroup covers VBLK = 16 VT NW value columns.
+template <int VT, int NW>
+constexpr int kPrefillVBlk = 16 * VT * NW;
 
-template <int VT, bool KDA, bool VF, typename TIn>
-__global__ __launch_bounds__(kPrefillThreads<VT>) __attribute__((amdgpu_waves_per_eu(8 / (2 * VT), 8 / (2 * VT))))
+template <int VT, int NW, bool KDA, bool VF, typename TIn>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(8 / (2 * VT), 8 / (2 * VT))))
 void prefill_kernel(const PrefillParams p) {
-  constexpr int K = 128, C = kChunk, NW = 8 / VT, SPW = C / NW;
-  static_assert(!KDA || NW * 64 == C * C, "KDA: one thread per (t, s) pair of the chunk");
+  constexpr int K = 128, C = kChunk, SPW = C / NW;
+  constexpr int VBLK = kPrefillVBlk<VT, NW>;
+  constexpr int VPL = VBLK / 64;   // staged v elements per lane
+  constexpr int PPT = C * C / (NW * 64);   // KDA: (t, s) pairs per thread
+  static_assert(VBLK % 64 == 0 && VPL <= 2 && C % NW == 0 && (C * C) % (NW * 64) == 0, "prefill shape");
   constexpr int LDK = K + 4;       // padded LDS rows
   constexpr int LDC = C + 1;
 
@@ -138,11 +142,12 @@ void prefill_kernel(const PrefillParams p) {
   const int64_t wrow = load_index(p.page_indices, pg_end - 1, p.idx64);
 
   const int64_t tile_elems = static_cast<int64_t>(K) * p.V;
-  const int vcol = vb * 128 + 16 * VT * w;   // first value column of this wave
+  const int vcol = vb * VBLK + 16 * VT * w;   // first value column of this wave
 
   // ---- raw inputs of one chunk's slots 4 w .. 4 w + 3 (issued a chunk ahead)
   constexpr int GPL = KDA ? 2 : 1;  // gate elements per lane
-  Raw<TIn, 2> rq[SPW], rk[SPW], rv[SPW];
+  Raw<TIn, 2> rq[SPW], rk[SPW];
+  Raw<TIn, VPL> rv[SPW];
   Raw<TIn, GPL> ra[SPW];
   Raw<TIn, 1> rb[SPW];
   auto load_chunk = [&](int cpos) {
@@ -153,7 +158,7 @@ void prefill_kernel(const PrefillParams p) {
         const int64_t t = t0 + (pos - pos0);
         load_raw_n<2>(gq, (t * p.HK + hk) * K + 2 * lane, rq[i]);
         load_raw_n<2>(gk, (t * p.HK + hk) * K + 2 * lane, rk[i]);
-        load_raw_n<2>(gv, (t * p.HV + h) * p.V + vb * 128 + 2 * lane, rv[i]);
+        load_raw_n<VPL>(gv, (t * p.HV + h) * p.V + vb * VBLK + VPL * lane, rv[i]);
         if constexpr (KDA) load_raw_n<2>(gg, (t * p.HV + h) * K + 2 * lane, ra[i]);
         else load_raw_n<1>(gg, t * p.HV + h, ra[i]);
         load_raw_n<1>(gb, t * p.HV + h, rb[i]);
@@ -170,7 +175,7 @@ void prefill_kernel(const PrefillParams p) {
     for (int i = 0; i < SPW; ++i) {
       const int slot = w * SPW + i;
       const int pos = cpos + slot;
-      float xq[2] = {0.0f, 0.0f}, xk[2] = {0.0f, 0.0f}, xv[2] = {0.0f, 0.0f};
+      float xq[2] = {0.0f, 0.0f}, xk[2] = {0.0f, 0.0f}, xv[VPL] = {};
       float gt[GPL] = {}, bt = 0.0f;
       if (pos >= pos0 && pos <= pos_last) {
         decode_raw(rq[i], xq);
@@ -194,7 +199,8 @@ void prefill_kernel(const PrefillParams p) {
       }
       *reinterpret_cast<float2*>(&s_q[slot][2 * lane]) = make_float2(xq[0], xq[1]);
       *reinterpret_cast<float2*>(&s_k[slot][2 * lane]) = make_float2(xk[0], xk[1]);
-      *reinterpret_cast<float2*>(&s_v[slot][2 * lane]) = make_float2(xv[0], xv[1]);
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) s_v[slot][VPL * lane + e] = xv[e];
       if constexpr (KDA) *reinterpret_cast<float2*>(&s_G[slot][2 * lane]) = make_float2(gt[0], gt[1]);
       if (lane == 0) {
         if constexpr (!KDA) s_g[slot] = gt[0];
@@ -298,25 +304,29 @@ void prefill_kernel(const PrefillParams p) {
     // ---- key interaction A' and output score P, 16 x 16 over K
     if constexpr (KDA) {
       // per-channel decay: sum_c x_tc k_sc exp(G_tc - G_sc) does not factor into
-      // one product without overflow risk; one thread per (t, s) on the VALU
-      const int t = tid >> 4, s = tid & 15;
-      float a = 0.0f, pq = 0.0f;
-      if (s <= t) {
+      // one product without overflow risk; pairs (t, s) on the VALU, PPT per thread
+#pragma unroll
+      for (int pp = 0; pp < PPT; ++pp) {
+        const int pi = tid + pp * NW * 64;
+        const int t = pi >> 4, s = pi & 15;
+        float a = 0.0f, pq = 0.0f;
+        if (s <= t) {
 #pragma unroll 4
-        for (int c = 0; c < K; c += 4) {
-          const float4 kt = *reinterpret_cast<const float4*>(&s_k[t][c]);
-          const float4 qt = *reinterpret_cast<const float4*>(&s_q[t][c]);
-          const float4 Gt = *reinterpret_cast<const float4*>(&s_G[t][c]);
-          const float4 ks = *reinterpret_cast<const float4*>(&s_k[s][c]);
-          const float4 Gs = *reinterpret_cast<const float4*>(&s_G[s][c]);
-          const float e0 = exp_hw(fminf(Gt.x - Gs.x, 0.0f)) * ks.x, e1 = exp_hw(fminf(Gt.y - Gs.y, 0.0f)) * ks.y;
-          const float e2 = exp_hw(fminf(Gt.z - Gs.z, 0.0f)) * ks.z, e3 = exp_hw(fminf(Gt.w - Gs.w, 0.0f)) * ks.w;
-          a = fmaf(kt.x, e0, fmaf(kt.y, e1, fmaf(kt.z, e2, fmaf(kt.w, e3, a))));
-          pq = fmaf(qt.x, e0, fmaf(qt.y, e1, fmaf(qt.z, e2, fmaf(qt.w, e3, pq))));
+          for (int c = 0; c < K; c += 4) {
+            const float4 kt = *reinterpret_cast<const float4*>(&s_k[t][c]);
+            const float4 qt = *reinterpret_cast<const float4*>(&s_q[t][c]);
+            const float4 Gt = *reinterpret_cast<const float4*>(&s_G[t][c]);
+            const float4 ks = *reinterpret_cast<const float4*>(&s_k[s][c]);
+            const float4 Gs = *reinterpret_cast<const float4*>(&s_G[s][c]);
+            const float e0 = exp_hw(fminf(Gt.x - Gs.x, 0.0f)) * ks.x, e1 = exp_hw(fminf(Gt.y - Gs.y, 0.0f)) * ks.y;
+            const float e2 = exp_hw(fminf(Gt.z - Gs.z, 0.0f)) * ks.z, e3 = exp_hw(fminf(Gt.w - Gs.w, 0.0f)) * ks.w;
+            a = fmaf(kt.x, e0, fmaf(kt.y, e1, fmaf(kt.z, e2, fmaf(kt.w, e3, a))));
+            pq = fmaf(qt.x, e0, fmaf(qt.y, e1, fmaf(qt.z, e2, fmaf(qt.w, e3, pq))));
+          }
         }
+        s_a[t][s] = (s < t) ? s_b[t] * a : 0.0f;
+        s_p[t][s] = (s <= t) ? pq : 0.0f;
       }
-      s_a[t][s] = (s < t) ? s_b[t] * a : 0.0f;
-      s_p[t][s] = (s <= t) ? pq : 0.0f;
     } else if (w < 2) {
       const float(*left)[LDK] = (w == 0) ? s_k : s_q;
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
