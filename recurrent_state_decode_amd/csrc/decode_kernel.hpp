@@ -44,8 +44,8 @@
 // turn.  The kernel renumbers them so that runs of xcd_group consecutive work
 // units (neighbouring V-blocks and heads of one sequence) execute on the same
 // XCD: they share that XCD's L2 for q/k/v and stream one contiguous slice of
-// the work instead of eight interleaved ones.  The state tile is read with
-// non-temporal loads: it is touched once per call.
+// the work instead of eight interleaved ones.  The state tile is read and
+// written with non-temporal loads and stores: it is touched once per call.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -886,19 +886,20 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
     }
   };
 
-  // write the true state (scale * registers) to a pool row
+  // write the true state (scale * registers) to a pool row, with
+  // non-temporal stores like the loads: the row is not read again by this call
   auto store_tile = [&](float* row_base) {
     if constexpr (!HAD) {
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int f = 0; f < EV / 4; ++f) {
-          float4 x;
+          f32x4 x;
           x.x = S[s][4 * f + 0] * cs[KDA ? slot(s, 4 * f + 0) : 0];
           x.y = S[s][4 * f + 1] * cs[KDA ? slot(s, 4 * f + 1) : 0];
           x.z = S[s][4 * f + 2] * cs[KDA ? slot(s, 4 * f + 2) : 0];
           x.w = S[s][4 * f + 3] * cs[KDA ? slot(s, 4 * f + 3) : 0];
-          *reinterpret_cast<float4*>(row_base + row_off(s, f)) = x;
+          __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(row_base + row_off(s, f)));
         }
     } else {
       // back to the original value basis: S = c R H / 32
@@ -917,7 +918,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
       if constexpr (!TRANS) {
 #pragma unroll
         for (int s = 0; s < NS; ++s)
-          *reinterpret_cast<float4*>(row_base + row_off(s, 0)) = make_float4(X[s][0], X[s][1], X[s][2], X[s][3]);
+          __builtin_nontemporal_store(f32x4{X[s][0], X[s][1], X[s][2], X[s][3]},
+                                      reinterpret_cast<f32x4*>(row_base + row_off(s, 0)));
       } else {
         __syncthreads();           // earlier readers of s_t are done
 #pragma unroll
@@ -930,8 +932,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
 #pragma unroll
           for (int f = 0; f < 2; ++f) {
             const int a = trans_lds(s, f);
-            *reinterpret_cast<float4*>(row_base + trans_off(s, f)) =
-                make_float4(s_t[a + 0], s_t[a + 1], s_t[a + 2], s_t[a + 3]);
+            __builtin_nontemporal_store(f32x4{s_t[a + 0], s_t[a + 1], s_t[a + 2], s_t[a + 3]},
+                                        reinterpret_cast<f32x4*>(row_base + trans_off(s, f)));
           }
       }
     }
