@@ -41,6 +41,9 @@ enum class Kind { GdnPooled, GdnPaged, KdaPooled, KdaPaged, GdnPagedVar, KdaPage
 //                            GDN: VB=8,  NT=128 (4 KiB of state per workgroup)
 //                            KDA: VB=16, NT=128 (its per-channel gates cost
 //                            more per V-block; measured 12 % faster than VB=8)
+//   K=128, K_FIRST, no QDQ, T <= 1.5 B:
+//                            VB=32, NT=256 (128-byte row segments; 5-7 %
+//                            faster than VB=64, VB=16 is 25 % slower)
 //   K=128, otherwise:        VB=64, NT=256 (fp8 tiles need block_v == VB; the
 //                            int8_hadamard32 codec is compiled for this shape)
 //   K=16:                    VB=16, NT=64
@@ -52,7 +55,8 @@ struct Shape {
 bool is_kda(Kind k) { return k == Kind::KdaPooled || k == Kind::KdaPaged || k == Kind::KdaPagedVar; }
 
 Shape shape_for(int K, bool vfirst, bool qdq, int64_t T, int64_t B, bool kda) {
-  if (K == 128) return (vfirst && !qdq && 2 * T <= 3 * B) ? Shape{kda ? 16 : 8, 128} : Shape{64, 256};
+  if (K == 128 && !qdq && 2 * T <= 3 * B) return vfirst ? Shape{kda ? 16 : 8, 128} : Shape{32, 256};
+  if (K == 128) return Shape{64, 256};
   if (K == 16) return Shape{16, 64};
   return Shape{0, 0};
 }
@@ -126,14 +130,14 @@ bool head_supported(int K, int V) {
   return vb > 0 && V % vb == 0;
 }
 
-// Small V_FIRST workgroups (K=128, no QDQ): one instantiation per kind and io type.
-template <int VB, int NT>
-hipError_t launch_small_vfirst(Kind kind, const gdn::Params& p, int64_t units, Sel sel, hipStream_t s) {
+// Single-token workgroups (K=128, no QDQ, one layout): one instantiation per kind and io type.
+template <bool VF, int VB, int NT>
+hipError_t launch_single(Kind kind, const gdn::Params& p, int64_t units, Sel sel, hipStream_t s) {
   auto go = [&](auto kda, auto addr) -> hipError_t {
     constexpr bool KDA = decltype(kda)::value;
     constexpr int ADDR = decltype(addr)::value;
-    return sel.bf16 ? launch_one<128, VB, NT, true, KDA, gdn::kQdqNone, ADDR, gdn::bf16_t>(p, units, s)
-                    : launch_one<128, VB, NT, true, KDA, gdn::kQdqNone, ADDR, float>(p, units, s);
+    return sel.bf16 ? launch_one<128, VB, NT, VF, KDA, gdn::kQdqNone, ADDR, gdn::bf16_t>(p, units, s)
+                    : launch_one<128, VB, NT, VF, KDA, gdn::kQdqNone, ADDR, float>(p, units, s);
   };
   using F = std::false_type;
   using Tr = std::true_type;
@@ -246,8 +250,9 @@ int run(Kind kind, const gdn::Params& p, int K, int32_t T, const gdn_options* o,
     case 16: err = launch_kind<16, 16, 64>(kind, p, units, sel, s); break;
     case 128:
       switch (shape_for(K, sel.vfirst, sel.qdq != gdn::kQdqNone, T, p.B, is_kda(kind)).VB) {
-        case 8: err = launch_small_vfirst<8, 128>(kind, p, units, sel, s); break;
-        case 16: err = launch_small_vfirst<16, 128>(kind, p, units, sel, s); break;
+        case 8: err = launch_single<true, 8, 128>(kind, p, units, sel, s); break;
+        case 16: err = launch_single<true, 16, 128>(kind, p, units, sel, s); break;
+        case 32: err = launch_single<false, 32, 256>(kind, p, units, sel, s); break;
         default: err = launch_kind<128, 64, 256>(kind, p, units, sel, s);
       }
       break;

@@ -244,6 +244,21 @@ def test_single_token_vfirst_no_cu_seqlens():
     _report("narrow/no_cu", rep)
 
 
+@pytest.mark.parametrize("layout", ["V_FIRST", "K_FIRST"])
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("io", [torch.bfloat16, torch.float32])
+def test_single_token_shapes_v192(layout, kind, io):
+    # one token per sequence selects the narrow single-token workgroups of each layout and
+    # kind; V = 192 is 24, 12 and 6 of their V-blocks and 3 of the general 64-column block
+    if kind == "gdn":
+        w = wl.gdn_pooled(20, 2, 4, 128, 192, lengths=None, num_slots=23, state_layout=layout, io_dtype=io, seed=49)
+    else:
+        w = wl.kda_pooled(20, 4, 4, 128, 192, lengths=[1] * 20, num_slots=23, state_layout=layout, io_dtype=io,
+                          seed=49)
+    rep, _, _ = P.run_and_check(w)
+    _report(f"single/{kind}/{layout}/{io}", rep)
+
+
 # ---------------------------------------------------------------- paged KDA, paged suffixes, precomputed slots
 
 @pytest.mark.parametrize("layout", ["V_FIRST", "K_FIRST"])
