@@ -44,6 +44,10 @@ enum class Kind { GdnPooled, GdnPaged, KdaPooled, KdaPaged, GdnPagedVar, KdaPage
 //   K=128, K_FIRST, no QDQ, T <= 1.5 B:
 //                            VB=32, NT=256 (128-byte row segments; 5-7 %
 //                            faster than VB=64, VB=16 is 25 % slower)
+//   K=128, V_FIRST, GDN, no QDQ, longer suffixes:
+//                            VB=32, NT=256 (5-6 % faster than VB=64 on 4-token
+//                            suffixes; on a K_FIRST pool it is 5 % slower,
+//                            and KDA's per-channel gates favour VB=64)
 //   K=128, otherwise:        VB=64, NT=256 (fp8 tiles need block_v == VB; the
 //                            int8_hadamard32 codec is compiled for this shape)
 //   K=16:                    VB=16, NT=64
@@ -56,6 +60,7 @@ bool is_kda(Kind k) { return k == Kind::KdaPooled || k == Kind::KdaPaged || k ==
 
 Shape shape_for(int K, bool vfirst, bool qdq, int64_t T, int64_t B, bool kda) {
   if (K == 128 && !qdq && 2 * T <= 3 * B) return vfirst ? Shape{kda ? 16 : 8, 128} : Shape{32, 256};
+  if (K == 128 && !qdq && !kda && vfirst) return Shape{32, 256};
   if (K == 128) return Shape{64, 256};
   if (K == 16) return Shape{16, 64};
   return Shape{0, 0};
@@ -130,9 +135,9 @@ bool head_supported(int K, int V) {
   return vb > 0 && V % vb == 0;
 }
 
-// Single-token workgroups (K=128, no QDQ, one layout): one instantiation per kind and io type.
+// Shapes used without QDQ only (K=128, one layout): one instantiation per kind and io type.
 template <bool VF, int VB, int NT>
-hipError_t launch_single(Kind kind, const gdn::Params& p, int64_t units, Sel sel, hipStream_t s) {
+hipError_t launch_noqdq(Kind kind, const gdn::Params& p, int64_t units, Sel sel, hipStream_t s) {
   auto go = [&](auto kda, auto addr) -> hipError_t {
     constexpr bool KDA = decltype(kda)::value;
     constexpr int ADDR = decltype(addr)::value;
@@ -250,9 +255,12 @@ int run(Kind kind, const gdn::Params& p, int K, int32_t T, const gdn_options* o,
     case 16: err = launch_kind<16, 16, 64>(kind, p, units, sel, s); break;
     case 128:
       switch (shape_for(K, sel.vfirst, sel.qdq != gdn::kQdqNone, T, p.B, is_kda(kind)).VB) {
-        case 8: err = launch_single<true, 8, 128>(kind, p, units, sel, s); break;
-        case 16: err = launch_single<true, 16, 128>(kind, p, units, sel, s); break;
-        case 32: err = launch_single<false, 32, 256>(kind, p, units, sel, s); break;
+        case 8: err = launch_noqdq<true, 8, 128>(kind, p, units, sel, s); break;
+        case 16: err = launch_noqdq<true, 16, 128>(kind, p, units, sel, s); break;
+        case 32:
+          err = sel.vfirst ? launch_noqdq<true, 32, 256>(kind, p, units, sel, s)
+                           : launch_noqdq<false, 32, 256>(kind, p, units, sel, s);
+          break;
         default: err = launch_kind<128, 64, 256>(kind, p, units, sel, s);
       }
       break;
