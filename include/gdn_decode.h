@@ -43,7 +43,9 @@
  *   leave these unchecked on the device too): index values inside the pool,
  *   distinct state_indices, distinct write pages, a write page that another
  *   sequence of the same call reads, non-decreasing cu_seqlens, and
- *   last_page_len == 1 with fewer than two pages.
+ *   last_page_len == 1 with fewer than two pages.  The gdn_check_* calls
+ *   check them on host copies, and a GDN_DEVICE_CHECKS build checks them in
+ *   every call (see gdn_check_pooled below).
  */
 #ifndef GDN_DECODE_H
 #define GDN_DECODE_H
@@ -62,7 +64,9 @@ enum gdn_status {
   GDN_ERR_INVALID = 1,      /* null required pointer, dimension <= 0, HV % HK != 0, bad enum */
   GDN_ERR_SHAPE = 2,        /* extents disagree (e.g. T != B without cu_seqlens) */
   GDN_ERR_UNSUPPORTED = 3,  /* valid request with no compiled kernel (head dims, block_v, gate_mode) */
-  GDN_ERR_HIP = 4           /* the HIP launch reported an error */
+  GDN_ERR_HIP = 4,          /* the HIP launch reported an error */
+  GDN_ERR_PRECONDITION = 5  /* an index precondition does not hold: gdn_check_* calls, and every
+                               call of a library built with GDN_DEVICE_CHECKS */
 };
 
 /* Element types of the I/O tensors and of the page table. */
@@ -302,6 +306,47 @@ const char* gdn_status_string(int status);
 /* Message of the calling thread's last failed call ("" if none).  The
  * pointer stays valid until the thread's next call into the library. */
 const char* gdn_last_error(void);
+
+/*
+ * Host-side checks of the index preconditions the kernels do not check (the
+ * "Not checked" list above; flashinfer.gdn_paged,
+ * gated_delta_rule_decode_paged, slots, and max.nn.state_space.kda_decode,
+ * Raises, leave them to debug builds).  Every pointer here is HOST memory
+ * holding a copy of the arrays a call would receive; nothing touches the
+ * GPU.  Returns GDN_OK, GDN_ERR_PRECONDITION with gdn_last_error() naming
+ * the first violation and the sequence, or GDN_ERR_INVALID for a NULL
+ * pointer or a non-positive size.
+ *
+ * gdn_check_pooled: cu_seqlens (NULL: T == B) has cu[0] == 0, never
+ *   decreases and ends at T; the slot of every non-empty suffix is in
+ *   [0, num_slots) and no two non-empty suffixes share one.
+ * gdn_check_paged (single-token calls): page_indptr[0] >= 0, every sequence
+ *   has a page, page_indptr[B] <= nnz, last_page_len in [1, page_size]
+ *   (page_size 0: >= 1), a sequence with last_page_len == 1 has a previous
+ *   page, read and write pages are in [0, num_pages), no two sequences write
+ *   one page, no sequence writes a page another reads, and `slots` (NULL or
+ *   [B][2] int64) equals the (read, write) rows of the table.
+ * gdn_check_paged_varlen (paged varlen decode and prefill calls): the table
+ *   and cu_seqlens as above, last_page_len <= page_size, a token before
+ *   every non-empty suffix, the page read and every page written in range,
+ *   and no page written by one sequence is read or written by another.
+ *
+ * A library compiled with GDN_DEVICE_CHECKS (libgdn_decode_checked.so) runs
+ * the same checks in every entry point on host copies of its index arrays
+ * (synchronising `stream` first) and returns GDN_ERR_PRECONDITION without
+ * launching anything when one fails; gdn_paged_decode_slots, which has no
+ * nnz or num_pages, checks the table's structure only.  gdn_checked_build()
+ * returns 1 in such a build and 0 otherwise.
+ */
+int gdn_check_pooled(const int32_t* cu_seqlens, const int32_t* state_indices, int32_t B, int32_t T,
+                     int64_t num_slots);
+int gdn_check_paged(const void* page_indices, const void* page_indptr, const void* last_page_len,
+                    int32_t index_dtype, const int64_t* slots, int32_t B, int32_t page_size,
+                    int64_t num_pages, int64_t nnz);
+int gdn_check_paged_varlen(const int32_t* cu_seqlens, const void* page_indices,
+                           const void* page_indptr, const void* last_page_len, int32_t index_dtype,
+                           int32_t B, int32_t T, int32_t page_size, int64_t num_pages, int64_t nnz);
+int gdn_checked_build(void);
 
 /* Head dims with a compiled kernel: writes up to `cap` (K, VB) pairs as
  * 2*n ints into `pairs` (NULL allowed) and returns the number of pairs

@@ -6,8 +6,13 @@ thin Python binding plus the seeded workload generators used by the tests
 and the bench.  PyTorch only provides device memory and streams.
 """
 from ._binding import (  # noqa: F401
+    CHECKED_LIB_PATH,
     GdnError,
     LIB_PATH,
+    check_paged,
+    check_paged_varlen,
+    check_pooled,
+    checked_library,
     gdn_decode_paged,
     gdn_decode_paged_varlen,
     gdn_decode_pooled,

@@ -6,6 +6,7 @@ current torch stream of the tensors' device.  Every step of the decode runs
 in the library's HIP kernels; there is no fallback.  If the library is not
 built, every call raises.
 """
+import contextlib
 import ctypes
 import os
 import threading
@@ -15,8 +16,9 @@ import torch
 from . import build as _build
 
 LIB_PATH = _build.LIB
+CHECKED_LIB_PATH = _build.LIB_CHECKED
 
-GDN_OK, GDN_ERR_INVALID, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = range(5)
+GDN_OK, GDN_ERR_INVALID, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP, GDN_ERR_PRECONDITION = range(6)
 GDN_F32, GDN_BF16, GDN_I32, GDN_I64 = range(4)
 _LAYOUT = {"K_FIRST": 0, "V_FIRST": 1}
 _BETA = {"logits": 0, "probability": 1}
@@ -72,6 +74,10 @@ _SIGNATURES = {
     "gdn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "gdn_last_error": (ctypes.c_char_p, []),
     "gdn_supported_head_dims": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int32), ctypes.c_int]),
+    "gdn_check_pooled": (ctypes.c_int, [_P, _P, _I32, _I32, _I64]),
+    "gdn_check_paged": (ctypes.c_int, [_P, _P, _P, _I32, _P, _I32, _I32, _I64, _I64]),
+    "gdn_check_paged_varlen": (ctypes.c_int, [_P] * 4 + [_I32] * 4 + [_I64, _I64]),
+    "gdn_checked_build": (ctypes.c_int, []),
 }
 
 _lib = None
@@ -96,6 +102,29 @@ def load_library(path=None):
         if path is None:
             _lib = lib
         return lib
+
+
+_checked = None
+
+
+@contextlib.contextmanager
+def checked_library():
+    """Route this module's calls, inside the ``with`` block, to libgdn_decode_checked.so.
+
+    That build validates every call's index arrays on the host before it
+    launches anything (and synchronises the stream to copy them), so a bad
+    table becomes a GdnError with status GDN_ERR_PRECONDITION.  Not
+    thread-safe against concurrent calls that expect the release library.
+    """
+    global _lib, _checked
+    release = load_library()
+    if _checked is None:
+        _checked = load_library(CHECKED_LIB_PATH)
+    _lib = _checked
+    try:
+        yield _checked
+    finally:
+        _lib = release
 
 
 def supported_head_dims():
@@ -341,6 +370,73 @@ def gdn_paged_decode_slots(page_indices, page_indptr, last_page_len, slots=None,
     if st != GDN_OK:
         _raise(lib, st)
     return slots
+
+
+def _host_index(name, t, dtypes):
+    """Contiguous CPU copy of an index array for the host-side checks (marshalling only)."""
+    if t is None:
+        return None
+    t = torch.as_tensor(t).detach().to("cpu").contiguous()
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return t
+
+
+def check_pooled(state_indices, num_slots, cu_seqlens=None, T=None):
+    """Host-side preconditions of a pooled call (gdn_check_pooled); raises GdnError if one fails.
+
+    T defaults to B without cu_seqlens and to cu_seqlens[-1] with it."""
+    lib = load_library()
+    si = _host_index("state_indices", state_indices, (torch.int32,))
+    cu = _host_index("cu_seqlens", cu_seqlens, (torch.int32,))
+    B = si.numel()
+    if cu is not None and cu.numel() != B + 1:
+        raise ValueError("cu_seqlens must have B+1 entries")
+    if T is None:
+        T = B if cu is None else int(cu[-1])
+    st = lib.gdn_check_pooled(_ptr(cu), _ptr(si), B, int(T), int(num_slots))
+    if st != GDN_OK:
+        _raise(lib, st)
+
+
+def _host_table(page_indices, page_indptr, last_page_len):
+    idt = torch.as_tensor(page_indices).dtype
+    if idt not in _IDX:
+        raise TypeError("page table must be int32 or int64")
+    pi = _host_index("page_indices", page_indices, (idt,))
+    ptr = _host_index("page_indptr", page_indptr, (idt,))
+    lpl = _host_index("last_page_len", last_page_len, (idt,))
+    B = ptr.numel() - 1
+    if lpl.numel() != B:
+        raise ValueError("last_page_len must have B entries (page_indptr has B+1)")
+    return pi, ptr, lpl, B, _IDX[idt]
+
+
+def check_paged(page_indices, page_indptr, last_page_len, num_pages, slots=None, page_size=0):
+    """Host-side preconditions of a single-token paged call (gdn_check_paged); raises GdnError if one fails."""
+    lib = load_library()
+    pi, ptr, lpl, B, idt = _host_table(page_indices, page_indptr, last_page_len)
+    sl = _host_index("slots", slots, (torch.int64,))
+    if sl is not None and sl.shape != (B, 2):
+        raise ValueError("slots must be [B, 2]")
+    st = lib.gdn_check_paged(_ptr(pi), _ptr(ptr), _ptr(lpl), idt, _ptr(sl), B, int(page_size), int(num_pages),
+                             pi.numel())
+    if st != GDN_OK:
+        _raise(lib, st)
+
+
+def check_paged_varlen(cu_seqlens, page_indices, page_indptr, last_page_len, page_size, num_pages, T=None):
+    """Host-side preconditions of a paged varlen decode or prefill call (gdn_check_paged_varlen)."""
+    lib = load_library()
+    pi, ptr, lpl, B, idt = _host_table(page_indices, page_indptr, last_page_len)
+    cu = _host_index("cu_seqlens", cu_seqlens, (torch.int32,))
+    if cu.numel() != B + 1:
+        raise ValueError("cu_seqlens must have B+1 entries")
+    T = int(cu[-1]) if T is None else int(T)
+    st = lib.gdn_check_paged_varlen(_ptr(cu), _ptr(pi), _ptr(ptr), _ptr(lpl), idt, B, T, int(page_size),
+                                    int(num_pages), pi.numel())
+    if st != GDN_OK:
+        _raise(lib, st)
 
 
 def kda_decode_pooled(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_indices, state_pool,

@@ -3,7 +3,9 @@
 //
 // Error convention (max.nn.state_space.kda_decode, Raises): a request whose
 // types or extents bind no kernel is refused on the host before anything is
-// launched; device-side index ranges are not checked.
+// launched; device-side index ranges are not checked.  A build compiled with
+// GDN_DEVICE_CHECKS copies every call's index arrays to the host and
+// validates them (host_checks.hpp) before it launches anything.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -11,9 +13,11 @@
 #include <cstdio>
 #include <string>
 #include <type_traits>
+#include <vector>
 
 #include "gdn_decode.h"
 #include "decode_kernel.hpp"
+#include "host_checks.hpp"
 #include "prefill_kernel.hpp"
 
 namespace {
@@ -31,6 +35,56 @@ int fail(int code, const char* fmt, ...) {
 }
 
 enum class Kind { GdnPooled, GdnPaged, KdaPooled, KdaPaged, GdnPagedVar, KdaPagedVar };
+
+#ifdef GDN_DEVICE_CHECKS
+constexpr bool kChecked = true;
+#else
+constexpr bool kChecked = false;
+#endif
+
+// Host copy of n elements of `bytes` each from device memory, after the work
+// queued on `stream` before the call (which may produce the array) is done.
+bool fetch(const void* dev, int64_t n, size_t bytes, std::vector<unsigned char>& host, hipStream_t stream) {
+  host.resize(static_cast<size_t>(n > 0 ? n : 0) * bytes);
+  if (n <= 0) return true;
+  if (hipMemcpyAsync(host.data(), dev, host.size(), hipMemcpyDeviceToHost, stream) != hipSuccess) return false;
+  return hipStreamSynchronize(stream) == hipSuccess;
+}
+
+// Checked builds: the preconditions of a pooled call (no-op otherwise).
+int checked_pooled(const int32_t* cu, const int32_t* si, int32_t B, int32_t T, int64_t rows, void* stream) {
+  if (!kChecked) return GDN_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<unsigned char> hcu, hsi;
+  if ((cu && !fetch(cu, B + 1, 4, hcu, s)) || !fetch(si, B, 4, hsi, s))
+    return fail(GDN_ERR_HIP, "copying the index arrays to the host failed");
+  std::string msg;
+  if (!gdn_host::check_pooled(cu ? reinterpret_cast<const int32_t*>(hcu.data()) : nullptr,
+                              reinterpret_cast<const int32_t*>(hsi.data()), B, T, rows, msg))
+    return fail(GDN_ERR_PRECONDITION, "%s", msg.c_str());
+  return GDN_OK;
+}
+
+// Checked builds: the preconditions of a paged call (no-op otherwise).
+// page_size 0 and cu NULL: one token per sequence (with optional slots).
+int checked_paged(const int32_t* cu, const void* pi, const void* ptr, const void* lpl, bool i64, const int64_t* slots,
+                  int32_t B, int32_t T, int32_t page_size, int64_t rows, int64_t nnz, void* stream) {
+  if (!kChecked) return GDN_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t ib = i64 ? 8 : 4;
+  std::vector<unsigned char> hcu, hpi, hptr, hlpl, hsl;
+  if ((cu && !fetch(cu, B + 1, 4, hcu, s)) || !fetch(pi, nnz, ib, hpi, s) || !fetch(ptr, B + 1, ib, hptr, s) ||
+      !fetch(lpl, B, ib, hlpl, s) || (slots && !fetch(slots, 2 * int64_t(B), 8, hsl, s)))
+    return fail(GDN_ERR_HIP, "copying the index arrays to the host failed");
+  std::string msg;
+  const bool ok = cu ? gdn_host::check_paged_varlen(reinterpret_cast<const int32_t*>(hcu.data()), hpi.data(),
+                                                    hptr.data(), hlpl.data(), i64, B, T, page_size, rows, nnz, msg)
+                     : gdn_host::check_paged(hpi.data(), hptr.data(), hlpl.data(), i64,
+                                             slots ? reinterpret_cast<const int64_t*>(hsl.data()) : nullptr, B,
+                                             page_size, rows, nnz, msg);
+  if (!ok) return fail(GDN_ERR_PRECONDITION, "%s", msg.c_str());
+  return GDN_OK;
+}
 
 // Workgroup shapes: V-block width VB (one workgroup per V-block of one
 // sequence and value head) and threads per workgroup NT.  Chosen per key
@@ -311,6 +365,7 @@ int gdn_decode_pooled(const void* q, const void* k, const void* v, const void* a
   p.cu_seqlens = cu_seqlens; p.state_indices = state_indices;
   p.pool = state_pool; p.out = out;
   fill_common(p, opt, Kind::GdnPooled, B, T, HK, HV, K, V);
+  if (int rc = checked_pooled(cu_seqlens, state_indices, B, T, num_slots, stream)) return rc;
   if (T == 0) { g_last_error.clear(); return GDN_OK; }
   return run(Kind::GdnPooled, p, K, T, opt, stream);
 }
@@ -346,6 +401,9 @@ int paged_call(Kind kind, const void* q, const void* k, const void* v, const voi
   p.page_size = page_size;
   p.pool = state_pool; p.out = out;
   fill_common(p, opt, kind, B, T, HK, HV, K, V);
+  if (int rc = checked_paged(cu_seqlens, page_indices, page_indptr, last_page_len, p.idx64 != 0, opt->slots, B, T,
+                             page_size, num_pages, nnz, stream))
+    return rc;
   if (T == 0) { g_last_error.clear(); return GDN_OK; }
   return run(kind, p, K, T, opt, stream);
 }
@@ -397,6 +455,22 @@ int gdn_paged_decode_slots(const void* page_indices, const void* page_indptr, co
   if (B <= 0) return fail(GDN_ERR_INVALID, "B must be positive (got %d)", B);
   if (index_dtype != GDN_I32 && index_dtype != GDN_I64)
     return fail(GDN_ERR_INVALID, "index_dtype must be GDN_I32 or GDN_I64 (got %d)", index_dtype);
+  if (kChecked) {
+    // no nnz or num_pages here: the table's structure only (the decode call
+    // that takes these slots checks them against the whole table)
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool i64 = index_dtype == GDN_I64;
+    std::vector<unsigned char> hptr, hlpl;
+    if (!fetch(page_indptr, B + 1, i64 ? 8 : 4, hptr, s) || !fetch(last_page_len, B, i64 ? 8 : 4, hlpl, s))
+      return fail(GDN_ERR_HIP, "copying the index arrays to the host failed");
+    std::string msg;
+    if (!gdn_host::check_table(hptr.data(), hlpl.data(), i64, B, 0, -1, msg))
+      return fail(GDN_ERR_PRECONDITION, "%s", msg.c_str());
+    for (int32_t b = 0; b < B; ++b)
+      if (gdn_host::index_at(hlpl.data(), b, i64) == 1 &&
+          gdn_host::index_at(hptr.data(), b + 1, i64) - gdn_host::index_at(hptr.data(), b, i64) < 2)
+        return fail(GDN_ERR_PRECONDITION, "sequence %d opens a new page but has no previous page", b);
+  }
   hipLaunchKernelGGL(gdn::paged_slots_kernel, dim3((B + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
                      page_indices, page_indptr, last_page_len, B, index_dtype == GDN_I64 ? 1 : 0, slots);
   const hipError_t err = hipGetLastError();
@@ -433,6 +507,9 @@ int prefill_call(bool kda, const void* q, const void* k, const void* v, const vo
   if (int rc = check_options(opt, K, V, kda ? Kind::KdaPagedVar : Kind::GdnPagedVar)) return rc;
   if (opt->slots) return fail(GDN_ERR_INVALID, "slots apply to single-token paged calls only");
   if (opt->qdq != GDN_QDQ_NONE) return fail(GDN_ERR_UNSUPPORTED, "the chunked prefill has no state quantisation");
+  if (int rc = checked_paged(cu_seqlens, page_indices, page_indptr, last_page_len, opt->index_dtype == GDN_I64,
+                             nullptr, B, T, page_size, num_pages, nnz, stream))
+    return rc;
   if (T == 0) { g_last_error.clear(); return GDN_OK; }
   gdn::PrefillParams p{};
   p.q = q; p.k = k; p.v = v; p.gate = gate; p.beta = beta;
@@ -516,6 +593,7 @@ int kda_decode_pooled(const void* q, const void* k, const void* v, const void* r
   p.cu_seqlens = cu_seqlens; p.state_indices = state_indices;
   p.pool = state_pool; p.out = out;
   fill_common(p, opt, Kind::KdaPooled, B, T, HK, HV, K, V);
+  if (int rc = checked_pooled(cu_seqlens, state_indices, B, T, num_slots, stream)) return rc;
   if (T == 0) { g_last_error.clear(); return GDN_OK; }
   return run(Kind::KdaPooled, p, K, T, opt, stream);
 }
@@ -527,11 +605,57 @@ const char* gdn_status_string(int status) {
     case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE";
     case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
     case GDN_ERR_HIP: return "GDN_ERR_HIP";
+    case GDN_ERR_PRECONDITION: return "GDN_ERR_PRECONDITION";
   }
   return "unknown status";
 }
 
 const char* gdn_last_error(void) { return g_last_error.c_str(); }
+
+int gdn_check_pooled(const int32_t* cu_seqlens, const int32_t* state_indices, int32_t B, int32_t T,
+                     int64_t num_slots) {
+  if (!state_indices) return fail(GDN_ERR_INVALID, "state_indices is NULL");
+  if (B <= 0 || T < 0 || num_slots <= 0) return fail(GDN_ERR_INVALID, "B and num_slots must be positive, T >= 0");
+  std::string msg;
+  if (!gdn_host::check_pooled(cu_seqlens, state_indices, B, T, num_slots, msg))
+    return fail(GDN_ERR_PRECONDITION, "%s", msg.c_str());
+  g_last_error.clear();
+  return GDN_OK;
+}
+
+int gdn_check_paged(const void* page_indices, const void* page_indptr, const void* last_page_len, int32_t index_dtype,
+                    const int64_t* slots, int32_t B, int32_t page_size, int64_t num_pages, int64_t nnz) {
+  if (!page_indices || !page_indptr || !last_page_len) return fail(GDN_ERR_INVALID, "a required pointer is NULL");
+  if (index_dtype != GDN_I32 && index_dtype != GDN_I64)
+    return fail(GDN_ERR_INVALID, "index_dtype must be GDN_I32 or GDN_I64 (got %d)", index_dtype);
+  if (B <= 0 || page_size < 0 || num_pages <= 0 || nnz <= 0)
+    return fail(GDN_ERR_INVALID, "B, num_pages and nnz must be positive, page_size >= 0");
+  std::string msg;
+  if (!gdn_host::check_paged(page_indices, page_indptr, last_page_len, index_dtype == GDN_I64, slots, B, page_size,
+                             num_pages, nnz, msg))
+    return fail(GDN_ERR_PRECONDITION, "%s", msg.c_str());
+  g_last_error.clear();
+  return GDN_OK;
+}
+
+int gdn_check_paged_varlen(const int32_t* cu_seqlens, const void* page_indices, const void* page_indptr,
+                           const void* last_page_len, int32_t index_dtype, int32_t B, int32_t T, int32_t page_size,
+                           int64_t num_pages, int64_t nnz) {
+  if (!cu_seqlens || !page_indices || !page_indptr || !last_page_len)
+    return fail(GDN_ERR_INVALID, "a required pointer is NULL");
+  if (index_dtype != GDN_I32 && index_dtype != GDN_I64)
+    return fail(GDN_ERR_INVALID, "index_dtype must be GDN_I32 or GDN_I64 (got %d)", index_dtype);
+  if (B <= 0 || T < 0 || page_size <= 0 || num_pages <= 0 || nnz <= 0)
+    return fail(GDN_ERR_INVALID, "B, page_size, num_pages and nnz must be positive, T >= 0");
+  std::string msg;
+  if (!gdn_host::check_paged_varlen(cu_seqlens, page_indices, page_indptr, last_page_len, index_dtype == GDN_I64, B, T,
+                                    page_size, num_pages, nnz, msg))
+    return fail(GDN_ERR_PRECONDITION, "%s", msg.c_str());
+  g_last_error.clear();
+  return GDN_OK;
+}
+
+int gdn_checked_build(void) { return kChecked ? 1 : 0; }
 
 int gdn_supported_head_dims(int32_t* pairs, int cap) {
   const int n = static_cast<int>(sizeof(kHeads) / sizeof(kHeads[0]));

@@ -29,11 +29,14 @@ def declared_functions():
 
 
 def test_library_exports_every_declared_symbol():
-    lib = rsd.load_library()
     names = declared_functions()
-    assert {"gdn_decode_pooled", "gdn_decode_paged", "kda_decode_pooled", "gdn_status_string"} <= set(names)
-    for n in names:
-        assert hasattr(lib, n), n
+    assert {"gdn_decode_pooled", "gdn_decode_paged", "kda_decode_pooled", "gdn_status_string",
+            "gdn_check_paged", "gdn_checked_build"} <= set(names)
+    for path, checked in ((rsd.LIB_PATH, 0), (rsd.CHECKED_LIB_PATH, 1)):
+        lib = bnd.load_library(path)
+        for n in names:
+            assert hasattr(lib, n), (path, n)
+        assert lib.gdn_checked_build() == checked, path
 
 
 def test_missing_library_fails_loudly(tmp_path):
@@ -47,8 +50,8 @@ def test_options_defaults_and_status_strings():
     assert (o.beta_mode, o.gate_mode, o.index_dtype, o.qdq, o.block_v, o.quantize_initial, o.readout) == \
         (0, 0, bnd.GDN_I32, 0, 64, 0, 0)
     lib = rsd.load_library()
-    assert [lib.gdn_status_string(i).decode() for i in range(5)] == \
-        ["GDN_OK", "GDN_ERR_INVALID", "GDN_ERR_SHAPE", "GDN_ERR_UNSUPPORTED", "GDN_ERR_HIP"]
+    assert [lib.gdn_status_string(i).decode() for i in range(6)] == \
+        ["GDN_OK", "GDN_ERR_INVALID", "GDN_ERR_SHAPE", "GDN_ERR_UNSUPPORTED", "GDN_ERR_HIP", "GDN_ERR_PRECONDITION"]
     assert lib.gdn_status_string(99).decode() == "unknown status"
     assert (128, 64) in rsd.supported_head_dims() and (16, 16) in rsd.supported_head_dims()
 
