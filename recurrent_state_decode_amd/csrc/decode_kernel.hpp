@@ -734,11 +734,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   auto had_quant = [&]() {
     // amax of each row's group (8 lanes), one reduction step for all rows at
     // a time so that the steps of different rows interleave
+    // (in-thread: v_maximum3_f32 with |x| source modifiers, two per row)
     float m[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      m[s] = OpMaxNonNeg::f(OpMaxNonNeg::f(fabsf(S[s][0]), fabsf(S[s][1])),
-                            OpMaxNonNeg::f(fabsf(S[s][2]), fabsf(S[s][3])));
+      m[s] = __builtin_elementwise_maximum(
+          __builtin_elementwise_maximum(fabsf(S[s][0]), fabsf(S[s][1])),
+          __builtin_elementwise_maximum(fabsf(S[s][2]), fabsf(S[s][3])));
 #pragma unroll
     for (int s = 0; s < NS; ++s) m[s] = OpMaxNonNeg::f(m[s], dpp<0xB1>(m[s]));
 #pragma unroll
@@ -1029,7 +1031,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
       }
       if constexpr (!HAD) {
         if (!stored) store_outputs(out_row, o);
-      } else if (!stored) {        // o back to the original value basis
+      } else if (!stored && __builtin_amdgcn_readfirstlane(w) == 0) {   // o back to the original basis (wave 0 stores it)
         float ow[1][NO];
 #pragma unroll
         for (int j = 0; j < NO; ++j) ow[0][j] = o[j];

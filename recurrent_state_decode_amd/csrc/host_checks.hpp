@@ -27,6 +27,7 @@
 
 #include <stdint.h>
 
+#include <cstdarg>
 #include <cstdio>
 #include <string>
 #include <unordered_map>
@@ -37,10 +38,12 @@ inline int64_t index_at(const void* p, int64_t i, bool i64) {
   return i64 ? static_cast<const int64_t*>(p)[i] : static_cast<const int32_t*>(p)[i];
 }
 
-template <typename... A>
-inline bool violation(std::string& msg, const char* fmt, A... args) {
+__attribute__((format(printf, 2, 3))) inline bool violation(std::string& msg, const char* fmt, ...) {
   char buf[256];
-  std::snprintf(buf, sizeof(buf), fmt, args...);
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
   msg = buf;
   return false;
 }
