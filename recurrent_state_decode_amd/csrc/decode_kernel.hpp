@@ -164,6 +164,23 @@ __device__ __forceinline__ int64_t load_index(const void* p, int64_t i, int idx6
   return idx64 ? static_cast<const int64_t*>(p)[i] : static_cast<int64_t>(static_cast<const int32_t*>(p)[i]);
 }
 
+// The same entry read through the constant address space: with a uniform
+// index it becomes a scalar-cache load, which is counted apart from the
+// vector memory operations, so waiting for it never waits for earlier
+// stores.  Only for tables the kernel never writes (the page table).
+// s_waitcnt vmcnt(0), with expcnt and lgkmcnt at their maxima (gfx9 encoding).
+// Issued where only a tile's loads are in flight: the compiler cannot prove
+// that they complete on every path to the tile's later uses and would
+// otherwise wait there, behind the stores issued since (the counter retires
+// loads and stores in order).
+constexpr int kWaitVmem0 = 0x0F70;
+
+typedef const __attribute__((address_space(4))) int64_t* ConstI64;
+typedef const __attribute__((address_space(4))) int32_t* ConstI32;
+__device__ __forceinline__ int64_t load_index_uniform(const void* p, int64_t i, int idx64) {
+  return idx64 ? ((ConstI64)p)[i] : static_cast<int64_t>(((ConstI32)p)[i]);
+}
+
 __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
   const __bf16 h = static_cast<__bf16>(x);   // round to nearest even
   return __builtin_bit_cast(uint16_t, h);
@@ -612,6 +629,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
         S[s][4 * f + 3] = x.w;
       }
     finish_raw(n0);                // overlaps the tile load
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);   // the tile (see kWaitVmem0)
   } else {
     f32x4 L[VB / 16][2];
 #pragma unroll
@@ -1075,7 +1093,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
         // page is written after the loop)
         const int64_t pos = pos0 + (t - t0);
         if (pos > 0 && pos % p.page_size == 0 && pos != pos_last) {
-          const int64_t row = load_index(p.page_indices, pg_start + (pos - 1) / p.page_size, p.idx64);
+          const int64_t row = load_index_uniform(p.page_indices, pg_start + (pos - 1) / p.page_size, p.idx64);
           store_tile(p.pool + (row * p.HV + h) * tile_elems);
         }
       }

@@ -264,9 +264,23 @@ void prefill_kernel(const PrefillParams p) {
       }
   };
 
+  // GDN stages chunk j at the end of iteration j - 1 (the first one before
+  // the loop), so the raw input registers never cross the loop's back edge
+  // and waiting for them never waits for the stores of earlier chunks
+  // (about 10 % on 16 x 1024 tokens).  KDA, whose chunk starts with the
+  // per-channel gate prefix, measured 4 % slower that way and stages each
+  // chunk at the top of its own iteration.
+  constexpr bool kStageLate = !KDA;
+  if constexpr (kStageLate) {
+    stage_chunk(jfirst * C + 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);   // the state tile (see kWaitVmem0)
+  }
   for (int j = jfirst; j <= jlast; ++j) {
     const int cpos = j * C + 1;              // position of slot 0
-    stage_chunk(cpos);
+    // the pool row of a page this chunk fills (GDN: scalar load, see load_index_uniform)
+    const bool page_end = to_page_end == 0 && cpos + C - 1 < pos_last;
+    const int64_t page_row = (page_end && kStageLate) ? load_index_uniform(p.page_indices, page_slot, p.idx64) : 0;
+    if constexpr (!kStageLate) stage_chunk(cpos);
     if (j < jlast) load_chunk(cpos + C);     // next chunk's inputs, in flight during this chunk
     __syncthreads();
 
@@ -449,12 +463,15 @@ void prefill_kernel(const PrefillParams p) {
 
     // ---- a page that ends inside the suffix gets the state after its last token
     if (to_page_end == 0) {
-      if (cpos + C - 1 < pos_last) store_state(load_index(p.page_indices, page_slot, p.idx64));
+      if (page_end) store_state(kStageLate ? page_row : load_index(p.page_indices, page_slot, p.idx64));
       to_page_end = cpp;
       ++page_slot;
     }
     --to_page_end;
     __syncthreads();                // LDS is rewritten by the next chunk
+    if constexpr (kStageLate) {
+      if (j < jlast) stage_chunk(cpos + C);
+    }
   }
 
   store_state(wrow);
