@@ -21,6 +21,7 @@ Prints one JSON line:
 """
 import argparse
 import hashlib
+import inspect
 import json
 import os
 import sys
@@ -278,7 +279,7 @@ def main():
                     choices=["paged_gdn_b256", "pooled_gdn_b64", "pooled_kda_varlen_b128", "fp8_qdq_gdn_b512",
                              "tiny_gdn", "paged_kda_b256", "paged_gdn_varlen_b256_t4", "int8h32_gdn_b512",
                              "paged_gdn_prefill_b16_t1024", "paged_kda_prefill_b16_t1024"])
-    ap.add_argument("--layout", default=None, help="override the pool layout (K_FIRST / V_FIRST)")
+    ap.add_argument("--layout", default=None, help="override the pool layout (K_FIRST / V_FIRST); a layout other than the workload's own gets a +LAYOUT suffix on its name")
     ap.add_argument("--qdq", default=None, choices=["none", "fp8_e4m3_tile", "int8_hadamard32"],
                     help="override the workload's state quantisation (the workload name gets a +qdq suffix)")
     ap.add_argument("--token-path", action="store_true",
@@ -323,9 +324,16 @@ def main():
     maker = wl.NAMED[args.workload]
     paged_makers = ("paged_gdn_b256", "paged_kda_b256", "paged_gdn_varlen_b256_t4", "paged_gdn_prefill_b16_t1024",
                     "paged_kda_prefill_b16_t1024")
-    w = maker(state_layout=args.layout) if (args.layout and args.workload in paged_makers) else maker()
-    if args.layout and args.workload not in paged_makers:
-        w.state_layout = args.layout
+    if args.workload in paged_makers:
+        default_layout = inspect.signature(maker).parameters["state_layout"].default
+        w = maker(state_layout=args.layout) if args.layout else maker()
+    else:
+        w = maker()
+        default_layout = w.state_layout
+        if args.layout:
+            w.state_layout = args.layout
+    if args.layout and args.layout != default_layout:
+        w.name = f"{w.name}+{args.layout}"     # its own profiles and traffic figure
     if args.token_path and w.chunked:
         w.chunked = False
         w.name = f"{w.name}+token_path"
