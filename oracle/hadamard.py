@@ -31,6 +31,15 @@ rint(f32(z * inv)), result = f32(code H) * f32(f32(amax|z| / 127) / 32) --
 so that both sides decide each code in float32; ``'float64'`` is the same
 rule in float64.
 
+Packed storage (this repository's format; the pages describe the codec as a
+quantise/dequantise emulation and claim no compressed storage): a state is
+kept as its codes and scales, int8 code[h, k, v] and scale[h, k, g] =
+amax|z| / 127 of group g in the +-1 Hadamard basis z = x H, and stands for
+(code H) * scale / 32 -- exactly what int8_hadamard32_qdq returns.
+``int8_hadamard32_encode`` / ``int8_hadamard32_decode`` convert, and
+``pack_tiles`` / ``unpack_tiles`` lay one (row, head) tile out as its K V
+code bytes followed by its K V / 32 float32 scales.
+
 Pins (tests/test_oracle_hadamard.py): H / sqrt(32) is orthonormal and
 symmetric, the butterfly transform equals the matrix product, the folded
 form equals the definition with explicit normalisation, code points
@@ -96,3 +105,69 @@ def int8_hadamard32_qdq(S, precision="float32"):
         out = np.where(amax > 0, xq, x.astype(f))
         return out.reshape(Hh, K, V).astype(np.float64)
     raise ValueError(f"unknown precision {precision!r}")
+
+
+def int8_hadamard32_encode(S, precision="float32"):
+    """Codes (int8) and scales (float64) of S [H, K, V] under the codec; decode(encode(S)) == qdq(S).
+
+    scale = amax|z| / 127 per (head, key row, group of 32) with z = S H (the +-1 matrix); an
+    all-zero group has scale 0 and codes 0.  The codes are decided exactly as in
+    int8_hadamard32_qdq at the same precision.
+    """
+    S = np.asarray(S, dtype=np.float64)
+    Hh, K, V = S.shape
+    if V % GROUP != 0:
+        raise ValueError("the value head dim must be a multiple of 32")
+    x = S.reshape(Hh, K, V // GROUP, GROUP)
+    if precision == "float64":
+        z = x @ hadamard_matrix()
+        amax = np.max(np.abs(z), axis=-1, keepdims=True)
+        safe = np.where(amax > 0, amax, 1.0)
+        code = np.clip(np.rint(z * INT8_MAX / safe), -INT8_MAX, INT8_MAX)
+        scale = amax / INT8_MAX
+    elif precision == "float32":
+        f = np.float32
+        z = fwht_butterflies(x.astype(f), dtype=f)
+        amax = np.max(np.abs(z), axis=-1, keepdims=True)
+        safe = np.where(amax > 0, amax, f(1.0)).astype(f)
+        inv = (f(INT8_MAX) / safe).astype(f)
+        code = np.clip(np.rint((z * inv).astype(f)), -INT8_MAX, INT8_MAX)
+        scale = (amax / f(INT8_MAX)).astype(f).astype(np.float64)
+    else:
+        raise ValueError(f"unknown precision {precision!r}")
+    code = np.where(amax > 0, code, 0.0)
+    return code.reshape(Hh, K, V).astype(np.int8), scale.reshape(Hh, K, V // GROUP)
+
+
+def int8_hadamard32_decode(code, scale):
+    """The state [H, K, V] that codes [H, K, V] and scales [H, K, V / 32] stand for: (code H) scale / 32."""
+    code = np.asarray(code, dtype=np.float64)
+    Hh, K, V = code.shape
+    z = code.reshape(Hh, K, V // GROUP, GROUP)
+    x = (z @ hadamard_matrix()) * (np.asarray(scale, dtype=np.float64)[..., None] / GROUP)
+    return x.reshape(Hh, K, V)
+
+
+def packed_tile_bytes(K, V):
+    """Bytes of one packed (row, head) tile: K V codes, then K V / 32 float32 scales."""
+    return K * V + 4 * K * (V // GROUP)
+
+
+def pack_tiles(code, scale):
+    """codes [..., K, V] int8 and scales [..., K, V / 32] -> bytes [..., packed_tile_bytes(K, V)] (uint8)."""
+    code = np.asarray(code, dtype=np.int8)
+    lead, (K, V) = code.shape[:-2], code.shape[-2:]
+    c = code.reshape(lead + (K * V,)).view(np.uint8)
+    s = np.ascontiguousarray(np.asarray(scale, dtype=np.float32).reshape(lead + (K * (V // GROUP),)))
+    return np.concatenate([c, s.view(np.uint8).reshape(lead + (4 * K * (V // GROUP),))], axis=-1)
+
+
+def unpack_tiles(tiles, K, V):
+    """Inverse of pack_tiles: bytes [..., packed_tile_bytes(K, V)] -> (codes int8 [..., K, V], scales float64)."""
+    t = np.ascontiguousarray(np.asarray(tiles, dtype=np.uint8))
+    lead = t.shape[:-1]
+    if t.shape[-1] != packed_tile_bytes(K, V):
+        raise ValueError("tile size does not match K and V")
+    code = t[..., :K * V].copy().view(np.int8).reshape(lead + (K, V))
+    scale = t[..., K * V:].copy().view(np.float32).reshape(lead + (K, V // GROUP)).astype(np.float64)
+    return code, scale

@@ -108,3 +108,55 @@ def test_zero_group_unchanged_and_float32_agrees_with_float64():
     diff = np.abs((a - b).reshape(4, 8, 2, 32) @ H)
     assert np.all(diff <= step * (1 + 1e-4) + 1e-7)      # at most one code step apart
     assert np.mean(diff > 0.5 * step) < 0.02            # code flips are rare ties
+
+
+# ---------------------------------------------------------------- packed storage (codes + scales)
+
+@pytest.mark.parametrize("precision", ["float64", "float32"])
+def test_decode_of_encode_is_the_qdq(precision):
+    rng = np.random.default_rng(21)
+    S = rng.standard_normal((3, 5, 96)) * 0.05
+    S[1, 2, 32:64] = 0.0                                   # an all-zero group
+    code, scale = hd.int8_hadamard32_encode(S, precision)
+    assert code.dtype == np.int8 and np.abs(code.astype(int)).max() == 127
+    assert np.all(scale[1, 2, 1] == 0) and np.all(code[1, 2, 32:64] == 0)
+    tol = 0 if precision == "float64" else 1e-7 * np.abs(S).max()
+    np.testing.assert_allclose(hd.int8_hadamard32_decode(code, scale), hd.int8_hadamard32_qdq(S, precision),
+                               rtol=0, atol=tol + 1e-17)
+
+
+def test_encode_of_decode_returns_the_codes_and_scales():
+    """A stored state re-encodes to the same codes (every group holds +-127) and the same scales."""
+    rng = np.random.default_rng(22)
+    code = rng.integers(-127, 128, (2, 4, 64)).astype(np.int8)
+    code[..., 5] = 127
+    code[..., 40] = -127
+    scale = rng.uniform(1e-4, 1e-1, (2, 4, 2))
+    for precision in ("float64", "float32"):
+        c2, s2 = hd.int8_hadamard32_encode(hd.int8_hadamard32_decode(code, scale), precision)
+        assert np.array_equal(c2, code)
+        np.testing.assert_allclose(s2, scale, rtol=1e-6 if precision == "float32" else 1e-13)
+
+
+def test_scale_is_amax_over_127_in_the_pm1_basis():
+    """A single 1 in a group rotates to a row of H: every |z| = 1, scale = 1/127, codes = 127 H[j]."""
+    S = np.zeros((1, 1, 32))
+    S[0, 0, 9] = 1.0
+    code, scale = hd.int8_hadamard32_encode(S, "float64")
+    assert scale[0, 0, 0] == 1.0 / 127
+    assert np.array_equal(code[0, 0], (127 * hd.hadamard_matrix()[9]).astype(np.int8))
+
+
+def test_pack_layout_and_round_trip():
+    rng = np.random.default_rng(23)
+    code = rng.integers(-127, 128, (3, 2, 4, 64)).astype(np.int8)
+    scale = rng.uniform(0, 1, (3, 2, 4, 2))
+    t = hd.pack_tiles(code, scale)
+    assert t.shape == (3, 2, hd.packed_tile_bytes(4, 64)) == (3, 2, 4 * 64 + 4 * 4 * 2)
+    # codes first, row-major [K][V]; then the float32 scales [K][V / 32]
+    assert t[1, 0, 64 + 7] == np.uint8(code[1, 0, 1, 7].view(np.uint8))
+    assert t[2, 1, 256:260].view(np.float32)[0] == np.float32(scale[2, 1, 0, 0])
+    assert t[2, 1, 256 + 4 * 3:256 + 4 * 4].view(np.float32)[0] == np.float32(scale[2, 1, 1, 1])
+    c2, s2 = hd.unpack_tiles(t, 4, 64)
+    assert np.array_equal(c2, code)
+    assert np.array_equal(s2, scale.astype(np.float32).astype(np.float64))
