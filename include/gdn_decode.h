@@ -111,6 +111,25 @@ enum gdn_qdq { GDN_QDQ_NONE = 0, GDN_QDQ_FP8_E4M3_TILE = 1, GDN_QDQ_INT8_HADAMAR
  * 'stored' from the rounded state. */
 enum gdn_readout { GDN_READOUT_WORKING = 0, GDN_READOUT_STORED = 1 };
 
+/* How the pool holds the state.  GDN_STORAGE_F32: fp32 states in the
+ * state_layout order (every entry point's default).  GDN_STORAGE_I8H32:
+ * the int8_hadamard32 codec's own codes -- this library's format; the
+ * pages (modelopt ... linear_attention.config, LinearAttentionConfig)
+ * describe the codec as a quantise/dequantise emulation with no
+ * compressed-storage claim.  Each (row, value head) tile is
+ * gdn_packed_tile_bytes(K, V) bytes: K V int8 codes in [K][V] order,
+ * then K V / 32 float32 scales in [K][V / 32] order; code c[k][v] and
+ * scale s[k][g] stand for the state row S[k][32 g .. 32 g + 31] =
+ * (c[k][32 g ..] H) * s[k][g] / 32 (H the +-1 Sylvester Hadamard matrix of
+ * order 32), so s is amax/127 of the group in the +-1 Hadamard basis.
+ * state_pool then points to rows * HV such tiles (4-byte aligned) and is
+ * read and written as such.  Requires qdq = GDN_QDQ_INT8_HADAMARD32 (else
+ * GDN_ERR_INVALID) and state_layout = GDN_K_FIRST (else
+ * GDN_ERR_UNSUPPORTED); results equal those of GDN_STORAGE_F32 with the
+ * codec up to float32 rounding, with about 3.6x fewer pool bytes at
+ * K = V = 128. */
+enum gdn_storage { GDN_STORAGE_F32 = 0, GDN_STORAGE_I8H32 = 1 };
+
 /* Options of a call.  Fill with gdn_options_init() and change fields. */
 typedef struct gdn_options {
   float scale;              /* query scale; 0 means 1/sqrt(K)                     (default 0) */
@@ -129,6 +148,7 @@ typedef struct gdn_options {
                                from gdn_paged_decode_slots() for the same page table, or NULL to
                                resolve the rows inside the call (default NULL).  Not checked
                                against the table (flashinfer.gdn_paged, slots). */
+  int32_t state_storage;    /* gdn_storage                                      (default F32) */
 } gdn_options;
 
 /* Fill `opt` with the defaults listed above.  `opt` must not be NULL. */
@@ -347,6 +367,10 @@ int gdn_check_paged_varlen(const int32_t* cu_seqlens, const void* page_indices,
                            const void* page_indptr, const void* last_page_len, int32_t index_dtype,
                            int32_t B, int32_t T, int32_t page_size, int64_t num_pages, int64_t nnz);
 int gdn_checked_build(void);
+
+/* Bytes of one packed (row, value head) tile of a GDN_STORAGE_I8H32 pool:
+ * K V + 4 K (V / 32); -1 if V is not a positive multiple of 32 or K <= 0. */
+int64_t gdn_packed_tile_bytes(int32_t K, int32_t V);
 
 /* Head dims with a compiled kernel: writes up to `cap` (K, VB) pairs as
  * 2*n ints into `pairs` (NULL allowed) and returns the number of pairs

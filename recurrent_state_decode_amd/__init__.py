@@ -23,5 +23,6 @@ from ._binding import (  # noqa: F401
     kda_decode_pooled,
     kda_prefill_paged,
     load_library,
+    packed_tile_bytes,
     supported_head_dims,
 )

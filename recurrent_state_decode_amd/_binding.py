@@ -44,6 +44,7 @@ class GdnOptions(ctypes.Structure):
         ("quantize_initial", ctypes.c_int32),
         ("readout", ctypes.c_int32),
         ("slots", ctypes.c_void_p),
+        ("state_storage", ctypes.c_int32),
     ]
 
 
@@ -78,6 +79,7 @@ _SIGNATURES = {
     "gdn_check_paged": (ctypes.c_int, [_P, _P, _P, _I32, _P, _I32, _I32, _I64, _I64]),
     "gdn_check_paged_varlen": (ctypes.c_int, [_P] * 4 + [_I32] * 4 + [_I64, _I64]),
     "gdn_checked_build": (ctypes.c_int, []),
+    "gdn_packed_tile_bytes": (ctypes.c_int64, [_I32, _I32]),
 }
 
 _lib = None
@@ -172,18 +174,38 @@ def _raise(lib, status):
 
 
 def _common_opts(io_dtype, out_dtype, scale, use_qk_l2norm, beta_mode, state_layout, qdq, block_v,
-                 quantize_initial, readout, gate_mode="original", index_dtype=GDN_I32, slots=None):
+                 quantize_initial, readout, gate_mode="original", index_dtype=GDN_I32, slots=None, state_storage=0):
     return _options(scale=0.0 if scale is None else float(scale), use_qk_l2norm=int(bool(use_qk_l2norm)),
                     io_dtype=_IO[io_dtype], out_dtype=_IO[out_dtype], state_layout=_LAYOUT[state_layout],
                     beta_mode=_BETA[beta_mode], gate_mode=_GATE[gate_mode], index_dtype=index_dtype,
                     qdq=_QDQ[qdq], block_v=int(block_v), quantize_initial=int(bool(quantize_initial)),
-                    readout=_READOUT[readout], slots=None if slots is None else slots.data_ptr())
+                    readout=_READOUT[readout], slots=None if slots is None else slots.data_ptr(),
+                    state_storage=int(state_storage))
+
+
+GDN_STORAGE_F32, GDN_STORAGE_I8H32 = 0, 1
+
+
+def packed_tile_bytes(K, V):
+    """Bytes of one (row, value head) tile of a packed int8_hadamard32 pool (gdn_packed_tile_bytes)."""
+    n = load_library().gdn_packed_tile_bytes(int(K), int(V))
+    if n < 0:
+        raise ValueError(f"no packed tile for K={K}, V={V} (V must be a multiple of 32)")
+    return n
 
 
 def _pool_check(state_pool, HV, K, V, state_layout):
+    """Check the pool's shape; return its storage: a uint8 pool [rows, HV, packed_tile_bytes(K, V)] holds
+    packed int8_hadamard32 tiles (GDN_STORAGE_I8H32), a float32 pool fp32 states."""
+    if state_pool.dtype == torch.uint8:
+        tail = (HV, packed_tile_bytes(K, V))
+        if state_pool.dim() != 3 or tuple(state_pool.shape[1:]) != tail:
+            raise ValueError(f"packed state_pool shape {tuple(state_pool.shape)} does not match [rows, {tail}]")
+        return GDN_STORAGE_I8H32
     tail = (HV, K, V) if state_layout == "K_FIRST" else (HV, V, K)
     if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != tail:
         raise ValueError(f"state_pool shape {tuple(state_pool.shape)} does not match [rows, {tail}] for {state_layout}")
+    return GDN_STORAGE_F32
 
 
 def gdn_decode_pooled(q, k, v, a, b, A_log, dt_bias, cu_seqlens, state_indices, state_pool, out=None, *,
@@ -204,21 +226,21 @@ def gdn_decode_pooled(q, k, v, a, b, A_log, dt_bias, cu_seqlens, state_indices, 
     _check_dev("dt_bias", dt_bias, dev, (torch.float32,))
     _check_dev("cu_seqlens", cu_seqlens, dev, (torch.int32,))
     _check_dev("state_indices", state_indices, dev, (torch.int32,))
-    _check_dev("state_pool", state_pool, dev, (torch.float32,))
+    _check_dev("state_pool", state_pool, dev, (torch.float32, torch.uint8))
     if k.shape != q.shape or v.shape[0] != T or a.shape != (T, HV) or b.shape != (T, HV):
         raise ValueError("q/k/v/a/b shapes disagree")
     if A_log.shape != (HV,) or dt_bias.shape != (HV,):
         raise ValueError("A_log and dt_bias must be [HV]")
     if cu_seqlens is not None and cu_seqlens.shape != (B + 1,):
         raise ValueError("cu_seqlens must be [B+1]")
-    _pool_check(state_pool, HV, K, V, state_layout)
+    storage = _pool_check(state_pool, HV, K, V, state_layout)
     if out is None:
         out = torch.empty((T, HV, V), dtype=out_dtype, device=dev)
     _check_dev("out", out, dev, (out_dtype,))
     if out.shape != (T, HV, V):
         raise ValueError("out must be [T, HV, V]")
     opt = _common_opts(io, out_dtype, scale, use_qk_l2norm, beta_mode, state_layout, qdq, block_v,
-                       quantize_initial, readout)
+                       quantize_initial, readout, state_storage=storage)
     st = lib.gdn_decode_pooled(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
                                _ptr(cu_seqlens), _ptr(state_indices), _ptr(state_pool), _ptr(out),
                                B, T, HK, HV, K, V, state_pool.shape[0], ctypes.byref(opt),
@@ -249,7 +271,7 @@ def _paged(kind, q, k, v, gate, beta_in, a_log, dt_bias, cu_seqlens, page_indice
         raise TypeError("page table must be int32 or int64")
     for n, t in (("page_indices", page_indices), ("page_indptr", page_indptr), ("last_page_len", last_page_len)):
         _check_dev(n, t, dev, (idt,))
-    _check_dev("state_pool", state_pool, dev, (torch.float32,))
+    _check_dev("state_pool", state_pool, dev, (torch.float32, torch.uint8))
     _check_dev("slots", slots, dev, (torch.int64,))
     if var:
         _check_dev("cu_seqlens", cu_seqlens, dev, (torch.int32,))
@@ -268,14 +290,15 @@ def _paged(kind, q, k, v, gate, beta_in, a_log, dt_bias, cu_seqlens, page_indice
         raise ValueError("last_page_len must be [B]")
     if slots is not None and slots.shape != (B, 2):
         raise ValueError("slots must be [B, 2]")
-    _pool_check(state_pool, HV, K, V, state_layout)
+    storage = _pool_check(state_pool, HV, K, V, state_layout)
     if out is None:
         out = torch.empty((T, HV, V), dtype=out_dtype, device=dev)
     _check_dev("out", out, dev, (out_dtype,))
     if out.numel() != T * HV * V:
         raise ValueError("out must hold [T, HV, V]")
     opt = _common_opts(io, out_dtype, scale, use_qk_l2norm, beta_mode, state_layout, qdq, block_v,
-                       quantize_initial, readout, gate_mode=gate_mode, index_dtype=_IDX[idt], slots=slots)
+                       quantize_initial, readout, gate_mode=gate_mode, index_dtype=_IDX[idt], slots=slots,
+                       state_storage=storage)
     common_tail = (B, HK, HV, K, V) if not var else (B, T, HK, HV, K, V)
     ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta_in), _ptr(a_log), _ptr(dt_bias))
     table = (_ptr(page_indices), _ptr(page_indptr), _ptr(last_page_len))
@@ -457,7 +480,7 @@ def kda_decode_pooled(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens
     _check_dev("dt_bias", dt_bias, dev, (torch.float32,))
     _check_dev("cu_seqlens", cu_seqlens, dev, (torch.int32,))
     _check_dev("state_indices", state_indices, dev, (torch.int32,))
-    _check_dev("state_pool", state_pool, dev, (torch.float32,))
+    _check_dev("state_pool", state_pool, dev, (torch.float32, torch.uint8))
     if cu_seqlens is None:
         raise ValueError("cu_seqlens is required for KDA decode")
     if k.shape != q.shape or v.shape[0] != T or raw_gate.shape != (T, HV, K) or beta_logits.shape != (T, HV):
@@ -466,14 +489,14 @@ def kda_decode_pooled(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens
         raise ValueError("a_log must be [HV] and dt_bias [HV, K]")
     if cu_seqlens.shape != (B + 1,):
         raise ValueError("cu_seqlens must be [B+1]")
-    _pool_check(state_pool, HV, K, V, state_layout)
+    storage = _pool_check(state_pool, HV, K, V, state_layout)
     if out is None:
         out = torch.empty((T, HV, V), dtype=out_dtype, device=dev)
     _check_dev("out", out, dev, (out_dtype,))
     if out.shape != (T, HV, V):
         raise ValueError("out must be [T, HV, V]")
     opt = _common_opts(io, out_dtype, scale, use_qk_l2norm, beta_mode, state_layout, qdq, block_v,
-                       quantize_initial, readout, gate_mode=gate_mode)
+                       quantize_initial, readout, gate_mode=gate_mode, state_storage=storage)
     st = lib.kda_decode_pooled(_ptr(q), _ptr(k), _ptr(v), _ptr(raw_gate), _ptr(beta_logits), _ptr(a_log),
                                _ptr(dt_bias), _ptr(cu_seqlens), _ptr(state_indices), _ptr(state_pool), _ptr(out),
                                B, T, HK, HV, K, V, state_pool.shape[0], ctypes.byref(opt),

@@ -103,6 +103,7 @@ enum Qdq : int {
   kQdqNone = 0,
   kQdqTile = 1,     // fp8 e4m3, one amax/448 scale per [K, VB] tile
   kQdqHad = 2,      // int8 codes of the 32-point Hadamard rotation, one scale per (key row, 32 values)
+  kQdqHadPacked = 3,  // the same codec with the pool holding the codes and scales (packed tiles)
 };
 
 constexpr float kL2Eps = 1e-6f;
@@ -389,7 +390,12 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   // Register arrangement: V_FIRST rows (value columns) for a V_FIRST pool,
   // except with the int8_hadamard32 codec, which needs each key row's values
   // in lanes; the pool layout VF itself only shapes the tile's load and store.
-  constexpr bool HAD = QDQ == kQdqHad;
+  // PACKED: each (row, head) tile of the pool is K V int8 codes ([K][V], in
+  // the +-1 Hadamard basis of each 32-value group) followed by K V / 32
+  // float32 scales; the codes load straight into the rotated registers.
+  constexpr bool PACKED = QDQ == kQdqHadPacked;
+  constexpr bool HAD = QDQ == kQdqHad || PACKED;
+  static_assert(!PACKED || !VF, "packed tiles have one layout ([K][V] codes)");
   constexpr bool AV = VF && !HAD;
   using Cfg = Tile<K, VB, NT, AV>;
   constexpr int NW = Cfg::NW, LR = Cfg::LR, RPW = Cfg::RPW, NS = Cfg::NS, LB = Cfg::LB;
@@ -597,8 +603,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   }
 
   const int64_t tile_elems = static_cast<int64_t>(K) * p.V;
-  const float* src = p.pool + (rrow * p.HV + h) * tile_elems;
-  float* dst = p.pool + (wrow * p.HV + h) * tile_elems;
+  const int64_t tile_bytes = static_cast<int64_t>(K) * p.V + 4 * static_cast<int64_t>(K) * (p.V / 32);
+  auto tile_base = [&](int64_t row) -> float* {
+    if constexpr (PACKED) return reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(p.pool) + (row * p.HV + h) * tile_bytes);
+    else return p.pool + (row * p.HV + h) * tile_elems;
+  };
+  const float* src = tile_base(rrow);
+  float* dst = tile_base(wrow);
 
   auto row_idx = [&](int s) -> int { return s * (NW * RPW) + w * RPW + rg; };
   // memory offset of this thread's float4 number f (0 .. EV/4-1) in row s
@@ -617,7 +628,22 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   auto kf_lds = [&](int s, int j) -> int { return (4 * lr + j) * LD + row_idx(s); };
 
   float S[NS][EV];
-  if constexpr (!TRANS) {
+  if constexpr (PACKED) {
+    // 4 codes (one dword) and their group's scale per row: R = code * scale
+    const unsigned char* sb = reinterpret_cast<const unsigned char*>(src);
+    const float* sc = reinterpret_cast<const float*>(sb + tile_elems);
+    const int col = vb * VB + 4 * lr;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int r = row_idx(s);
+      const uint32_t c4 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sb + static_cast<int64_t>(r) * p.V + col));
+      const float scale = __builtin_nontemporal_load(sc + r * (p.V / 32) + col / 32);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[s][j] = static_cast<float>(static_cast<int8_t>(c4 >> (8 * j))) * scale;
+    }
+    finish_raw(n0);                // overlaps the tile load
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);   // the tile (see kWaitVmem0)
+  } else if constexpr (!TRANS) {
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -664,7 +690,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   const uint32_t sg1 = (static_cast<uint32_t>(lane) & 1u) << 31;   // sign masks of the butterflies
   const uint32_t sg2 = (static_cast<uint32_t>(lane) & 2u) << 30;
   const uint32_t sg4 = (static_cast<uint32_t>(lane) & 4u) << 29;
-  if constexpr (HAD) wht32(S, sg1, sg2, sg4);
+  if constexpr (HAD && !PACKED) wht32(S, sg1, sg2, sg4);
 
   // true state = scale * S: one scale (GDN) or one per key slot (KDA)
   constexpr int NC = KDA ? NKEY : 1;
@@ -779,7 +805,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   };
   auto quantize = [&]() {
     if constexpr (QDQ == kQdqTile) qdq_tile();
-    else if constexpr (QDQ == kQdqHad) had_quant();
+    else if constexpr (HAD) had_quant();
   };
 
   // output stores: 4 consecutive values (K_FIRST) or one (V_FIRST)
@@ -909,7 +935,40 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   // write the true state (scale * registers) to a pool row, with
   // non-temporal stores like the loads: the row is not read again by this call
   auto store_tile = [&](float* row_base) {
-    if constexpr (!HAD) {
+    if constexpr (PACKED) {
+      // Every token ends with had_quant, so the registers hold code * c per
+      // (row, group): the group's amax is 127 c up to one rounding and
+      // rint(R * 127 / amax) gives the codes back exactly.  The stored scale
+      // carries the workgroup's decay scale: true R = scale * code.
+      unsigned char* tb = reinterpret_cast<unsigned char*>(row_base);
+      float* tsc = reinterpret_cast<float*>(tb + tile_elems);
+      const int col = vb * VB + 4 * lr;
+      float m[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        m[s] = __builtin_elementwise_maximum(
+            __builtin_elementwise_maximum(fabsf(S[s][0]), fabsf(S[s][1])),
+            __builtin_elementwise_maximum(fabsf(S[s][2]), fabsf(S[s][3])));
+#pragma unroll
+      for (int s = 0; s < NS; ++s) m[s] = OpMaxNonNeg::f(m[s], dpp<0xB1>(m[s]));
+#pragma unroll
+      for (int s = 0; s < NS; ++s) m[s] = OpMaxNonNeg::f(m[s], dpp<0x4E>(m[s]));
+#pragma unroll
+      for (int s = 0; s < NS; ++s) m[s] = OpMaxNonNeg::f(m[s], dpp<0x141>(m[s]));
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int r = row_idx(s);
+        const float mf = OpMaxNonNeg::f(m[s], kTinyAmax);
+        const float inv = div127_by(mf);
+        uint32_t c4 = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          c4 |= (static_cast<uint32_t>(static_cast<int32_t>(__builtin_rintf(S[s][j] * inv))) & 0xffu) << (8 * j);
+        __builtin_nontemporal_store(c4, reinterpret_cast<uint32_t*>(tb + static_cast<int64_t>(r) * p.V + col));
+        if ((lr & 7) == 0)
+          __builtin_nontemporal_store(cs[KDA ? s : 0] * (mf * (1.0f / 127.0f)), tsc + r * (p.V / 32) + col / 32);
+      }
+    } else if constexpr (!HAD) {
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -1094,7 +1153,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
         const int64_t pos = pos0 + (t - t0);
         if (pos > 0 && pos % p.page_size == 0 && pos != pos_last) {
           const int64_t row = load_index_uniform(p.page_indices, pg_start + (pos - 1) / p.page_size, p.idx64);
-          store_tile(p.pool + (row * p.HV + h) * tile_elems);
+          store_tile(tile_base(row));
         }
       }
     }

@@ -150,6 +150,11 @@ hipError_t launch_qdq(const gdn::Params& p, int64_t units, int qdq, hipStream_t 
     if constexpr (kHadShape<K, VB, NT>) return launch_one<K, VB, NT, VF, KDA, gdn::kQdqHad, ADDR, TIn>(p, units, s);
     return hipErrorInvalidValue;
   }
+  if (qdq == gdn::kQdqHadPacked) {   // packed tiles: one layout, so VF is not instantiated
+    if constexpr (kHadShape<K, VB, NT> && !VF)
+      return launch_one<K, VB, NT, false, KDA, gdn::kQdqHadPacked, ADDR, TIn>(p, units, s);
+    return hipErrorInvalidValue;
+  }
   return launch_one<K, VB, NT, VF, KDA, gdn::kQdqNone, ADDR, TIn>(p, units, s);
 }
 
@@ -253,6 +258,15 @@ int check_options(const gdn_options* o, int K, int V, Kind kind) {
                   o->block_v, V);
     if (K != 128) return fail(GDN_ERR_UNSUPPORTED, "the int8_hadamard32 codec is compiled for K=128 (got K=%d)", K);
   }
+  if (o->state_storage != GDN_STORAGE_F32 && o->state_storage != GDN_STORAGE_I8H32)
+    return fail(GDN_ERR_INVALID, "state_storage must be GDN_STORAGE_F32 or GDN_STORAGE_I8H32 (got %d)",
+                o->state_storage);
+  if (o->state_storage == GDN_STORAGE_I8H32) {
+    if (o->qdq != GDN_QDQ_INT8_HADAMARD32)
+      return fail(GDN_ERR_INVALID, "state_storage I8H32 holds int8_hadamard32 codes: qdq must be INT8_HADAMARD32");
+    if (o->state_layout != GDN_K_FIRST)
+      return fail(GDN_ERR_UNSUPPORTED, "packed tiles have one layout ([K][V] codes): state_layout must be K_FIRST");
+  }
   return GDN_OK;
 }
 
@@ -301,7 +315,9 @@ int run(Kind kind, const gdn::Params& p, int K, int32_t T, const gdn_options* o,
   const int64_t units = static_cast<int64_t>(p.B) * p.HV * p.nvb;
   if (units > 0x7fffffffLL) return fail(GDN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)units);
   const int qdq = o->qdq == GDN_QDQ_FP8_E4M3_TILE ? gdn::kQdqTile
-                  : o->qdq == GDN_QDQ_INT8_HADAMARD32 ? gdn::kQdqHad : gdn::kQdqNone;
+                  : o->qdq == GDN_QDQ_INT8_HADAMARD32
+                      ? (o->state_storage == GDN_STORAGE_I8H32 ? gdn::kQdqHadPacked : gdn::kQdqHad)
+                      : gdn::kQdqNone;
   const Sel sel{o->state_layout == GDN_V_FIRST, qdq, o->io_dtype == GDN_BF16};
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err = hipErrorInvalidValue;
@@ -344,6 +360,7 @@ void gdn_options_init(gdn_options* o) {
   o->quantize_initial = 0;
   o->readout = GDN_READOUT_WORKING;
   o->slots = nullptr;
+  o->state_storage = GDN_STORAGE_F32;
 }
 
 int gdn_decode_pooled(const void* q, const void* k, const void* v, const void* a, const void* b,
@@ -656,6 +673,11 @@ int gdn_check_paged_varlen(const int32_t* cu_seqlens, const void* page_indices, 
 }
 
 int gdn_checked_build(void) { return kChecked ? 1 : 0; }
+
+int64_t gdn_packed_tile_bytes(int32_t K, int32_t V) {
+  if (K <= 0 || V <= 0 || V % 32 != 0) return -1;
+  return static_cast<int64_t>(K) * V + 4 * static_cast<int64_t>(K) * (V / 32);
+}
 
 int gdn_supported_head_dims(int32_t* pairs, int cap) {
   const int n = static_cast<int>(sizeof(kHeads) / sizeof(kHeads[0]));

@@ -37,6 +37,11 @@ Tolerances (readings of the stated contract, listed in the design doc):
   bound that holds for any code choice; so the fraction of rotated
   coordinates that differ by more than a quarter step (a different code)
   must stay below 1e-3.
+* packed int8_hadamard32 pools: the written tiles, decoded, meet the codec
+  bound above; their codes equal the oracle's encoding of its final state
+  except for at most 1e-3 of them, each off by one (a rounding decided the
+  other way), and their scales agree to 1e-5 relative except in at most 1 %
+  of the groups (those an earlier such rounding moved), never by 1 % or more.
 """
 import math
 
@@ -383,4 +388,92 @@ def run_and_check(w, seqs=None, report=None, pool=None, snapshot=True, check_all
     assert sorted(ref_written) == sorted(set(writes))
     if snap is not None:
         check_untouched(snap, pool, all_writes)
+    return report, out, pool
+
+
+# ---------------------------------------------------------------- packed int8_hadamard32 pools
+
+def make_packed_pool(w, device="cuda", rows=None):
+    """Packed pool [rows, HV, tile bytes] for workload ``w`` (K_FIRST, codec): the oracle's encoding of
+    make_pool's fp32 states for ``rows`` (all if None); the other rows hold random codes with positive scales."""
+    K, V, HV, n = w.K, w.V, w.HV, w.num_rows
+    tb = ohad.packed_tile_bytes(K, V)
+    g = torch.Generator(device=device)
+    g.manual_seed(w.pool_seed + 7)
+    packed = torch.randint(0, 256, (n, HV, tb), dtype=torch.uint8, device=device, generator=g)
+    sc = torch.empty((n, HV, K * V // 32), dtype=torch.float32, device=device).uniform_(1e-3, 1e-2, generator=g)
+    packed[:, :, K * V:] = sc.view(torch.uint8)
+    rows = list(range(n)) if rows is None else sorted(set(rows))
+    if rows:
+        fp32 = wl.make_pool(w, device)
+        idx = torch.tensor(rows, dtype=torch.int64, device=device)
+        tiles = fp32.index_select(0, idx).cpu().numpy().astype(np.float64)
+        del fp32
+        code, scale = ohad.int8_hadamard32_encode(tiles.reshape(-1, K, V), "float32")
+        t = ohad.pack_tiles(code.reshape(len(rows), HV, K, V), scale.reshape(len(rows), HV, K, V // 32))
+        packed[idx] = torch.from_numpy(t).to(device)
+    return packed
+
+
+def gather_packed(pool, rows, K, V):
+    """{row: (codes int8 [HV, K, V], scales [HV, K, V / 32])} read back from a packed pool."""
+    rows = sorted(set(rows))
+    if not rows:
+        return {}
+    t = pool.index_select(0, torch.tensor(rows, dtype=torch.int64, device=pool.device)).cpu().numpy()
+    return {r: ohad.unpack_tiles(t[i], K, V) for i, r in enumerate(rows)}
+
+
+def run_and_check_packed(w, seqs=None, report=None, pool=None, **over):
+    """Parity of a call on a packed pool: outputs as for the codec on fp32 states; the written tiles,
+    decoded, as the codec's states; their codes and scales against the oracle's encoding of its final
+    states; every other byte of the pool unchanged."""
+    assert w.options.get("qdq") == "int8_hadamard32" and w.state_layout == "K_FIRST"
+    report = report if report is not None else Report()
+    d = device_inputs(w)
+    all_reads, all_writes = rows_for(w)
+    reads, writes = rows_for(w, seqs)
+    if pool is None:
+        pool = make_packed_pool(w, "cuda", rows=all_reads)
+    before = {r: ohad.int8_hadamard32_decode(c, s) for r, (c, s) in gather_packed(pool, reads, w.K, w.V).items()}
+    snap = pool.clone()
+    out = gpu_call(w, pool, d, **over)
+    torch.cuda.synchronize()
+    trace = {}
+    ref_out, ref_written = oracle_call(w, before, seqs=seqs, trace=trace, **over)
+    seq_list = list(range(w.B)) if seqs is None else list(seqs)
+    trows = token_rows(w, seq_list)
+    out_b, seq_b = qdq_bounds(w, trace, seq_list)
+    full = np.zeros(ref_out.shape)
+    for t, bnd in out_b.items():
+        full[t] = bnd
+    if len(trows):
+        compare_outputs(out, ref_out, w, trows, report, qdq_bound=full[trows])
+    state_bound = {row: seq_b[b][i] for b in seq_list if b in seq_b for i, row in written_rows(w, b)}
+    got = gather_packed(pool, list(ref_written), w.K, w.V)
+    compare_states({r: ohad.int8_hadamard32_decode(c, s) for r, (c, s) in got.items()}, ref_written, report,
+                   qdq_bound=state_bound, layout="K_FIRST", codec="int8_hadamard32")
+    flips, total, worst_scale, off_scales, groups = 0, 0, 0.0, 0, 0
+    for r, ref in ref_written.items():
+        code_e, scale_e = ohad.int8_hadamard32_encode(ref, "float32")
+        code_g, scale_g = got[r]
+        dc = np.abs(code_g.astype(np.int32) - code_e.astype(np.int32))
+        assert dc.max() <= 1, f"row {r}: a code differs by {dc.max()}"
+        flips += int(np.sum(dc))
+        total += dc.size
+        pos = scale_e > 0
+        rel = np.abs(scale_g[pos] - scale_e[pos]) / scale_e[pos]
+        worst_scale = max(worst_scale, float(rel.max()))
+        off_scales += int(np.sum(rel > 1e-5))
+        groups += int(rel.size)
+        assert np.all(scale_g[~pos] < 1e-30)
+    report.add("packed_code_flip_frac", flips / max(total, 1))
+    report.add("packed_scale_max_rel", worst_scale)
+    assert flips / max(total, 1) < 1e-3, f"{flips} of {total} codes differ"
+    # a code rounded the other way at an earlier token moves that group's next amax (so its scale) by
+    # up to about a step, 1/127 of it; such groups must stay rare, like the flips themselves
+    assert worst_scale < 1e-2, f"scale relative error {worst_scale}"
+    assert off_scales <= max(1, groups // 100), f"{off_scales} of {groups} scales differ by more than 1e-5"
+    assert sorted(ref_written) == sorted(set(writes))
+    check_untouched(snap, pool, all_writes)
     return report, out, pool

@@ -23,7 +23,7 @@ def declared_functions():
     for path in HEADERS:
         text = open(path).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        for m in re.finditer(r"^\s*(?:const\s+)?(?:int|void|char)\s*\*?\s*(\w+)\s*\(", text, flags=re.M):
+        for m in re.finditer(r"^\s*(?:const\s+)?(?:int64_t|int|void|char)\s*\*?\s*(\w+)\s*\(", text, flags=re.M):
             names.append(m.group(1))
     return names
 
@@ -31,7 +31,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"gdn_decode_pooled", "gdn_decode_paged", "kda_decode_pooled", "gdn_status_string",
-            "gdn_check_paged", "gdn_checked_build"} <= set(names)
+            "gdn_check_paged", "gdn_checked_build", "gdn_packed_tile_bytes"} <= set(names)
     for path, checked in ((rsd.LIB_PATH, 0), (rsd.CHECKED_LIB_PATH, 1)):
         lib = bnd.load_library(path)
         for n in names:
@@ -91,6 +91,22 @@ def test_pooled_argument_errors():
     assert _pooled(lib, scale=float("inf")) == bnd.GDN_ERR_INVALID
     # an empty call (T = 0 with cu_seqlens) launches nothing and succeeds
     assert _pooled(lib, T=0) == bnd.GDN_OK
+
+
+@no_gpu
+def test_packed_storage_argument_errors():
+    lib = rsd.load_library()
+    assert bnd._options().state_storage == bnd.GDN_STORAGE_F32
+    assert rsd.packed_tile_bytes(128, 128) == 128 * 128 + 4 * 128 * 4 == 18432
+    assert lib.gdn_packed_tile_bytes(128, 48) == -1
+    with pytest.raises(ValueError):
+        rsd.packed_tile_bytes(128, 48)
+    assert _pooled(lib, state_storage=1) == bnd.GDN_ERR_INVALID                 # packed needs the codec
+    assert "INT8_HADAMARD32" in lib.gdn_last_error().decode()
+    assert _pooled(lib, state_storage=1, qdq=1) == bnd.GDN_ERR_INVALID
+    assert _pooled(lib, state_storage=1, qdq=2, state_layout=1) == bnd.GDN_ERR_UNSUPPORTED
+    assert _pooled(lib, state_storage=2, qdq=2) == bnd.GDN_ERR_INVALID
+    assert _pooled(lib, state_storage=1, qdq=2, T=0) == bnd.GDN_OK               # accepted (nothing to launch)
 
 
 @no_gpu

@@ -469,3 +469,80 @@ def test_kda_prefill_strong_decay():
     w.inputs["a_log"] = torch.full_like(w.inputs["a_log"], float(np.log(16.0)))
     rep, _, _ = P.run_and_check(w)
     _report("kda_prefill_strong_decay", rep)
+
+
+# ---------------------------------------------------------------- packed int8_hadamard32 pools (codes + scales)
+
+CODEC = dict(qdq="int8_hadamard32", block_v=64)
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("io", [torch.bfloat16, torch.float32])
+def test_packed_pooled_small(kind, io):
+    mk = wl.gdn_pooled if kind == "gdn" else wl.kda_pooled
+    w = mk(6, 2, 4, 128, 128, lengths=[4, 1, 0, 9, 2, 3], num_slots=8, state_layout="K_FIRST", io_dtype=io,
+           seed=71, **CODEC)
+    rep, _, _ = P.run_and_check_packed(w)
+    _report(f"packed/{kind}/{io}", rep)
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("idx", [torch.int32, torch.int64])
+def test_packed_paged(kind, idx):
+    w = wl.paged(kind, 24, 2, 4, 128, 128, max_prefix=40, page_size=4, share_frac=0.3, state_layout="K_FIRST",
+                 index_dtype=idx, seed=72, **CODEC)
+    rep, _, _ = P.run_and_check_packed(w)
+    _report(f"packed_paged/{kind}/{idx}", rep)
+    suffix = np.array([0, 1, 2, 3, 4, 5, 8, 9, 7, 1, 4, 0, 6, 2, 9, 3])
+    w = wl.paged(kind, len(suffix), 2, 4, 128, 128, max_prefix=30, page_size=4, share_frac=0.3,
+                 suffix_lengths=suffix, state_layout="K_FIRST", index_dtype=idx, seed=73, **CODEC)
+    rep, _, _ = P.run_and_check_packed(w)
+    _report(f"packed_paged_varlen/{kind}/{idx}", rep)
+
+
+@pytest.mark.parametrize("extra", [dict(readout="stored"), dict(quantize_initial=True), dict(V=256),
+                                   dict(use_qk_l2norm=False, scale=0.2)])
+def test_packed_options(extra):
+    extra = dict(extra)
+    V = extra.pop("V", 128)
+    w = wl.gdn_pooled(5, 1, 2, 128, V, lengths=[2, 7, 1, 0, 3], num_slots=6, state_layout="K_FIRST", seed=74,
+                      **CODEC, **{k: v for k, v in extra.items() if k in ("readout", "quantize_initial")})
+    over = {k: v for k, v in extra.items() if k not in ("readout", "quantize_initial")}
+    rep, _, _ = P.run_and_check_packed(w, **over)
+    _report(f"packed_opts/{extra}/V{V}", rep)
+
+
+def test_packed_equals_fp32_codec_path():
+    """The packed pool and an fp32 pool holding its decoded states give the same outputs and, decoded,
+    the same states (the registers start from code * scale either way; float32 rounding apart)."""
+    from oracle import hadamard as ohad
+    w = wl.gdn_pooled(8, 2, 4, 128, 128, lengths=[3, 1, 4, 2, 5, 1, 2, 6], num_slots=10, state_layout="K_FIRST",
+                      seed=75, **CODEC)
+    d = P.device_inputs(w)
+    packed = P.make_packed_pool(w, "cuda")
+    tiles = packed.cpu().numpy()
+    code, scale = ohad.unpack_tiles(tiles, w.K, w.V)
+    fp32 = torch.from_numpy(ohad.int8_hadamard32_decode(code.reshape(-1, w.K, w.V), scale.reshape(-1, w.K, w.V // 32))
+                            .reshape(w.pool_shape()).astype(np.float32)).cuda()
+    out_p = P.gpu_call(w, packed, d)
+    out_f = P.gpu_call(w, fp32, d)
+    torch.cuda.synchronize()
+    a, b = out_p.float(), out_f.float()
+    assert float((a - b).abs().max()) <= 2e-3 * float(b.abs().max())
+    assert float((a - b).norm() / b.norm()) < 1e-3
+    c2, s2 = ohad.unpack_tiles(packed.cpu().numpy(), w.K, w.V)
+    dec = ohad.int8_hadamard32_decode(c2.reshape(-1, w.K, w.V), s2.reshape(-1, w.K, w.V // 32)).reshape(w.pool_shape())
+    ref = fp32.cpu().numpy().astype(np.float64)
+    rows = sorted(set(P.rows_for(w)[1]))
+    err = np.abs(dec[rows] - ref[rows]).max() / np.abs(ref[rows]).max()
+    assert err < 2e-2, err          # a code flip moves an element by up to a step / sqrt(32) of the group
+
+
+def test_packed_b512_t4_sampled():
+    w = wl.gdn_pooled(512, 16, 32, 128, 128, lengths=np.full(512, 4), num_slots=1024, state_layout="K_FIRST",
+                      seed=1008, **CODEC)
+    seqs = sorted(np.random.default_rng(9).choice(w.B, 24, replace=False).tolist())
+    reads, _ = P.rows_for(w, seqs)
+    pool = P.make_packed_pool(w, "cuda", rows=reads)
+    rep, _, _ = P.run_and_check_packed(w, seqs=seqs, pool=pool)
+    _report("packed/b512_t4_sampled", rep)
