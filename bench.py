@@ -48,8 +48,11 @@ def source_hash(chunked=False):
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w):
-    """State read+write for every (sequence, head) with a non-empty suffix, plus per-token I/O."""
+def algorithmic_bytes(w, packed=False):
+    """State read+write for every (sequence, head) with a non-empty suffix, plus per-token I/O.
+
+    A packed int8_hadamard32 pool moves K V code bytes and K V / 32 float32 scales per tile instead
+    of K V float32 states."""
     import numpy as np
     import torch
     esz = 2 if w.io_dtype == torch.bfloat16 else 4
@@ -58,12 +61,13 @@ def algorithmic_bytes(w):
         active = w.B
     else:
         active = int(np.sum(np.diff(w.inputs["cu_seqlens"].numpy()) > 0))
-    state = 2 * active * w.HV * w.K * w.V * 4
+    tile = (w.K * w.V + 4 * w.K * (w.V // 32)) if packed else w.K * w.V * 4
+    state = 2 * active * w.HV * tile
     if w.kind.endswith("paged_varlen"):
         # one tile read per sequence; every page a suffix fills or ends on is written
         from tests import parity as P
         n_writes = len(P.rows_for(w)[1])
-        state = (active + n_writes) * w.HV * w.K * w.V * 4
+        state = (active + n_writes) * w.HV * tile
     T = w.T
     per_tok = 2 * w.HK * w.K * esz + w.HV * w.V * esz + w.HV * w.V * osz
     if w.kind.startswith("kda"):
@@ -240,6 +244,7 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir, commands):
 def cpu_baseline(w, pool, budget_s):
     """Time the oracle on the first sequences of the workload until about ``budget_s`` seconds."""
     import numpy as np
+    import torch
     from threadpoolctl import threadpool_limits
     from tests import parity as P
 
@@ -254,7 +259,12 @@ def cpu_baseline(w, pool, budget_s):
             start = done % len(seqs_all)
             seqs = seqs_all[start:start + batch]
             r, _ = P.rows_for(w, seqs)
-            rows = P.gather_rows(pool, r)
+            if pool.dtype == torch.uint8:        # packed codes and scales: the oracle takes the states
+                from oracle import hadamard as ohad
+                rows = {k: ohad.int8_hadamard32_decode(c, sc) for k, (c, sc) in
+                        P.gather_packed(pool, r, w.K, w.V).items()}
+            else:
+                rows = P.gather_rows(pool, r)
             t0 = time.perf_counter()
             P.oracle_call(w, rows, seqs=seqs)
             t_used += time.perf_counter() - t0
@@ -282,6 +292,9 @@ def main():
     ap.add_argument("--layout", default=None, help="override the pool layout (K_FIRST / V_FIRST); a layout other than the workload's own gets a +LAYOUT suffix on its name")
     ap.add_argument("--qdq", default=None, choices=["none", "fp8_e4m3_tile", "int8_hadamard32"],
                     help="override the workload's state quantisation (the workload name gets a +qdq suffix)")
+    ap.add_argument("--storage", default="f32", choices=["f32", "i8h32"],
+                    help="i8h32: a packed int8_hadamard32 pool (codes + scales; implies --qdq int8_hadamard32 and a "
+                         "K_FIRST layout; the workload name gets a +i8h32 suffix)")
     ap.add_argument("--token-path", action="store_true",
                     help="run a chunked-prefill workload through the token-by-token paged call instead")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
@@ -324,6 +337,11 @@ def main():
     maker = wl.NAMED[args.workload]
     paged_makers = ("paged_gdn_b256", "paged_kda_b256", "paged_gdn_varlen_b256_t4", "paged_gdn_prefill_b16_t1024",
                     "paged_kda_prefill_b16_t1024")
+    packed = args.storage == "i8h32"
+    if packed:
+        if args.qdq not in (None, "int8_hadamard32") or args.layout not in (None, "K_FIRST"):
+            raise SystemExit("--storage i8h32 holds int8_hadamard32 codes in a K_FIRST layout")
+        args.qdq, args.layout = "int8_hadamard32", "K_FIRST"
     if args.workload in paged_makers:
         default_layout = inspect.signature(maker).parameters["state_layout"].default
         w = maker(state_layout=args.layout) if args.layout else maker()
@@ -344,13 +362,16 @@ def main():
             w.options["qdq"] = args.qdq
             w.options.setdefault("block_v", 64)
         w.name = f"{w.name}+{args.qdq}"
+    if packed:
+        w.name = f"{w.name}+i8h32"
     d = P.device_inputs(w, dev)
-    pool = wl.make_pool(w, dev)
+    # (a packed pool for timing: seeded random codes and scales)
+    pool = P.make_packed_pool(w, dev, rows=[]) if packed else wl.make_pool(w, dev)
     out = torch.empty((w.T, w.HV, w.V), dtype=w.out_dtype, device=dev)
     flush = None if args.no_flush else torch.empty(512 * 1024 * 1024, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     print(f"[bench] workload {w.name} layout {w.state_layout} pool {tuple(pool.shape)} "
-          f"({pool.numel() * 4 / 2**30:.1f} GiB)", file=sys.stderr, flush=True)
+          f"({pool.numel() * pool.element_size() / 2**30:.1f} GiB)", file=sys.stderr, flush=True)
 
     def step(i):
         if flush is not None:
@@ -378,7 +399,7 @@ def main():
     med_ms = sorted(times_ms)[len(times_ms) // 2]
 
     tokens = w.T
-    state_b, io_b = algorithmic_bytes(w)
+    state_b, io_b = algorithmic_bytes(w, packed)
     achieved = (state_b + io_b) / (mean_ms * 1e-3) / 1e9
     traffic = load_traffic(w.name, w.chunked)
     res = {
@@ -397,7 +418,8 @@ def main():
         "config": {"workload": w.name, "kind": w.kind, "B": w.B, "HK": w.HK, "HV": w.HV, "K": w.K, "V": w.V,
                    "tokens_per_step": tokens, "state_layout": w.state_layout,
                    "io_dtype": str(w.io_dtype).replace("torch.", ""), "pool_rows": w.num_rows,
-                   "cache_flush_between_steps": flush is not None, **{k: v for k, v in w.options.items()}},
+                   "cache_flush_between_steps": flush is not None, "state_storage": args.storage,
+                   **{k: v for k, v in w.options.items()}},
         "state_pool_gbps": round(state_b / (mean_ms * 1e-3) / 1e9, 1),
         "state_pool_pct_peak": round(100 * state_b / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
         "ms_per_step_median": round(med_ms, 5),
