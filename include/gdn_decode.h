@@ -117,10 +117,11 @@ enum gdn_readout { GDN_READOUT_WORKING = 0, GDN_READOUT_STORED = 1 };
  * pages (modelopt ... linear_attention.config, LinearAttentionConfig)
  * describe the codec as a quantise/dequantise emulation with no
  * compressed-storage claim.  Each (row, value head) tile is
- * gdn_packed_tile_bytes(K, V) bytes: K V int8 codes in [K][V] order,
- * then K V / 32 float32 scales in [K][V / 32] order; code c[k][v] and
- * scale s[k][g] stand for the state row S[k][32 g .. 32 g + 31] =
- * (c[k][32 g ..] H) * s[k][g] / 32 (H the +-1 Sylvester Hadamard matrix of
+ * gdn_packed_tile_bytes(K, V) bytes: K V int8 codes in [V / 32][K][32]
+ * order (one 32-value group of every key row after another), then
+ * K V / 32 float32 scales in [V / 32][K] order; codes c[g][k][0..31] and
+ * scale s[g][k] stand for the state row S[k][32 g .. 32 g + 31] =
+ * (c[g][k] H) * s[g][k] / 32 (H the +-1 Sylvester Hadamard matrix of
  * order 32), so s is amax/127 of the group in the +-1 Hadamard basis.
  * state_pool then points to rows * HV such tiles (4-byte aligned) and is
  * read and written as such.  Requires qdq = GDN_QDQ_INT8_HADAMARD32 (else

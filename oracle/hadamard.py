@@ -38,7 +38,8 @@ amax|z| / 127 of group g in the +-1 Hadamard basis z = x H, and stands for
 (code H) * scale / 32 -- exactly what int8_hadamard32_qdq returns.
 ``int8_hadamard32_encode`` / ``int8_hadamard32_decode`` convert, and
 ``pack_tiles`` / ``unpack_tiles`` lay one (row, head) tile out as its K V
-code bytes followed by its K V / 32 float32 scales.
+code bytes in [V / 32][K][32] order (each group's codes for all key rows
+together) followed by its K V / 32 float32 scales in [V / 32][K] order.
 
 Pins (tests/test_oracle_hadamard.py): H / sqrt(32) is orthonormal and
 symmetric, the butterfly transform equals the matrix product, the folded
@@ -154,12 +155,16 @@ def packed_tile_bytes(K, V):
 
 
 def pack_tiles(code, scale):
-    """codes [..., K, V] int8 and scales [..., K, V / 32] -> bytes [..., packed_tile_bytes(K, V)] (uint8)."""
+    """codes [..., K, V] int8 and scales [..., K, V / 32] -> bytes [..., packed_tile_bytes(K, V)] (uint8):
+    the codes in [V / 32][K][32] order, then the scales in [V / 32][K] order."""
     code = np.asarray(code, dtype=np.int8)
     lead, (K, V) = code.shape[:-2], code.shape[-2:]
-    c = code.reshape(lead + (K * V,)).view(np.uint8)
-    s = np.ascontiguousarray(np.asarray(scale, dtype=np.float32).reshape(lead + (K * (V // GROUP),)))
-    return np.concatenate([c, s.view(np.uint8).reshape(lead + (4 * K * (V // GROUP),))], axis=-1)
+    G = V // GROUP
+    cg = np.moveaxis(code.reshape(lead + (K, G, GROUP)), -2, -3)           # [..., G, K, 32]
+    c = np.ascontiguousarray(cg).reshape(lead + (K * V,)).view(np.uint8)
+    sg = np.moveaxis(np.asarray(scale, dtype=np.float32).reshape(lead + (K, G)), -1, -2)   # [..., G, K]
+    s = np.ascontiguousarray(sg).reshape(lead + (K * G,))
+    return np.concatenate([c, s.view(np.uint8).reshape(lead + (4 * K * G,))], axis=-1)
 
 
 def unpack_tiles(tiles, K, V):
@@ -168,6 +173,9 @@ def unpack_tiles(tiles, K, V):
     lead = t.shape[:-1]
     if t.shape[-1] != packed_tile_bytes(K, V):
         raise ValueError("tile size does not match K and V")
-    code = t[..., :K * V].copy().view(np.int8).reshape(lead + (K, V))
-    scale = t[..., K * V:].copy().view(np.float32).reshape(lead + (K, V // GROUP)).astype(np.float64)
+    G = V // GROUP
+    cg = t[..., :K * V].copy().view(np.int8).reshape(lead + (G, K, GROUP))
+    code = np.ascontiguousarray(np.moveaxis(cg, -3, -2)).reshape(lead + (K, V))
+    sg = t[..., K * V:].copy().view(np.float32).reshape(lead + (G, K))
+    scale = np.ascontiguousarray(np.moveaxis(sg, -1, -2)).astype(np.float64)
     return code, scale

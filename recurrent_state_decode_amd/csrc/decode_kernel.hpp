@@ -390,12 +390,15 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   // Register arrangement: V_FIRST rows (value columns) for a V_FIRST pool,
   // except with the int8_hadamard32 codec, which needs each key row's values
   // in lanes; the pool layout VF itself only shapes the tile's load and store.
-  // PACKED: each (row, head) tile of the pool is K V int8 codes ([K][V], in
-  // the +-1 Hadamard basis of each 32-value group) followed by K V / 32
-  // float32 scales; the codes load straight into the rotated registers.
+  // PACKED: each (row, head) tile of the pool is K V int8 codes in
+  // [V / 32][K][32] order (the +-1 Hadamard basis of each 32-value group;
+  // a group's codes for all key rows contiguous) followed by K V / 32
+  // float32 scales in [V / 32][K] order; the codes load straight into the
+  // rotated registers.  A workgroup's V-block is then whole groups: every
+  // line it reads or writes is its own.
   constexpr bool PACKED = QDQ == kQdqHadPacked;
   constexpr bool HAD = QDQ == kQdqHad || PACKED;
-  static_assert(!PACKED || !VF, "packed tiles have one layout ([K][V] codes)");
+  static_assert(!PACKED || !VF, "packed tiles have one layout");
   constexpr bool AV = VF && !HAD;
   using Cfg = Tile<K, VB, NT, AV>;
   constexpr int NW = Cfg::NW, LR = Cfg::LR, RPW = Cfg::RPW, NS = Cfg::NS, LB = Cfg::LB;
@@ -426,7 +429,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   constexpr bool TRANS = VF && HAD;
   constexpr int LD = K + 1;
   __shared__ float s_t[TRANS ? VB * LD : 1];
-  static_assert(!HAD || (K == 128 && VB == 64 && NT == 256 && LR == 16 && EV == 4 && NS == K / 16 && VPL == 1),
+  // the codec works on 8-lane groups of 32 values; the V_FIRST transpose
+  // through LDS is written for the 64-column, 4-wave shape
+  static_assert(!HAD || (K == 128 && EV == 4 && VPL == 1 && VB % 32 == 0 &&
+                         (!TRANS || (VB == 64 && NT == 256 && LR == 16 && NS == K / 16))),
                 "int8_hadamard32 codec shape");
 
   const TIn* __restrict__ gq = static_cast<const TIn*>(p.q);
@@ -632,12 +638,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
     // 4 codes (one dword) and their group's scale per row: R = code * scale
     const unsigned char* sb = reinterpret_cast<const unsigned char*>(src);
     const float* sc = reinterpret_cast<const float*>(sb + tile_elems);
-    const int col = vb * VB + 4 * lr;
+    const int col = vb * VB + 4 * lr, grp = col / 32;
+    const unsigned char* gb = sb + grp * (K * 32) + col % 32;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int r = row_idx(s);
-      const uint32_t c4 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sb + static_cast<int64_t>(r) * p.V + col));
-      const float scale = __builtin_nontemporal_load(sc + r * (p.V / 32) + col / 32);
+      const uint32_t c4 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(gb + r * 32));
+      const float scale = __builtin_nontemporal_load(sc + grp * K + r);
 #pragma unroll
       for (int j = 0; j < 4; ++j) S[s][j] = static_cast<float>(static_cast<int8_t>(c4 >> (8 * j))) * scale;
     }
@@ -936,13 +943,15 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   // non-temporal stores like the loads: the row is not read again by this call
   auto store_tile = [&](float* row_base) {
     if constexpr (PACKED) {
-      // Every token ends with had_quant, so the registers hold code * c per
-      // (row, group): the group's amax is 127 c up to one rounding and
-      // rint(R * 127 / amax) gives the codes back exactly.  The stored scale
-      // carries the workgroup's decay scale: true R = scale * code.
+      // The registers hold the last token's state, either rounded already
+      // (code * c per (row, group): the group's amax is 127 c up to one
+      // rounding, so rint(R * 127 / amax) gives the codes back exactly) or
+      // not (then this is that token's rounding).  The stored scale carries
+      // the workgroup's decay scale: true R = scale * code.
       unsigned char* tb = reinterpret_cast<unsigned char*>(row_base);
       float* tsc = reinterpret_cast<float*>(tb + tile_elems);
-      const int col = vb * VB + 4 * lr;
+      const int col = vb * VB + 4 * lr, grp = col / 32;
+      unsigned char* gb = tb + grp * (K * 32) + col % 32;
       float m[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s)
@@ -964,9 +973,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           c4 |= (static_cast<uint32_t>(static_cast<int32_t>(__builtin_rintf(S[s][j] * inv))) & 0xffu) << (8 * j);
-        __builtin_nontemporal_store(c4, reinterpret_cast<uint32_t*>(tb + static_cast<int64_t>(r) * p.V + col));
-        if ((lr & 7) == 0)
-          __builtin_nontemporal_store(cs[KDA ? s : 0] * (mf * (1.0f / 127.0f)), tsc + r * (p.V / 32) + col / 32);
+        __builtin_nontemporal_store(c4, reinterpret_cast<uint32_t*>(gb + r * 32));
+        if ((lr & 7) == 0) __builtin_nontemporal_store(cs[KDA ? s : 0] * (mf * (1.0f / 127.0f)), tsc + grp * K + r);
       }
     } else if constexpr (!HAD) {
 #pragma unroll
@@ -1128,7 +1136,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
         }
 
       if constexpr (QDQ != kQdqNone) {
-        quantize();
+        // (packed tiles: the store after the last token encodes the same
+        // codes and scales from the unrounded registers, so that token's
+        // rounding is skipped unless the readout needs the rounded state)
+        if (!(PACKED && !stored && t == t1 - 1)) quantize();
         if (stored) {
           // o = q_hat^T S after rounding
           float q2[NKEY];

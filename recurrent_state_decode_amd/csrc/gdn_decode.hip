@@ -112,7 +112,11 @@ struct Shape {
 
 bool is_kda(Kind k) { return k == Kind::KdaPooled || k == Kind::KdaPaged || k == Kind::KdaPagedVar; }
 
-Shape shape_for(int K, bool vfirst, bool qdq, int64_t T, int64_t B, bool kda) {
+// Packed int8_hadamard32 tiles, about one token per sequence.
+constexpr int kPackedVB = 64, kPackedNT = 256;
+
+Shape shape_for(int K, bool vfirst, bool qdq, int64_t T, int64_t B, bool kda, bool packed) {
+  if (K == 128 && packed && 2 * T <= 3 * B) return Shape{kPackedVB, kPackedNT};
   if (K == 128 && !qdq && 2 * T <= 3 * B) return vfirst ? Shape{kda ? 16 : 8, 128} : Shape{32, 256};
   if (K == 128 && !qdq && !kda && vfirst) return Shape{32, 256};
   if (K == 128) return Shape{64, 256};
@@ -219,6 +223,31 @@ hipError_t launch_noqdq(Kind kind, const gdn::Params& p, int64_t units, Sel sel,
   return hipErrorInvalidValue;
 }
 
+// Packed int8_hadamard32 tiles in a narrower shape (single-token calls): one instantiation per kind and io type.
+template <int VB, int NT>
+hipError_t launch_packed(Kind kind, const gdn::Params& p, int64_t units, Sel sel, hipStream_t s) {
+  auto go = [&](auto kda, auto addr) -> hipError_t {
+    constexpr bool KDA = decltype(kda)::value;
+    constexpr int ADDR = decltype(addr)::value;
+    return sel.bf16 ? launch_one<128, VB, NT, false, KDA, gdn::kQdqHadPacked, ADDR, gdn::bf16_t>(p, units, s)
+                    : launch_one<128, VB, NT, false, KDA, gdn::kQdqHadPacked, ADDR, float>(p, units, s);
+  };
+  using F = std::false_type;
+  using Tr = std::true_type;
+  using Pool = std::integral_constant<int, gdn::kPooled>;
+  using Pg1 = std::integral_constant<int, gdn::kPaged1>;
+  using PgV = std::integral_constant<int, gdn::kPagedVar>;
+  switch (kind) {
+    case Kind::GdnPooled: return go(F{}, Pool{});
+    case Kind::GdnPaged: return go(F{}, Pg1{});
+    case Kind::KdaPooled: return go(Tr{}, Pool{});
+    case Kind::KdaPaged: return go(Tr{}, Pg1{});
+    case Kind::GdnPagedVar: return go(F{}, PgV{});
+    case Kind::KdaPagedVar: return go(Tr{}, PgV{});
+  }
+  return hipErrorInvalidValue;
+}
+
 int check_options(const gdn_options* o, int K, int V, Kind kind) {
   if (!o) return fail(GDN_ERR_INVALID, "options pointer is NULL");
   if (o->io_dtype != GDN_F32 && o->io_dtype != GDN_BF16)
@@ -294,7 +323,8 @@ void fill_common(gdn::Params& p, const gdn_options* o, Kind kind, int32_t B, int
   p.HK = HK;
   p.HV = HV;
   p.V = V;
-  const Shape sh = shape_for(K, o->state_layout == GDN_V_FIRST, o->qdq != GDN_QDQ_NONE, T, B, is_kda(kind));
+  const Shape sh = shape_for(K, o->state_layout == GDN_V_FIRST, o->qdq != GDN_QDQ_NONE, T, B, is_kda(kind),
+                             o->state_storage == GDN_STORAGE_I8H32);
   p.nvb = V / sh.VB;
   p.xcd_shift = 6;   // 64 consecutive work units per XCD
   fast_div_consts(static_cast<uint32_t>(p.nvb), p.div_nvb_m, p.div_nvb_s);
@@ -324,7 +354,11 @@ int run(Kind kind, const gdn::Params& p, int K, int32_t T, const gdn_options* o,
   switch (K) {
     case 16: err = launch_kind<16, 16, 64>(kind, p, units, sel, s); break;
     case 128:
-      switch (shape_for(K, sel.vfirst, sel.qdq != gdn::kQdqNone, T, p.B, is_kda(kind)).VB) {
+      if (sel.qdq == gdn::kQdqHadPacked && 2 * T <= 3 * p.B) {   // the packed single-token shape
+        err = launch_packed<kPackedVB, kPackedNT>(kind, p, units, sel, s);
+        break;
+      }
+      switch (shape_for(K, sel.vfirst, sel.qdq != gdn::kQdqNone, T, p.B, is_kda(kind), false).VB) {
         case 8: err = launch_noqdq<true, 8, 128>(kind, p, units, sel, s); break;
         case 16: err = launch_noqdq<true, 16, 128>(kind, p, units, sel, s); break;
         case 32:

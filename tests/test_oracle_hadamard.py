@@ -153,10 +153,11 @@ def test_pack_layout_and_round_trip():
     scale = rng.uniform(0, 1, (3, 2, 4, 2))
     t = hd.pack_tiles(code, scale)
     assert t.shape == (3, 2, hd.packed_tile_bytes(4, 64)) == (3, 2, 4 * 64 + 4 * 4 * 2)
-    # codes first, row-major [K][V]; then the float32 scales [K][V / 32]
-    assert t[1, 0, 64 + 7] == np.uint8(code[1, 0, 1, 7].view(np.uint8))
+    # codes first in [V / 32][K][32] order; then the float32 scales in [V / 32][K] order
+    assert t[1, 0, 1 * 32 + 7] == np.uint8(code[1, 0, 1, 7].view(np.uint8))            # group 0, row 1
+    assert t[1, 0, 4 * 32 + 2 * 32 + 5] == np.uint8(code[1, 0, 2, 37].view(np.uint8))   # group 1, row 2
     assert t[2, 1, 256:260].view(np.float32)[0] == np.float32(scale[2, 1, 0, 0])
-    assert t[2, 1, 256 + 4 * 3:256 + 4 * 4].view(np.float32)[0] == np.float32(scale[2, 1, 1, 1])
+    assert t[2, 1, 256 + 4 * (4 + 1):256 + 4 * (4 + 2)].view(np.float32)[0] == np.float32(scale[2, 1, 1, 1])
     c2, s2 = hd.unpack_tiles(t, 4, 64)
     assert np.array_equal(c2, code)
     assert np.array_equal(s2, scale.astype(np.float32).astype(np.float64))
