@@ -126,3 +126,96 @@ def e4m3_spacing(y):
     _, ex = np.frexp(a)
     e = np.clip(ex - 1, E4M3_MIN_NORMAL_EXP, 8)
     return np.ldexp(1.0, e - 3)
+
+
+# ---------------------------------------------------------------- packed storage (codes + tile scales)
+#
+# This repository's format (the pages keep fp8 states fake-decoded next to
+# their scales and claim no compressed storage): a state is kept as its
+# E4M3 bytes and its per-tile scales s = amax / 448, and stands for
+# code_value * s -- exactly what tile_qdq returns.
+
+def e4m3_encode_value(v):
+    """Byte (0..255) of E4M3 grid values v (finite, |v| <= 448, on the grid): sign, exponent, mantissa
+    fields; -0.0 gives 0x80."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    sign = np.signbit(v).astype(np.int64) << 7
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))          # a = f * 2^ex, f in [0.5, 1)
+    e = ex - 1                                          # a in [2^e, 2^(e+1))
+    normal = e >= E4M3_MIN_NORMAL_EXP
+    field_e = np.where(normal, e + E4M3_BIAS, 0)
+    mant = np.where(normal, a / np.ldexp(1.0, e) - 1.0, a / 2.0 ** (1 - E4M3_BIAS)) * 8.0
+    code = sign | (field_e.astype(np.int64) << 3) | np.rint(mant).astype(np.int64)
+    return np.where(a > 0, code, sign).astype(np.uint8)
+
+
+def tile_encode(S, block_v=64, precision="float32"):
+    """E4M3 bytes [H, K, V] (uint8) and per-tile scales [H, V // block_v] of S [H, K, V];
+    tile_decode(tile_encode(S)) == tile_qdq(S).  An all-zero tile has scale 0 and codes 0."""
+    S = np.asarray(S, dtype=np.float64)
+    H, K, V = S.shape
+    if V % block_v != 0:
+        raise ValueError("block_v must divide the value head dim")
+    codes = np.zeros((H, K, V), dtype=np.uint8)
+    scales = np.zeros((H, V // block_v))
+    for t, j0 in enumerate(range(0, V, block_v)):
+        for h in range(H):
+            tile = S[h, :, j0:j0 + block_v]
+            if precision == "float64":
+                amax = np.max(np.abs(tile))
+                if amax == 0.0:
+                    continue
+                s = amax / E4M3_MAX
+                y = tile / s
+            elif precision == "float32":
+                x = tile.astype(np.float32)
+                amax = np.max(np.abs(x))
+                if amax == 0.0:
+                    continue
+                inv = np.float32(np.float32(E4M3_MAX) / amax)
+                s = np.float32(amax / np.float32(E4M3_MAX))
+                y = (x * inv).astype(np.float32).astype(np.float64)
+            else:
+                raise ValueError(f"unknown precision {precision!r}")
+            codes[h, :, j0:j0 + block_v] = e4m3_encode_value(e4m3_round(y))
+            scales[h, t] = float(s)
+    return codes, scales
+
+
+def tile_decode(codes, scales, block_v=64):
+    """The state [H, K, V] that E4M3 bytes and per-tile scales stand for: code value * scale."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    vals = e4m3_table()[codes]
+    return vals * np.repeat(np.asarray(scales, dtype=np.float64), block_v, axis=-1)[:, None, :]
+
+
+def fp8_tile_bytes(K, V, block_v=64):
+    """Bytes of one packed (row, head) tile: K V codes, then V / block_v float32 scales padded to 16 bytes."""
+    return K * V + 16 * ((4 * (V // block_v) + 15) // 16)
+
+
+def pack_fp8_tiles(codes, scales, state_layout="K_FIRST", block_v=64):
+    """codes [..., K, V] (logical order) and scales [..., V // block_v] -> bytes [..., fp8_tile_bytes]:
+    the codes in the pool layout's order (K_FIRST [K][V], V_FIRST [V][K]), then the scales."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    lead, (K, V) = codes.shape[:-2], codes.shape[-2:]
+    c = codes if state_layout == "K_FIRST" else np.swapaxes(codes, -1, -2)
+    c = np.ascontiguousarray(c).reshape(lead + (K * V,))
+    nt = V // block_v
+    s = np.zeros(lead + (fp8_tile_bytes(K, V, block_v) - K * V,), dtype=np.uint8)
+    s[..., :4 * nt] = np.ascontiguousarray(np.asarray(scales, dtype=np.float32)).view(np.uint8).reshape(lead + (4 * nt,))
+    return np.concatenate([c, s], axis=-1)
+
+
+def unpack_fp8_tiles(tiles, K, V, state_layout="K_FIRST", block_v=64):
+    """Inverse of pack_fp8_tiles -> (codes uint8 [..., K, V] in logical order, scales float64)."""
+    t = np.ascontiguousarray(np.asarray(tiles, dtype=np.uint8))
+    lead = t.shape[:-1]
+    if t.shape[-1] != fp8_tile_bytes(K, V, block_v):
+        raise ValueError("tile size does not match K, V and block_v")
+    c = t[..., :K * V].reshape(lead + ((K, V) if state_layout == "K_FIRST" else (V, K)))
+    codes = np.ascontiguousarray(c if state_layout == "K_FIRST" else np.swapaxes(c, -1, -2))
+    nt = V // block_v
+    scales = t[..., K * V:K * V + 4 * nt].copy().view(np.float32).reshape(lead + (nt,)).astype(np.float64)
+    return codes, scales

@@ -135,3 +135,54 @@ def test_tile_groups_all_key_rows_and_block_v_value_columns():
     Q3 = e4m3.tile_qdq(S3, 4, "float64")
     assert np.array_equal(Q3[:, :, 4:], base[:, :, 4:])
     assert not np.array_equal(Q3[0, 0, :4], base[0, 0, :4])
+
+
+# ---------------------------------------------------------------- packed storage (codes + tile scales)
+
+def test_encode_value_inverts_the_table_and_matches_torch_bytes():
+    import torch
+    tab = e4m3.e4m3_table()
+    finite = [c for c in range(256) if not np.isnan(tab[c])]
+    assert np.array_equal(e4m3.e4m3_encode_value(tab[finite]), np.array(finite, dtype=np.uint8))
+    vals = tab[finite]
+    ref = torch.tensor(vals, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(e4m3.e4m3_encode_value(vals), ref)
+
+
+@pytest.mark.parametrize("precision", ["float64", "float32"])
+def test_tile_decode_of_encode_is_the_qdq(precision):
+    rng = np.random.default_rng(31)
+    S = rng.standard_normal((3, 5, 128)) * 0.05
+    S[1, :, 64:] = 0.0                                     # an all-zero tile
+    codes, scales = e4m3.tile_encode(S, 64, precision)
+    assert codes.dtype == np.uint8 and scales.shape == (3, 2)
+    assert scales[1, 1] == 0 and np.all(codes[1, :, 64:] == 0)
+    tol = 0 if precision == "float64" else 1e-7 * np.abs(S).max()
+    np.testing.assert_allclose(e4m3.tile_decode(codes, scales, 64), e4m3.tile_qdq(S, 64, precision),
+                               rtol=0, atol=tol + 1e-17)
+    # each non-zero tile holds the top code +-448 and its scale is amax / 448
+    for h in range(3):
+        for t in range(2):
+            if scales[h, t] > 0:
+                assert np.max(np.abs(e4m3.e4m3_table()[codes[h, :, 64 * t:64 * t + 64]])) == 448.0
+                np.testing.assert_allclose(scales[h, t], np.abs(S[h, :, 64 * t:64 * t + 64]).max() / 448,
+                                           rtol=1e-6 if precision == "float32" else 1e-15)
+
+
+@pytest.mark.parametrize("layout", ["K_FIRST", "V_FIRST"])
+def test_fp8_pack_layout_and_round_trip(layout):
+    rng = np.random.default_rng(32)
+    K, V = 4, 128
+    codes = rng.integers(0, 256, (2, 3, K, V)).astype(np.uint8)
+    scales = rng.uniform(0, 1, (2, 3, 2))
+    t = e4m3.pack_fp8_tiles(codes, scales, layout)
+    assert t.shape == (2, 3, e4m3.fp8_tile_bytes(K, V)) == (2, 3, K * V + 16)
+    # element (k, v) at byte k V + v (K_FIRST) or v K + k (V_FIRST); then the float32 scales; zero padding
+    k, v = 3, 77
+    pos = k * V + v if layout == "K_FIRST" else v * K + k
+    assert t[1, 2, pos] == codes[1, 2, k, v]
+    assert t[1, 2, K * V + 4:K * V + 8].view(np.float32)[0] == np.float32(scales[1, 2, 1])
+    assert np.all(t[..., K * V + 8:] == 0)
+    c2, s2 = e4m3.unpack_fp8_tiles(t, K, V, layout)
+    assert np.array_equal(c2, codes)
+    assert np.array_equal(s2, scales.astype(np.float32).astype(np.float64))
