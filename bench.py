@@ -48,11 +48,12 @@ def source_hash(chunked=False):
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, packed=False):
+def algorithmic_bytes(w, storage="f32"):
     """State read+write for every (sequence, head) with a non-empty suffix, plus per-token I/O.
 
-    A packed int8_hadamard32 pool moves K V code bytes and K V / 32 float32 scales per tile instead
-    of K V float32 states."""
+    A packed int8_hadamard32 pool moves K V code bytes and K V / 32 float32 scales per tile, a packed
+    fp8 pool K V code bytes and V / block_v float32 scales (padded to 16 bytes), instead of K V float32
+    states."""
     import numpy as np
     import torch
     esz = 2 if w.io_dtype == torch.bfloat16 else 4
@@ -61,7 +62,12 @@ def algorithmic_bytes(w, packed=False):
         active = w.B
     else:
         active = int(np.sum(np.diff(w.inputs["cu_seqlens"].numpy()) > 0))
-    tile = (w.K * w.V + 4 * w.K * (w.V // 32)) if packed else w.K * w.V * 4
+    if storage == "i8h32":
+        tile = w.K * w.V + 4 * w.K * (w.V // 32)
+    elif storage == "fp8":
+        tile = w.K * w.V + 16 * ((4 * (w.V // w.options.get("block_v", 64)) + 15) // 16)
+    else:
+        tile = w.K * w.V * 4
     state = 2 * active * w.HV * tile
     if w.kind.endswith("paged_varlen"):
         # one tile read per sequence; every page a suffix fills or ends on is written
@@ -259,7 +265,9 @@ def cpu_baseline(w, pool, budget_s):
             start = done % len(seqs_all)
             seqs = seqs_all[start:start + batch]
             r, _ = P.rows_for(w, seqs)
-            if pool.dtype == torch.uint8:        # packed codes and scales: the oracle takes the states
+            if pool.dtype == torch.uint8 and w.options.get("qdq") == "fp8_e4m3_tile":
+                rows = {k: P.decode_fp8(c, sc, w) for k, (c, sc) in P.gather_fp8(pool, r, w).items()}
+            elif pool.dtype == torch.uint8:      # packed codes and scales: the oracle takes the states
                 from oracle import hadamard as ohad
                 rows = {k: ohad.int8_hadamard32_decode(c, sc) for k, (c, sc) in
                         P.gather_packed(pool, r, w.K, w.V).items()}
@@ -292,9 +300,10 @@ def main():
     ap.add_argument("--layout", default=None, help="override the pool layout (K_FIRST / V_FIRST); a layout other than the workload's own gets a +LAYOUT suffix on its name")
     ap.add_argument("--qdq", default=None, choices=["none", "fp8_e4m3_tile", "int8_hadamard32"],
                     help="override the workload's state quantisation (the workload name gets a +qdq suffix)")
-    ap.add_argument("--storage", default="f32", choices=["f32", "i8h32"],
+    ap.add_argument("--storage", default="f32", choices=["f32", "i8h32", "fp8"],
                     help="i8h32: a packed int8_hadamard32 pool (codes + scales; implies --qdq int8_hadamard32 and a "
-                         "K_FIRST layout; the workload name gets a +i8h32 suffix)")
+                         "K_FIRST layout); fp8: a packed fp8 tile pool (E4M3 bytes + tile scales; implies --qdq "
+                         "fp8_e4m3_tile, any layout); the workload name gets a +i8h32 / +fp8 suffix")
     ap.add_argument("--token-path", action="store_true",
                     help="run a chunked-prefill workload through the token-by-token paged call instead")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
@@ -337,11 +346,15 @@ def main():
     maker = wl.NAMED[args.workload]
     paged_makers = ("paged_gdn_b256", "paged_kda_b256", "paged_gdn_varlen_b256_t4", "paged_gdn_prefill_b16_t1024",
                     "paged_kda_prefill_b16_t1024")
-    packed = args.storage == "i8h32"
-    if packed:
+    packed = args.storage != "f32"
+    if args.storage == "i8h32":
         if args.qdq not in (None, "int8_hadamard32") or args.layout not in (None, "K_FIRST"):
             raise SystemExit("--storage i8h32 holds int8_hadamard32 codes in a K_FIRST layout")
         args.qdq, args.layout = "int8_hadamard32", "K_FIRST"
+    elif args.storage == "fp8":
+        if args.qdq not in (None, "fp8_e4m3_tile"):
+            raise SystemExit("--storage fp8 holds fp8_e4m3_tile codes")
+        args.qdq = "fp8_e4m3_tile"
     if args.workload in paged_makers:
         default_layout = inspect.signature(maker).parameters["state_layout"].default
         w = maker(state_layout=args.layout) if args.layout else maker()
@@ -363,7 +376,7 @@ def main():
             w.options.setdefault("block_v", 64)
         w.name = f"{w.name}+{args.qdq}"
     if packed:
-        w.name = f"{w.name}+i8h32"
+        w.name = f"{w.name}+{args.storage}"
     d = P.device_inputs(w, dev)
     # (a packed pool for timing: seeded random codes and scales)
     pool = P.make_packed_pool(w, dev, rows=[]) if packed else wl.make_pool(w, dev)
@@ -399,7 +412,7 @@ def main():
     med_ms = sorted(times_ms)[len(times_ms) // 2]
 
     tokens = w.T
-    state_b, io_b = algorithmic_bytes(w, packed)
+    state_b, io_b = algorithmic_bytes(w, args.storage)
     achieved = (state_b + io_b) / (mean_ms * 1e-3) / 1e9
     traffic = load_traffic(w.name, w.chunked)
     res = {

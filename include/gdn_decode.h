@@ -129,7 +129,18 @@ enum gdn_readout { GDN_READOUT_WORKING = 0, GDN_READOUT_STORED = 1 };
  * GDN_ERR_UNSUPPORTED); results equal those of GDN_STORAGE_F32 with the
  * codec up to float32 rounding, with about 3.6x fewer pool bytes at
  * K = V = 128. */
-enum gdn_storage { GDN_STORAGE_F32 = 0, GDN_STORAGE_I8H32 = 1 };
+/* GDN_STORAGE_FP8_TILE: the fp8 tile QDQ's own codes, again this library's
+ * format (modelopt ... linear_attention.decode, EncodedLinearAttentionTensor,
+ * holds dequantised values beside their scales and claims no compressed
+ * storage).  Each (row, value head) tile is
+ * gdn_fp8_tile_bytes(K, V, block_v) bytes: the K V OCP E4M3 bytes in the
+ * pool's state_layout order (K_FIRST [K][V], V_FIRST [V][K]), then the
+ * V / block_v float32 tile scales amax/448 (scale 0 for an all-zero tile),
+ * zero-padded to a multiple of 16 bytes; element x = e4m3(byte) * scale of
+ * its [K, block_v] tile.  Requires qdq = GDN_QDQ_FP8_E4M3_TILE (else
+ * GDN_ERR_INVALID); results equal those of GDN_STORAGE_F32 with the fp8
+ * tiles up to float32 rounding, with about 4x fewer pool bytes. */
+enum gdn_storage { GDN_STORAGE_F32 = 0, GDN_STORAGE_I8H32 = 1, GDN_STORAGE_FP8_TILE = 2 };
 
 /* Options of a call.  Fill with gdn_options_init() and change fields. */
 typedef struct gdn_options {
@@ -372,6 +383,11 @@ int gdn_checked_build(void);
 /* Bytes of one packed (row, value head) tile of a GDN_STORAGE_I8H32 pool:
  * K V + 4 K (V / 32); -1 if V is not a positive multiple of 32 or K <= 0. */
 int64_t gdn_packed_tile_bytes(int32_t K, int32_t V);
+
+/* Bytes of one (row, value head) tile of a GDN_STORAGE_FP8_TILE pool:
+ * K V + 4 (V / block_v) rounded up to a multiple of 16; -1 if block_v does
+ * not divide V or a size is not positive. */
+int64_t gdn_fp8_tile_bytes(int32_t K, int32_t V, int32_t block_v);
 
 /* Head dims with a compiled kernel: writes up to `cap` (K, VB) pairs as
  * 2*n ints into `pairs` (NULL allowed) and returns the number of pairs

@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     check_paged_varlen,
     check_pooled,
     checked_library,
+    fp8_tile_bytes,
     gdn_decode_paged,
     gdn_decode_paged_varlen,
     gdn_decode_pooled,

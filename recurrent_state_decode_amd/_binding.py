@@ -80,6 +80,7 @@ _SIGNATURES = {
     "gdn_check_paged_varlen": (ctypes.c_int, [_P] * 4 + [_I32] * 4 + [_I64, _I64]),
     "gdn_checked_build": (ctypes.c_int, []),
     "gdn_packed_tile_bytes": (ctypes.c_int64, [_I32, _I32]),
+    "gdn_fp8_tile_bytes": (ctypes.c_int64, [_I32, _I32, _I32]),
 }
 
 _lib = None
@@ -183,7 +184,7 @@ def _common_opts(io_dtype, out_dtype, scale, use_qk_l2norm, beta_mode, state_lay
                     state_storage=int(state_storage))
 
 
-GDN_STORAGE_F32, GDN_STORAGE_I8H32 = 0, 1
+GDN_STORAGE_F32, GDN_STORAGE_I8H32, GDN_STORAGE_FP8_TILE = 0, 1, 2
 
 
 def packed_tile_bytes(K, V):
@@ -194,14 +195,29 @@ def packed_tile_bytes(K, V):
     return n
 
 
-def _pool_check(state_pool, HV, K, V, state_layout):
-    """Check the pool's shape; return its storage: a uint8 pool [rows, HV, packed_tile_bytes(K, V)] holds
-    packed int8_hadamard32 tiles (GDN_STORAGE_I8H32), a float32 pool fp32 states."""
+def fp8_tile_bytes(K, V, block_v=64):
+    """Bytes of one (row, value head) tile of a packed fp8 tile pool (gdn_fp8_tile_bytes)."""
+    n = load_library().gdn_fp8_tile_bytes(int(K), int(V), int(block_v))
+    if n < 0:
+        raise ValueError(f"no fp8 tile for K={K}, V={V}, block_v={block_v}")
+    return n
+
+
+def _pool_check(state_pool, HV, K, V, state_layout, qdq=None, block_v=64):
+    """Check the pool's shape; return its storage.  A float32 pool holds fp32 states; a uint8 pool
+    holds the codes of the state quantisation in use: [rows, HV, packed_tile_bytes(K, V)] for the
+    int8_hadamard32 codec (GDN_STORAGE_I8H32), [rows, HV, fp8_tile_bytes(K, V, block_v)] for fp8 tiles
+    (GDN_STORAGE_FP8_TILE)."""
     if state_pool.dtype == torch.uint8:
-        tail = (HV, packed_tile_bytes(K, V))
+        if qdq == "int8_hadamard32":
+            tail, storage = (HV, packed_tile_bytes(K, V)), GDN_STORAGE_I8H32
+        elif qdq == "fp8_e4m3_tile":
+            tail, storage = (HV, fp8_tile_bytes(K, V, block_v)), GDN_STORAGE_FP8_TILE
+        else:
+            raise ValueError("a uint8 (packed) state_pool needs qdq='int8_hadamard32' or 'fp8_e4m3_tile'")
         if state_pool.dim() != 3 or tuple(state_pool.shape[1:]) != tail:
             raise ValueError(f"packed state_pool shape {tuple(state_pool.shape)} does not match [rows, {tail}]")
-        return GDN_STORAGE_I8H32
+        return storage
     tail = (HV, K, V) if state_layout == "K_FIRST" else (HV, V, K)
     if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != tail:
         raise ValueError(f"state_pool shape {tuple(state_pool.shape)} does not match [rows, {tail}] for {state_layout}")
@@ -233,7 +249,7 @@ def gdn_decode_pooled(q, k, v, a, b, A_log, dt_bias, cu_seqlens, state_indices, 
         raise ValueError("A_log and dt_bias must be [HV]")
     if cu_seqlens is not None and cu_seqlens.shape != (B + 1,):
         raise ValueError("cu_seqlens must be [B+1]")
-    storage = _pool_check(state_pool, HV, K, V, state_layout)
+    storage = _pool_check(state_pool, HV, K, V, state_layout, qdq, block_v)
     if out is None:
         out = torch.empty((T, HV, V), dtype=out_dtype, device=dev)
     _check_dev("out", out, dev, (out_dtype,))
@@ -290,7 +306,7 @@ def _paged(kind, q, k, v, gate, beta_in, a_log, dt_bias, cu_seqlens, page_indice
         raise ValueError("last_page_len must be [B]")
     if slots is not None and slots.shape != (B, 2):
         raise ValueError("slots must be [B, 2]")
-    storage = _pool_check(state_pool, HV, K, V, state_layout)
+    storage = _pool_check(state_pool, HV, K, V, state_layout, qdq, block_v)
     if out is None:
         out = torch.empty((T, HV, V), dtype=out_dtype, device=dev)
     _check_dev("out", out, dev, (out_dtype,))
@@ -489,7 +505,7 @@ def kda_decode_pooled(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens
         raise ValueError("a_log must be [HV] and dt_bias [HV, K]")
     if cu_seqlens.shape != (B + 1,):
         raise ValueError("cu_seqlens must be [B+1]")
-    storage = _pool_check(state_pool, HV, K, V, state_layout)
+    storage = _pool_check(state_pool, HV, K, V, state_layout, qdq, block_v)
     if out is None:
         out = torch.empty((T, HV, V), dtype=out_dtype, device=dev)
     _check_dev("out", out, dev, (out_dtype,))

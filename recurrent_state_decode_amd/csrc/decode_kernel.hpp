@@ -104,6 +104,7 @@ enum Qdq : int {
   kQdqTile = 1,     // fp8 e4m3, one amax/448 scale per [K, VB] tile
   kQdqHad = 2,      // int8 codes of the 32-point Hadamard rotation, one scale per (key row, 32 values)
   kQdqHadPacked = 3,  // the same codec with the pool holding the codes and scales (packed tiles)
+  kQdqTilePacked = 4, // fp8 tiles with the pool holding the e4m3 bytes and the tile scales
 };
 
 constexpr float kL2Eps = 1e-6f;
@@ -398,6 +399,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   // line it reads or writes is its own.
   constexpr bool PACKED = QDQ == kQdqHadPacked;
   constexpr bool HAD = QDQ == kQdqHad || PACKED;
+  // FP8P: each (row, head) tile of the pool is its K V e4m3 bytes in the pool
+  // layout's order, then its V / VB float32 tile scales (amax / 448; VB is
+  // the fp8 tile width) padded to 16 bytes.  The registers of the fp8 path
+  // hold grid values with the tile scale in cs, so bytes load and store as
+  // they are.
+  constexpr bool FP8P = QDQ == kQdqTilePacked;
+  constexpr bool TILE = QDQ == kQdqTile || FP8P;
   static_assert(!PACKED || !VF, "packed tiles have one layout");
   constexpr bool AV = VF && !HAD;
   using Cfg = Tile<K, VB, NT, AV>;
@@ -609,9 +617,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   }
 
   const int64_t tile_elems = static_cast<int64_t>(K) * p.V;
-  const int64_t tile_bytes = static_cast<int64_t>(K) * p.V + 4 * static_cast<int64_t>(K) * (p.V / 32);
+  const int64_t tile_bytes = PACKED ? static_cast<int64_t>(K) * p.V + 4 * static_cast<int64_t>(K) * (p.V / 32)
+                                     : static_cast<int64_t>(K) * p.V + 16 * ((4 * p.nvb + 15) / 16);
   auto tile_base = [&](int64_t row) -> float* {
-    if constexpr (PACKED) return reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(p.pool) + (row * p.HV + h) * tile_bytes);
+    if constexpr (PACKED || FP8P)
+      return reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(p.pool) + (row * p.HV + h) * tile_bytes);
     else return p.pool + (row * p.HV + h) * tile_elems;
   };
   const float* src = tile_base(rrow);
@@ -634,7 +644,27 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   auto kf_lds = [&](int s, int j) -> int { return (4 * lr + j) * LD + row_idx(s); };
 
   float S[NS][EV];
-  if constexpr (PACKED) {
+  float fp8_scale = 1.0f;          // FP8P: the stored tile scale
+  if constexpr (FP8P) {
+    // 4 e4m3 bytes for every 4 floats of the fp32 layout (same element order)
+    const unsigned char* sb = reinterpret_cast<const unsigned char*>(src);
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int f = 0; f < EV / 4; ++f) {
+        const uint32_t c4 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sb + row_off(s, f)));
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c4), false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c4), true);
+        S[s][4 * f + 0] = lo[0];
+        S[s][4 * f + 1] = lo[1];
+        S[s][4 * f + 2] = hi[0];
+        S[s][4 * f + 3] = hi[1];
+      }
+    const float sc = __builtin_nontemporal_load(reinterpret_cast<const float*>(sb + tile_elems) + vb);
+    fp8_scale = sc > 0.0f ? sc : 1.0f;   // an all-zero tile stores scale 0
+    finish_raw(n0);                // overlaps the tile load
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);   // the tile (see kWaitVmem0)
+  } else if constexpr (PACKED) {
     // 4 codes (one dword) and their group's scale per row: R = code * scale
     const unsigned char* sb = reinterpret_cast<const unsigned char*>(src);
     const float* sc = reinterpret_cast<const float*>(sb + tile_elems);
@@ -703,7 +733,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   constexpr int NC = KDA ? NKEY : 1;
   float cs[NC];
 #pragma unroll
-  for (int m = 0; m < NC; ++m) cs[m] = 1.0f;
+  for (int m = 0; m < NC; ++m) cs[m] = fp8_scale;
   // key slot of element (s, e)
   auto slot = [](int s, int e) -> int { return AV ? e : s; };
 
@@ -723,6 +753,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   };
 
   // fp8 tile QDQ of the true state; the codes stay in S, the tile scale goes to cs
+  bool tile_nz = true;             // the last qdq_tile saw a non-zero tile
   auto qdq_tile = [&]() {
     float m = 0.0f;
     if constexpr (!KDA) {
@@ -731,6 +762,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
 #pragma unroll
         for (int e = 0; e < EV; ++e) m = fmaxf(m, fabsf(S[s][e]));
       const float ms = block_max(m);       // amax of S_reg; the true amax is cs[0] * ms
+      tile_nz = ms > 0.0f;
       if (ms > 0.0f) {
         const float msf = fmaxf(ms, kTinyAmax);   // 448 / amax stays finite
         const float inv = kE4M3Max / msf;
@@ -756,6 +788,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
 #pragma unroll
       for (int k2 = 0; k2 < NC; ++k2) m = fmaxf(m, cs[k2] * rowm[k2]);
       const float mt = block_max(m);       // true amax
+      tile_nz = mt > 0.0f;
       if (mt > 0.0f) {
         const float mtf = fmaxf(mt, kTinyAmax);   // 448 / amax stays finite
         const float inv = kE4M3Max / mtf;
@@ -811,7 +844,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
     }
   };
   auto quantize = [&]() {
-    if constexpr (QDQ == kQdqTile) qdq_tile();
+    if constexpr (TILE) qdq_tile();
     else if constexpr (HAD) had_quant();
   };
 
@@ -976,6 +1009,21 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
         __builtin_nontemporal_store(c4, reinterpret_cast<uint32_t*>(gb + r * 32));
         if ((lr & 7) == 0) __builtin_nontemporal_store(cs[KDA ? s : 0] * (mf * (1.0f / 127.0f)), tsc + grp * K + r);
       }
+    } else if constexpr (FP8P) {
+      // every token ends with qdq_tile: grid values, converted exactly; the
+      // tile scale is cs (one value: GDN's single scale, KDA's are equal),
+      // 0 for an all-zero tile
+      unsigned char* tb = reinterpret_cast<unsigned char*>(row_base);
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int f = 0; f < EV / 4; ++f) {
+          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(S[s][4 * f + 0], S[s][4 * f + 1], 0, false);
+          pk = __builtin_amdgcn_cvt_pk_fp8_f32(S[s][4 * f + 2], S[s][4 * f + 3], pk, true);
+          __builtin_nontemporal_store(static_cast<uint32_t>(pk), reinterpret_cast<uint32_t*>(tb + row_off(s, f)));
+        }
+      if (tid == 0)
+        __builtin_nontemporal_store(tile_nz ? cs[0] : 0.0f, reinterpret_cast<float*>(tb + tile_elems) + vb);
     } else if constexpr (!HAD) {
 #pragma unroll
       for (int s = 0; s < NS; ++s)

@@ -150,6 +150,7 @@ constexpr bool kHadShape = K == 128 && VB == 64 && NT == 256;
 template <int K, int VB, int NT, bool VF, bool KDA, int ADDR, typename TIn>
 hipError_t launch_qdq(const gdn::Params& p, int64_t units, int qdq, hipStream_t s) {
   if (qdq == gdn::kQdqTile) return launch_one<K, VB, NT, VF, KDA, gdn::kQdqTile, ADDR, TIn>(p, units, s);
+  if (qdq == gdn::kQdqTilePacked) return launch_one<K, VB, NT, VF, KDA, gdn::kQdqTilePacked, ADDR, TIn>(p, units, s);
   if (qdq == gdn::kQdqHad) {
     if constexpr (kHadShape<K, VB, NT>) return launch_one<K, VB, NT, VF, KDA, gdn::kQdqHad, ADDR, TIn>(p, units, s);
     return hipErrorInvalidValue;
@@ -287,9 +288,12 @@ int check_options(const gdn_options* o, int K, int V, Kind kind) {
                   o->block_v, V);
     if (K != 128) return fail(GDN_ERR_UNSUPPORTED, "the int8_hadamard32 codec is compiled for K=128 (got K=%d)", K);
   }
-  if (o->state_storage != GDN_STORAGE_F32 && o->state_storage != GDN_STORAGE_I8H32)
-    return fail(GDN_ERR_INVALID, "state_storage must be GDN_STORAGE_F32 or GDN_STORAGE_I8H32 (got %d)",
+  if (o->state_storage != GDN_STORAGE_F32 && o->state_storage != GDN_STORAGE_I8H32 &&
+      o->state_storage != GDN_STORAGE_FP8_TILE)
+    return fail(GDN_ERR_INVALID, "state_storage must be GDN_STORAGE_F32, I8H32 or FP8_TILE (got %d)",
                 o->state_storage);
+  if (o->state_storage == GDN_STORAGE_FP8_TILE && o->qdq != GDN_QDQ_FP8_E4M3_TILE)
+    return fail(GDN_ERR_INVALID, "state_storage FP8_TILE holds fp8 tile codes: qdq must be FP8_E4M3_TILE");
   if (o->state_storage == GDN_STORAGE_I8H32) {
     if (o->qdq != GDN_QDQ_INT8_HADAMARD32)
       return fail(GDN_ERR_INVALID, "state_storage I8H32 holds int8_hadamard32 codes: qdq must be INT8_HADAMARD32");
@@ -344,7 +348,8 @@ void fill_common(gdn::Params& p, const gdn_options* o, Kind kind, int32_t B, int
 int run(Kind kind, const gdn::Params& p, int K, int32_t T, const gdn_options* o, void* stream) {
   const int64_t units = static_cast<int64_t>(p.B) * p.HV * p.nvb;
   if (units > 0x7fffffffLL) return fail(GDN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)units);
-  const int qdq = o->qdq == GDN_QDQ_FP8_E4M3_TILE ? gdn::kQdqTile
+  const int qdq = o->qdq == GDN_QDQ_FP8_E4M3_TILE
+                      ? (o->state_storage == GDN_STORAGE_FP8_TILE ? gdn::kQdqTilePacked : gdn::kQdqTile)
                   : o->qdq == GDN_QDQ_INT8_HADAMARD32
                       ? (o->state_storage == GDN_STORAGE_I8H32 ? gdn::kQdqHadPacked : gdn::kQdqHad)
                       : gdn::kQdqNone;
@@ -711,6 +716,11 @@ int gdn_checked_build(void) { return kChecked ? 1 : 0; }
 int64_t gdn_packed_tile_bytes(int32_t K, int32_t V) {
   if (K <= 0 || V <= 0 || V % 32 != 0) return -1;
   return static_cast<int64_t>(K) * V + 4 * static_cast<int64_t>(K) * (V / 32);
+}
+
+int64_t gdn_fp8_tile_bytes(int32_t K, int32_t V, int32_t block_v) {
+  if (K <= 0 || V <= 0 || block_v <= 0 || V % block_v != 0) return -1;
+  return static_cast<int64_t>(K) * V + 16 * ((4 * static_cast<int64_t>(V / block_v) + 15) / 16);
 }
 
 int gdn_supported_head_dims(int32_t* pairs, int cap) {

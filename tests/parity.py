@@ -393,30 +393,58 @@ def run_and_check(w, seqs=None, report=None, pool=None, snapshot=True, check_all
 
 # ---------------------------------------------------------------- packed int8_hadamard32 pools
 
+def _is_fp8(w):
+    return w.options.get("qdq") == "fp8_e4m3_tile"
+
+
+def _to_layout(x, w):
+    """Logical [..., K, V] -> the pool layout's order (V_FIRST: [..., V, K]); its own inverse."""
+    return x if w.state_layout == "K_FIRST" else np.swapaxes(x, -1, -2)
+
+
+def packed_bytes(w):
+    """Bytes per (row, head) of a packed pool for workload ``w`` (codec or fp8 tiles)."""
+    if _is_fp8(w):
+        return e4m3.fp8_tile_bytes(w.K, w.V, w.options.get("block_v", 64))
+    return ohad.packed_tile_bytes(w.K, w.V)
+
+
 def make_packed_pool(w, device="cuda", rows=None):
-    """Packed pool [rows, HV, tile bytes] for workload ``w`` (K_FIRST, codec): the oracle's encoding of
-    make_pool's fp32 states for ``rows`` (all if None); the other rows hold random codes with positive scales."""
+    """Packed pool [rows, HV, tile bytes] for workload ``w`` (codec: K_FIRST; fp8 tiles: either layout): the
+    oracle's encoding of make_pool's fp32 states for ``rows`` (all if None); the other rows hold random codes
+    with positive scales."""
     K, V, HV, n = w.K, w.V, w.HV, w.num_rows
-    tb = ohad.packed_tile_bytes(K, V)
+    fp8 = _is_fp8(w)
+    bv = w.options.get("block_v", 64)
+    tb = packed_bytes(w)
+    nsc = V // bv if fp8 else K * V // 32
     g = torch.Generator(device=device)
     g.manual_seed(w.pool_seed + 7)
     packed = torch.randint(0, 256, (n, HV, tb), dtype=torch.uint8, device=device, generator=g)
-    sc = torch.empty((n, HV, K * V // 32), dtype=torch.float32, device=device).uniform_(1e-3, 1e-2, generator=g)
-    packed[:, :, K * V:] = sc.view(torch.uint8)
+    if fp8:                                  # no NaN codes (0x7f, 0xff): they become +-448 (0x7e, 0xfe)
+        c = packed[:, :, :K * V]
+        packed[:, :, :K * V] = torch.where((c & 0x7F) == 0x7F, c ^ 1, c)
+    sc = torch.empty((n, HV, nsc), dtype=torch.float32, device=device).uniform_(1e-3, 1e-2, generator=g)
+    packed[:, :, K * V:K * V + 4 * nsc] = sc.view(torch.uint8)
     rows = list(range(n)) if rows is None else sorted(set(rows))
     if rows:
         fp32 = wl.make_pool(w, device)
         idx = torch.tensor(rows, dtype=torch.int64, device=device)
         tiles = fp32.index_select(0, idx).cpu().numpy().astype(np.float64)
         del fp32
-        code, scale = ohad.int8_hadamard32_encode(tiles.reshape(-1, K, V), "float32")
-        t = ohad.pack_tiles(code.reshape(len(rows), HV, K, V), scale.reshape(len(rows), HV, K, V // 32))
+        if fp8:
+            code, scale = e4m3.tile_encode(_to_layout(tiles, w).reshape(-1, K, V), bv, "float32")
+            t = e4m3.pack_fp8_tiles(code.reshape(len(rows), HV, K, V), scale.reshape(len(rows), HV, V // bv),
+                                    w.state_layout, bv)
+        else:
+            code, scale = ohad.int8_hadamard32_encode(tiles.reshape(-1, K, V), "float32")
+            t = ohad.pack_tiles(code.reshape(len(rows), HV, K, V), scale.reshape(len(rows), HV, K, V // 32))
         packed[idx] = torch.from_numpy(t).to(device)
     return packed
 
 
 def gather_packed(pool, rows, K, V):
-    """{row: (codes int8 [HV, K, V], scales [HV, K, V / 32])} read back from a packed pool."""
+    """{row: (codes int8 [HV, K, V], scales [HV, K, V / 32])} read back from a packed codec pool."""
     rows = sorted(set(rows))
     if not rows:
         return {}
@@ -424,10 +452,27 @@ def gather_packed(pool, rows, K, V):
     return {r: ohad.unpack_tiles(t[i], K, V) for i, r in enumerate(rows)}
 
 
+def gather_fp8(pool, rows, w):
+    """{row: (E4M3 bytes [HV, K, V] in logical order, tile scales [HV, V / block_v])} of a packed fp8 pool."""
+    rows = sorted(set(rows))
+    if not rows:
+        return {}
+    bv = w.options.get("block_v", 64)
+    t = pool.index_select(0, torch.tensor(rows, dtype=torch.int64, device=pool.device)).cpu().numpy()
+    return {r: e4m3.unpack_fp8_tiles(t[i], w.K, w.V, w.state_layout, bv) for i, r in enumerate(rows)}
+
+
+def decode_fp8(codes, scales, w):
+    """The fp64 state, in the pool layout's order, that E4M3 bytes and tile scales stand for."""
+    return _to_layout(e4m3.tile_decode(codes, scales, w.options.get("block_v", 64)), w)
+
+
 def run_and_check_packed(w, seqs=None, report=None, pool=None, **over):
     """Parity of a call on a packed pool: outputs as for the codec on fp32 states; the written tiles,
     decoded, as the codec's states; their codes and scales against the oracle's encoding of its final
     states; every other byte of the pool unchanged."""
+    if _is_fp8(w):
+        return _run_and_check_fp8(w, seqs, report, pool, **over)
     assert w.options.get("qdq") == "int8_hadamard32" and w.state_layout == "K_FIRST"
     report = report if report is not None else Report()
     d = device_inputs(w)
@@ -474,6 +519,64 @@ def run_and_check_packed(w, seqs=None, report=None, pool=None, **over):
     # up to about a step, 1/127 of it; such groups must stay rare, like the flips themselves
     assert worst_scale < 1e-2, f"scale relative error {worst_scale}"
     assert off_scales <= max(1, groups // 100), f"{off_scales} of {groups} scales differ by more than 1e-5"
+    assert sorted(ref_written) == sorted(set(writes))
+    check_untouched(snap, pool, all_writes)
+    return report, out, pool
+
+
+def _run_and_check_fp8(w, seqs, report, pool, **over):
+    """run_and_check_packed for fp8 tiles: outputs and decoded states within the fp8 QDQ bounds; the written
+    bytes and tile scales against the oracle's encoding of its final states; a non-zero tile's largest code is
+    +-448 (its scale is its amax / 448), an all-zero tile's scale is 0; every other byte unchanged."""
+    report = report if report is not None else Report()
+    d = device_inputs(w)
+    all_reads, all_writes = rows_for(w)
+    reads, writes = rows_for(w, seqs)
+    if pool is None:
+        pool = make_packed_pool(w, "cuda", rows=all_reads)
+    bv = w.options.get("block_v", 64)
+    before = {r: decode_fp8(c, s, w) for r, (c, s) in gather_fp8(pool, reads, w).items()}
+    snap = pool.clone()
+    out = gpu_call(w, pool, d, **over)
+    torch.cuda.synchronize()
+    trace = {}
+    ref_out, ref_written = oracle_call(w, before, seqs=seqs, trace=trace, **over)
+    seq_list = list(range(w.B)) if seqs is None else list(seqs)
+    trows = token_rows(w, seq_list)
+    out_b, seq_b = qdq_bounds(w, trace, seq_list)
+    full = np.zeros(ref_out.shape)
+    for t, bnd in out_b.items():
+        full[t] = bnd
+    if len(trows):
+        compare_outputs(out, ref_out, w, trows, report, qdq_bound=full[trows])
+    state_bound = {row: seq_b[b][i] for b in seq_list if b in seq_b for i, row in written_rows(w, b)}   # logical
+    got = gather_fp8(pool, list(ref_written), w)
+    compare_states({r: decode_fp8(c, s, w) for r, (c, s) in got.items()}, ref_written, report,
+                   qdq_bound=state_bound, layout=w.state_layout)
+    table = e4m3.e4m3_table()
+    flips, total, worst_scale = 0, 0, 0.0
+    for r, ref in ref_written.items():
+        code_e, scale_e = e4m3.tile_encode(_to_layout(ref, w), bv, "float32")
+        code_g, scale_g = got[r]
+        vg, ve = table[code_g], table[code_e]
+        assert np.all(np.isfinite(vg)), f"row {r}: a NaN code was stored"
+        # the decoded values are held to the propagated bounds above: a code rounded the other way at one
+        # token moves the whole key row's update at the next, which for an element near zero can be many
+        # of its own (small) steps; here only how often codes differ is checked
+        off = vg != ve
+        flips += int(np.sum(off))
+        total += off.size
+        zero = scale_e == 0
+        assert np.all(scale_g[zero] == 0), f"row {r}: an all-zero tile stored a non-zero scale"
+        peak = np.abs(vg).reshape(vg.shape[0], w.K, w.V // bv, bv).max(axis=(1, 3))
+        assert np.all(peak[~zero] == 448.0), f"row {r}: a non-zero tile's largest code is not 448"
+        rel = np.abs(scale_g[~zero] - scale_e[~zero]) / scale_e[~zero]
+        worst_scale = max(worst_scale, float(rel.max()) if rel.size else 0.0)
+    report.add("fp8_code_flip_frac", flips / max(total, 1))
+    report.add("fp8_scale_max_rel", worst_scale)
+    assert flips / max(total, 1) < 1e-3, f"{flips} of {total} codes differ"
+    # a code rounded the other way at an earlier token moves the tile's later amax by a fraction of a step
+    assert worst_scale < 1e-2, f"scale relative error {worst_scale}"
     assert sorted(ref_written) == sorted(set(writes))
     check_untouched(snap, pool, all_writes)
     return report, out, pool

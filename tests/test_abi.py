@@ -31,7 +31,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"gdn_decode_pooled", "gdn_decode_paged", "kda_decode_pooled", "gdn_status_string",
-            "gdn_check_paged", "gdn_checked_build", "gdn_packed_tile_bytes"} <= set(names)
+            "gdn_check_paged", "gdn_checked_build", "gdn_packed_tile_bytes", "gdn_fp8_tile_bytes"} <= set(names)
     for path, checked in ((rsd.LIB_PATH, 0), (rsd.CHECKED_LIB_PATH, 1)):
         lib = bnd.load_library(path)
         for n in names:
@@ -105,8 +105,26 @@ def test_packed_storage_argument_errors():
     assert "INT8_HADAMARD32" in lib.gdn_last_error().decode()
     assert _pooled(lib, state_storage=1, qdq=1) == bnd.GDN_ERR_INVALID
     assert _pooled(lib, state_storage=1, qdq=2, state_layout=1) == bnd.GDN_ERR_UNSUPPORTED
-    assert _pooled(lib, state_storage=2, qdq=2) == bnd.GDN_ERR_INVALID
+    assert _pooled(lib, state_storage=2, qdq=2) == bnd.GDN_ERR_INVALID           # fp8 storage needs fp8 tiles
+    assert "FP8_E4M3_TILE" in lib.gdn_last_error().decode()
+    assert _pooled(lib, state_storage=3, qdq=1) == bnd.GDN_ERR_INVALID
     assert _pooled(lib, state_storage=1, qdq=2, T=0) == bnd.GDN_OK               # accepted (nothing to launch)
+    assert _pooled(lib, state_storage=2, qdq=1, T=0) == bnd.GDN_OK
+    assert _pooled(lib, state_storage=2, qdq=1, state_layout=1, T=0) == bnd.GDN_OK   # either layout
+
+
+@no_gpu
+def test_fp8_tile_bytes():
+    from oracle import e4m3
+    lib = rsd.load_library()
+    assert rsd.fp8_tile_bytes(128, 128) == 128 * 128 + 16 == 16400               # two scales, padded to 16
+    for K, V, bv in ((128, 128, 64), (128, 256, 64), (16, 48, 16), (128, 64, 64), (16, 320, 16)):
+        assert lib.gdn_fp8_tile_bytes(K, V, bv) == e4m3.fp8_tile_bytes(K, V, bv)
+        assert lib.gdn_fp8_tile_bytes(K, V, bv) % 16 == 0
+    assert lib.gdn_fp8_tile_bytes(128, 100, 64) == -1
+    assert lib.gdn_fp8_tile_bytes(128, 128, 0) == -1
+    with pytest.raises(ValueError):
+        rsd.fp8_tile_bytes(128, 96)
 
 
 @no_gpu

@@ -546,3 +546,121 @@ def test_packed_b512_t4_sampled():
     pool = P.make_packed_pool(w, "cuda", rows=reads)
     rep, _, _ = P.run_and_check_packed(w, seqs=seqs, pool=pool)
     _report("packed/b512_t4_sampled", rep)
+
+
+# ---------------------------------------------------------------- packed fp8 tile pools (E4M3 bytes + tile scales)
+
+FP8 = dict(qdq="fp8_e4m3_tile", block_v=64)
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("layout", ["K_FIRST", "V_FIRST"])
+def test_fp8_packed_pooled_small(kind, layout):
+    mk = wl.gdn_pooled if kind == "gdn" else wl.kda_pooled
+    w = mk(6, 2, 4, 128, 128, lengths=[4, 1, 0, 9, 2, 3], num_slots=8, state_layout=layout, seed=81, **FP8)
+    rep, _, _ = P.run_and_check_packed(w)
+    _report(f"fp8_packed/{kind}/{layout}", rep)
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("layout,idx", [("K_FIRST", torch.int32), ("V_FIRST", torch.int64)])
+def test_fp8_packed_paged(kind, layout, idx):
+    w = wl.paged(kind, 24, 2, 4, 128, 128, max_prefix=40, page_size=4, share_frac=0.3, state_layout=layout,
+                 index_dtype=idx, seed=82, **FP8)
+    rep, _, _ = P.run_and_check_packed(w)
+    _report(f"fp8_packed_paged/{kind}/{layout}", rep)
+    suffix = np.array([0, 1, 2, 3, 4, 5, 8, 9, 7, 1, 4, 0, 6, 2, 9, 3])
+    w = wl.paged(kind, len(suffix), 2, 4, 128, 128, max_prefix=30, page_size=4, share_frac=0.3,
+                 suffix_lengths=suffix, state_layout=layout, index_dtype=idx, seed=83, **FP8)
+    rep, _, _ = P.run_and_check_packed(w)
+    _report(f"fp8_packed_paged_varlen/{kind}/{layout}", rep)
+
+
+@pytest.mark.parametrize("extra", [dict(readout="stored"), dict(quantize_initial=True), dict(V=256),
+                                   dict(use_qk_l2norm=False, scale=0.2), dict(io_dtype=torch.float32),
+                                   dict(K=16, V=48)])
+def test_fp8_packed_options(extra):
+    extra = dict(extra)
+    K, V = extra.pop("K", 128), extra.pop("V", 128)
+    fp8 = dict(FP8, block_v=16) if K == 16 else FP8
+    wkeys = ("readout", "quantize_initial", "io_dtype")
+    w = wl.gdn_pooled(5, 1, 2, K, V, lengths=[2, 7, 1, 0, 3], num_slots=6, state_layout="V_FIRST", seed=84,
+                      **fp8, **{k: v for k, v in extra.items() if k in wkeys})
+    over = {k: v for k, v in extra.items() if k not in wkeys}
+    rep, _, _ = P.run_and_check_packed(w, **over)
+    _report(f"fp8_packed_opts/{extra}/K{K}V{V}", rep)
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_fp8_packed_equals_fp32_fp8_path(kind):
+    """The packed pool and an fp32 pool holding its decoded states give the same outputs and the same
+    states (the registers start from the same grid values and scales; float32 rounding apart)."""
+    mk = wl.gdn_pooled if kind == "gdn" else wl.kda_pooled
+    w = mk(8, 2, 4, 128, 128, lengths=[3, 1, 4, 2, 5, 1, 2, 6], num_slots=10, state_layout="V_FIRST", seed=85,
+           **FP8)
+    d = P.device_inputs(w)
+    packed = P.make_packed_pool(w, "cuda")
+    dec = lambda pool: np.stack([P.decode_fp8(*P.gather_fp8(pool, [r], w)[r], w) for r in range(w.num_rows)])
+    fp32 = torch.from_numpy(np.ascontiguousarray(dec(packed), dtype=np.float32)).cuda()
+    out_p = P.gpu_call(w, packed, d)
+    out_f = P.gpu_call(w, fp32, d)
+    torch.cuda.synchronize()
+    a, b = out_p.float(), out_f.float()
+    assert float((a - b).abs().max()) <= 8e-3 * float(b.abs().max())   # one bf16 step at the largest output
+    assert float((a - b).norm() / b.norm()) < 1e-3
+    rows = sorted(set(P.rows_for(w)[1]))
+    got, ref = dec(packed)[rows], fp32.cpu().numpy().astype(np.float64)[rows]
+    flips = np.abs(got - ref) > 1e-6 * np.abs(ref).max()
+    assert flips.mean() < 1e-3, flips.mean()
+    assert np.abs(got - ref).max() <= 0.07 * np.abs(ref).max()   # at most one grid step (32 / 448 of amax)
+
+
+@pytest.mark.parametrize("layout", ["K_FIRST", "V_FIRST"])
+def test_fp8_packed_identity_step_keeps_every_byte(layout):
+    """alpha = 1 and beta = 0 leave the state unchanged: the tile QDQ of a decoded tile is the tile itself
+    (its amax is 448 s, so the scale is s again and every code maps to itself), so every byte written equals
+    the byte read, all-zero tiles (scale 0) included.  The one exception is the sign of a zero: the update
+    adds beta k (...) = +-0 to every element, and -0 + +0 is +0, so a -0 code (0x80) may come back as +0."""
+    B, HV, nb = 4, 4, 128 * 128
+    w = wl.gdn_pooled(B, 1, HV, 128, 128, lengths=[1] * B, num_slots=B, state_layout=layout, seed=86,
+                      io_dtype=torch.float32, **FP8)
+    w.inputs["a"] = torch.full((B, HV), -float("inf"))     # softplus(-inf) = 0 -> alpha = 1
+    w.inputs["b"] = torch.zeros((B, HV))                   # beta = b = 0 (probability mode)
+    w.options["beta_mode"] = "probability"
+    pool = P.make_packed_pool(w, "cuda")
+    pool[1, 2, :nb] = 0                                    # an all-zero head ...
+    pool[1, 2, nb:nb + 8] = 0                              # ... with scales 0
+    col = torch.arange(nb, device="cuda") % 128 if layout == "K_FIRST" else torch.arange(nb, device="cuda") // 128
+    pool[2, 0, :nb][col < 64] = 0                          # an all-zero first tile next to a non-zero one
+    pool[2, 0, nb:nb + 4] = 0
+    before = pool.clone()
+    P.gpu_call(w, pool, P.device_inputs(w))
+    torch.cuda.synchronize()
+    plus0 = lambda t: torch.where(t[..., :nb] == 0x80, torch.zeros_like(t[..., :nb]), t[..., :nb])
+    diff = torch.nonzero(plus0(pool) != plus0(before))
+    assert diff.numel() == 0, f"codes changed at {diff[:5].tolist()}"
+    assert torch.equal(pool[..., nb:], before[..., nb:]), "tile scales or padding changed"
+    n_neg0 = int((before[..., :nb] == 0x80).sum())
+    print(f"[identity] -0 codes before {n_neg0}, after {int((pool[..., :nb] == 0x80).sum())}")
+
+
+def test_fp8_packed_zero_state_tiles():
+    """A zero initial state and zero values in a head's first 64 columns keep that tile zero: its codes stay
+    0 and its scale 0, next to a non-zero tile of the same head."""
+    w = wl.gdn_pooled(4, 2, 4, 128, 128, lengths=[3, 1, 2, 4], num_slots=6, state_layout="K_FIRST", seed=87,
+                      zero_state=True, **FP8)
+    w.inputs["v"][:, 1, :64] = 0
+    rep, _, pool = P.run_and_check_packed(w)
+    rows = sorted(set(P.rows_for(w)[1]))
+    for r, (codes, scales) in P.gather_fp8(pool, rows, w).items():
+        assert scales[1, 0] == 0 and not codes[1, :, :64].any() and scales[1, 1] > 0
+    _report("fp8_packed/zero_tiles", rep)
+
+
+def test_fp8_packed_gdn_b512_t4_sampled():
+    w = wl.fp8_qdq_gdn_b512()
+    seqs = sorted(np.random.default_rng(8).choice(w.B, 24, replace=False).tolist())
+    reads, _ = P.rows_for(w, seqs)
+    pool = P.make_packed_pool(w, "cuda", rows=reads)
+    rep, _, _ = P.run_and_check_packed(w, seqs=seqs, pool=pool)
+    _report("fp8_packed/b512_t4_sampled", rep)
