@@ -102,6 +102,8 @@ int checked_paged(const int32_t* cu, const void* pi, const void* ptr, const void
 //                            VB=32, NT=256 (5-6 % faster than VB=64 on 4-token
 //                            suffixes; on a K_FIRST pool it is 5 % slower,
 //                            and KDA's per-channel gates favour VB=64)
+//   K=128, GDN, packed fp8 tiles on a V_FIRST pool, T <= 1.5 B:
+//                            VB=64, NT=128 (launch_fp8p_gdn_vfirst)
 //   K=128, otherwise:        VB=64, NT=256 (fp8 tiles need block_v == VB; the
 //                            int8_hadamard32 codec is compiled for this shape)
 //   K=16:                    VB=16, NT=64
@@ -249,6 +251,26 @@ hipError_t launch_packed(Kind kind, const gdn::Params& p, int64_t units, Sel sel
   return hipErrorInvalidValue;
 }
 
+// Packed fp8 tiles of a V_FIRST pool, GDN, about one token per sequence: the
+// 64-column tile over 128 threads (paged B=256: 0.080 against 0.088 ms with
+// 256 threads; KDA and K_FIRST pools measured slower or no faster that way).
+constexpr int kFp8SmallVB = 64, kFp8SmallNT = 128;
+
+template <int VB, int NT>
+hipError_t launch_fp8p_gdn_vfirst(Kind kind, const gdn::Params& p, int64_t units, Sel sel, hipStream_t s) {
+  auto go = [&](auto addr) -> hipError_t {
+    constexpr int ADDR = decltype(addr)::value;
+    return sel.bf16 ? launch_one<128, VB, NT, true, false, gdn::kQdqTilePacked, ADDR, gdn::bf16_t>(p, units, s)
+                    : launch_one<128, VB, NT, true, false, gdn::kQdqTilePacked, ADDR, float>(p, units, s);
+  };
+  switch (kind) {
+    case Kind::GdnPooled: return go(std::integral_constant<int, gdn::kPooled>{});
+    case Kind::GdnPaged: return go(std::integral_constant<int, gdn::kPaged1>{});
+    case Kind::GdnPagedVar: return go(std::integral_constant<int, gdn::kPagedVar>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
 int check_options(const gdn_options* o, int K, int V, Kind kind) {
   if (!o) return fail(GDN_ERR_INVALID, "options pointer is NULL");
   if (o->io_dtype != GDN_F32 && o->io_dtype != GDN_BF16)
@@ -361,6 +383,10 @@ int run(Kind kind, const gdn::Params& p, int K, int32_t T, const gdn_options* o,
     case 128:
       if (sel.qdq == gdn::kQdqHadPacked && 2 * T <= 3 * p.B) {   // the packed single-token shape
         err = launch_packed<kPackedVB, kPackedNT>(kind, p, units, sel, s);
+        break;
+      }
+      if (sel.qdq == gdn::kQdqTilePacked && sel.vfirst && !is_kda(kind) && 2 * T <= 3 * p.B) {
+        err = launch_fp8p_gdn_vfirst<kFp8SmallVB, kFp8SmallNT>(kind, p, units, sel, s);
         break;
       }
       switch (shape_for(K, sel.vfirst, sel.qdq != gdn::kQdqNone, T, p.B, is_kda(kind), false).VB) {

@@ -591,6 +591,22 @@ def test_fp8_packed_options(extra):
     _report(f"fp8_packed_opts/{extra}/K{K}V{V}", rep)
 
 
+@pytest.mark.parametrize("layout", ["V_FIRST", "K_FIRST"])
+@pytest.mark.parametrize("io", [torch.bfloat16, torch.float32])
+def test_fp8_packed_single_token_shapes(layout, io):
+    """Single-token calls on packed fp8 pools (GDN on a V_FIRST pool has its own 128-thread shape): pooled
+    with one token per sequence, and paged varlen with mostly one-token suffixes."""
+    w = wl.gdn_pooled(12, 2, 4, 128, 128, num_slots=16, state_layout=layout, io_dtype=io, seed=88, **FP8)
+    rep, _, _ = P.run_and_check_packed(w)
+    _report(f"fp8_packed_t1/{layout}/{io}", rep)
+    suffix = np.array([1, 1, 0, 1, 2, 1, 1, 1, 1, 3, 1, 1])
+    w = wl.paged("gdn", len(suffix), 2, 4, 128, 128, max_prefix=30, page_size=4, share_frac=0.3,
+                 suffix_lengths=suffix, state_layout=layout, io_dtype=io, seed=89, **FP8)
+    assert 2 * w.T <= 3 * w.B
+    rep, _, _ = P.run_and_check_packed(w)
+    _report(f"fp8_packed_varlen_t1/{layout}/{io}", rep)
+
+
 @pytest.mark.parametrize("kind", ["gdn", "kda"])
 def test_fp8_packed_equals_fp32_fp8_path(kind):
     """The packed pool and an fp32 pool holding its decoded states give the same outputs and the same
