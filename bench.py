@@ -322,6 +322,7 @@ def main():
         sel += f" --layout {args.layout}" if args.layout else ""
         sel += f" --qdq {args.qdq}" if args.qdq else ""
         sel += " --token-path" if args.token_path else ""
+        sel += f" --storage {args.storage}" if args.storage != "f32" else ""
         cmds = {"kt": f"rocprofv3 --kernel-trace --stats -d {kt} -o kt --output-format csv -- "
                       f"python3 bench.py{sel} --steps 20 --warmup 2 --no-cpu-baseline",
                 "fetch": f"rocprofv3 --pmc FETCH_SIZE -d {fe} -o f --output-format csv -- "
@@ -448,7 +449,9 @@ def main():
         res["frac_of_device_copy"] = round(achieved / cbw, 4)
     except RuntimeError:
         pass
-    res["gpu_clocks_after_run"] = gpu_clocks()
+    # (not in the counter runs: under rocprofv3 --pmc every child process starts with the GPU
+    # initialised, and rocm-smi, a Python script, execs its interpreter)
+    res["gpu_clocks_after_run"] = None if args.copy_calibration else gpu_clocks()
     if w.chunked:
         fl = chunked_flops(w)
         tf = fl / (mean_ms * 1e-3) / 1e12
