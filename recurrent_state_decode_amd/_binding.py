@@ -5,6 +5,11 @@ Argument marshalling only: shapes and dtypes are read off the tensors,
 current torch stream of the tensors' device.  Every step of the decode runs
 in the library's HIP kernels; there is no fallback.  If the library is not
 built, every call raises.
+
+``state_pool`` is float32 (fp32 states in the ``state_layout`` order) or
+uint8 (packed tiles: the int8_hadamard32 codes and scales with
+qdq='int8_hadamard32', the E4M3 bytes and tile scales with
+qdq='fp8_e4m3_tile'); the storage kind is taken from its dtype.
 """
 import contextlib
 import ctypes
