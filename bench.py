@@ -333,8 +333,9 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
-              "Every (sequence, value head) state is independent; see DESIGN.md for how the pool would shard.",
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Every (sequence, value head) state is independent, so the pool would shard by value heads or by "
+              "sequences with this same kernel on each GPU's share.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -10,7 +10,7 @@ Pages followed:
 * flashinfer.gdn_paged.gated_delta_rule_decode_paged -- signature: ``A_log``,
   ``a``, ``dt_bias``, ``b``, ``scale=None``, ``use_qk_l2norm=True``.
 
-Readings where the pages are silent (listed in the design doc):
+Readings where the pages are silent:
 * L2 norm epsilon: x / sqrt(sum(x^2) + 1e-6).
 * gate: g = -exp(A_log) * softplus(a + dt_bias), the log of the decay
   factor alpha = exp(g); for KDA the same per key channel.

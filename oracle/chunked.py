@@ -7,8 +7,8 @@ output_state, output_score, output_value, output_add, state_decay,
 state_update, state_add; LinearAttentionSolveConfig fixes an exact solve.
 The Circuit.LLM.Mixer page ("Chunked additive linear") states the principle
 that the chunked form matches the sequential one.  The pages give no
-formulas for it, so this form is derived here from the recurrence
-(derivation in the design doc) and written with those step names:
+formulas for it, so this form is derived here from the recurrence and
+written with those step names:
 
 Within a chunk of C tokens with initial state S0 [K, V], per-token log
 gates g_t ([K] vectors; a scalar gate is the same value on every channel):

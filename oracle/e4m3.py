@@ -13,7 +13,7 @@ floating point specification (E4M3): sign bit, 4 exponent bits with bias 7,
 pattern is S.1111.111, there are no infinities, the largest finite value is
 448.
 
-Readings (listed in DESIGN.md):
+Readings:
 * dynamic scale s = amax / 448, so the tile's largest magnitude maps to the
   top of the grid;
 * round to nearest, ties to even mantissa, saturating at +-448; subnormals

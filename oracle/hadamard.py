@@ -11,7 +11,7 @@ Pages followed:
   told otherwise -- the codec works in a rotated value basis and the state is
   handed back in the original one.
 
-Readings (listed in the design doc; the pages give no formulas):
+Readings (the pages give no formulas):
 * the rotation is the 32-point Walsh-Hadamard transform in Sylvester order,
   normalised to be orthonormal (H / sqrt(32), H the +-1 matrix), applied to
   each group of 32 consecutive value columns of every key row:

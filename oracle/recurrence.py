@@ -17,7 +17,7 @@ Pages followed:
 Reading of the KDA decay axis (the Haddock text says "column" while its
 own o = q S convention makes rows the key index, and the kda_decode gate is
 laid out over key_head_dim): alpha[c] scales ROW c of S[K, V], i.e. the key
-channel.  Listed in DESIGN.md.
+channel.
 
 The step runs on a stack of heads: S [H, K, V], q_hat/k_hat [H, K],
 v [H, V], alpha [H] (scalar gate) or [H, K] (per key channel), beta [H].

@@ -13,8 +13,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped, not failed, when no GPU is visible; the round-end
-    # run on the GPU machine selects them with -m gpu and they run there.
+    # GPU tests are skipped, not failed, when no GPU is visible; on a machine
+    # with an MI355X, -m gpu selects them and they run.
     try:
         import torch
         has_gpu = torch.cuda.is_available()

@@ -5,7 +5,7 @@ Python binding, run the CPU oracle on the same values (pool rows read back
 from the device before the call), and compare the two under the tolerances
 below.
 
-Tolerances (readings of the stated contract, listed in the design doc):
+Tolerances (readings of the stated contract):
 * index work is exact: the rows written are exactly the call's write rows,
   every other pool byte is bit-identical to its value before the call;
 * fp32 states: |gpu - ref| <= 2e-3 * (|ref| + rms(ref over the row's tile));
