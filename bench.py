@@ -24,6 +24,7 @@ import hashlib
 import inspect
 import json
 import os
+import re
 import sys
 import time
 
@@ -34,17 +35,25 @@ PEAK_HBM_GBPS = 8000.0
 METRIC = "tokens/s & state-pool HBM GB/s (% peak), GDN decode B=256,HV=32,K=V=128"
 
 
+def _code_only(text):
+    """C/C++ source without its comments and blank space, so that a comment edit keeps the hash."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash(chunked=False):
-    """Hash of the sources a kernel is built from (ties a profile to a kernel version): the decode
-    kernel's header, the host launch code and the C header; the chunked prefill adds its own header."""
+    """Hash of the code a kernel is built from (ties a profile to a kernel version): the decode
+    kernel's header, the host launch code and the C header, comments left out; the chunked prefill
+    adds its own header."""
     h = hashlib.sha256()
     files = ["recurrent_state_decode_amd/csrc/decode_kernel.hpp"]
     if chunked:
         files.append("recurrent_state_decode_amd/csrc/prefill_kernel.hpp")
     files += ["recurrent_state_decode_amd/csrc/gdn_decode.hip", "include/gdn_decode.h"]
     for rel in files:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -86,11 +86,13 @@ enum gdn_beta_mode { GDN_BETA_LOGITS = 0, GDN_BETA_PROBABILITY = 1 };
  * GDN_ERR_UNSUPPORTED. */
 enum gdn_gate_mode { GDN_GATE_ORIGINAL = 0, GDN_GATE_SAFE = 1 };
 
-/* State quantise/dequantise after every token.  The pool stays fp32; the
- * state written back is the dequantised value.
+/* State quantise/dequantise after every token.  On an fp32 pool
+ * (GDN_STORAGE_F32) the state written back is the dequantised value; the
+ * packed storages (gdn_storage) hold the codes and scales instead.
  *
  * GDN_QDQ_FP8_E4M3_TILE (modelopt ... linear_attention.config,
- * LinearAttentionConfig: one dynamic scale per [Dk, block_v] tile;
+ * LinearAttentionConfig, state.block_v: each [K, block_v] tile of a
+ * sequence's head state gets its own scale, recomputed every time;
  * ... linear_attention.decode: state_format 'fp8_e4m3'): OCP E4M3,
  * scale = amax / 448 per tile, nearest even, saturating.
  *
@@ -157,9 +159,9 @@ typedef struct gdn_options {
   int32_t quantize_initial; /* 1: also round the state read before the first token (default 0) */
   int32_t readout;          /* gdn_readout                                     (default WORKING) */
   const int64_t* slots;     /* single-token paged calls only: device [B][2] (read row, write row)
-                               from gdn_paged_decode_slots() for the same page table, or NULL to
-                               resolve the rows inside the call (default NULL).  Not checked
-                               against the table (flashinfer.gdn_paged, slots). */
+                               that gdn_paged_decode_slots() produced from this call's table, or
+                               NULL to resolve the rows inside the call (default NULL).  Not
+                               checked against the table (flashinfer.gdn_paged, slots). */
   int32_t state_storage;    /* gdn_storage                                      (default F32) */
 } gdn_options;
 
@@ -196,14 +198,14 @@ int gdn_decode_pooled(const void* q, const void* k, const void* v, const void* a
                       const gdn_options* opt, void* stream);
 
 /*
- * gdn_decode_paged -- single-token GDN decode on a CSR-paged pool
- * (flashinfer.gdn_paged.gated_delta_rule_decode_paged).  Token b is the
- * decoded token of sequence b and sits at position last_page_len[b] of the
- * sequence's last page, page_indices[page_indptr[b+1]-1].  If
- * last_page_len[b] == 1 the token opens that page: the state is read from
- * the previous page page_indices[page_indptr[b+1]-2] and written to the
- * last page, and the previous page (which may be shared) is left
- * untouched.  Otherwise the last page is read and updated in place.
+ * gdn_decode_paged -- GDN decode of one token per sequence on a CSR-paged pool
+ * (flashinfer.gdn_paged.gated_delta_rule_decode_paged).  Token b ends
+ * sequence b and occupies slot last_page_len[b] of its final page,
+ * page_indices[page_indptr[b+1]-1].  With last_page_len[b] == 1 the token
+ * starts that page: the starting state comes from the page before it,
+ * page_indices[page_indptr[b+1]-2], the result goes to the final page, and
+ * the page before (possibly shared with other sequences) keeps every byte.
+ * In any other slot the final page is read and rewritten in place.
  *
  *   q, k          [B, HK, K]   io_dtype   device
  *   v             [B, HV, V]   io_dtype   device
@@ -228,7 +230,7 @@ int gdn_decode_paged(const void* q, const void* k, const void* v, const void* a,
  *
  *   q, k          [T, HK, K]   io_dtype   device
  *   v             [T, HV, V]   io_dtype   device
- *   raw_gate      [T, HV, K]   io_dtype   device; gate pre-activation before dt_bias
+ *   raw_gate      [T, HV, K]   io_dtype   device; gate input, dt_bias not yet added
  *   beta_logits   [T, HV]      io_dtype   device
  *   a_log         [HV]         f32        device
  *   dt_bias       [HV, K]      f32        device
@@ -265,10 +267,10 @@ int kda_decode_paged(const void* q, const void* k, const void* v, const void* ra
  * the token axis, as in max.nn.state_space.kda_decode.  The page table
  * describes the sequences after the suffix: sequence b holds
  * n_b = (pages_b - 1) * page_size + last_page_len[b] tokens and the suffix is
- * its last T_b tokens; at least one token precedes the suffix.  The state is
- * read from the page holding token n_b - T_b; after a suffix token that fills
- * its page (position a multiple of page_size) the state is written to that
- * page; the final state is written to the last page.  Pages that hold no
+ * its last T_b tokens; the suffix never starts at token 1.  The starting
+ * state comes from the page holding token n_b - T_b; a suffix token at a
+ * position that is a multiple of page_size completes its page and stores its
+ * state there; the state after the last token goes to the final page.  Pages that hold no
  * suffix token are never written; pages a suffix writes must belong to that
  * sequence alone (not checked).  q, k [T, HK, K], v [T, HV, V], out
  * [T, HV, V]; other inputs as for the single-token calls with T rows.

@@ -13,8 +13,8 @@ and written to be checked by eye against the pages it cites:
 * ``activations`` -- L2 normalisation, softplus gate, sigmoid beta
   (max.nn.state_space.kda_decode, description and Parameters;
   flashinfer.gdn_paged.gated_delta_rule_decode_paged, signature).
-* ``recurrence``  -- the sequential per-token step, scalar (GDN) or
-  per-key-channel (KDA) decay (Circuit.LLM.Mixer, "Delta rule" and
+* ``recurrence``  -- the sequential per-token step, with one decay per head
+  (GDN) or one per key row (KDA) (Circuit.LLM.Mixer, "Delta rule" and
   "Gated memory").
 * ``e4m3``        -- OCP FP8 E4M3 decode table, round-to-nearest-even with
   saturation, and the per-[K, block_v]-tile amax quantise/dequantise

@@ -1,12 +1,12 @@
 """Fused input activations of the decode step, in float64.
 
 Pages followed:
-* max.nn.state_space.kda_decode -- description: q and k arrive raw, are
-  L2-normalised inside the op, and q is scaled by 1/sqrt(key_head_dim); the
-  gate and beta activations are folded in (``gate_mode``, ``beta_mode``).
-  Parameters: ``raw_gate`` is the forget-gate pre-activation before
-  ``dt_bias`` is added, ``a_log`` is per value head, ``beta_mode`` picks
-  whether the sigmoid is applied.
+* max.nn.state_space.kda_decode -- description: the op takes q and k
+  unnormalised, normalises both to unit L2 length itself and multiplies q by
+  1/sqrt(key_head_dim); it also applies the gate and beta nonlinearities
+  (``gate_mode``, ``beta_mode``).  Parameters: ``raw_gate`` is the gate
+  input to which ``dt_bias`` has not yet been added, ``a_log`` has one value
+  per value head, and ``beta_mode`` says whether a sigmoid is taken.
 * flashinfer.gdn_paged.gated_delta_rule_decode_paged -- signature: ``A_log``,
   ``a``, ``dt_bias``, ``b``, ``scale=None``, ``use_qk_l2norm=True``.
 

@@ -215,7 +215,7 @@ def gdn_decode_paged(q, k, v, a, b, A_log, dt_bias, page_indices, page_indptr, l
                      pool, *, scale=None, use_qk_l2norm=True, beta_mode="logits",
                      state_layout="V_FIRST", qdq=None, block_v=64, quantize_initial=False,
                      readout="working", seqs=None, trace=None):
-    """Single-token GDN decode on a CSR-paged pool (token b belongs to sequence b).
+    """GDN decode of one token per sequence on a CSR-paged pool (token b belongs to sequence b).
 
     q, k [B, HK, K]; v [B, HV, V]; a, b [B, HV]; returns out [B, HV, V]
     (the [B, 1, HV, V] output without its unit axis).

@@ -2,9 +2,11 @@
 
 Pages followed:
 * modelopt ... linear_attention.config, LinearAttentionConfig: ``state.block_v``
-  gives one dynamic scale per [Dk, block_v] tile of each sequence and head.
-* modelopt ... linear_attention.decode, EncodedLinearAttentionTensor: values
-  are kept fake-decoded next to their scales; there is no compressed storage.
+  sets the tile width; every [Dk, block_v] tile of a sequence's head state
+  has its own scale, recomputed from the tile each time.
+* modelopt ... linear_attention.decode, EncodedLinearAttentionTensor: the
+  encoded state holds dequantised values beside detached scales and claims
+  no compressed storage.
   ``recurrent_decode`` names ``state_format='fp8_e4m3'`` and ``block_v=64``.
 
 The FP8 format itself is not on the pages; it follows the OCP 8-bit

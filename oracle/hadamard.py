@@ -1,9 +1,9 @@
 """The int8_hadamard32 state codec: value-basis Hadamard rotation + int8 per (key channel, 32 values).
 
 Pages followed:
-* modelopt ... linear_attention.config, LinearAttentionConfig: decode's
-  int8_hadamard32 codec fixes the scales to one key channel and 32 values
-  (instead of one per [Dk, block_v] tile); ``state.block_v`` stays the
+* modelopt ... linear_attention.config, LinearAttentionConfig: with the
+  int8_hadamard32 codec a scale covers a single key row by a 32-value group
+  (not a [Dk, block_v] tile), while ``state.block_v`` keeps its role as the
   execution tile width.  LinearAttentionDecodeConfig: ``state_codec`` is
   'tile' or 'int8_hadamard32'.
 * modelopt ... linear_attention.decode, LinearAttentionCarry: the carry has a

@@ -5,16 +5,17 @@ Pages followed:
   exclusive prefix offsets of each sequence's suffix tokens;
   ``state_indices`` [B] names the pool slot of each sequence; the pool is
   mutated in place.
-* flashinfer.gdn_paged.gated_delta_rule_decode_paged, description: the
-  decoded token is the last token of its sequence, at position
-  ``last_page_len[b]`` of the sequence's last page.  If it opens a new page
-  (``last_page_len[b] == 1``) the state is read from the previous page and
-  written to the new one, leaving the previous (possibly shared) page
-  untouched; otherwise the last page is read and updated in place.
-  Parameters: CSR ``page_indptr`` [B+1] / ``page_indices`` [nnz].  Notes:
-  every sequence holds at least one token before the decoded one.
-* modelopt ... linear_attention.decode, recurrent_decode_reference: an empty
-  call performs no write.
+* flashinfer.gdn_paged.gated_delta_rule_decode_paged, description: sequence
+  b ends with its decoded token, which occupies slot ``last_page_len[b]``
+  of the final page in its table row.  A decoded token in slot 1 starts
+  that page, so the pre-token state comes from the page before it, the
+  post-token state goes to the final page, and the page before (which
+  other sequences may share) keeps its contents; in any other slot the
+  final page is both the source and the destination.  Parameters: a CSR
+  table, ``page_indptr`` [B+1] and ``page_indices`` [nnz].  Notes: the
+  decoded token is never a sequence's first token.
+* modelopt ... linear_attention.decode, recurrent_decode_reference: a call
+  with no tokens writes nothing.
 
 Pins (tests/test_oracle_paging.py): brute force over small CSR tables
 against a token-position model (the state after token n lives on the page
@@ -57,9 +58,10 @@ def paged_suffix_rows(page_indices, page_indptr, last_page_len, page_size, n_suf
     n - n_suffix + 1 .. n (1-based), and at least one token precedes it
     (flashinfer.gdn_paged, Notes).
 
-    Returns (read row, [(i, row), ...]): the state is read from the page of
-    token n - n_suffix; after suffix token i (0-based) it is written to
-    ``row`` when that token fills its page or is the last token.
+    Returns (read row, [(i, row), ...]): the page holding token
+    n - n_suffix supplies the starting state; suffix token i (0-based)
+    stores its state to ``row`` when it completes a page or ends the
+    suffix.
     """
     start = int(page_indptr[b])
     n = (int(page_indptr[b + 1]) - start - 1) * page_size + int(last_page_len[b])

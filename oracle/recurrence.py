@@ -9,10 +9,11 @@ Pages followed:
   the previous state first, then do the delta write.  alpha = 1 is the pure
   delta rule, alpha = 0 forgets everything before writing.  KDA-lite decays
   with a vector alpha over key channels.
-* modelopt ... linear_attention.decode, recurrent_decode_reference: one
-  preactivated sequence at a time, scalar GDN or per-key-channel KDA log
-  gates, keys already aligned with value heads; an empty call does no write
-  and no initial-state quantisation.
+* modelopt ... linear_attention.decode, recurrent_decode_reference: the
+  reference takes one sequence whose activations are already applied, log
+  gates that are either one number per head (GDN) or a vector over the key
+  rows (KDA), and keys already mapped onto the value heads; called with no
+  tokens it neither writes nor quantises the initial state.
 
 Reading of the KDA decay axis (the Haddock text says "column" while its
 own o = q S convention makes rows the key index, and the kda_decode gate is

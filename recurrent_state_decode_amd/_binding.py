@@ -339,7 +339,7 @@ def gdn_decode_paged(q, k, v, a, b, A_log, dt_bias, page_indices, page_indptr, l
                      out=None, *, scale=None, use_qk_l2norm=True, beta_mode="logits", state_layout="V_FIRST",
                      out_dtype=None, qdq=None, block_v=64, quantize_initial=False, readout="working",
                      slots=None, stream=None):
-    """Single-token GDN decode on a CSR-paged pool (see gdn_decode_paged). Returns ``out`` [B, HV, V]."""
+    """GDN decode of one token per sequence on a CSR-paged pool (see gdn_decode_paged). Returns ``out`` [B, HV, V]."""
     return _paged("gdn_decode_paged", q, k, v, a, b, A_log, dt_bias, None, page_indices, page_indptr,
                   last_page_len, 0, state_pool, out, scale, use_qk_l2norm, beta_mode, state_layout, "original",
                   out_dtype, qdq, block_v, quantize_initial, readout, slots, stream)

@@ -234,7 +234,7 @@ def paged(kind, B, HK, HV, K, V, *, prefix_lengths=None, max_prefix=2048, page_s
 
 
 def gdn_paged(B, HK, HV, K, V, **kw):
-    """Single-token GDN decode on a CSR-paged pool with shared prefix pages."""
+    """One decoded token per sequence, GDN, on a CSR-paged pool with shared prefix pages."""
     kw.setdefault("name", "gdn_paged")
     return paged("gdn", B, HK, HV, K, V, **kw)
 
