@@ -94,3 +94,20 @@ def test_checked_build_refuses_a_page_written_by_two_suffixes(case):
     b1, b2 = [b for b in range(w.B) if cu[b + 1] > cu[b]][:2]
     d["page_indices"][int(ptr[b2 + 1]) - 1] = d["page_indices"][int(ptr[b1 + 1]) - 1]
     _refused_untouched(w, d, "write page")
+
+
+@pytest.mark.parametrize("qdq", ["fp8_e4m3_tile", "int8_hadamard32"])
+def test_checked_build_matches_release_on_packed_pools(qdq):
+    layout = "V_FIRST" if qdq == "fp8_e4m3_tile" else "K_FIRST"
+    suffix = np.array([0, 1, 2, 3, 4, 5, 8, 9, 7, 1, 4, 0])
+    w = wl.paged("gdn", len(suffix), 2, 4, 128, 128, max_prefix=30, page_size=4, share_frac=0.3, seed=66,
+                 suffix_lengths=suffix, state_layout=layout, qdq=qdq, block_v=64)
+    d = P.device_inputs(w)
+    pool_a = P.make_packed_pool(w, "cuda")
+    pool_b = pool_a.clone()
+    out_a = P.gpu_call(w, pool_a, d)
+    with rsd.checked_library() as lib:
+        assert lib.gdn_checked_build() == 1
+        out_b = P.gpu_call(w, pool_b, d)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b) and torch.equal(pool_a, pool_b)
