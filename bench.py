@@ -79,9 +79,16 @@ def algorithmic_bytes(w, storage="f32"):
         tile = w.K * w.V * 4
     state = 2 * active * w.HV * tile
     if w.kind.endswith("paged_varlen"):
-        # one tile read per sequence; every page a suffix fills or ends on is written
-        from tests import parity as P
-        n_writes = len(P.rows_for(w)[1])
+        # one tile read per sequence; every page a suffix fills or ends on is written: sequence b
+        # holds n = (pages - 1) page_size + last_page_len tokens and decodes its last T_b, so it writes
+        # a page for each multiple of page_size in (n - T_b, n], plus the last page unless n is one
+        ps = w.options["page_size"]
+        cu = w.inputs["cu_seqlens"].numpy().astype(np.int64)
+        ptr = w.inputs["page_indptr"].numpy().astype(np.int64)
+        lpl = w.inputs["last_page_len"].numpy().astype(np.int64)
+        t_b = np.diff(cu)
+        n = (np.diff(ptr) - 1) * ps + lpl
+        n_writes = int(np.sum(np.where(t_b > 0, n // ps - (n - t_b) // ps + (n % ps != 0), 0)))
         state = (active + n_writes) * w.HV * tile
     T = w.T
     per_tok = 2 * w.HK * w.K * esz + w.HV * w.V * esz + w.HV * w.V * osz
@@ -350,7 +357,6 @@ def main():
 
     import torch
     from recurrent_state_decode_amd import workloads as wl
-    from tests import parity as P
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -388,9 +394,9 @@ def main():
         w.name = f"{w.name}+{args.qdq}"
     if packed:
         w.name = f"{w.name}+{args.storage}"
-    d = P.device_inputs(w, dev)
+    d = wl.device_inputs(w, dev)
     # (a packed pool for timing: seeded random codes and scales)
-    pool = P.make_packed_pool(w, dev, rows=[]) if packed else wl.make_pool(w, dev)
+    pool = wl.random_packed_pool(w, dev) if packed else wl.make_pool(w, dev)
     out = torch.empty((w.T, w.HV, w.V), dtype=w.out_dtype, device=dev)
     flush = None if args.no_flush else torch.empty(512 * 1024 * 1024, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -400,7 +406,7 @@ def main():
     def step(i):
         if flush is not None:
             flush.fill_(float(i & 7))
-        P.gpu_call(w, pool, d, out=out)
+        wl.run(w, pool, d, out=out)
 
     for i in range(args.warmup):
         step(i)
@@ -414,7 +420,7 @@ def main():
         if flush is not None:
             flush.fill_(float(i & 7))
         starts[i].record(stream)
-        P.gpu_call(w, pool, d, out=out)
+        wl.run(w, pool, d, out=out)
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

@@ -80,6 +80,80 @@ def make_pool(w, device, dtype=torch.float32):
     return pool
 
 
+def device_inputs(w, device="cuda"):
+    """The workload's input tensors on ``device`` (index arrays and activations alike)."""
+    return {k: (None if v is None else v.to(device)) for k, v in w.inputs.items() if k != "prefix_lengths"}
+
+
+def random_packed_pool(w, device):
+    """A uint8 packed pool [rows, HV, tile bytes] of seeded random codes with positive scales, for the
+    workload's state quantisation (qdq 'fp8_e4m3_tile' or 'int8_hadamard32'); fp8 NaN codes (0x7f,
+    0xff) are replaced by +-448 (0x7e, 0xfe)."""
+    from . import _binding as bnd
+    K, V, HV, n = w.K, w.V, w.HV, w.num_rows
+    fp8 = w.options.get("qdq") == "fp8_e4m3_tile"
+    bv = w.options.get("block_v", 64)
+    tb = bnd.fp8_tile_bytes(K, V, bv) if fp8 else bnd.packed_tile_bytes(K, V)
+    nsc = V // bv if fp8 else K * V // 32
+    g = torch.Generator(device=device)
+    g.manual_seed(w.pool_seed + 7)
+    packed = torch.randint(0, 256, (n, HV, tb), dtype=torch.uint8, device=device, generator=g)
+    if fp8:
+        c = packed[:, :, :K * V]
+        packed[:, :, :K * V] = torch.where((c & 0x7F) == 0x7F, c ^ 1, c)
+    sc = torch.empty((n, HV, nsc), dtype=torch.float32, device=device).uniform_(1e-3, 1e-2, generator=g)
+    packed[:, :, K * V:K * V + 4 * nsc] = sc.view(torch.uint8)
+    return packed
+
+
+def call_options(w, over, drop=()):
+    """The workload's binding options (``page_size`` removed), updated by ``over``, without ``drop``."""
+    o = dict(w.options)
+    o.pop("page_size", None)
+    o.update(over)
+    for k in drop:
+        o.pop(k, None)
+    return o
+
+
+def run(w, pool, d, out=None, **over):
+    """Run workload ``w`` on the device pool through the binding (inputs ``d`` from device_inputs).
+    Returns ``out``."""
+    import recurrent_state_decode_amd as rsd
+    common = dict(state_layout=w.state_layout, out_dtype=w.out_dtype, **call_options(w, over))
+    ps = w.options.get("page_size")
+    if w.kind == "gdn_pooled":
+        return rsd.gdn_decode_pooled(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                                     d["cu_seqlens"], d["state_indices"], pool, out, **common)
+    if w.kind == "kda_pooled":
+        return rsd.kda_decode_pooled(d["q"], d["k"], d["v"], d["raw_gate"], d["beta_logits"], d["a_log"],
+                                     d["dt_bias"], d["cu_seqlens"], d["state_indices"], pool, out, **common)
+    table = (d["page_indices"], d["page_indptr"], d["last_page_len"])
+    if w.kind == "gdn_paged":
+        return rsd.gdn_decode_paged(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"], *table,
+                                    pool, out, **common)
+    if w.kind == "kda_paged":
+        return rsd.kda_decode_paged(d["q"], d["k"], d["v"], d["raw_gate"], d["beta_logits"], d["a_log"],
+                                    d["dt_bias"], *table, pool, out, **common)
+    if w.kind == "gdn_paged_varlen" and w.chunked:
+        o = {k2: v2 for k2, v2 in common.items() if k2 in ("scale", "use_qk_l2norm", "beta_mode", "state_layout",
+                                                            "out_dtype")}
+        return rsd.gdn_prefill_paged(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                                     d["cu_seqlens"], *table, ps, pool, out, **o)
+    if w.kind == "gdn_paged_varlen":
+        return rsd.gdn_decode_paged_varlen(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                                           d["cu_seqlens"], *table, ps, pool, out, **common)
+    if w.kind == "kda_paged_varlen" and w.chunked:
+        o = {k2: v2 for k2, v2 in common.items() if k2 in ("scale", "use_qk_l2norm", "beta_mode", "state_layout",
+                                                            "out_dtype", "gate_mode")}
+        return rsd.kda_prefill_paged(d["q"], d["k"], d["v"], d["raw_gate"], d["beta_logits"], d["a_log"],
+                                     d["dt_bias"], d["cu_seqlens"], *table, ps, pool, out, **o)
+    if w.kind == "kda_paged_varlen":
+        return rsd.kda_decode_paged_varlen(d["q"], d["k"], d["v"], d["raw_gate"], d["beta_logits"], d["a_log"],
+                                           d["dt_bias"], d["cu_seqlens"], *table, ps, pool, out, **common)
+    raise ValueError(w.kind)
+
+
 def _cast(x, dtype):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dtype)
 

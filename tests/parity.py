@@ -59,8 +59,9 @@ STATE_RTOL = 2e-3
 OUT_REL_L2 = 2e-3
 
 
-def device_inputs(w, device="cuda"):
-    return {k: (None if v is None else v.to(device)) for k, v in w.inputs.items() if k != "prefix_lengths"}
+device_inputs = wl.device_inputs
+gpu_call = wl.run
+_opts = wl.call_options
 
 
 def host64(t):
@@ -69,51 +70,6 @@ def host64(t):
 
 def host_int(t):
     return None if t is None else t.detach().to("cpu").to(torch.int64).numpy()
-
-
-def _opts(w, over, drop=()):
-    o = dict(w.options)
-    o.pop("page_size", None)
-    o.update(over)
-    for k in drop:
-        o.pop(k, None)
-    return o
-
-
-def gpu_call(w, pool, d, out=None, **over):
-    """Run workload ``w`` on the device pool through the binding. Returns ``out``."""
-    common = dict(state_layout=w.state_layout, out_dtype=w.out_dtype, **_opts(w, over))
-    ps = w.options.get("page_size")
-    if w.kind == "gdn_pooled":
-        return rsd.gdn_decode_pooled(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
-                                     d["cu_seqlens"], d["state_indices"], pool, out, **common)
-    if w.kind == "kda_pooled":
-        return rsd.kda_decode_pooled(d["q"], d["k"], d["v"], d["raw_gate"], d["beta_logits"], d["a_log"],
-                                     d["dt_bias"], d["cu_seqlens"], d["state_indices"], pool, out, **common)
-    table = (d["page_indices"], d["page_indptr"], d["last_page_len"])
-    if w.kind == "gdn_paged":
-        return rsd.gdn_decode_paged(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"], *table,
-                                    pool, out, **common)
-    if w.kind == "kda_paged":
-        return rsd.kda_decode_paged(d["q"], d["k"], d["v"], d["raw_gate"], d["beta_logits"], d["a_log"],
-                                    d["dt_bias"], *table, pool, out, **common)
-    if w.kind == "gdn_paged_varlen" and w.chunked:
-        o = {k2: v2 for k2, v2 in common.items() if k2 in ("scale", "use_qk_l2norm", "beta_mode", "state_layout",
-                                                            "out_dtype")}
-        return rsd.gdn_prefill_paged(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
-                                     d["cu_seqlens"], *table, ps, pool, out, **o)
-    if w.kind == "gdn_paged_varlen":
-        return rsd.gdn_decode_paged_varlen(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
-                                           d["cu_seqlens"], *table, ps, pool, out, **common)
-    if w.kind == "kda_paged_varlen" and w.chunked:
-        o = {k2: v2 for k2, v2 in common.items() if k2 in ("scale", "use_qk_l2norm", "beta_mode", "state_layout",
-                                                            "out_dtype", "gate_mode")}
-        return rsd.kda_prefill_paged(d["q"], d["k"], d["v"], d["raw_gate"], d["beta_logits"], d["a_log"],
-                                     d["dt_bias"], d["cu_seqlens"], *table, ps, pool, out, **o)
-    if w.kind == "kda_paged_varlen":
-        return rsd.kda_decode_paged_varlen(d["q"], d["k"], d["v"], d["raw_gate"], d["beta_logits"], d["a_log"],
-                                           d["dt_bias"], d["cu_seqlens"], *table, ps, pool, out, **common)
-    raise ValueError(w.kind)
 
 
 def written_rows(w, b):
@@ -416,16 +372,8 @@ def make_packed_pool(w, device="cuda", rows=None):
     K, V, HV, n = w.K, w.V, w.HV, w.num_rows
     fp8 = _is_fp8(w)
     bv = w.options.get("block_v", 64)
-    tb = packed_bytes(w)
-    nsc = V // bv if fp8 else K * V // 32
-    g = torch.Generator(device=device)
-    g.manual_seed(w.pool_seed + 7)
-    packed = torch.randint(0, 256, (n, HV, tb), dtype=torch.uint8, device=device, generator=g)
-    if fp8:                                  # no NaN codes (0x7f, 0xff): they become +-448 (0x7e, 0xfe)
-        c = packed[:, :, :K * V]
-        packed[:, :, :K * V] = torch.where((c & 0x7F) == 0x7F, c ^ 1, c)
-    sc = torch.empty((n, HV, nsc), dtype=torch.float32, device=device).uniform_(1e-3, 1e-2, generator=g)
-    packed[:, :, K * V:K * V + 4 * nsc] = sc.view(torch.uint8)
+    assert packed_bytes(w) == (rsd.fp8_tile_bytes(K, V, bv) if fp8 else rsd.packed_tile_bytes(K, V))
+    packed = wl.random_packed_pool(w, device)
     rows = list(range(n)) if rows is None else sorted(set(rows))
     if rows:
         fp32 = wl.make_pool(w, device)
