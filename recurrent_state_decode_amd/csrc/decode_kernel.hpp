@@ -964,10 +964,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
     if constexpr (!AV) {
       if (w == 0 && rg == 0) store_out4(out_row + 4 * lr, o);
     } else {
+      // a select per row; the empty asm keeps the compiler from turning the
+      // chain into an indexed load from a stack copy of o (scratch memory)
       float my_o = o[0];
 #pragma unroll
-      for (int s = 1; s < NS; ++s)
-        if (lr == s) my_o = o[s];
+      for (int s = 1; s < NS; ++s) {
+        my_o = (lr == s) ? o[s] : my_o;
+        asm volatile("" : "+v"(my_o));
+      }
       if (lr < NS) store_out1(out_row + row_idx(lr), my_o);
     }
   };
