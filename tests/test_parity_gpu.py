@@ -154,6 +154,36 @@ def test_qdq_rounding_matches_e4m3_grid_exactly(layout):
     _report(f"qdq_exact/{layout}", rep)
 
 
+@pytest.mark.parametrize("layout", ["K_FIRST", "V_FIRST"])
+def test_qdq_tiny_tiles_use_the_amax_floor(layout):
+    """A tile whose amax is below 2^-100 is rounded as if its amax were 2^-100 (the kernel's floor, so that
+    448 / amax stays finite): with alpha = 1 and beta = 0 the stored state is exactly
+    fp32(e4m3(x * 448 * 2^100) * fp32(2^-100 / 448)), every product in float32; an all-zero tile stays
+    zero."""
+    from oracle import e4m3
+    B, HV, K, V = 4, 2, 128, 128
+    w = wl.gdn_pooled(B, 1, HV, K, V, lengths=[1] * B, num_slots=B, state_layout=layout, seed=39,
+                      io_dtype=torch.float32, qdq="fp8_e4m3_tile", block_v=64)
+    w.inputs["a"] = torch.full((B, HV), -float("inf"))     # alpha = 1
+    w.inputs["b"] = torch.zeros((B, HV))                   # beta = 0 (probability mode)
+    w.options["beta_mode"] = "probability"
+    rng = np.random.default_rng(40)
+    logical = (rng.standard_normal((B, HV, K, V)) * 1e-33).astype(np.float32)   # amax ~ 5e-33 < 2^-100
+    logical[1, 1, :, 64:] = 0.0                                                  # one all-zero tile
+    tiles = logical if layout == "K_FIRST" else np.swapaxes(logical, -1, -2)
+    pool = torch.from_numpy(np.ascontiguousarray(tiles)).cuda()
+    P.gpu_call(w, pool, P.device_inputs(w))
+    torch.cuda.synchronize()
+    got = pool.cpu().numpy()
+    got_logical = got if layout == "K_FIRST" else np.swapaxes(got, -1, -2)
+    assert float(np.abs(logical).max()) < 2.0 ** -100
+    y = (logical * np.float32(448.0 * 2.0 ** 100)).astype(np.float32)
+    codes = e4m3.e4m3_round(y.astype(np.float64)).astype(np.float32)
+    expect = codes * np.float32(2.0 ** -100 / 448.0)
+    assert np.array_equal(got_logical, expect)
+    assert not got_logical[1, 1, :, 64:].any()
+
+
 # ---------------------------------------------------------------- closed forms on the GPU
 
 @pytest.mark.parametrize("layout", ["K_FIRST", "V_FIRST"])
