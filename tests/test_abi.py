@@ -91,6 +91,10 @@ def test_pooled_argument_errors():
     assert _pooled(lib, scale=float("inf")) == bnd.GDN_ERR_INVALID
     # an empty call (T = 0 with cu_seqlens) launches nothing and succeeds
     assert _pooled(lib, T=0) == bnd.GDN_OK
+    # a grid beyond 2^31 - 1 workgroups is refused before any launch (B HV V / VB units)
+    big = 1 << 26
+    assert _pooled(lib, cu=None, B=big, T=big, HK=16, HV=32, state_layout=1) == bnd.GDN_ERR_UNSUPPORTED
+    assert "too large" in lib.gdn_last_error().decode()
 
 
 @no_gpu
