@@ -57,13 +57,14 @@ extern "C" {
 #endif
 
 /* Status codes.  The mapping follows max.nn.state_space.kda_decode, Raises:
- * a dtype grouping that binds no kernel, or ranks/extents that disagree,
- * are reported on the host before any launch. */
+ * a type combination with no compiled kernel, or tensor extents that do not
+ * fit together, are reported on the host before any launch. */
 enum gdn_status {
   GDN_OK = 0,
   GDN_ERR_INVALID = 1,      /* null required pointer, dimension <= 0, HV % HK != 0, bad enum */
   GDN_ERR_SHAPE = 2,        /* extents disagree (e.g. T != B without cu_seqlens) */
-  GDN_ERR_UNSUPPORTED = 3,  /* valid request with no compiled kernel (head dims, block_v, gate_mode) */
+  GDN_ERR_UNSUPPORTED = 3,  /* valid request with no compiled kernel (head dims, block_v, gate_mode,
+                               storage and layout, a grid beyond 2^31 - 1 workgroups) */
   GDN_ERR_HIP = 4,          /* the HIP launch reported an error */
   GDN_ERR_PRECONDITION = 5  /* an index precondition does not hold: gdn_check_* calls, and every
                                call of a library built with GDN_DEVICE_CHECKS */
