@@ -209,7 +209,9 @@ def qdq_bounds(w, trace, seqs):
             al = al[:, None, None] if al.ndim == 1 else al[:, :, None]
             aE = al * E
             kabs = np.abs(rec["k_hat"])
-            carried = aE + rec["beta"][:, None, None] * kabs[:, :, None] * np.einsum("hk,hkv->hv", kabs, aE)[:, None, :]
+            # |beta|: in probability mode beta is b itself, any real number
+            babs = np.abs(rec["beta"])
+            carried = aE + babs[:, None, None] * kabs[:, :, None] * np.einsum("hk,hkv->hv", kabs, aE)[:, None, :]
             S = rec["S_out"]
             E_new = carried + rounding(S, carried) + 1e-5 * np.abs(S)
             if stored:
@@ -217,7 +219,7 @@ def qdq_bounds(w, trace, seqs):
             else:
                 qk = np.abs(np.sum(rec["q_hat"] * rec["k_hat"], axis=-1))
                 bound = (np.einsum("hk,hkv->hv", np.abs(rec["q_hat"]), aE)
-                         + (qk * rec["beta"])[:, None] * np.einsum("hk,hkv->hv", kabs, aE))
+                         + (qk * babs)[:, None] * np.einsum("hk,hkv->hv", kabs, aE))
             out_b[t0 + i] = bound
             E = E_new
             state_b.setdefault(b, []).append(E)

@@ -120,6 +120,22 @@ def test_qdq_variants(layout, kind, extra):
     _report(f"qdq/{kind}/{layout}/{extra}", rep)
 
 
+@pytest.mark.parametrize("qdq", ["fp8_e4m3_tile", "int8_hadamard32"])
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_qdq_with_probability_beta_of_either_sign(qdq, kind):
+    """beta_mode='probability' passes b as beta unchanged; with b ~ N(0, 1) beta takes both signs and
+    values above 1, and the rounding errors must still stay within the bounds propagated with |beta|."""
+    mk = wl.gdn_pooled if kind == "gdn" else wl.kda_pooled
+    w = mk(8, 1, 2, 128, 128, lengths=[5, 1, 0, 8, 3, 2, 6, 4], num_slots=10, state_layout="K_FIRST", seed=41,
+           qdq=qdq, block_v=64, beta_mode="probability")
+    beta = w.inputs["b" if kind == "gdn" else "beta_logits"].float()
+    assert bool((beta < 0).any()) and bool((beta > 1).any())
+    rep, _, _ = P.run_and_check(w)
+    _report(f"qdq_prob_beta/{qdq}/{kind}", rep)
+    rep, _, _ = P.run_and_check_packed(w)
+    _report(f"qdq_prob_beta_packed/{qdq}/{kind}", rep)
+
+
 @pytest.mark.parametrize("layout", ["K_FIRST", "V_FIRST"])
 def test_qdq_rounding_matches_e4m3_grid_exactly(layout):
     """alpha = 1 and beta = 0 leave the state unchanged, so the stored state is the tile QDQ of the
