@@ -226,6 +226,19 @@ def qdq_bounds(w, trace, seqs):
     return out_b, state_b
 
 
+def non_expanding(trace):
+    """True when no traced token amplifies an error along its key: |1 - beta |k_hat|^2| <= 1.  The
+    delta write maps an error E to (I - beta k k^T) E along k, so with unnormalised keys or beta
+    outside [0, 1] one rounding difference grows every token; the flip-rate checks below (which
+    catch a wrong rounding rule) only apply when it cannot.  The element-wise bounds apply always."""
+    for recs in trace.values():
+        for rec in recs:
+            kk = np.sum(np.asarray(rec["k_hat"], dtype=np.float64) ** 2, axis=-1)
+            if np.any(np.abs(1.0 - np.asarray(rec["beta"], dtype=np.float64) * kk) > 1.0 + 1e-9):
+                return False
+    return True
+
+
 class Report:
     """Collects worst normalised errors for printing next to the pass/fail assertions."""
 
@@ -264,7 +277,7 @@ def compare_outputs(gpu_out, ref, w, rows, report, qdq_bound=None):
     assert rel <= l2_tol, f"output relative L2 error {rel} > {l2_tol}"
 
 
-def compare_states(gpu_rows, ref_rows, report, qdq_bound=None, layout="K_FIRST", codec=None):
+def compare_states(gpu_rows, ref_rows, report, qdq_bound=None, layout="K_FIRST", codec=None, flip_check=True):
     """fp32 states within the relative tolerance, or (QDQ) within the propagated bounds {row: [H, K, V]}."""
     assert set(gpu_rows) == set(ref_rows)
     flips, total = 0, 0
@@ -295,7 +308,8 @@ def compare_states(gpu_rows, ref_rows, report, qdq_bound=None, layout="K_FIRST",
         assert bad.size == 0, f"row {row}: {len(bad)} state elements out of tolerance, first {bad[:3].tolist()}"
     if qdq_bound is not None and total:
         report.add("qdq_state_diff_frac", flips / total)
-        assert flips / total < 1e-3, f"{flips} of {total} QDQ state elements differ: rounding rule mismatch?"
+        assert not flip_check or flips / total < 1e-3, \
+            f"{flips} of {total} QDQ state elements differ: rounding rule mismatch?"
 
 
 def check_untouched(pool_before, pool_after, write_rows, chunk_rows=256):
@@ -342,7 +356,7 @@ def run_and_check(w, seqs=None, report=None, pool=None, snapshot=True, check_all
         compare_outputs(out, ref_out, w, trows, report, qdq_bound=bound)
     got = gather_rows(pool, list(ref_written))
     compare_states(got, ref_written, report, qdq_bound=state_bound, layout=w.state_layout,
-                   codec=w.options.get("qdq"))
+                   codec=w.options.get("qdq"), flip_check=trace is None or non_expanding(trace))
     assert sorted(ref_written) == sorted(set(writes))
     if snap is not None:
         check_untouched(snap, pool, all_writes)
@@ -446,14 +460,15 @@ def run_and_check_packed(w, seqs=None, report=None, pool=None, **over):
         compare_outputs(out, ref_out, w, trows, report, qdq_bound=full[trows])
     state_bound = {row: seq_b[b][i] for b in seq_list if b in seq_b for i, row in written_rows(w, b)}
     got = gather_packed(pool, list(ref_written), w.K, w.V)
+    stable = non_expanding(trace)
     compare_states({r: ohad.int8_hadamard32_decode(c, s) for r, (c, s) in got.items()}, ref_written, report,
-                   qdq_bound=state_bound, layout="K_FIRST", codec="int8_hadamard32")
+                   qdq_bound=state_bound, layout="K_FIRST", codec="int8_hadamard32", flip_check=stable)
     flips, total, worst_scale, off_scales, groups = 0, 0, 0.0, 0, 0
     for r, ref in ref_written.items():
         code_e, scale_e = ohad.int8_hadamard32_encode(ref, "float32")
         code_g, scale_g = got[r]
         dc = np.abs(code_g.astype(np.int32) - code_e.astype(np.int32))
-        assert dc.max() <= 1, f"row {r}: a code differs by {dc.max()}"
+        assert not stable or dc.max() <= 1, f"row {r}: a code differs by {dc.max()}"
         flips += int(np.sum(dc))
         total += dc.size
         pos = scale_e > 0
@@ -464,11 +479,12 @@ def run_and_check_packed(w, seqs=None, report=None, pool=None, **over):
         assert np.all(scale_g[~pos] < 1e-30)
     report.add("packed_code_flip_frac", flips / max(total, 1))
     report.add("packed_scale_max_rel", worst_scale)
-    assert flips / max(total, 1) < 1e-3, f"{flips} of {total} codes differ"
-    # a code rounded the other way at an earlier token moves that group's next amax (so its scale) by
-    # up to about a step, 1/127 of it; such groups must stay rare, like the flips themselves
-    assert worst_scale < 1e-2, f"scale relative error {worst_scale}"
-    assert off_scales <= max(1, groups // 100), f"{off_scales} of {groups} scales differ by more than 1e-5"
+    if stable:
+        assert flips / max(total, 1) < 1e-3, f"{flips} of {total} codes differ"
+        # a code rounded the other way at an earlier token moves that group's next amax (so its scale)
+        # by up to about a step, 1/127 of it; such groups must stay rare, like the flips themselves
+        assert worst_scale < 1e-2, f"scale relative error {worst_scale}"
+        assert off_scales <= max(1, groups // 100), f"{off_scales} of {groups} scales differ by more than 1e-5"
     assert sorted(ref_written) == sorted(set(writes))
     check_untouched(snap, pool, all_writes)
     return report, out, pool
@@ -501,8 +517,9 @@ def _run_and_check_fp8(w, seqs, report, pool, **over):
         compare_outputs(out, ref_out, w, trows, report, qdq_bound=full[trows])
     state_bound = {row: seq_b[b][i] for b in seq_list if b in seq_b for i, row in written_rows(w, b)}   # logical
     got = gather_fp8(pool, list(ref_written), w)
+    stable = non_expanding(trace)
     compare_states({r: decode_fp8(c, s, w) for r, (c, s) in got.items()}, ref_written, report,
-                   qdq_bound=state_bound, layout=w.state_layout)
+                   qdq_bound=state_bound, layout=w.state_layout, flip_check=stable)
     table = e4m3.e4m3_table()
     flips, total, worst_scale = 0, 0, 0.0
     for r, ref in ref_written.items():
@@ -524,9 +541,11 @@ def _run_and_check_fp8(w, seqs, report, pool, **over):
         worst_scale = max(worst_scale, float(rel.max()) if rel.size else 0.0)
     report.add("fp8_code_flip_frac", flips / max(total, 1))
     report.add("fp8_scale_max_rel", worst_scale)
-    assert flips / max(total, 1) < 1e-3, f"{flips} of {total} codes differ"
-    # a code rounded the other way at an earlier token moves the tile's later amax by a fraction of a step
-    assert worst_scale < 1e-2, f"scale relative error {worst_scale}"
+    if stable:
+        assert flips / max(total, 1) < 1e-3, f"{flips} of {total} codes differ"
+        # a code rounded the other way at an earlier token moves the tile's later amax by a fraction of
+        # a step
+        assert worst_scale < 1e-2, f"scale relative error {worst_scale}"
     assert sorted(ref_written) == sorted(set(writes))
     check_untouched(snap, pool, all_writes)
     return report, out, pool
