@@ -75,3 +75,20 @@ def test_random_case(i):
           f"packed={packed} options={w.options}", flush=True)
     rep, _, _ = P.run_and_check_packed(w) if packed else P.run_and_check(w)
     print(f"[sweep {i}] {rep}", flush=True)
+
+
+@pytest.mark.parametrize("i", range(0, N_CASES, 4))
+def test_random_case_checked_build_accepts_and_matches(i):
+    """The GDN_DEVICE_CHECKS build accepts every drawn (valid) call and gives the release build's outputs
+    and pool bit for bit."""
+    import recurrent_state_decode_amd as rsd
+    w, packed = _case(i)
+    d = P.device_inputs(w)
+    pool_a = P.make_packed_pool(w, "cuda") if packed else wl.make_pool(w, "cuda")
+    pool_b = pool_a.clone()
+    out_a = P.gpu_call(w, pool_a, d)
+    with rsd.checked_library() as lib:
+        assert lib.gdn_checked_build() == 1
+        out_b = P.gpu_call(w, pool_b, d)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b) and torch.equal(pool_a, pool_b)
