@@ -726,3 +726,17 @@ def test_fp8_packed_gdn_b512_t4_sampled():
     pool = P.make_packed_pool(w, "cuda", rows=reads)
     rep, _, _ = P.run_and_check_packed(w, seqs=seqs, pool=pool)
     _report("fp8_packed/b512_t4_sampled", rep)
+
+
+@pytest.mark.parametrize("storage", ["fp8", "i8h32"])
+def test_packed_paged_gdn_b256_sampled(storage):
+    """The headline paged shape (B=256, HV=32, K=V=128, page size 16) on a packed pool, as bench.py
+    --storage times it (fp8: its V_FIRST pool and 128-thread shape; i8h32: K_FIRST), sampled sequences."""
+    layout = "V_FIRST" if storage == "fp8" else "K_FIRST"
+    w = wl.paged_gdn_b256(state_layout=layout)
+    w.options.update(qdq="fp8_e4m3_tile" if storage == "fp8" else "int8_hadamard32", block_v=64)
+    seqs = sorted(np.random.default_rng(11).choice(w.B, 32, replace=False).tolist())
+    reads, _ = P.rows_for(w, seqs)
+    pool = P.make_packed_pool(w, "cuda", rows=reads)
+    rep, _, _ = P.run_and_check_packed(w, seqs=seqs, pool=pool)
+    _report(f"packed_{storage}/paged_gdn_b256_sampled", rep)
