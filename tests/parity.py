@@ -277,8 +277,13 @@ def compare_outputs(gpu_out, ref, w, rows, report, qdq_bound=None):
     assert rel <= l2_tol, f"output relative L2 error {rel} > {l2_tol}"
 
 
-def compare_states(gpu_rows, ref_rows, report, qdq_bound=None, layout="K_FIRST", codec=None, flip_check=True):
-    """fp32 states within the relative tolerance, or (QDQ) within the propagated bounds {row: [H, K, V]}."""
+def compare_states(gpu_rows, ref_rows, report, qdq_bound=None, layout="K_FIRST", codec=None, flip_check=True,
+                   block_v=64):
+    """fp32 states within the relative tolerance, or (QDQ) within the propagated bounds {row: [H, K, V]}.
+
+    With QDQ, an element counts as rounded the other way (a flip) when it moves by more than half a
+    quantisation step of its tile (fp8) or group (codec); a scale that moved because an earlier flip
+    changed the tile's amax shifts every element by much less than that and is not counted."""
     assert set(gpu_rows) == set(ref_rows)
     flips, total = 0, 0
     for row, ref in ref_rows.items():
@@ -295,7 +300,12 @@ def compare_states(gpu_rows, ref_rows, report, qdq_bound=None, layout="K_FIRST",
                 flips += int(np.sum(dy > 0.25 * np.max(np.abs(yr), axis=-1, keepdims=True) / 127))
                 total += dy.size
             else:
-                flips += int(np.sum(diff > 1e-5 * np.abs(logical) + 1e-30))
+                # the oracle's state is on its tiles' grids: scale = amax / 448 per [K, block_v] tile
+                H, K, V = logical.shape
+                amax = np.abs(logical).reshape(H, K, V // block_v, block_v).max(axis=(1, 3))
+                sc = np.repeat(amax / 448.0, block_v, axis=-1)[:, None, :]
+                step = e4m3.e4m3_spacing(np.abs(logical) / np.where(sc > 0, sc, 1.0)) * sc
+                flips += int(np.sum(diff > 0.5 * step + 1e-30))
                 total += diff.size
             report.add("qdq_state_bound_ratio", (diff / np.maximum(tol, 1e-300)).max())
         else:
@@ -356,7 +366,8 @@ def run_and_check(w, seqs=None, report=None, pool=None, snapshot=True, check_all
         compare_outputs(out, ref_out, w, trows, report, qdq_bound=bound)
     got = gather_rows(pool, list(ref_written))
     compare_states(got, ref_written, report, qdq_bound=state_bound, layout=w.state_layout,
-                   codec=w.options.get("qdq"), flip_check=trace is None or non_expanding(trace))
+                   codec=w.options.get("qdq"), flip_check=trace is None or non_expanding(trace),
+                   block_v=w.options.get("block_v", 64))
     assert sorted(ref_written) == sorted(set(writes))
     if snap is not None:
         check_untouched(snap, pool, all_writes)
@@ -468,7 +479,13 @@ def run_and_check_packed(w, seqs=None, report=None, pool=None, **over):
         code_e, scale_e = ohad.int8_hadamard32_encode(ref, "float32")
         code_g, scale_g = got[r]
         dc = np.abs(code_g.astype(np.int32) - code_e.astype(np.int32))
-        assert not stable or dc.max() <= 1, f"row {r}: a code differs by {dc.max()}"
+        # codes of a group whose scale agrees differ by at most two: a code rounded the other way at one
+        # token is carried into the next by the decay (alpha ~ 1), and that token's own rounding can land
+        # one more step away; a group whose scale moved (an earlier flip changed its amax) is held by the
+        # scale checks below, every group by the element-wise bounds above
+        same = np.abs(scale_g - scale_e) <= 1e-5 * np.abs(scale_e)
+        dcg = dc.reshape(dc.shape[0], dc.shape[1], dc.shape[2] // 32, 32).max(axis=-1)
+        assert not stable or dcg[same].max(initial=0) <= 2, f"row {r}: a code differs by {dcg[same].max()}"
         flips += int(np.sum(dc))
         total += dc.size
         pos = scale_e > 0
@@ -519,7 +536,7 @@ def _run_and_check_fp8(w, seqs, report, pool, **over):
     got = gather_fp8(pool, list(ref_written), w)
     stable = non_expanding(trace)
     compare_states({r: decode_fp8(c, s, w) for r, (c, s) in got.items()}, ref_written, report,
-                   qdq_bound=state_bound, layout=w.state_layout, flip_check=stable)
+                   qdq_bound=state_bound, layout=w.state_layout, flip_check=stable, block_v=bv)
     table = e4m3.e4m3_table()
     flips, total, worst_scale = 0, 0, 0.0
     for r, ref in ref_written.items():

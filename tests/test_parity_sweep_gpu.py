@@ -10,10 +10,13 @@ from tests import parity as P
 
 pytestmark = pytest.mark.gpu
 N_CASES = 200
+N_LARGE = 120
 
 
-def _case(i):
-    rng = np.random.default_rng([20261203, i])
+def _case(i, large=False):
+    """Case i of the small draw, or (large) of the draw with 20-63 sequences, 8 value heads and V up to 320
+    (several V-blocks per head, ragged tails of the grid)."""
+    rng = np.random.default_rng([777 if large else 20261203, i])
     kind = str(rng.choice(["gdn", "kda"]))
     layout = str(rng.choice(["K_FIRST", "V_FIRST"]))
     path = str(rng.choice(["pooled", "paged", "varlen", "prefill", "k16"]))
@@ -37,21 +40,25 @@ def _case(i):
             opts["readout"] = "stored"
         if rng.random() < 0.3:
             opts["quantize_initial"] = True
-    B = int(rng.integers(1, 20))
-    V = int(rng.choice([64, 128, 192])) if not q.startswith("codec") else int(rng.choice([64, 128]))
+    B = int(rng.integers(20, 64)) if large else int(rng.integers(1, 20))
+    if large:
+        V = int(rng.choice([128, 256, 320])) if not q.startswith("codec") else int(rng.choice([128, 256]))
+    else:
+        V = int(rng.choice([64, 128, 192])) if not q.startswith("codec") else int(rng.choice([64, 128]))
+    HK, HV = (2, 8) if large else (1, 2)
     if path == "pooled":
         lens = rng.integers(0, 7, B).tolist()
         lens[0] = max(1, lens[0])
         mk = wl.gdn_pooled if kind == "gdn" else wl.kda_pooled
-        w = mk(B, 1, 2, 128, V, lengths=lens, num_slots=B + 3, state_layout=layout, io_dtype=io, out_dtype=out,
+        w = mk(B, HK, HV, 128, V, lengths=lens, num_slots=B + 3, state_layout=layout, io_dtype=io, out_dtype=out,
                seed=seed, **opts)
     elif path == "paged":
-        w = wl.paged(kind, B, 1, 2, 128, V, max_prefix=40, page_size=4, share_frac=0.3, state_layout=layout,
+        w = wl.paged(kind, B, HK, HV, 128, V, max_prefix=40, page_size=4, share_frac=0.3, state_layout=layout,
                      io_dtype=io, out_dtype=out, seed=seed, **opts)
     elif path == "varlen":
         suf = rng.integers(0, 8, B)
         suf[0] = max(1, suf[0])
-        w = wl.paged(kind, B, 1, 2, 128, V, max_prefix=30, page_size=int(rng.choice([2, 4, 16])), share_frac=0.3,
+        w = wl.paged(kind, B, HK, HV, 128, V, max_prefix=30, page_size=int(rng.choice([2, 4, 16])), share_frac=0.3,
                      suffix_lengths=suf, state_layout=layout, io_dtype=io, out_dtype=out, seed=seed, **opts)
     elif path == "prefill":
         suf = rng.integers(0, 70, min(B, 5))
@@ -68,13 +75,22 @@ def _case(i):
     return w, q in ("fp8p", "codecp")
 
 
-@pytest.mark.parametrize("i", range(N_CASES))
-def test_random_case(i):
-    w, packed = _case(i)
-    print(f"[sweep {i}] {w.kind} {w.state_layout} B={w.B} K={w.K} V={w.V} T={w.T} chunked={w.chunked} "
-          f"packed={packed} options={w.options}", flush=True)
+def _run(i, large):
+    w, packed = _case(i, large)
+    print(f"[sweep {'large ' if large else ''}{i}] {w.kind} {w.state_layout} B={w.B} K={w.K} V={w.V} T={w.T} "
+          f"chunked={w.chunked} packed={packed} options={w.options}", flush=True)
     rep, _, _ = P.run_and_check_packed(w) if packed else P.run_and_check(w)
     print(f"[sweep {i}] {rep}", flush=True)
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_case(i):
+    _run(i, large=False)
+
+
+@pytest.mark.parametrize("i", range(N_LARGE))
+def test_random_large_case(i):
+    _run(i, large=True)
 
 
 @pytest.mark.parametrize("i", range(0, N_CASES, 4))
