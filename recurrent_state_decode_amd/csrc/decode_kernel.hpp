@@ -1011,7 +1011,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
         for (int j = 0; j < 4; ++j)
           c4 |= (static_cast<uint32_t>(static_cast<int32_t>(__builtin_rintf(S[s][j] * inv))) & 0xffu) << (8 * j);
         __builtin_nontemporal_store(c4, reinterpret_cast<uint32_t*>(gb + r * 32));
-        if ((lr & 7) == 0) __builtin_nontemporal_store(cs[KDA ? s : 0] * (mf * (1.0f / 127.0f)), tsc + grp * K + r);
+        // a plain store: the group's scales are 4-byte pieces from many lanes and waves, which L2 merges into
+        // whole lines before writing them back (streamed past L2 each would cost a line)
+        if ((lr & 7) == 0) tsc[grp * K + r] = cs[KDA ? s : 0] * (mf * (1.0f / 127.0f));
       }
     } else if constexpr (FP8P) {
       // every token ends with qdq_tile: grid values, converted exactly; the
