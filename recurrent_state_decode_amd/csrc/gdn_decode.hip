@@ -604,6 +604,9 @@ int prefill_call(bool kda, const void* q, const void* k, const void* v, const vo
   constexpr int VT = 2, NW = 4;     // two 16-column value tiles per wave, 4 waves: 128 columns per workgroup
   p.nvb = V / gdn::kPrefillVBlk<VT, NW>;
   p.gqa = HV / HK;
+  // keep the units that share a key head (gqa heads x nvb V-blocks) on one XCD
+  p.xcd_shift = 0;
+  while ((1 << p.xcd_shift) < p.gqa * p.nvb && p.xcd_shift < 6) ++p.xcd_shift;
   p.scale = opt->scale > 0.0f ? opt->scale : 1.0f / std::sqrt(static_cast<float>(K));
   p.l2norm = opt->use_qk_l2norm ? 1 : 0;
   p.out_bf16 = opt->out_dtype == GDN_BF16;
