@@ -2,9 +2,9 @@
 
 Each mutation replaces one piece of ``oracle.recurrence``,
 ``oracle.activations`` or ``oracle.hadamard`` with a wrong variant; the pin
-tests of tests/test_oracle_recurrence.py, tests/test_oracle_activations.py
-and tests/test_oracle_hadamard.py are then run against the mutated oracle
-and at least one of them must fail.
+tests of tests/test_oracle_recurrence.py, tests/test_oracle_activations.py,
+tests/test_oracle_hadamard.py and tests/test_oracle_qdq_placement.py are
+then run against the mutated oracle and at least one of them must fail.
 """
 import numpy as np
 import pytest
@@ -14,10 +14,13 @@ import oracle.hadamard as had
 import oracle.recurrence as rec
 import tests.test_oracle_activations as pins_act
 import tests.test_oracle_hadamard as pins_had
+import tests.test_oracle_qdq_placement as pins_qdq
 import tests.test_oracle_recurrence as pins
 
 _true_hadamard = had.hadamard_matrix
 _true_qdq = had.int8_hadamard32_qdq
+_true_step = rec.gated_delta_step
+_true_run = rec.run_suffix
 
 
 def _order_write_then_decay(S, q_hat, k_hat, v, alpha, beta, state_qdq=None, readout_mode="working"):
@@ -110,6 +113,40 @@ def _qdq_no_back_rotation(S, precision="float32"):
     return (s * np.rint(y / s)).reshape(Hh, K, V)
 
 
+# ---- where the state rounding sits (LinearAttentionDecodeConfig: readout, quantize_initial)
+
+def _qdq_before_decay(S, q_hat, k_hat, v, alpha, beta, state_qdq=None, readout_mode="working"):
+    if state_qdq is not None:
+        S = state_qdq(S)
+    return _true_step(S, q_hat, k_hat, v, alpha, beta)
+
+
+def _readout_swapped(S, q_hat, k_hat, v, alpha, beta, state_qdq=None, readout_mode="working"):
+    other = {"working": "stored", "stored": "working"}[readout_mode]
+    return _true_step(S, q_hat, k_hat, v, alpha, beta, state_qdq=state_qdq, readout_mode=other)
+
+
+def _quantize_initial_ignored(S0, q_hat, k_hat, v, alpha, beta, state_qdq=None, quantize_initial=False,
+                              readout_mode="working", trace=None):
+    return _true_run(S0, q_hat, k_hat, v, alpha, beta, state_qdq=state_qdq, quantize_initial=False,
+                     readout_mode=readout_mode, trace=trace)
+
+
+def _last_token_unrounded(S0, q_hat, k_hat, v, alpha, beta, state_qdq=None, quantize_initial=False,
+                          readout_mode="working", trace=None):
+    T = q_hat.shape[0]
+    if T == 0:
+        return _true_run(S0, q_hat, k_hat, v, alpha, beta, state_qdq=state_qdq,
+                         quantize_initial=quantize_initial, readout_mode=readout_mode, trace=trace)
+    o, S = _true_run(S0, q_hat[:-1], k_hat[:-1], v[:-1], alpha[:-1], beta[:-1], state_qdq=state_qdq,
+                     quantize_initial=quantize_initial, readout_mode=readout_mode, trace=trace)
+    S_in = S
+    o_last, S = _true_step(S, q_hat[-1], k_hat[-1], v[-1], alpha[-1], beta[-1])
+    if trace is not None:
+        trace.append(dict(S_in=S_in, q_hat=q_hat[-1], k_hat=k_hat[-1], alpha=alpha[-1], beta=beta[-1], S_out=S))
+    return np.concatenate([o, o_last[None]]), S
+
+
 MUTATIONS = {
     "hadamard_entry_sign": [(had, "hadamard_matrix", _hadamard_one_sign)],
     "butterfly_swapped": [(had, "fwht_butterflies", _butterfly_swapped)],
@@ -127,7 +164,22 @@ MUTATIONS = {
     "transposed_read": [(rec, "delta_write", _transposed_read)],
     "softplus_sign": [(act, "softplus", _softplus_wrong_sign)],
     "sigmoid_sign": [(act, "sigmoid", _sigmoid_wrong_sign)],
+    "qdq_before_decay": [(rec, "gated_delta_step", _qdq_before_decay)],
+    "readout_swapped": [(rec, "gated_delta_step", _readout_swapped)],
+    "quantize_initial_ignored": [(rec, "run_suffix", _quantize_initial_ignored)],
+    "qdq_skipped_on_last_token": [(rec, "run_suffix", _last_token_unrounded)],
 }
+
+# hand-worked QDQ tokens (tests/golden/qdq_steps.txt); each placement mistake must fail one of these,
+# not only a property
+GOLDEN_PLACEMENT_PINS = [
+    lambda: pins_qdq.test_fp8_two_hand_worked_tokens("float64", "working", False),
+    lambda: pins_qdq.test_fp8_two_hand_worked_tokens("float64", "stored", False),
+    lambda: pins_qdq.test_fp8_two_hand_worked_tokens("float64", "working", True),
+    lambda: pins_qdq.test_codec_hand_worked_token("float64", "working", True),
+    lambda: pins_qdq.test_codec_hand_worked_token("float64", "stored", False),
+]
+PLACEMENT = ("qdq_before_decay", "readout_swapped", "quantize_initial_ignored", "qdq_skipped_on_last_token")
 
 PIN_TESTS = [
     lambda: pins.test_golden_worked_step("gated_scalar"),
@@ -151,6 +203,12 @@ PIN_TESTS = [
     lambda: pins_had.test_code_points_round_trip("float32"),
     lambda: pins_had.test_error_within_half_step_per_rotated_coordinate("float64"),
     pins_had.test_a_spike_spreads_over_the_group_and_comes_back_exactly,
+    *GOLDEN_PLACEMENT_PINS,
+    lambda: pins_qdq.test_every_state_leaving_a_token_is_rounded("fp8", pins_qdq._fp8("float64", 4), 8, False, 3),
+    lambda: pins_qdq.test_readouts_and_rounding_against_the_unrounded_step(
+        "codec", pins_qdq._codec("float64"), 32, True),
+    lambda: pins_qdq.test_quantize_initial_equals_starting_from_the_rounded_state(
+        "fp8", pins_qdq._fp8("float64", 4), 8, "working", 4),
 ]
 
 
@@ -170,3 +228,16 @@ def test_each_planted_mistake_is_caught(name, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             caught += 1
     assert caught >= 1, f"mutation {name} passed every pin"
+
+
+@pytest.mark.parametrize("name", PLACEMENT)
+def test_placement_mistakes_fail_a_hand_worked_case(name, monkeypatch):
+    for mod, attr, fn in MUTATIONS[name]:
+        monkeypatch.setattr(mod, attr, fn)
+    caught = 0
+    for t in GOLDEN_PLACEMENT_PINS:
+        try:
+            t()
+        except (AssertionError, ValueError, IndexError, TypeError):
+            caught += 1
+    assert caught >= 1, f"mutation {name} passed every hand-worked QDQ case"
