@@ -23,7 +23,9 @@ h // (HV / HK), i.e. consecutive value heads share a key head.
 rows the call reads).  Each function returns ``(out, written)``:
 ``out`` [T, HV, V] float64 (rows of sequences not in ``seqs`` are NaN) and
 ``written`` a dict {row id: new tile in pool layout, float64}.  Rows not in
-``written`` are not modified by the call.  ``trace`` (a dict, optional)
+``written`` are not modified by the call.  ``qdq_precision`` is the
+precision in which the state rounding decides its codes (oracle.e4m3,
+oracle.hadamard): float64 by default.  ``trace`` (a dict, optional)
 receives per sequence the per-token record of ``recurrence.run_suffix``.
 """
 import numpy as np
@@ -35,14 +37,14 @@ from . import paging
 from .recurrence import run_suffix
 
 
-def _qdq_fn(qdq, block_v):
+def _qdq_fn(qdq, block_v, precision="float64"):
     if qdq is None or qdq == "none":
         return None
     if qdq == "fp8_e4m3_tile":
-        return lambda S: e4m3.tile_qdq(S, block_v)
+        return lambda S: e4m3.tile_qdq(S, block_v, precision)
     if qdq == "int8_hadamard32":
         # block_v is only the execution tile width for this codec
-        return hadamard.int8_hadamard32_qdq
+        return lambda S: hadamard.int8_hadamard32_qdq(S, precision)
     raise ValueError(f"unknown qdq {qdq!r}")
 
 
@@ -68,7 +70,7 @@ def _run_one(tile, state_layout, q, k, v, alpha, beta, hk_of_h, scale, use_qk_l2
 def gdn_decode_pooled(q, k, v, a, b, A_log, dt_bias, cu_seqlens, state_indices, pool, *,
                       scale=None, use_qk_l2norm=True, beta_mode="logits", state_layout="K_FIRST",
                       qdq=None, block_v=64, quantize_initial=False, readout="working", seqs=None,
-                      trace=None):
+                      trace=None, qdq_precision="float64"):
     """GDN (scalar gate per value head) decode on a slot pool, varlen suffixes.
 
     q, k [T, HK, K]; v [T, HV, V]; a, b [T, HV]; A_log, dt_bias [HV];
@@ -79,7 +81,7 @@ def gdn_decode_pooled(q, k, v, a, b, A_log, dt_bias, cu_seqlens, state_indices, 
     HV, V = v.shape[1], v.shape[2]
     B = len(state_indices)
     hk_of_h = _key_head_map(HK, HV)
-    qdq_fn = _qdq_fn(qdq, block_v)
+    qdq_fn = _qdq_fn(qdq, block_v, qdq_precision)
     out = np.full((T, HV, V), np.nan)
     written = {}
     for bi in (range(B) if seqs is None else seqs):
@@ -100,7 +102,7 @@ def gdn_decode_pooled(q, k, v, a, b, A_log, dt_bias, cu_seqlens, state_indices, 
 def kda_decode_pooled(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_indices,
                       pool, *, scale=None, use_qk_l2norm=True, beta_mode="logits",
                       state_layout="K_FIRST", qdq=None, block_v=64, quantize_initial=False,
-                      readout="working", seqs=None, trace=None):
+                      readout="working", seqs=None, trace=None, qdq_precision="float64"):
     """KDA (per-key-channel gate) decode on a slot pool, varlen suffixes.
 
     q, k [T, HK, K]; v [T, HV, V]; raw_gate [T, HV, K]; beta_logits [T, HV];
@@ -110,7 +112,7 @@ def kda_decode_pooled(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens
     HV, V = v.shape[1], v.shape[2]
     B = len(state_indices)
     hk_of_h = _key_head_map(HK, HV)
-    qdq_fn = _qdq_fn(qdq, block_v)
+    qdq_fn = _qdq_fn(qdq, block_v, qdq_precision)
     out = np.full((T, HV, V), np.nan)
     written = {}
     for bi in (range(B) if seqs is None else seqs):
@@ -130,7 +132,7 @@ def kda_decode_pooled(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens
 
 def _paged_varlen(kind, q, k, v, gate, beta_in, A_log, dt_bias, cu_seqlens, page_indices, page_indptr,
                   last_page_len, page_size, pool, scale, use_qk_l2norm, beta_mode, state_layout, qdq, block_v,
-                  quantize_initial, readout, seqs, trace):
+                  quantize_initial, readout, seqs, trace, qdq_precision):
     """Several decoded tokens per sequence on a CSR-paged pool (see paging.paged_suffix_rows).
 
     Each page that a suffix token fills receives the state after that token;
@@ -140,7 +142,7 @@ def _paged_varlen(kind, q, k, v, gate, beta_in, A_log, dt_bias, cu_seqlens, page
     HV, V = v.shape[1], v.shape[2]
     B = len(cu_seqlens) - 1
     hk_of_h = _key_head_map(HK, HV)
-    qdq_fn = _qdq_fn(qdq, block_v)
+    qdq_fn = _qdq_fn(qdq, block_v, qdq_precision)
     out = np.full((T, HV, V), np.nan)
     written = {}
     for bi in (range(B) if seqs is None else seqs):
@@ -170,32 +172,35 @@ def _paged_varlen(kind, q, k, v, gate, beta_in, A_log, dt_bias, cu_seqlens, page
 def gdn_decode_paged_varlen(q, k, v, a, b, A_log, dt_bias, cu_seqlens, page_indices, page_indptr,
                             last_page_len, page_size, pool, *, scale=None, use_qk_l2norm=True,
                             beta_mode="logits", state_layout="V_FIRST", qdq=None, block_v=64,
-                            quantize_initial=False, readout="working", seqs=None, trace=None):
+                            quantize_initial=False, readout="working", seqs=None, trace=None,
+                            qdq_precision="float64"):
     """GDN decode of varlen suffixes on a CSR-paged pool; cu_seqlens [B+1] as in kda_decode."""
     return _paged_varlen("gdn", q, k, v, a, b, A_log, dt_bias, cu_seqlens, page_indices, page_indptr,
                          last_page_len, page_size, pool, scale, use_qk_l2norm, beta_mode, state_layout, qdq,
-                         block_v, quantize_initial, readout, seqs, trace)
+                         block_v, quantize_initial, readout, seqs, trace, qdq_precision)
 
 
 def kda_decode_paged_varlen(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, page_indices, page_indptr,
                             last_page_len, page_size, pool, *, scale=None, use_qk_l2norm=True,
                             beta_mode="logits", state_layout="V_FIRST", qdq=None, block_v=64,
-                            quantize_initial=False, readout="working", seqs=None, trace=None):
+                            quantize_initial=False, readout="working", seqs=None, trace=None,
+                            qdq_precision="float64"):
     """KDA decode of varlen suffixes on a CSR-paged pool (per-key-channel gate)."""
     return _paged_varlen("kda", q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, page_indices,
                          page_indptr, last_page_len, page_size, pool, scale, use_qk_l2norm, beta_mode,
-                         state_layout, qdq, block_v, quantize_initial, readout, seqs, trace)
+                         state_layout, qdq, block_v, quantize_initial, readout, seqs, trace, qdq_precision)
 
 
 def kda_decode_paged(q, k, v, raw_gate, beta_logits, a_log, dt_bias, page_indices, page_indptr, last_page_len,
                      pool, *, scale=None, use_qk_l2norm=True, beta_mode="logits", state_layout="V_FIRST",
-                     qdq=None, block_v=64, quantize_initial=False, readout="working", seqs=None, trace=None):
+                     qdq=None, block_v=64, quantize_initial=False, readout="working", seqs=None, trace=None,
+                     qdq_precision="float64"):
     """Single-token KDA decode on a CSR-paged pool: the paging of gated_delta_rule_decode_paged
     (flashinfer.gdn_paged) with the gate of kda_decode (max.nn.state_space)."""
     B, HK, K = q.shape
     HV, V = v.shape[1], v.shape[2]
     hk_of_h = _key_head_map(HK, HV)
-    qdq_fn = _qdq_fn(qdq, block_v)
+    qdq_fn = _qdq_fn(qdq, block_v, qdq_precision)
     out = np.full((B, HV, V), np.nan)
     written = {}
     for bi in (range(B) if seqs is None else seqs):
@@ -214,7 +219,7 @@ def kda_decode_paged(q, k, v, raw_gate, beta_logits, a_log, dt_bias, page_indice
 def gdn_decode_paged(q, k, v, a, b, A_log, dt_bias, page_indices, page_indptr, last_page_len,
                      pool, *, scale=None, use_qk_l2norm=True, beta_mode="logits",
                      state_layout="V_FIRST", qdq=None, block_v=64, quantize_initial=False,
-                     readout="working", seqs=None, trace=None):
+                     readout="working", seqs=None, trace=None, qdq_precision="float64"):
     """GDN decode of one token per sequence on a CSR-paged pool (token b belongs to sequence b).
 
     q, k [B, HK, K]; v [B, HV, V]; a, b [B, HV]; returns out [B, HV, V]
@@ -223,7 +228,7 @@ def gdn_decode_paged(q, k, v, a, b, A_log, dt_bias, page_indices, page_indptr, l
     B, HK, K = q.shape
     HV, V = v.shape[1], v.shape[2]
     hk_of_h = _key_head_map(HK, HV)
-    qdq_fn = _qdq_fn(qdq, block_v)
+    qdq_fn = _qdq_fn(qdq, block_v, qdq_precision)
     out = np.full((B, HV, V), np.nan)
     written = {}
     for bi in (range(B) if seqs is None else seqs):

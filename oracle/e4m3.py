@@ -21,10 +21,13 @@ Readings:
 * round to nearest, ties to even mantissa, saturating at +-448; subnormals
   kept; a tile whose amax is 0 is left as it is; NaN propagates.
 * the pages do not fix the precision in which the code of each element is
-  chosen; it is taken in float32, as the GPU kernel takes it:
-  y = f32(f32(x) * f32(448 / amax)), code = E4M3(y), value =
-  f32(code * f32(amax / 448)).  ``precision='float64'`` gives the same
-  rule in float64 throughout (x / s with s = amax / 448).
+  chosen; the plain reading, and the default, is float64 throughout:
+  s = amax / 448, code = E4M3(x / s), value = s * code.
+  ``precision='float32'`` is the same rule with every operation rounded to
+  float32 in the order y = f32(f32(x) * f32(448 / amax)), value =
+  f32(code * f32(amax / 448)); it agrees with float64 except for values
+  within a few float32 ulps of a midpoint between two codes, and serves to
+  compare code decisions taken in that precision.
 
 Pins (tests/test_oracle_e4m3.py): the 256-code table built from the bit
 fields is checked against PyTorch's CPU ``float8_e4m3fn`` decode; every
@@ -76,42 +79,42 @@ def e4m3_round(y):
     return np.copysign(r, y)
 
 
-def tile_qdq(S, block_v=64, precision="float32"):
+def _tiles(S, block_v):
+    """S [H, K, V] -> a view [H, K, V // block_v, block_v]: axes 1 and 3 span one [K, block_v] tile."""
+    S = np.asarray(S, dtype=np.float64)
+    H, K, V = S.shape
+    if V % block_v != 0:
+        raise ValueError("block_v must divide the value head dim")
+    return S.reshape(H, K, V // block_v, block_v)
+
+
+def tile_qdq(S, block_v=64, precision="float64"):
     """Quantise/dequantise S [H, K, V] with one scale per [K, block_v] tile of each head.
 
     For each tile: amax = max |S|; if amax == 0 the tile is unchanged;
     otherwise each element x becomes s * E4M3(x / s) with s = amax / 448,
     the division and the product evaluated in ``precision`` (see the module
-    docstring for the float32 reading).
+    docstring).  Every tile of every head is handled at once; the arithmetic
+    per element is the same as tile by tile.
     """
-    S = np.asarray(S, dtype=np.float64)
-    H, K, V = S.shape
-    if V % block_v != 0:
-        raise ValueError("block_v must divide the value head dim")
-    out = S.copy()
-    for j0 in range(0, V, block_v):
-        for h in range(H):
-            tile = S[h, :, j0:j0 + block_v]
-            if precision == "float64":
-                amax = np.max(np.abs(tile))
-                if amax == 0.0:
-                    continue
-                s = amax / E4M3_MAX
-                out[h, :, j0:j0 + block_v] = s * e4m3_round(tile / s)
-            elif precision == "float32":
-                x = tile.astype(np.float32)
-                amax = np.max(np.abs(x))
-                if amax == 0.0:
-                    out[h, :, j0:j0 + block_v] = x
-                    continue
-                inv = np.float32(np.float32(E4M3_MAX) / amax)
-                sc = np.float32(amax / np.float32(E4M3_MAX))
-                y = (x * inv).astype(np.float32)
-                code = e4m3_round(y.astype(np.float64)).astype(np.float32)
-                out[h, :, j0:j0 + block_v] = (code * sc).astype(np.float32)
-            else:
-                raise ValueError(f"unknown precision {precision!r}")
-    return out
+    x = _tiles(S, block_v)
+    H, K, nt, bv = x.shape
+    if precision == "float64":
+        amax = np.max(np.abs(x), axis=(1, 3), keepdims=True)
+        s = np.where(amax == 0.0, 1.0, amax / E4M3_MAX)
+        out = np.where(amax == 0.0, x, s * e4m3_round(x / s))
+    elif precision == "float32":
+        f = np.float32
+        x = x.astype(f)
+        amax = np.max(np.abs(x), axis=(1, 3), keepdims=True)
+        safe = np.where(amax == 0.0, f(1.0), amax).astype(f)
+        inv = (f(E4M3_MAX) / safe).astype(f)
+        sc = (safe / f(E4M3_MAX)).astype(f)
+        code = e4m3_round((x * inv).astype(f).astype(np.float64)).astype(f)
+        out = np.where(amax == 0.0, x, (code * sc).astype(f)).astype(np.float64)
+    else:
+        raise ValueError(f"unknown precision {precision!r}")
+    return out.reshape(H, K, nt * bv)
 
 
 def tile_scales(S, block_v=64):
@@ -152,37 +155,29 @@ def e4m3_encode_value(v):
     return np.where(a > 0, code, sign).astype(np.uint8)
 
 
-def tile_encode(S, block_v=64, precision="float32"):
+def tile_encode(S, block_v=64, precision="float64"):
     """E4M3 bytes [H, K, V] (uint8) and per-tile scales [H, V // block_v] of S [H, K, V];
-    tile_decode(tile_encode(S)) == tile_qdq(S).  An all-zero tile has scale 0 and codes 0."""
-    S = np.asarray(S, dtype=np.float64)
-    H, K, V = S.shape
-    if V % block_v != 0:
-        raise ValueError("block_v must divide the value head dim")
-    codes = np.zeros((H, K, V), dtype=np.uint8)
-    scales = np.zeros((H, V // block_v))
-    for t, j0 in enumerate(range(0, V, block_v)):
-        for h in range(H):
-            tile = S[h, :, j0:j0 + block_v]
-            if precision == "float64":
-                amax = np.max(np.abs(tile))
-                if amax == 0.0:
-                    continue
-                s = amax / E4M3_MAX
-                y = tile / s
-            elif precision == "float32":
-                x = tile.astype(np.float32)
-                amax = np.max(np.abs(x))
-                if amax == 0.0:
-                    continue
-                inv = np.float32(np.float32(E4M3_MAX) / amax)
-                s = np.float32(amax / np.float32(E4M3_MAX))
-                y = (x * inv).astype(np.float32).astype(np.float64)
-            else:
-                raise ValueError(f"unknown precision {precision!r}")
-            codes[h, :, j0:j0 + block_v] = e4m3_encode_value(e4m3_round(y))
-            scales[h, t] = float(s)
-    return codes, scales
+    tile_decode(tile_encode(S)) == tile_qdq(S) at the same precision.  An all-zero tile has
+    scale 0 and codes 0."""
+    x = _tiles(S, block_v)
+    H, K, nt, bv = x.shape
+    if precision == "float64":
+        amax = np.max(np.abs(x), axis=(1, 3), keepdims=True)
+        s = np.where(amax == 0.0, 1.0, amax / E4M3_MAX)
+        y = x / s
+        scale = amax / E4M3_MAX
+    elif precision == "float32":
+        f = np.float32
+        x32 = x.astype(f)
+        amax = np.max(np.abs(x32), axis=(1, 3), keepdims=True)
+        safe = np.where(amax == 0.0, f(1.0), amax).astype(f)
+        inv = (f(E4M3_MAX) / safe).astype(f)
+        y = (x32 * inv).astype(f).astype(np.float64)
+        scale = np.where(amax == 0.0, f(0.0), (safe / f(E4M3_MAX)).astype(f)).astype(np.float64)
+    else:
+        raise ValueError(f"unknown precision {precision!r}")
+    codes = np.where(amax == 0.0, np.uint8(0), e4m3_encode_value(e4m3_round(y)))
+    return codes.reshape(H, K, nt * bv).astype(np.uint8), scale.reshape(H, nt)
 
 
 def tile_decode(codes, scales, block_v=64):

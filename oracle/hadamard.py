@@ -24,12 +24,13 @@ Readings (the pages give no formulas):
 Written with z = x H the 1/sqrt(32) factors cancel: y / s = 127 z / amax|z|
 and (s * code) H / sqrt(32) = (code H) * amax|z| / (127 * 32).  The code
 below uses that form, so that values whose rotation is exactly on the code
-grid (ties included) are decided exactly.  With ``precision='float32'``
-every operation is rounded to float32 -- z by radix-2 butterflies (a + b,
-a - b) over strides 1, 2, 4, 8, 16, inv = f32(127 / amax|z|), code =
-rint(f32(z * inv)), result = f32(code H) * f32(f32(amax|z| / 127) / 32) --
-so that both sides decide each code in float32; ``'float64'`` is the same
-rule in float64.
+grid (ties included) are decided exactly.  The pages do not fix the
+precision of the decision; the default is float64 (the plain reading).
+With ``precision='float32'`` every operation is rounded to float32 -- z by
+radix-2 butterflies (a + b, a - b) over strides 1, 2, 4, 8, 16, inv =
+f32(127 / amax|z|), code = rint(f32(z * inv)), result = f32(code H) *
+f32(f32(amax|z| / 127) / 32) -- which serves to compare code decisions
+taken in that precision.
 
 Packed storage (this repository's format; the pages describe the codec as a
 quantise/dequantise emulation and claim no compressed storage): a state is
@@ -79,7 +80,7 @@ def fwht_butterflies(x, dtype=np.float64):
     return y
 
 
-def int8_hadamard32_qdq(S, precision="float32"):
+def int8_hadamard32_qdq(S, precision="float64"):
     """Quantise/dequantise S [H, K, V] with the int8_hadamard32 codec (V a multiple of 32)."""
     S = np.asarray(S, dtype=np.float64)
     Hh, K, V = S.shape
@@ -108,7 +109,7 @@ def int8_hadamard32_qdq(S, precision="float32"):
     raise ValueError(f"unknown precision {precision!r}")
 
 
-def int8_hadamard32_encode(S, precision="float32"):
+def int8_hadamard32_encode(S, precision="float64"):
     """Codes (int8) and scales (float64) of S [H, K, V] under the codec; decode(encode(S)) == qdq(S).
 
     scale = amax|z| / 127 per (head, key row, group of 32) with z = S H (the +-1 matrix); an

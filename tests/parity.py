@@ -3,7 +3,10 @@
 They move seeded workloads to the device, call the HIP library through its
 Python binding, run the CPU oracle on the same values (pool rows read back
 from the device before the call), and compare the two under the tolerances
-below.
+below.  The oracle runs on groups of at most 64 QDQ tokens (1024 otherwise)
+so that its per-token trace stays bounded in host memory, on a few threads
+side by side; sums over the whole call (the outputs' relative L2 error, the
+flip counts) decide the call-wide checks.
 
 Tolerances (readings of the stated contract):
 * index work is exact: the rows written are exactly the call's write rows,
@@ -27,8 +30,18 @@ Tolerances (readings of the stated contract):
   + |q_hat . k_hat| beta |k_hat|^T (alpha E_{t-1}); a stored-readout output by
   its ulp + |q_hat|^T E_t.  Since a bound of this kind would also accept a
   systematically different rounding rule, the fraction of state elements
-  that differ at all must stay below 1e-3 (exact agreement of the rounding
-  itself is tested separately with a scale of exactly 1).
+  rounded the other way (moved by more than half a step) must stay below
+  1e-3 over the whole call (exact agreement of the rounding itself is
+  tested separately with a scale of exactly 1).  Where a token amplifies an
+  error along its key (|1 - beta |k_hat|^2| > 1: unnormalised keys, or a
+  probability-mode beta outside [0, 1]) a carried difference can grow, so
+  the flip rate is then counted only on states no earlier difference
+  reached: a suffix's state after its first token, without quantize_initial.
+* the oracle decides every rounding in float64 (the pages fix only the
+  amax / 448 tile scale and the codec's per-group scale; float64 is the
+  plain reading); a second comparison with the decisions taken in float32,
+  as the kernel takes them, shows how often the two precisions decide
+  differently and is held to the same bounds.
 * int8_hadamard32 codec: per (key row, 32 values) group the two sides'
   rounding errors in the rotated basis are each at most half a step
   amax|y| / 127 (amax taken over the larger of the two states, i.e. the
@@ -43,7 +56,9 @@ Tolerances (readings of the stated contract):
   other way), and their scales agree to 1e-5 relative except in at most 1 %
   of the groups (those an earlier such rounding moved), never by 1 % or more.
 """
+import concurrent.futures
 import math
+import os
 
 import numpy as np
 import torch
@@ -112,11 +127,12 @@ def rows_for(w, seqs=None):
     return reads, writes
 
 
-def oracle_call(w, pool_rows, seqs=None, trace=None, **over):
-    """Run the CPU oracle for workload ``w`` on ``pool_rows`` {row: float64 tile}."""
+def oracle_call(w, pool_rows, seqs=None, trace=None, qdq_precision="float64", **over):
+    """Run the CPU oracle for workload ``w`` on ``pool_rows`` {row: float64 tile}; ``qdq_precision`` is the
+    precision of the oracle's rounding decisions (float64, the pages' plain reading, or float32)."""
     o = _opts(w, over, drop=("out_dtype", "slots"))
     inp = w.inputs
-    common = dict(state_layout=w.state_layout, seqs=seqs, trace=trace, **o)
+    common = dict(state_layout=w.state_layout, seqs=seqs, trace=trace, qdq_precision=qdq_precision, **o)
     kda = w.kind.startswith("kda")
     gate = host64(inp["raw_gate"] if kda else inp["a"])
     beta = host64(inp["beta_logits"] if kda else inp["b"])
@@ -136,13 +152,31 @@ def oracle_call(w, pool_rows, seqs=None, trace=None, **over):
     raise ValueError(w.kind)
 
 
-def gather_rows(pool, rows):
+def gather_rows(pool, rows, dtype=torch.float64):
+    """{row: host copy of pool[row]} (as ``dtype``) for the given rows."""
     rows = sorted(set(rows))
     if not rows:
         return {}
     idx = torch.tensor(rows, dtype=torch.int64, device=pool.device)
-    vals = pool.index_select(0, idx).to("cpu").to(torch.float64).numpy()
+    vals = pool.index_select(0, idx).to("cpu").to(dtype).numpy()
     return {r: vals[i] for i, r in enumerate(rows)}
+
+
+def seq_batches(w, seqs, max_tokens):
+    """Consecutive groups of the sequences ``seqs`` holding at most ``max_tokens`` suffix tokens each (a longer
+    suffix is a group of its own): the oracle runs and is compared one group at a time, so that its
+    per-token trace stays bounded in host memory."""
+    cu = host_int(w.inputs.get("cu_seqlens"))
+    batch, ntok = [], 0
+    for b in seqs:
+        nb = 1 if (cu is None or w.kind in ("gdn_paged", "kda_paged")) else int(cu[b + 1] - cu[b])
+        if batch and ntok + nb > max_tokens:
+            yield batch
+            batch, ntok = [], 0
+        batch.append(b)
+        ntok += nb
+    if batch:
+        yield batch
 
 
 def bf16_ulp(x):
@@ -229,14 +263,28 @@ def qdq_bounds(w, trace, seqs):
 def non_expanding(trace):
     """True when no traced token amplifies an error along its key: |1 - beta |k_hat|^2| <= 1.  The
     delta write maps an error E to (I - beta k k^T) E along k, so with unnormalised keys or beta
-    outside [0, 1] one rounding difference grows every token; the flip-rate checks below (which
-    catch a wrong rounding rule) only apply when it cannot.  The element-wise bounds apply always."""
+    outside [0, 1] one rounding difference grows every token."""
     for recs in trace.values():
         for rec in recs:
             kk = np.sum(np.asarray(rec["k_hat"], dtype=np.float64) ** 2, axis=-1)
             if np.any(np.abs(1.0 - np.asarray(rec["beta"], dtype=np.float64) * kk) > 1.0 + 1e-9):
                 return False
     return True
+
+
+def flip_rows(w, trace, seqs):
+    """Written rows whose elements count towards the flip-rate check, or None for all of them.
+
+    The flip rate catches a wrong rounding rule: it is the fraction of elements that the two sides
+    rounded to different codes.  Where no token amplifies an error (non_expanding) every written
+    state counts.  Where one does, a rounding difference carried from an earlier token can grow and
+    move later decisions, so only states that no earlier difference reached count: the state after a
+    suffix's first token, without quantize_initial (both sides round the same state once)."""
+    if non_expanding(trace):
+        return None
+    if w.options.get("quantize_initial"):
+        return set()
+    return {row for b in seqs for i, row in written_rows(w, b) if i == 0}
 
 
 class Report:
@@ -248,12 +296,40 @@ class Report:
     def add(self, k, v):
         self.items[k] = max(self.items.get(k, 0.0), float(v))
 
+    def merge(self, other):
+        for k, v in other.items.items():
+            self.add(k, v)
+
     def __str__(self):
         return " ".join(f"{k}={v:.3g}" for k, v in self.items.items())
 
 
-def compare_outputs(gpu_out, ref, w, rows, report, qdq_bound=None):
-    g = gpu_out.detach().to("cpu").to(torch.float64).numpy()[rows]
+class Totals:
+    """Whole-call sums that single batches of sequences cannot decide: the relative L2 error of the
+    outputs and the counts behind the flip-rate checks."""
+
+    SUMS = ("d2", "r2", "flips", "total", "code_flips", "codes", "off_scales", "groups")
+
+    def __init__(self):
+        self.d2 = 0.0          # sum (gpu - ref)^2 over compared outputs
+        self.r2 = 0.0          # sum ref^2
+        self.flips = 0         # state elements (or rotated coordinates) rounded the other way
+        self.total = 0
+        self.code_flips = 0    # packed pools: stored codes that differ from the oracle's encoding
+        self.codes = 0
+        self.off_scales = 0    # packed codec: group scales off by more than 1e-5
+        self.groups = 0
+        self.worst_scale = 0.0
+
+    def merge(self, other):
+        for k in self.SUMS:
+            setattr(self, k, getattr(self, k) + getattr(other, k))
+        self.worst_scale = max(self.worst_scale, other.worst_scale)
+
+
+def compare_outputs(host_out, ref, w, rows, report, totals, qdq_bound=None):
+    """Element-wise output check of the token rows ``rows`` (host_out: the GPU's outputs as float64 NumPy)."""
+    g = host_out[rows]
     r = ref[rows]
     assert np.all(np.isfinite(r)), "oracle produced non-finite outputs"
     assert np.all(np.isfinite(g)), "GPU produced non-finite outputs"
@@ -262,33 +338,39 @@ def compare_outputs(gpu_out, ref, w, rows, report, qdq_bound=None):
     diff = np.abs(g - r_round)
     if w.out_dtype == torch.bfloat16:
         tol = bf16_ulp(np.maximum(np.abs(g), np.abs(r_round))) + 1e-5 * rms
-        l2_tol = OUT_REL_L2 + 2.0 ** -9
     else:
         tol = STATE_RTOL * (np.abs(r) + rms)
-        l2_tol = OUT_REL_L2
     if qdq_bound is not None:
         tol = tol + qdq_bound
     ratio = diff / tol
     report.add("out_max_tol_ratio", ratio.max() if ratio.size else 0)
     bad = np.argwhere(diff > tol)
     assert bad.size == 0, f"{len(bad)} outputs out of tolerance; first {bad[:5].tolist()} gpu={g[tuple(bad[0])]} ref={r[tuple(bad[0])]}"
-    rel = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
+    totals.d2 += float(np.sum((g - r) ** 2))
+    totals.r2 += float(np.sum(r * r))
+
+
+def check_output_l2(w, report, totals):
+    """Relative L2 error of all compared outputs against the unrounded oracle."""
+    l2_tol = OUT_REL_L2 + (2.0 ** -9 if w.out_dtype == torch.bfloat16 else 0.0)
+    rel = math.sqrt(totals.d2) / max(math.sqrt(totals.r2), 1e-30)
     report.add("out_rel_l2", rel)
     assert rel <= l2_tol, f"output relative L2 error {rel} > {l2_tol}"
 
 
-def compare_states(gpu_rows, ref_rows, report, qdq_bound=None, layout="K_FIRST", codec=None, flip_check=True,
-                   block_v=64):
+def compare_states(gpu_rows, ref_rows, report, totals, qdq_bound=None, layout="K_FIRST", codec=None, block_v=64,
+                   flip_rows=None):
     """fp32 states within the relative tolerance, or (QDQ) within the propagated bounds {row: [H, K, V]}.
 
     With QDQ, an element counts as rounded the other way (a flip) when it moves by more than half a
     quantisation step of its tile (fp8) or group (codec); a scale that moved because an earlier flip
-    changed the tile's amax shifts every element by much less than that and is not counted."""
+    changed the tile's amax shifts every element by much less than that and is not counted.  Flips are
+    counted in the rows ``flip_rows`` (None: all)."""
     assert set(gpu_rows) == set(ref_rows)
-    flips, total = 0, 0
     for row, ref in ref_rows.items():
         g = gpu_rows[row]
         assert np.all(np.isfinite(g)), f"non-finite GPU state in row {row}"
+        counted = flip_rows is None or row in flip_rows
         if qdq_bound is not None:
             logical = ref if layout == "K_FIRST" else np.swapaxes(ref, -1, -2)
             gl = g if layout == "K_FIRST" else np.swapaxes(g, -1, -2)
@@ -297,16 +379,18 @@ def compare_states(gpu_rows, ref_rows, report, qdq_bound=None, layout="K_FIRST",
             if codec == "int8_hadamard32":
                 yr = _rotate32(logical)
                 dy = np.abs(_rotate32(gl) - yr)
-                flips += int(np.sum(dy > 0.25 * np.max(np.abs(yr), axis=-1, keepdims=True) / 127))
-                total += dy.size
+                if counted:
+                    totals.flips += int(np.sum(dy > 0.25 * np.max(np.abs(yr), axis=-1, keepdims=True) / 127))
+                    totals.total += dy.size
             else:
                 # the oracle's state is on its tiles' grids: scale = amax / 448 per [K, block_v] tile
                 H, K, V = logical.shape
                 amax = np.abs(logical).reshape(H, K, V // block_v, block_v).max(axis=(1, 3))
                 sc = np.repeat(amax / 448.0, block_v, axis=-1)[:, None, :]
                 step = e4m3.e4m3_spacing(np.abs(logical) / np.where(sc > 0, sc, 1.0)) * sc
-                flips += int(np.sum(diff > 0.5 * step + 1e-30))
-                total += diff.size
+                if counted:
+                    totals.flips += int(np.sum(diff > 0.5 * step + 1e-30))
+                    totals.total += diff.size
             report.add("qdq_state_bound_ratio", (diff / np.maximum(tol, 1e-300)).max())
         else:
             rms = np.sqrt(np.mean(ref * ref, axis=(-1, -2), keepdims=True))
@@ -316,10 +400,18 @@ def compare_states(gpu_rows, ref_rows, report, qdq_bound=None, layout="K_FIRST",
             report.add("state_max_rel", (diff / (np.abs(ref) + rms)).max())
         bad = np.argwhere(diff > tol)
         assert bad.size == 0, f"row {row}: {len(bad)} state elements out of tolerance, first {bad[:3].tolist()}"
-    if qdq_bound is not None and total:
-        report.add("qdq_state_diff_frac", flips / total)
-        assert not flip_check or flips / total < 1e-3, \
-            f"{flips} of {total} QDQ state elements differ: rounding rule mismatch?"
+
+
+FLIP_RATE = 1e-3
+
+
+def check_flip_rate(report, totals, what="QDQ state elements"):
+    """The fraction of elements rounded the other way, over every counted row of the call."""
+    if totals.total:
+        frac = totals.flips / totals.total
+        report.add("qdq_state_diff_frac", frac)
+        report.add("qdq_flip_counted_elems", totals.total)
+        assert frac < FLIP_RATE, f"{totals.flips} of {totals.total} {what} differ: rounding rule mismatch?"
 
 
 def check_untouched(pool_before, pool_after, write_rows, chunk_rows=256):
@@ -338,37 +430,99 @@ def check_untouched(pool_before, pool_after, write_rows, chunk_rows=256):
     assert not stray, f"rows modified that the call does not write: {stray[:10]}"
 
 
-def run_and_check(w, seqs=None, report=None, pool=None, snapshot=True, check_all_written=True, **over):
-    """Full parity check of workload ``w``: GPU call vs oracle on the sequences ``seqs``."""
+def _host_out(out):
+    return out.detach().to("cpu").to(torch.float64).numpy()
+
+
+def _batch_bounds(w, trace, batch, ref_shape):
+    """(output bound for the batch's token rows, {written row: state bound}) from one batch's trace."""
+    out_b, seq_b = qdq_bounds(w, trace, batch)
+    full = np.zeros(ref_shape)
+    for t, bnd in out_b.items():
+        full[t] = bnd
+    state_bound = {row: seq_b[b][i] for b in batch if b in seq_b for i, row in written_rows(w, b)}
+    return full, state_bound
+
+
+# threads that run the oracle on batches of sequences side by side (NumPy releases the interpreter lock
+# inside its large element-wise operations); every batch is checked on its own and the results are merged
+# in batch order
+CHECK_THREADS = max(1, min(8, len(os.sched_getaffinity(0))))
+
+
+def _check_batches(w, seq_list, before, got_state, host_out, report, totals, qdq_precision, over, per_row=None):
+    """Run the oracle one batch of sequences at a time on the pre-call rows ``before`` {row: array} and
+    compare the GPU's outputs and written states (``got_state(rows)`` -> {row: float64 state}).
+    ``per_row(row, ref_state, stable, totals)`` adds checks of a written row (packed pools).  Returns the
+    written rows."""
+    qdq = bool(w.options.get("qdq"))
+
+    def check(batch):
+        rep, tot = Report(), Totals()
+        reads_b, _ = rows_for(w, batch)
+        before_b = {r: np.asarray(before[r], dtype=np.float64) for r in reads_b}
+        trace = {} if qdq else None
+        ref_out, ref_written = oracle_call(w, before_b, seqs=batch, trace=trace, qdq_precision=qdq_precision, **over)
+        trows = token_rows(w, batch)
+        bound, state_bound, frows, stable = None, None, None, True
+        if qdq:
+            full, state_bound = _batch_bounds(w, trace, batch, ref_out.shape)
+            bound = full[trows]
+            frows = flip_rows(w, trace, batch)
+            stable = frows is None
+        del trace
+        if len(trows):
+            compare_outputs(host_out, ref_out, w, trows, rep, tot, qdq_bound=bound)
+        got = got_state(list(ref_written))
+        compare_states(got, ref_written, rep, tot, qdq_bound=state_bound, layout=w.state_layout,
+                       codec=w.options.get("qdq"), block_v=w.options.get("block_v", 64), flip_rows=frows)
+        if per_row is not None:
+            for row, ref in ref_written.items():
+                per_row(row, ref, stable, tot)
+        return rep, tot, set(ref_written)
+
+    batches = list(seq_batches(w, seq_list, 64 if qdq else 1024))
+    written = set()
+    if CHECK_THREADS == 1 or len(batches) == 1:
+        results = map(check, batches)
+    else:
+        pool = concurrent.futures.ThreadPoolExecutor(CHECK_THREADS)
+        results = pool.map(check, batches)
+    try:
+        for rep, tot, wr in results:
+            report.merge(rep)
+            totals.merge(tot)
+            written.update(wr)
+    finally:
+        if not (CHECK_THREADS == 1 or len(batches) == 1):
+            pool.shutdown(cancel_futures=True)
+    return written
+
+
+def run_and_check(w, seqs=None, report=None, pool=None, snapshot=True, qdq_precision="float64", **over):
+    """Full parity check of workload ``w``: GPU call vs oracle on the sequences ``seqs`` (all if None).
+
+    The oracle decides the state rounding in ``qdq_precision`` (float64 by default; float32 compares the
+    code decisions taken in the kernel's own precision)."""
     report = report if report is not None else Report()
+    totals = Totals()
     d = device_inputs(w)
     if pool is None:
         pool = wl.make_pool(w, "cuda")
     all_reads, all_writes = rows_for(w)
-    reads, writes = rows_for(w, seqs)
-    before = gather_rows(pool, reads)
+    seq_list = list(range(w.B)) if seqs is None else list(seqs)
+    reads, writes = rows_for(w, seq_list)
+    before = gather_rows(pool, reads, torch.float32)
     snap = pool.clone() if snapshot else None
     out = gpu_call(w, pool, d, **over)
     torch.cuda.synchronize()
-    trace = {} if w.options.get("qdq") else None
-    ref_out, ref_written = oracle_call(w, before, seqs=seqs, trace=trace, **over)
-    seq_list = list(range(w.B)) if seqs is None else list(seqs)
-    trows = token_rows(w, seq_list)
-    bound, state_bound = None, None
-    if trace is not None:
-        out_b, seq_b = qdq_bounds(w, trace, seq_list)
-        full = np.zeros(ref_out.shape)
-        for t, bnd in out_b.items():
-            full[t] = bnd
-        bound = full[trows]
-        state_bound = {row: seq_b[b][i] for b in seq_list if b in seq_b for i, row in written_rows(w, b)}
-    if len(trows):
-        compare_outputs(out, ref_out, w, trows, report, qdq_bound=bound)
-    got = gather_rows(pool, list(ref_written))
-    compare_states(got, ref_written, report, qdq_bound=state_bound, layout=w.state_layout,
-                   codec=w.options.get("qdq"), flip_check=trace is None or non_expanding(trace),
-                   block_v=w.options.get("block_v", 64))
-    assert sorted(ref_written) == sorted(set(writes))
+    host_out = _host_out(out)
+    after = gather_rows(pool, writes, torch.float32)
+    written = _check_batches(w, seq_list, before, lambda rows: {r: after[r].astype(np.float64) for r in rows},
+                             host_out, report, totals, qdq_precision, over)
+    check_output_l2(w, report, totals)
+    check_flip_rate(report, totals)
+    assert sorted(written) == sorted(set(writes))
     if snap is not None:
         check_untouched(snap, pool, all_writes)
     return report, out, pool
@@ -404,17 +558,19 @@ def make_packed_pool(w, device="cuda", rows=None):
     rows = list(range(n)) if rows is None else sorted(set(rows))
     if rows:
         fp32 = wl.make_pool(w, device)
-        idx = torch.tensor(rows, dtype=torch.int64, device=device)
-        tiles = fp32.index_select(0, idx).cpu().numpy().astype(np.float64)
+        for r0 in range(0, len(rows), 64):
+            part = rows[r0:r0 + 64]
+            idx = torch.tensor(part, dtype=torch.int64, device=device)
+            tiles = fp32.index_select(0, idx).cpu().numpy().astype(np.float64)
+            if fp8:
+                code, scale = e4m3.tile_encode(_to_layout(tiles, w).reshape(-1, K, V), bv, "float32")
+                t = e4m3.pack_fp8_tiles(code.reshape(len(part), HV, K, V), scale.reshape(len(part), HV, V // bv),
+                                        w.state_layout, bv)
+            else:
+                code, scale = ohad.int8_hadamard32_encode(tiles.reshape(-1, K, V), "float32")
+                t = ohad.pack_tiles(code.reshape(len(part), HV, K, V), scale.reshape(len(part), HV, K, V // 32))
+            packed[idx] = torch.from_numpy(t).to(device)
         del fp32
-        if fp8:
-            code, scale = e4m3.tile_encode(_to_layout(tiles, w).reshape(-1, K, V), bv, "float32")
-            t = e4m3.pack_fp8_tiles(code.reshape(len(rows), HV, K, V), scale.reshape(len(rows), HV, V // bv),
-                                    w.state_layout, bv)
-        else:
-            code, scale = ohad.int8_hadamard32_encode(tiles.reshape(-1, K, V), "float32")
-            t = ohad.pack_tiles(code.reshape(len(rows), HV, K, V), scale.reshape(len(rows), HV, K, V // 32))
-        packed[idx] = torch.from_numpy(t).to(device)
     return packed
 
 
@@ -442,41 +598,42 @@ def decode_fp8(codes, scales, w):
     return _to_layout(e4m3.tile_decode(codes, scales, w.options.get("block_v", 64)), w)
 
 
-def run_and_check_packed(w, seqs=None, report=None, pool=None, **over):
+class _Lazy(dict):
+    """{row: value} computed on first access from fn(row) (decoded packed tiles, one batch at a time)."""
+
+    def __init__(self, fn):
+        super().__init__()
+        self.fn = fn
+
+    def __missing__(self, row):
+        return self.fn(row)
+
+
+def run_and_check_packed(w, seqs=None, report=None, pool=None, qdq_precision="float64", **over):
     """Parity of a call on a packed pool: outputs as for the codec on fp32 states; the written tiles,
     decoded, as the codec's states; their codes and scales against the oracle's encoding of its final
-    states; every other byte of the pool unchanged."""
+    states (at the oracle's decision precision); every other byte of the pool unchanged."""
     if _is_fp8(w):
-        return _run_and_check_fp8(w, seqs, report, pool, **over)
+        return _run_and_check_fp8(w, seqs, report, pool, qdq_precision, **over)
     assert w.options.get("qdq") == "int8_hadamard32" and w.state_layout == "K_FIRST"
     report = report if report is not None else Report()
+    totals = Totals()
     d = device_inputs(w)
     all_reads, all_writes = rows_for(w)
-    reads, writes = rows_for(w, seqs)
+    seq_list = list(range(w.B)) if seqs is None else list(seqs)
+    reads, writes = rows_for(w, seq_list)
     if pool is None:
         pool = make_packed_pool(w, "cuda", rows=all_reads)
-    before = {r: ohad.int8_hadamard32_decode(c, s) for r, (c, s) in gather_packed(pool, reads, w.K, w.V).items()}
+    raw_before = gather_packed(pool, reads, w.K, w.V)
+    before = _Lazy(lambda r: ohad.int8_hadamard32_decode(*raw_before[r]))
     snap = pool.clone()
     out = gpu_call(w, pool, d, **over)
     torch.cuda.synchronize()
-    trace = {}
-    ref_out, ref_written = oracle_call(w, before, seqs=seqs, trace=trace, **over)
-    seq_list = list(range(w.B)) if seqs is None else list(seqs)
-    trows = token_rows(w, seq_list)
-    out_b, seq_b = qdq_bounds(w, trace, seq_list)
-    full = np.zeros(ref_out.shape)
-    for t, bnd in out_b.items():
-        full[t] = bnd
-    if len(trows):
-        compare_outputs(out, ref_out, w, trows, report, qdq_bound=full[trows])
-    state_bound = {row: seq_b[b][i] for b in seq_list if b in seq_b for i, row in written_rows(w, b)}
-    got = gather_packed(pool, list(ref_written), w.K, w.V)
-    stable = non_expanding(trace)
-    compare_states({r: ohad.int8_hadamard32_decode(c, s) for r, (c, s) in got.items()}, ref_written, report,
-                   qdq_bound=state_bound, layout="K_FIRST", codec="int8_hadamard32", flip_check=stable)
-    flips, total, worst_scale, off_scales, groups = 0, 0, 0.0, 0, 0
-    for r, ref in ref_written.items():
-        code_e, scale_e = ohad.int8_hadamard32_encode(ref, "float32")
+    host_out = _host_out(out)
+    got = gather_packed(pool, writes, w.K, w.V)
+
+    def per_row(r, ref, stable, totals):
+        code_e, scale_e = ohad.int8_hadamard32_encode(ref, qdq_precision)
         code_g, scale_g = got[r]
         dc = np.abs(code_g.astype(np.int32) - code_e.astype(np.int32))
         # codes of a group whose scale agrees differ by at most two: a code rounded the other way at one
@@ -486,83 +643,88 @@ def run_and_check_packed(w, seqs=None, report=None, pool=None, **over):
         same = np.abs(scale_g - scale_e) <= 1e-5 * np.abs(scale_e)
         dcg = dc.reshape(dc.shape[0], dc.shape[1], dc.shape[2] // 32, 32).max(axis=-1)
         assert not stable or dcg[same].max(initial=0) <= 2, f"row {r}: a code differs by {dcg[same].max()}"
-        flips += int(np.sum(dc))
-        total += dc.size
         pos = scale_e > 0
         rel = np.abs(scale_g[pos] - scale_e[pos]) / scale_e[pos]
-        worst_scale = max(worst_scale, float(rel.max()))
-        off_scales += int(np.sum(rel > 1e-5))
-        groups += int(rel.size)
         assert np.all(scale_g[~pos] < 1e-30)
-    report.add("packed_code_flip_frac", flips / max(total, 1))
-    report.add("packed_scale_max_rel", worst_scale)
-    if stable:
-        assert flips / max(total, 1) < 1e-3, f"{flips} of {total} codes differ"
+        if stable:
+            totals.code_flips += int(np.sum(dc))
+            totals.codes += dc.size
+            totals.worst_scale = max(totals.worst_scale, float(rel.max()) if rel.size else 0.0)
+            totals.off_scales += int(np.sum(rel > 1e-5))
+            totals.groups += int(rel.size)
+
+    written = _check_batches(w, seq_list, before,
+                             lambda rows: {r: ohad.int8_hadamard32_decode(*got[r]) for r in rows},
+                             host_out, report, totals, qdq_precision, over, per_row=per_row)
+    check_output_l2(w, report, totals)
+    check_flip_rate(report, totals, "rotated coordinates")
+    report.add("packed_code_flip_frac", totals.code_flips / max(totals.codes, 1))
+    report.add("packed_scale_max_rel", totals.worst_scale)
+    if totals.codes:
+        assert totals.code_flips / totals.codes < FLIP_RATE, f"{totals.code_flips} of {totals.codes} codes differ"
         # a code rounded the other way at an earlier token moves that group's next amax (so its scale)
         # by up to about a step, 1/127 of it; such groups must stay rare, like the flips themselves
-        assert worst_scale < 1e-2, f"scale relative error {worst_scale}"
-        assert off_scales <= max(1, groups // 100), f"{off_scales} of {groups} scales differ by more than 1e-5"
-    assert sorted(ref_written) == sorted(set(writes))
+        assert totals.worst_scale < 1e-2, f"scale relative error {totals.worst_scale}"
+        assert totals.off_scales <= max(1, totals.groups // 100), \
+            f"{totals.off_scales} of {totals.groups} scales differ by more than 1e-5"
+    assert sorted(written) == sorted(set(writes))
     check_untouched(snap, pool, all_writes)
     return report, out, pool
 
 
-def _run_and_check_fp8(w, seqs, report, pool, **over):
+def _run_and_check_fp8(w, seqs, report, pool, qdq_precision="float64", **over):
     """run_and_check_packed for fp8 tiles: outputs and decoded states within the fp8 QDQ bounds; the written
     bytes and tile scales against the oracle's encoding of its final states; a non-zero tile's largest code is
     +-448 (its scale is its amax / 448), an all-zero tile's scale is 0; every other byte unchanged."""
     report = report if report is not None else Report()
+    totals = Totals()
     d = device_inputs(w)
     all_reads, all_writes = rows_for(w)
-    reads, writes = rows_for(w, seqs)
+    seq_list = list(range(w.B)) if seqs is None else list(seqs)
+    reads, writes = rows_for(w, seq_list)
     if pool is None:
         pool = make_packed_pool(w, "cuda", rows=all_reads)
     bv = w.options.get("block_v", 64)
-    before = {r: decode_fp8(c, s, w) for r, (c, s) in gather_fp8(pool, reads, w).items()}
+    raw_before = gather_fp8(pool, reads, w)
+    before = _Lazy(lambda r: decode_fp8(*raw_before[r], w))
     snap = pool.clone()
     out = gpu_call(w, pool, d, **over)
     torch.cuda.synchronize()
-    trace = {}
-    ref_out, ref_written = oracle_call(w, before, seqs=seqs, trace=trace, **over)
-    seq_list = list(range(w.B)) if seqs is None else list(seqs)
-    trows = token_rows(w, seq_list)
-    out_b, seq_b = qdq_bounds(w, trace, seq_list)
-    full = np.zeros(ref_out.shape)
-    for t, bnd in out_b.items():
-        full[t] = bnd
-    if len(trows):
-        compare_outputs(out, ref_out, w, trows, report, qdq_bound=full[trows])
-    state_bound = {row: seq_b[b][i] for b in seq_list if b in seq_b for i, row in written_rows(w, b)}   # logical
-    got = gather_fp8(pool, list(ref_written), w)
-    stable = non_expanding(trace)
-    compare_states({r: decode_fp8(c, s, w) for r, (c, s) in got.items()}, ref_written, report,
-                   qdq_bound=state_bound, layout=w.state_layout, flip_check=stable, block_v=bv)
+    host_out = _host_out(out)
+    got = gather_fp8(pool, writes, w)
     table = e4m3.e4m3_table()
-    flips, total, worst_scale = 0, 0, 0.0
-    for r, ref in ref_written.items():
-        code_e, scale_e = e4m3.tile_encode(_to_layout(ref, w), bv, "float32")
+
+    def per_row(r, ref, stable, totals):
+        code_e, scale_e = e4m3.tile_encode(_to_layout(ref, w), bv, qdq_precision)
         code_g, scale_g = got[r]
         vg, ve = table[code_g], table[code_e]
         assert np.all(np.isfinite(vg)), f"row {r}: a NaN code was stored"
-        # the decoded values are held to the propagated bounds above: a code rounded the other way at one
-        # token moves the whole key row's update at the next, which for an element near zero can be many
-        # of its own (small) steps; here only how often codes differ is checked
-        off = vg != ve
-        flips += int(np.sum(off))
-        total += off.size
         zero = scale_e == 0
         assert np.all(scale_g[zero] == 0), f"row {r}: an all-zero tile stored a non-zero scale"
         peak = np.abs(vg).reshape(vg.shape[0], w.K, w.V // bv, bv).max(axis=(1, 3))
         assert np.all(peak[~zero] == 448.0), f"row {r}: a non-zero tile's largest code is not 448"
-        rel = np.abs(scale_g[~zero] - scale_e[~zero]) / scale_e[~zero]
-        worst_scale = max(worst_scale, float(rel.max()) if rel.size else 0.0)
-    report.add("fp8_code_flip_frac", flips / max(total, 1))
-    report.add("fp8_scale_max_rel", worst_scale)
-    if stable:
-        assert flips / max(total, 1) < 1e-3, f"{flips} of {total} codes differ"
+        # the decoded values are held to the propagated bounds: a code rounded the other way at one
+        # token moves the whole key row's update at the next, which for an element near zero can be many
+        # of its own (small) steps; here only how often codes differ is checked
+        if stable:
+            off = vg != ve
+            totals.code_flips += int(np.sum(off))
+            totals.codes += off.size
+            rel = np.abs(scale_g[~zero] - scale_e[~zero]) / scale_e[~zero]
+            totals.worst_scale = max(totals.worst_scale, float(rel.max()) if rel.size else 0.0)
+
+    written = _check_batches(w, seq_list, before,
+                             lambda rows: {r: decode_fp8(*got[r], w) for r in rows},
+                             host_out, report, totals, qdq_precision, over, per_row=per_row)
+    check_output_l2(w, report, totals)
+    check_flip_rate(report, totals)
+    report.add("fp8_code_flip_frac", totals.code_flips / max(totals.codes, 1))
+    report.add("fp8_scale_max_rel", totals.worst_scale)
+    if totals.codes:
+        assert totals.code_flips / totals.codes < FLIP_RATE, f"{totals.code_flips} of {totals.codes} codes differ"
         # a code rounded the other way at an earlier token moves the tile's later amax by a fraction of
         # a step
-        assert worst_scale < 1e-2, f"scale relative error {worst_scale}"
-    assert sorted(ref_written) == sorted(set(writes))
+        assert totals.worst_scale < 1e-2, f"scale relative error {totals.worst_scale}"
+    assert sorted(written) == sorted(set(writes))
     check_untouched(snap, pool, all_writes)
     return report, out, pool
