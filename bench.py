@@ -16,8 +16,14 @@ Prints one JSON line:
                traffic = HBM bytes per launch measured with rocprofv3
                FETCH_SIZE/WRITE_SIZE (from profiles/, only if taken on the
                same kernel sources), else null
-  cpu_baseline the CPU oracle timed on this host on a bounded sample of the
-               same workload (rank 0, one GPU only)
+  cpu_baseline the CPU oracle timed on this host's cores (worker processes
+               forked before any GPU call) on a bounded sample of the same
+               workload, with a one-core figure beside it
+  state_stream_reference
+               the step's state bytes moved with no arithmetic over the same
+               rows (gdn_stream_rows), timed like the decode
+  gpu_clocks_during_timed_steps
+               shader / memory clocks sampled while the timed steps run
 """
 import argparse
 import hashlib
@@ -124,20 +130,60 @@ def chunked_flops(w):
     return chunks * w.HV * (w.V // 128) * per
 
 
-def gpu_clocks():
-    """Current shader / memory clocks as rocm-smi reports them (None where it is unavailable)."""
-    import re
-    import subprocess
-    try:
-        txt = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
-    except Exception:
+class ClockSampler:
+    """Samples the GPU's current shader and memory clocks from a thread while the timed steps run: the
+    amdgpu sysfs files pp_dpm_sclk / pp_dpm_mclk list the clock levels, and the one marked '*' carries the
+    current frequency.  summary() gives min / median / max per clock over the samples."""
+
+    def __init__(self, period_s=0.0005):
+        import glob
+        import threading
+        self.period = period_s
+        self.paths = {}
+        for key in ("sclk", "mclk"):
+            found = sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{key}"))
+            if found:
+                self.paths[key] = found[0]
+        self.samples = {k: [] for k in self.paths}
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self, path):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if "*" in line:
+                        m = re.search(r"(\d+)\s*Mhz", line, re.IGNORECASE)
+                        return int(m.group(1)) if m else None
+        except OSError:
+            return None
         return None
-    out = {}
-    for key in ("sclk", "mclk", "fclk"):
-        m = re.search(key + r"[^(\n]*\((\d+)\s*Mhz\)", txt, re.IGNORECASE)
-        if m:
-            out[key + "_mhz"] = int(m.group(1))
-    return out or None
+
+    def _run(self):
+        while not self._stop.is_set():
+            for k, path in self.paths.items():
+                v = self._read(path)
+                if v is not None:
+                    self.samples[k].append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.paths:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def summary(self):
+        import statistics
+        out = {}
+        for k, v in self.samples.items():
+            if v:
+                out[k + "_mhz"] = {"min": min(v), "median": statistics.median(v), "max": max(v), "samples": len(v)}
+        return out or None
 
 
 def copy_bandwidth(torch, dev, flush):
@@ -158,6 +204,46 @@ def copy_bandwidth(torch, dev, flush):
         best = ms if best is None else min(best, ms)
     del src, dst
     return 2 * n * 4 / (best * 1e-3) / 1e9
+
+
+def stream_reference(torch, rsd, w, pool, d, flush, steps, warmup, stream, state_bytes):
+    """The step's state traffic without its arithmetic: gdn_stream_rows over the same (read row, write row)
+    pairs as the decode (paged: from gdn_paged_decode_slots; pooled: (slot, slot) of every non-empty
+    suffix), timed the same way (cache flush before each launch, HIP events around it).  Its rate is what
+    this access pattern reaches on this machine, a reference for the decode kernel's.  None for packed pools
+    and multi-token paged workloads (their row pattern is not one read and one write per sequence)."""
+    import numpy as np
+    if pool.dtype != torch.float32:
+        return None
+    if w.kind in ("gdn_paged", "kda_paged"):
+        slots = rsd.gdn_paged_decode_slots(d["page_indices"], d["page_indptr"], d["last_page_len"])
+    elif w.kind in ("gdn_pooled", "kda_pooled"):
+        si = w.inputs["state_indices"].to(torch.int64)
+        cu = w.inputs.get("cu_seqlens")
+        if cu is not None:
+            si = si[torch.from_numpy(np.diff(cu.numpy()) > 0)]
+        slots = torch.stack([si, si], dim=1).contiguous().to(pool.device)
+    else:
+        return None
+    if pool[0].numel() % 1024:
+        return None
+    for i in range(warmup):
+        if flush is not None:
+            flush.fill_(float(i & 7))
+        rsd.stream_rows(pool, pool, slots)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        if flush is not None:
+            flush.fill_(float(i & 7))
+        starts[i].record(stream)
+        rsd.stream_rows(pool, pool, slots)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / steps
+    return {"kernel": "gdn::stream_rows_kernel", "ms_per_step": round(ms, 5),
+            "state_gbps": round(state_bytes / (ms * 1e-3) / 1e9, 1), "rows": int(slots.shape[0])}
 
 
 def kernel_name(w):
@@ -263,45 +349,78 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir, commands):
     print("\n".join(tl))
 
 
-def cpu_baseline(w, pool, budget_s):
-    """Time the oracle on the first sequences of the workload until about ``budget_s`` seconds."""
+# ---------------------------------------------------------------- the oracle on the host cores (cpu_baseline)
+#
+# The oracle runs in worker processes forked before this process makes any GPU call (a process that
+# holds the GPU must not fork or exec).  Each worker takes every n-th sequence of the workload, draws
+# the pool rows those sequences read (N(0, 0.05), the workload's state distribution: the timing does
+# not depend on the values), waits for the others at a barrier, and runs the oracle over its sequences
+# in batches of 8, round after round, until the time budget is spent.  Only the oracle's arithmetic is
+# timed; the whole-host rate is the tokens all workers finished divided by the budget's wall time.
+
+_CPU = {}
+
+
+def cpu_cores():
+    """Host cores this process may use: its CPU affinity, capped by OMP_NUM_THREADS when that is set (the
+    share of the host that belongs to one GPU)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def _cpu_oracle_worker(idx):
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
     from tests import parity as P
 
-    seqs_all = list(range(w.B))
-    # pool rows are read back before timing; only the oracle arithmetic is timed.
-    # Sequences are taken in order, in batches of 8; a small workload is passed
-    # over again until the time budget is spent.
+    torch.set_num_threads(1)         # a forked child runs torch's CPU ops inline
+    w, n, budget, barrier = _CPU["w"], _CPU["n"], _CPU["budget"], _CPU["barrier"]
+    seqs = list(range(idx, w.B, n)) or [idx % w.B]
+    rng = np.random.default_rng(7000 + idx)
+    shape = w.pool_shape()[1:]
+    reads, _ = P.rows_for(w, seqs)
+    rows = {r: rng.standard_normal(shape) * 0.05 for r in set(reads)}
     with threadpool_limits(limits=1):
-        done, t_used, toks, passes = 0, 0.0, 0, 0
-        batch = 8
-        while t_used < budget_s:
-            start = done % len(seqs_all)
-            seqs = seqs_all[start:start + batch]
-            r, _ = P.rows_for(w, seqs)
-            if pool.dtype == torch.uint8 and w.options.get("qdq") == "fp8_e4m3_tile":
-                rows = {k: P.decode_fp8(c, sc, w) for k, (c, sc) in P.gather_fp8(pool, r, w).items()}
-            elif pool.dtype == torch.uint8:      # packed codes and scales: the oracle takes the states
-                from oracle import hadamard as ohad
-                rows = {k: ohad.int8_hadamard32_decode(c, sc) for k, (c, sc) in
-                        P.gather_packed(pool, r, w.K, w.V).items()}
-            else:
-                rows = P.gather_rows(pool, r)
-            t0 = time.perf_counter()
-            P.oracle_call(w, rows, seqs=seqs)
-            t_used += time.perf_counter() - t0
-            toks += len(P.token_rows(w, seqs))
-            done += len(seqs)
-            if done % len(seqs_all) == 0:
-                passes += 1
-    if passes:
-        sample = f"{done} sequences ({toks} tokens): {done / len(seqs_all):.1f} passes over all {w.B} sequences"
-    else:
-        sample = f"first {done} of {w.B} sequences ({toks} tokens)"
-    return {"value": toks / t_used, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{sample} of {w.name}, float64 NumPy, one thread", "seconds": round(t_used, 3)}
+        barrier.wait(timeout=300)
+        t0 = time.perf_counter()
+        toks, nseq, i = 0, 0, 0
+        while time.perf_counter() - t0 < budget:
+            batch = [seqs[(i + j) % len(seqs)] for j in range(min(8, len(seqs)))]
+            P.oracle_call(w, rows, seqs=batch)
+            toks += len(P.token_rows(w, batch))
+            nseq += len(batch)
+            i += len(batch)
+        return toks, nseq, time.perf_counter() - t0
+
+
+def cpu_baseline(w, budget_s, single_budget_s):
+    """Time the oracle on the host cores (and, beside it, on one core); call before any GPU work."""
+    import multiprocessing as mp
+    ctx = mp.get_context("fork")
+
+    def leg(n, budget):
+        _CPU.update(w=w, n=n, budget=budget, barrier=ctx.Barrier(n))
+        with ctx.Pool(n) as pool:
+            res = pool.map(_cpu_oracle_worker, range(n), chunksize=1)
+        toks = sum(r[0] for r in res)
+        nseq = sum(r[1] for r in res)
+        wall = max(r[2] for r in res)
+        return toks, nseq, wall
+
+    n = cpu_cores()
+    toks, nseq, wall = leg(n, budget_s)
+    toks1, nseq1, wall1 = leg(1, single_budget_s)
+    return {"value": round(toks / wall, 1), "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": f"{nseq} sequences ({toks} tokens) of {w.name}: each of {n} worker processes takes every "
+                      f"{n}-th sequence, batches of 8, repeated for {budget_s:.0f} s of wall time; float64 NumPy, "
+                      f"one thread per worker",
+            "seconds": round(wall, 3), "host_cpus": len(os.sched_getaffinity(0)),
+            "single_core": {"value": round(toks1 / wall1, 1), "cores": 1, "seconds": round(wall1, 3),
+                            "sample": f"{nseq1} sequences ({toks1} tokens), one worker"}}
 
 
 def main():
@@ -323,7 +442,8 @@ def main():
     ap.add_argument("--token-path", action="store_true",
                     help="run a chunked-prefill workload through the token-by-token paged call instead")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="wall seconds of the oracle on all host cores for cpu_baseline (one core: a third of it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 output directories (no GPU needed)")
@@ -359,7 +479,6 @@ def main():
     from recurrent_state_decode_amd import workloads as wl
 
     dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
     maker = wl.NAMED[args.workload]
     paged_makers = ("paged_gdn_b256", "paged_kda_b256", "paged_gdn_varlen_b256_t4", "paged_gdn_prefill_b16_t1024",
                     "paged_kda_prefill_b16_t1024")
@@ -394,6 +513,9 @@ def main():
         w.name = f"{w.name}+{args.qdq}"
     if packed:
         w.name = f"{w.name}+{args.storage}"
+    # the oracle on the host cores first: its worker processes are forked before this process touches the GPU
+    cpu_res = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget, args.cpu_budget / 3)
+    torch.cuda.set_device(dev)
     d = wl.device_inputs(w, dev)
     # (a packed pool for timing: seeded random codes and scales)
     pool = wl.random_packed_pool(w, dev) if packed else wl.make_pool(w, dev)
@@ -415,15 +537,16 @@ def main():
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if flush is not None:
-            flush.fill_(float(i & 7))
-        starts[i].record(stream)
-        wl.run(w, pool, d, out=out)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clocks:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            if flush is not None:
+                flush.fill_(float(i & 7))
+            starts[i].record(stream)
+            wl.run(w, pool, d, out=out)
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     times_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     mean_ms = sum(times_ms) / len(times_ms)
     med_ms = sorted(times_ms)[len(times_ms) // 2]
@@ -459,15 +582,21 @@ def main():
                      "traffic": traffic, "algorithmic_bytes_per_launch": state_b + io_b,
                      "kernel": kernel_name(w), "source_hash": source_hash(w.chunked)},
     }
+    if not args.copy_calibration:
+        import recurrent_state_decode_amd as rsd
+        ref = stream_reference(torch, rsd, w, pool, d, flush, args.steps, args.warmup, stream, state_b)
+        if ref is not None:
+            # the decode kernel's state rate as a fraction of the plain stream's over the same rows
+            ref["decode_frac_of_stream"] = round(ref["ms_per_step"] / mean_ms, 4)
+            res["state_stream_reference"] = ref
     try:
         cbw = copy_bandwidth(torch, dev, flush)
         res["device_copy_gbps"] = round(cbw, 1)        # torch's 1 GiB device-to-device copy, best of 3
         res["frac_of_device_copy"] = round(achieved / cbw, 4)
     except RuntimeError:
         pass
-    # (not in the counter runs: under rocprofv3 --pmc every child process starts with the GPU
-    # initialised, and rocm-smi, a Python script, execs its interpreter)
-    res["gpu_clocks_after_run"] = None if args.copy_calibration else gpu_clocks()
+    # clocks sampled while the timed steps ran (the GPU idles before and after them)
+    res["gpu_clocks_during_timed_steps"] = clocks.summary()
     if w.chunked:
         fl = chunked_flops(w)
         tf = fl / (mean_ms * 1e-3) / 1e12
@@ -483,8 +612,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = n * 4
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, pool, args.cpu_budget)
+    if cpu_res is not None:
+        res["cpu_baseline"] = cpu_res
     print(json.dumps(res), flush=True)
 
 

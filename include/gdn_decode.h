@@ -399,6 +399,33 @@ int64_t gdn_fp8_tile_bytes(int32_t K, int32_t V, int32_t block_v);
  * int8_hadamard32 codec needs VB >= 32. */
 int gdn_supported_head_dims(int32_t* pairs, int cap);
 
+/*
+ * Measurement and launch-order helpers (not operations of the pages).
+ *
+ * gdn_stream_rows -- the state traffic of a single-token step with no
+ * arithmetic: for each of the n pairs slots[i] = (read row, write row)
+ * (int64, device, as gdn_paged_decode_slots writes them; a pooled call's
+ * pair is (slot, slot)), copy row_floats consecutive floats from src_pool +
+ * read row * row_floats to dst_pool + write row * row_floats, 4 KiB per
+ * workgroup with non-temporal 128-bit loads and stores, workgroups ordered
+ * on the XCDs as the decode kernels order theirs.  src_pool and dst_pool
+ * may be the same pool (the decode's in-place read-modify-write); no read
+ * row may be another pair's write row.  A reference for the bandwidth a
+ * decode step's state stream can reach: its time is a floor for the decode
+ * kernel's.  row_floats must be a positive multiple of 1024 and n >= 0
+ * (else GDN_ERR_INVALID); asynchronous on stream.
+ */
+int gdn_stream_rows(const float* src_pool, float* dst_pool, const int64_t* slots, int32_t n,
+                    int64_t row_floats, void* stream);
+
+/*
+ * gdn_workgroup_order -- host only: units[bx] = the work unit that workgroup
+ * bx of a grid of `grid` workgroups runs when the kernels keep runs of
+ * 2^xcd_shift consecutive units on one XCD (the same function the kernels
+ * call).  grid >= 0 and 0 <= xcd_shift <= 16, else GDN_ERR_INVALID.
+ */
+int gdn_workgroup_order(int32_t grid, int32_t xcd_shift, int32_t* units);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,5 +25,7 @@ from ._binding import (  # noqa: F401
     kda_prefill_paged,
     load_library,
     packed_tile_bytes,
+    stream_rows,
     supported_head_dims,
+    workgroup_order,
 )

@@ -86,6 +86,8 @@ _SIGNATURES = {
     "gdn_checked_build": (ctypes.c_int, []),
     "gdn_packed_tile_bytes": (ctypes.c_int64, [_I32, _I32]),
     "gdn_fp8_tile_bytes": (ctypes.c_int64, [_I32, _I32, _I32]),
+    "gdn_stream_rows": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _P]),
+    "gdn_workgroup_order": (ctypes.c_int, [_I32, _I32, ctypes.POINTER(ctypes.c_int32)]),
 }
 
 _lib = None
@@ -414,6 +416,34 @@ def gdn_paged_decode_slots(page_indices, page_indptr, last_page_len, slots=None,
     if st != GDN_OK:
         _raise(lib, st)
     return slots
+
+
+def stream_rows(src_pool, dst_pool, slots, stream=None):
+    """Copy each pair's read row of ``src_pool`` to its write row of ``dst_pool`` (see gdn_stream_rows):
+    the state traffic of a single-token step without its arithmetic.  ``slots`` [n, 2] int64 on the
+    pools' device; a row is one [HV, ...] slice of the pool's leading axis."""
+    lib = load_library()
+    dev = src_pool.device
+    _check_dev("src_pool", src_pool, dev, (torch.float32,))
+    _check_dev("dst_pool", dst_pool, dev, (torch.float32,))
+    _check_dev("slots", slots, dev, (torch.int64,))
+    if src_pool.shape[1:] != dst_pool.shape[1:] or slots.dim() != 2 or slots.shape[1] != 2:
+        raise ValueError("pools must have the same row shape and slots must be [n, 2]")
+    row_floats = src_pool[0].numel()
+    st = lib.gdn_stream_rows(_ptr(src_pool), _ptr(dst_pool), _ptr(slots), slots.shape[0], row_floats,
+                             _stream_handle(dev, stream))
+    if st != GDN_OK:
+        _raise(lib, st)
+
+
+def workgroup_order(grid, xcd_shift):
+    """The work unit each workgroup id of a grid runs (see gdn_workgroup_order); host only."""
+    lib = load_library()
+    units = (ctypes.c_int32 * max(int(grid), 1))()
+    st = lib.gdn_workgroup_order(int(grid), int(xcd_shift), units)
+    if st != GDN_OK:
+        _raise(lib, st)
+    return list(units)[:int(grid)]
 
 
 def _host_index(name, t, dtypes):

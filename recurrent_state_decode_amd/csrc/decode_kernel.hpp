@@ -86,6 +86,20 @@ struct Params {
   int32_t div_nvb_s, div_hv_s, div_gqa_s;
 };
 
+// Work unit run by workgroup id bx of a grid of n workgroups.  The hardware
+// hands consecutive workgroup ids to the 8 XCDs in turn; within each span of
+// 8 * 2^gs ids, XCD x (= id % 8) gets the units [x 2^gs, (x + 1) 2^gs) of
+// that span, so each run of 2^gs consecutive units executes on one XCD and
+// shares its L2.  Ids past the last whole span keep their number.  A
+// permutation of [0, n) for every gs >= 0 (host and device share this code;
+// gdn_workgroup_order exports it for the host-side test of that property).
+__host__ __device__ inline int xcd_unit(int bx, int n, int gs) {
+  const int span = gs + 3;
+  const int nfull = (n >> span) << span;
+  if (bx >= nfull) return bx;
+  return ((bx >> span) << span) | ((bx & 7) << gs) | ((bx >> 3) & ((1 << gs) - 1));
+}
+
 __device__ __forceinline__ int fast_div(int n, uint64_t m, int sh) {
   return static_cast<int>((static_cast<uint64_t>(static_cast<uint32_t>(n)) * m) >> sh);
 }
@@ -455,14 +469,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   const int lr = lane % LR;        // position inside a memory row
   const int rg = lane / LR;        // row group inside the wave
 
-  // renumber workgroups: within each span of 8 * G ids, XCD x (id % 8) gets
-  // units [x * G, (x + 1) * G) of that span; ids past the last full span keep
-  // their number.  A permutation of [0, gridDim.x) for every G = 2^gs.
-  const int bx = blockIdx.x;
-  const int gs = p.xcd_shift;                       // G = 1 << gs
-  const int nfull = (static_cast<int>(gridDim.x) >> (gs + 3)) << (gs + 3);
-  const int unit = bx < nfull ? (((bx >> (gs + 3)) << (gs + 3)) | ((bx & 7) << gs) | ((bx >> 3) & ((1 << gs) - 1)))
-                              : bx;
+  // runs of 2^xcd_shift consecutive work units on one XCD (xcd_unit)
+  const int unit = xcd_unit(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x), p.xcd_shift);
   const int q1 = fast_div(unit, p.div_nvb_m, p.div_nvb_s);
   const int vb = unit - q1 * p.nvb;
   const int bs = fast_div(q1, p.div_hv_m, p.div_hv_s);
@@ -1225,6 +1233,27 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   }
 
   store_tile(dst);
+}
+
+// The state traffic of a single-token step without its arithmetic
+// (gdn_stream_rows): work unit u = r * chunks + c copies floats
+// [1024 c, 1024 (c + 1)) of pair r's read row to its write row, 128 threads
+// with two 128-bit non-temporal loads and stores each, half a chunk apart --
+// the 4 KiB per workgroup, access hints and XCD order of the decode kernel's
+// V_FIRST single-token shape.
+__global__ __launch_bounds__(128) void stream_rows_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                          const int64_t* __restrict__ slots, int64_t row_floats,
+                                                          int32_t chunks, int32_t xcd_shift) {
+  const int unit = xcd_unit(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x), xcd_shift);
+  const int r = unit / chunks;
+  const int c = unit - r * chunks;
+  const int64_t off = static_cast<int64_t>(c) * 1024 + 4 * static_cast<int>(threadIdx.x);
+  const f32x4* s = reinterpret_cast<const f32x4*>(src + slots[2 * r] * row_floats + off);
+  f32x4* d = reinterpret_cast<f32x4*>(dst + slots[2 * r + 1] * row_floats + off);
+  const f32x4 a = __builtin_nontemporal_load(s);
+  const f32x4 b = __builtin_nontemporal_load(s + 128);
+  __builtin_nontemporal_store(a, d);
+  __builtin_nontemporal_store(b, d + 128);
 }
 
 // (read row, write row) of every sequence for one decoded token on a CSR

@@ -752,6 +752,36 @@ int64_t gdn_fp8_tile_bytes(int32_t K, int32_t V, int32_t block_v) {
   return static_cast<int64_t>(K) * V + 16 * ((4 * static_cast<int64_t>(V / block_v) + 15) / 16);
 }
 
+int gdn_stream_rows(const float* src_pool, float* dst_pool, const int64_t* slots, int32_t n, int64_t row_floats,
+                    void* stream) {
+  if (!src_pool || !dst_pool || (n > 0 && !slots)) return fail(GDN_ERR_INVALID, "a required pointer is NULL");
+  if (n < 0 || row_floats <= 0 || row_floats % 1024 != 0)
+    return fail(GDN_ERR_INVALID, "n must be >= 0 and row_floats a positive multiple of 1024 (n=%d row_floats=%lld)", n,
+                (long long)row_floats);
+  if (n == 0) {
+    g_last_error.clear();
+    return GDN_OK;
+  }
+  const int64_t chunks = row_floats / 1024;
+  const int64_t units = chunks * n;
+  if (units > 0x7fffffffLL) return fail(GDN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)units);
+  hipLaunchKernelGGL(gdn::stream_rows_kernel, dim3(static_cast<uint32_t>(units)), dim3(128), 0,
+                     static_cast<hipStream_t>(stream), src_pool, dst_pool, slots, row_floats,
+                     static_cast<int32_t>(chunks), 6);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  g_last_error.clear();
+  return GDN_OK;
+}
+
+int gdn_workgroup_order(int32_t grid, int32_t xcd_shift, int32_t* units) {
+  if (grid < 0 || xcd_shift < 0 || xcd_shift > 16 || (grid > 0 && !units))
+    return fail(GDN_ERR_INVALID, "grid must be >= 0, xcd_shift in [0, 16] and units non-NULL");
+  for (int32_t bx = 0; bx < grid; ++bx) units[bx] = gdn::xcd_unit(bx, grid, xcd_shift);
+  g_last_error.clear();
+  return GDN_OK;
+}
+
 int gdn_supported_head_dims(int32_t* pairs, int cap) {
   const int n = static_cast<int>(sizeof(kHeads) / sizeof(kHeads[0]));
   for (int i = 0; i < n && i < cap && pairs; ++i) {

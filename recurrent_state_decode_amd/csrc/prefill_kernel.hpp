@@ -119,16 +119,10 @@ void prefill_kernel(const PrefillParams p) {
   const int n16 = lane & 15;       // MFMA row / column inside a tile
   const int g4 = lane >> 4;        // MFMA k group
 
-  // Consecutive workgroup ids go to the 8 XCDs in turn.  Renumber them so
-  // that each run of 2^xcd_shift consecutive units (the value heads that read
-  // one key head's q / k, and their V-blocks) lands on one XCD and shares its
-  // L2; ids past the last whole span of 8 runs keep their number.  A
-  // permutation of [0, gridDim.x).
-  const int bx = blockIdx.x;
-  const int gs = p.xcd_shift;
-  const int nfull = (static_cast<int>(gridDim.x) >> (gs + 3)) << (gs + 3);
-  const int unit = bx < nfull ? (((bx >> (gs + 3)) << (gs + 3)) | ((bx & 7) << gs) | ((bx >> 3) & ((1 << gs) - 1)))
-                              : bx;
+  // Each run of 2^xcd_shift consecutive units (the value heads that read one
+  // key head's q / k, and their V-blocks) executes on one XCD and shares its
+  // L2 (xcd_unit: a permutation of [0, gridDim.x)).
+  const int unit = xcd_unit(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x), p.xcd_shift);
   const int q1 = unit / p.nvb;
   const int vb = unit - q1 * p.nvb;
   const int bs = q1 / p.HV;

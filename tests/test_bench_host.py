@@ -54,3 +54,31 @@ def test_timed_leg_does_not_import_the_oracle():
             "assert not bad, bad")
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-2000:]
+
+
+def test_cpu_baseline_runs_on_every_core_of_the_share():
+    """The oracle leg forks one worker per host core of this process's share and reports that count;
+    the parent process itself never imports the oracle."""
+    code = ("import sys, json, bench; from recurrent_state_decode_amd import workloads as wl; "
+            "r = bench.cpu_baseline(wl.pooled_gdn_b64(), 1.0, 0.5); "
+            "bad = [m for m in sys.modules if m == 'oracle' or m.startswith('oracle.') or m.startswith('tests')]; "
+            "assert not bad, bad; print(json.dumps(r))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    import json
+    res = json.loads(r.stdout.strip().splitlines()[-1])
+    assert res["cores"] == bench.cpu_cores() and res["kind"] == "oracle" and res["value"] > 0
+    assert res["single_core"]["cores"] == 1 and res["single_core"]["value"] > 0
+
+
+def test_clock_sampler_reads_the_marked_level(tmp_path):
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("0: 500Mhz\n1: 2103Mhz *\n2: 2400Mhz\n")
+    c = bench.ClockSampler(period_s=0.001)
+    c.paths = {"sclk": str(f)}
+    c.samples = {"sclk": []}
+    import time
+    with c:
+        time.sleep(0.02)
+    s = c.summary()["sclk_mhz"]
+    assert s["min"] == s["max"] == 2103 and s["samples"] >= 2
