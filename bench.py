@@ -361,6 +361,56 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir, commands):
 _CPU = {}
 
 
+COUNTERS = ("VALUBusy", "VALUUtilization", "OccupancyPercent", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
+            "SQ_WAVES")
+
+
+def summarize_counters(run_dir, command):
+    """profiles/counters_<workload>.txt from one rocprofv3 run with --pmc COUNTERS and --kernel-trace.
+
+    Per dispatch of the kernel the bench times (medians over its dispatches): VALUBusy (percent of the
+    active time some VALU instruction issues), VALUUtilization (active lanes), OccupancyPercent (resident
+    waves against 32 per CU), VALU and LDS instructions per wave, and the shader clock the kernel ran at,
+    GRBM_GUI_ACTIVE cycles over the dispatch's duration."""
+    import csv
+    import statistics
+
+    with open(run_dir.rstrip("/") + ".json") as f:
+        bench_line = json.loads(f.read().strip().splitlines()[-1])
+    name = bench_line["config"]["workload"]
+    kern = bench_line["roofline"]["kernel"]
+    rows = [r for f in _csvs(run_dir, "counter_collection.csv") for r in csv.DictReader(open(f))]
+    trace = [r for f in _csvs(run_dir, "kernel_trace.csv") for r in csv.DictReader(open(f))]
+    dur = {r["Dispatch_Id"]: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+           for r in trace if kern in r["Kernel_Name"]}
+    per = {}
+    meta = {}
+    for r in rows:
+        if kern not in r["Kernel_Name"]:
+            continue
+        per.setdefault(r["Counter_Name"], {})[r["Dispatch_Id"]] = float(r["Counter_Value"])
+        meta = {k: r.get(k) for k in ("VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "LDS_Block_Size",
+                                      "Scratch_Size", "Workgroup_Size", "Grid_Size")}
+    med = {k: statistics.median(v.values()) for k, v in per.items()}
+    waves = med.get("SQ_WAVES", 0) or 1
+    clocks = [per["GRBM_GUI_ACTIVE"][d] / dur[d] for d in per.get("GRBM_GUI_ACTIVE", {}) if d in dur and dur[d] > 0]
+    lines = [f"# rocprofv3 activity counters: {name}", "", "Command (from the repository root):", "",
+             "    " + command, "",
+             f"kernel: {kern}", f"source_hash: {bench_line['roofline']['source_hash']}",
+             f"dispatches: {len(dur)}; kernel duration median {statistics.median(dur.values()):.1f} us" if dur else
+             "dispatches: 0",
+             *(f"{k}: {v}" for k, v in meta.items()),
+             *(f"{k} (median per dispatch): {med[k]:.4g}" for k in COUNTERS if k in med),
+             f"VALU instructions per wave: {med.get('SQ_INSTS_VALU', 0) / waves:.1f}",
+             f"LDS instructions per wave: {med.get('SQ_INSTS_LDS', 0) / waves:.1f}",
+             f"GRBM_GUI_ACTIVE per us of the dispatch (median): {statistics.median(clocks):.0f}" if clocks else
+             "GRBM_GUI_ACTIVE per us: n/a"]
+    path = os.path.join(ROOT, "profiles", f"counters_{name}.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_cores():
     """Host cores this process may use: its CPU affinity, capped by OMP_NUM_THREADS when that is set (the
     share of the host that belongs to one GPU)."""
@@ -447,6 +497,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 output directories (no GPU needed)")
+    ap.add_argument("--summarize-counters", metavar="RUN_DIR",
+                    help="write profiles/counters_<workload>.txt from a rocprofv3 --pmc run of COUNTERS with "
+                         "--kernel-trace (no GPU needed)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a plain 1 GiB -> 1 GiB copy 3 times (a kernel of known traffic for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -466,6 +519,17 @@ def main():
                 "write": f"rocprofv3 --pmc WRITE_SIZE -d {wr} -o w --output-format csv -- "
                          f"python3 bench.py{sel} --steps 10 --warmup 1 --no-cpu-baseline --copy-calibration"}
         summarize_profiles(kt, fe, wr, cmds)
+        return
+
+    if args.summarize_counters:
+        sel = "" if args.workload == "paged_gdn_b256" else f" --workload {args.workload}"
+        sel += f" --layout {args.layout}" if args.layout else ""
+        sel += f" --qdq {args.qdq}" if args.qdq else ""
+        sel += " --token-path" if args.token_path else ""
+        sel += f" --storage {args.storage}" if args.storage != "f32" else ""
+        d = args.summarize_counters
+        summarize_counters(d, f"rocprofv3 --pmc {' '.join(COUNTERS)} --kernel-trace -d {d} -o c --output-format csv "
+                              f"-- python3 bench.py{sel} --steps 10 --warmup 1 --no-cpu-baseline > {d}.json")
         return
 
     if args.gpus != 1:
