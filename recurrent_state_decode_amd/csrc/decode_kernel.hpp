@@ -6,16 +6,16 @@
 // the key retrieves, write the delta, read the updated state out.
 //
 // Scaled state.  Registers hold S_reg with the true state S = c * S_reg,
-// where c is one scalar per workgroup (GDN: the decay is one factor per head)
-// or one factor per key row (KDA).  A token then needs one pass over the
-// tile and one FMA per element for the write:
+// where c is one scalar per workgroup.  GDN's decay is one factor per head,
+// so it goes into c and a token needs one pass over the tile and one FMA per
+// element for the write:
 //     c' = c * alpha                                 (the decay)
 //     r  = k_hat^T S = c' (k_hat^T S_reg),  p = c' (q_hat^T S_reg)
 //     u  = beta (v - r),   o = p + (q_hat . k_hat) u  (= q_hat^T S_new)
 //     S_reg += k_hat (u / c')                         (S_new = c' S_reg)
-// (for KDA the per-row c' folds into the coefficients: r = sum_i k_hat_i c'_i
-// S_reg[i,:], S_reg[i,:] += (k_hat_i / c'_i) u).  A factor below 1e-20 is
-// applied to the registers and reset to 1, so S_reg never overflows.  The
+// KDA's decay is one factor per key channel: it multiplies the registers'
+// key rows directly (c' = c), one multiply per element.  A scale below 1e-20
+// is applied to the registers and reset to 1, so S_reg never overflows.  The
 // fp8 tile quantisation keeps the codes in S_reg and moves the tile scale
 // amax/448 into c.  With the int8_hadamard32 codec the registers carry the
 // state rotated along V (each 32-value group times the Hadamard matrix) from
@@ -303,13 +303,40 @@ __device__ __forceinline__ float rs_rows16(float a, float b) {
   return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
 }
 
-// Round x0, x1 (already divided by the tile scale) to the E4M3 grid and back
-// with the gfx950 OCP fp8 conversions (nearest even).
-__device__ __forceinline__ void e4m3_roundtrip2(float& x0, float& x1) {
-  const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-  const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(pk, false);
-  x0 = back[0];
-  x1 = back[1];
+// Round x0 .. x3 (already divided by the tile scale) to the E4M3 grid and
+// back with the gfx950 OCP fp8 conversions (nearest even).  The two pairs
+// fill the low and the high half of one packed word, so no destination needs
+// clearing first (the first conversion's "old" operand is any value whose
+// high half the second conversion replaces).  The scaled conversions of
+// gfx950 are no help here: they take only the exponent of their scale
+// operand (checked on the device), and the tile scale amax / 448 is not a
+// power of two.
+__device__ __forceinline__ void e4m3_roundtrip4(float& x0, float& x1, float& x2, float& x3) {
+  int pk = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, __float_as_int(x0), false);
+  pk = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, pk, true);
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(pk, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(pk, true);
+  x0 = lo[0];
+  x1 = lo[1];
+  x2 = hi[0];
+  x3 = hi[1];
+}
+
+// 448 / m and m / 448 for the tile scale, m >= 2^-100: the hardware
+// reciprocal (or the rounded constant 1/448) and one residual correction
+// q + (n - q d) / d, a few instructions instead of a full division; the
+// result is the correctly rounded quotient except within an ulp of a
+// rounding boundary, and exact whenever the quotient is representable
+// (m = 448 * 2^k: an exact scale keeps the grid exact).
+__device__ __forceinline__ float div448_by(float m) {
+  const float r = __builtin_amdgcn_rcpf(m);
+  const float q = 448.0f * r;
+  return fmaf(fmaf(-q, m, 448.0f), r, q);
+}
+__device__ __forceinline__ float div_by448(float m) {
+  constexpr float c = 1.0f / 448.0f;
+  const float q = m * c;
+  return fmaf(fmaf(-q, 448.0f, m), c, q);
 }
 
 // ---- int8_hadamard32 codec (modelopt ... linear_attention.config,
@@ -737,11 +764,12 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   const uint32_t sg4 = (static_cast<uint32_t>(lane) & 4u) << 29;
   if constexpr (HAD && !PACKED) wht32(S, sg1, sg2, sg4);
 
-  // true state = scale * S: one scale (GDN) or one per key slot (KDA)
-  constexpr int NC = KDA ? NKEY : 1;
-  float cs[NC];
-#pragma unroll
-  for (int m = 0; m < NC; ++m) cs[m] = fp8_scale;
+  // true state = cs * S: one scale per workgroup.  The GDN decay (one factor
+  // per head) goes into it; the KDA decay (one factor per key channel) is
+  // applied to the registers, one multiply per element, which is no more work
+  // than folding per-row factors into the coefficients and keeps no per-row
+  // scales live.  fp8 tile QDQ puts the tile scale in cs.
+  float cs = fp8_scale;
   // key slot of element (s, e)
   auto slot = [](int s, int e) -> int { return AV ? e : s; };
 
@@ -760,62 +788,34 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
     return m;
   };
 
-  // fp8 tile QDQ of the true state; the codes stay in S, the tile scale goes to cs
+  // fp8 tile QDQ of the true state cs * S: the codes stay in S, the tile
+  // scale goes to cs (one scale per workgroup for GDN and KDA alike)
   bool tile_nz = true;             // the last qdq_tile saw a non-zero tile
   auto qdq_tile = [&]() {
+    // in-thread amax: v_max3_f32 with |x| source modifiers
     float m = 0.0f;
-    if constexpr (!KDA) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int e = 0; e < EV; e += 2)
+        m = __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(fabsf(S[s][e]), fabsf(S[s][e + 1])));
+    const float ms = block_max(m);       // amax of S_reg; the true amax is cs * ms
+    tile_nz = ms > 0.0f;
+    if (ms > 0.0f) {
+      const float msf = fmaxf(ms, kTinyAmax);   // 448 / amax stays finite
+      const float inv = div448_by(msf);
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int e = 0; e < EV; ++e) m = fmaxf(m, fabsf(S[s][e]));
-      const float ms = block_max(m);       // amax of S_reg; the true amax is cs[0] * ms
-      tile_nz = ms > 0.0f;
-      if (ms > 0.0f) {
-        const float msf = fmaxf(ms, kTinyAmax);   // 448 / amax stays finite
-        const float inv = kE4M3Max / msf;
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-          for (int e = 0; e < EV; e += 2) {
-            float x0 = S[s][e] * inv, x1 = S[s][e + 1] * inv;
-            e4m3_roundtrip2(x0, x1);
-            S[s][e] = x0;
-            S[s][e + 1] = x1;
-          }
-        cs[0] = cs[0] * (msf / kE4M3Max);
-      }
-    } else {
-      float rowm[NC];
-#pragma unroll
-      for (int k2 = 0; k2 < NC; ++k2) rowm[k2] = 0.0f;
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int e = 0; e < EV; ++e) rowm[slot(s, e)] = fmaxf(rowm[slot(s, e)], fabsf(S[s][e]));
-#pragma unroll
-      for (int k2 = 0; k2 < NC; ++k2) m = fmaxf(m, cs[k2] * rowm[k2]);
-      const float mt = block_max(m);       // true amax
-      tile_nz = mt > 0.0f;
-      if (mt > 0.0f) {
-        const float mtf = fmaxf(mt, kTinyAmax);   // 448 / amax stays finite
-        const float inv = kE4M3Max / mtf;
-        float f[NC];
-#pragma unroll
-        for (int k2 = 0; k2 < NC; ++k2) f[k2] = cs[k2] * inv;
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-          for (int e = 0; e < EV; e += 2) {
-            float x0 = S[s][e] * f[slot(s, e)], x1 = S[s][e + 1] * f[slot(s, e + 1)];
-            e4m3_roundtrip2(x0, x1);
-            S[s][e] = x0;
-            S[s][e + 1] = x1;
-          }
-        const float sc = mtf / kE4M3Max;
-#pragma unroll
-        for (int k2 = 0; k2 < NC; ++k2) cs[k2] = sc;
-      }
+        for (int e = 0; e < EV; e += 4) {
+          float x0 = S[s][e] * inv, x1 = S[s][e + 1] * inv, x2 = S[s][e + 2] * inv, x3 = S[s][e + 3] * inv;
+          e4m3_roundtrip4(x0, x1, x2, x3);
+          S[s][e] = x0;
+          S[s][e + 1] = x1;
+          S[s][e + 2] = x2;
+          S[s][e + 3] = x3;
+        }
+      cs = cs * div_by448(msf);
     }
   };
 
@@ -1021,7 +1021,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
         __builtin_nontemporal_store(c4, reinterpret_cast<uint32_t*>(gb + r * 32));
         // a plain store: the group's scales are 4-byte pieces from many lanes and waves, which L2 merges into
         // whole lines before writing them back (streamed past L2 each would cost a line)
-        if ((lr & 7) == 0) tsc[grp * K + r] = cs[KDA ? s : 0] * (mf * (1.0f / 127.0f));
+        if ((lr & 7) == 0) tsc[grp * K + r] = cs * (mf * (1.0f / 127.0f));
       }
     } else if constexpr (FP8P) {
       // every token ends with qdq_tile: grid values, converted exactly; the
@@ -1032,22 +1032,23 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int f = 0; f < EV / 4; ++f) {
-          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(S[s][4 * f + 0], S[s][4 * f + 1], 0, false);
+          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(S[s][4 * f + 0], S[s][4 * f + 1], __float_as_int(S[s][4 * f]),
+                                                   false);
           pk = __builtin_amdgcn_cvt_pk_fp8_f32(S[s][4 * f + 2], S[s][4 * f + 3], pk, true);
           __builtin_nontemporal_store(static_cast<uint32_t>(pk), reinterpret_cast<uint32_t*>(tb + row_off(s, f)));
         }
       if (tid == 0)
-        __builtin_nontemporal_store(tile_nz ? cs[0] : 0.0f, reinterpret_cast<float*>(tb + tile_elems) + vb);
+        __builtin_nontemporal_store(tile_nz ? cs : 0.0f, reinterpret_cast<float*>(tb + tile_elems) + vb);
     } else if constexpr (!HAD) {
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int f = 0; f < EV / 4; ++f) {
           f32x4 x;
-          x.x = S[s][4 * f + 0] * cs[KDA ? slot(s, 4 * f + 0) : 0];
-          x.y = S[s][4 * f + 1] * cs[KDA ? slot(s, 4 * f + 1) : 0];
-          x.z = S[s][4 * f + 2] * cs[KDA ? slot(s, 4 * f + 2) : 0];
-          x.w = S[s][4 * f + 3] * cs[KDA ? slot(s, 4 * f + 3) : 0];
+          x.x = S[s][4 * f + 0] * cs;
+          x.y = S[s][4 * f + 1] * cs;
+          x.z = S[s][4 * f + 2] * cs;
+          x.w = S[s][4 * f + 3] * cs;
           __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(row_base + row_off(s, f)));
         }
     } else {
@@ -1060,7 +1061,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
       wht32(X, sg1, sg2, sg4);
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const float sc = cs[KDA ? s : 0] * 0.03125f;
+        const float sc = cs * 0.03125f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) X[s][j] *= sc;
       }
@@ -1112,69 +1113,36 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
       lds_keys(&s_k[tt][0], kh);
       lds_keys(&s_q[tt][0], qh);
 
-      // decay into the scale; reduction and write coefficients
-      float kr[NKEY], qr[NKEY], kt[NKEY];
-      float cn_g = 1.0f, icn_g = 1.0f;
-      if constexpr (!KDA) {
-        float cn = cs[0] * s_sc[tt][0];
-        if (cn < kTinyScale) {                 // uniform: one scale per workgroup
+      // the decay: GDN into the scale, KDA onto the registers' key rows
+      float cn = KDA ? cs : cs * s_sc[tt][0];
+      if (cn < kTinyScale) {                   // uniform: one scale per workgroup
 #pragma unroll
-          for (int s = 0; s < NS; ++s)
+        for (int s = 0; s < NS; ++s)
 #pragma unroll
-            for (int e = 0; e < EV; ++e) S[s][e] *= cn;
-          cn = 1.0f;
-        }
-        cs[0] = cn;
-        cn_g = cn;
-        icn_g = rcp_hw(cn);
-#pragma unroll
-        for (int m = 0; m < NKEY; ++m) {
-          kr[m] = kh[m];
-          qr[m] = qh[m];
-          kt[m] = kh[m];
-        }
-      } else {
-        float al[NKEY], cn[NKEY];
+          for (int e = 0; e < EV; ++e) S[s][e] *= cn;
+        cn = 1.0f;
+      }
+      cs = cn;
+      const float icn = rcp_hw(cn);
+      if constexpr (KDA) {
+        float al[NKEY];
         lds_keys(&s_al[tt][0], al);
-        bool tiny = false;
 #pragma unroll
-        for (int m = 0; m < NKEY; ++m) {
-          cn[m] = cs[m] * al[m];
-          tiny |= cn[m] < kTinyScale;
-        }
-        if (tiny) {                            // rare: apply small factors to their key rows
+        for (int s = 0; s < NS; ++s)
 #pragma unroll
-          for (int m = 0; m < NKEY; ++m) {
-            const float f = cn[m] < kTinyScale ? cn[m] : 1.0f;
-#pragma unroll
-            for (int s = 0; s < NS; ++s)
-#pragma unroll
-              for (int e = 0; e < EV; ++e)
-                if (slot(s, e) == m) S[s][e] *= f;
-            cn[m] = cn[m] < kTinyScale ? 1.0f : cn[m];
-          }
-        }
-#pragma unroll
-        for (int m = 0; m < NKEY; ++m) {
-          cs[m] = cn[m];
-          kr[m] = kh[m] * cn[m];
-          qr[m] = qh[m] * cn[m];
-          kt[m] = kh[m] * rcp_hw(cn[m]);
-        }
+          for (int e = 0; e < EV; ++e) S[s][e] *= al[slot(s, e)];
       }
 
       float r[NO], pp[NO];
-      reduce_pass(kr, qr, r, pp);
+      reduce_pass(kh, qh, r, pp);
 
       float u[NO], o[NO], wv[NO];
 #pragma unroll
       for (int j = 0; j < NO; ++j) {
         const int col = AV ? row_idx(j) : 4 * lr + j;
-        const float rr = KDA ? r[j] : cn_g * r[j];
-        const float pj = KDA ? pp[j] : cn_g * pp[j];
-        u[j] = beta * (s_v[tt][col] - rr);
-        o[j] = fmaf(qk, u[j], pj);
-        wv[j] = KDA ? u[j] : u[j] * icn_g;
+        u[j] = beta * (s_v[tt][col] - cn * r[j]);
+        o[j] = fmaf(qk, u[j], cn * pp[j]);
+        wv[j] = u[j] * icn;
       }
       if constexpr (!HAD) {
         if (!stored) store_outputs(out_row, o);
@@ -1188,13 +1156,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
         store_outputs(out_row, o);
       }
 
-      // S_reg += kt (x) wv
+      // S_reg += k_hat (x) wv
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int e = 0; e < EV; ++e) {
-          if constexpr (AV) S[s][e] = fmaf(kt[e], wv[s], S[s][e]);
-          else S[s][e] = fmaf(kt[s], wv[e], S[s][e]);
+          if constexpr (AV) S[s][e] = fmaf(kh[e], wv[s], S[s][e]);
+          else S[s][e] = fmaf(kh[s], wv[e], S[s][e]);
         }
 
       if constexpr (QDQ != kQdqNone) {
@@ -1206,7 +1174,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
           // o = q_hat^T S after rounding
           float q2[NKEY];
 #pragma unroll
-          for (int m = 0; m < NKEY; ++m) q2[m] = qh[m] * cs[KDA ? m : 0];
+          for (int m = 0; m < NKEY; ++m) q2[m] = qh[m] * cs;
           float ps[NO], dummy[NO];
           reduce_pass(q2, q2, ps, dummy);
           if constexpr (HAD) {
