@@ -193,6 +193,7 @@ constexpr int kWaitVmem0 = 0x0F70;
 
 typedef const __attribute__((address_space(4))) int64_t* ConstI64;
 typedef const __attribute__((address_space(4))) int32_t* ConstI32;
+typedef const __attribute__((address_space(4))) float* ConstF32;
 __device__ __forceinline__ int64_t load_index_uniform(const void* p, int64_t i, int idx64) {
   return idx64 ? ((ConstI64)p)[i] : static_cast<int64_t>(((ConstI32)p)[i]);
 }
@@ -534,6 +535,21 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   }
   if (t1 <= t0) return;            // empty suffix: no read, no write
 
+  // the head's gate parameters, loaded before the tile: vector loads retire in
+  // order, so a value loaded after the tile could only be waited for together
+  // with the whole tile (and the input normalisation could not overlap it);
+  // the head-uniform ones come through the scalar cache
+  const float rate_h = exp_hw(((ConstF32)p.a_log)[h]);
+  float dtb[GPL];
+  if constexpr (KDA) {
+    if (lane < EL) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dtb[e] = p.dt_bias[h * K + EPL * lane + e];
+    }
+  } else {
+    dtb[0] = ((ConstF32)p.dt_bias)[h];
+  }
+
   // ---- raw per-token inputs of one chunk (each wave loads its own tokens)
   Raw<TIn, EPL> rq[TPW], rk[TPW];
   Raw<TIn, GPL> rgt[TPW];
@@ -594,14 +610,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
         qk = lane_reduce<0, 6>(qk);
         const float beta = p.beta_prob ? xb[0] : sigmoid_f(xb[0]);
         if (lane < EL) {
-          const float rate = KDA ? exp_hw(p.a_log[h]) : 0.0f;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) {
             const int c = EPL * lane + e;
             const int pos = lds_pos(c);
             s_q[tt][pos] = xq[e];
             s_k[tt][pos] = xk[e];
-            if constexpr (KDA) s_al[tt][pos] = exp_hw(-rate * softplus_f(xg[e] + p.dt_bias[h * K + c]));
+            if constexpr (KDA) s_al[tt][pos] = exp_hw(-rate_h * softplus_f(xg[e] + dtb[e]));
           }
         }
         if constexpr (HAD) xv[0] = wht32_lanes(xv[0], lane);   // v in the rotated basis (VPL == 1)
@@ -610,7 +625,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
           for (int e = 0; e < VPL; ++e) s_v[tt][VPL * lane + e] = xv[e];
         }
         if (lane == 0) {
-          if constexpr (!KDA) s_sc[tt][0] = exp_hw(-exp_hw(p.a_log[h]) * softplus_f(xg[0] + p.dt_bias[h]));
+          if constexpr (!KDA) s_sc[tt][0] = exp_hw(-rate_h * softplus_f(xg[0] + dtb[0]));
           s_sc[tt][1] = beta;
           s_sc[tt][2] = qk;
         }
