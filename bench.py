@@ -225,7 +225,7 @@ def stream_reference(torch, rsd, w, pool, d, flush, steps, warmup, stream, state
         slots = torch.stack([si, si], dim=1).contiguous().to(pool.device)
     else:
         return None
-    if pool[0].numel() % 1024:
+    if pool[0].numel() % 512:
         return None
     for i in range(warmup):
         if flush is not None:

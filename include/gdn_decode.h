@@ -406,14 +406,15 @@ int gdn_supported_head_dims(int32_t* pairs, int cap);
  * arithmetic: for each of the n pairs slots[i] = (read row, write row)
  * (int64, device, as gdn_paged_decode_slots writes them; a pooled call's
  * pair is (slot, slot)), copy row_floats consecutive floats from src_pool +
- * read row * row_floats to dst_pool + write row * row_floats, 4 KiB per
+ * read row * row_floats to dst_pool + write row * row_floats, 2 KiB per
  * workgroup with non-temporal 128-bit loads and stores, workgroups ordered
  * on the XCDs as the decode kernels order theirs.  src_pool and dst_pool
  * may be the same pool (the decode's in-place read-modify-write); no read
  * row may be another pair's write row.  A reference for the bandwidth a
- * decode step's state stream can reach: its time is a floor for the decode
- * kernel's.  row_floats must be a positive multiple of 1024 and n >= 0
- * (else GDN_ERR_INVALID); asynchronous on stream.
+ * decode step's state stream reaches: the fastest of the plain stream
+ * shapes measured for that row pattern.  row_floats must be a positive
+ * multiple of 512 and n >= 0 (else GDN_ERR_INVALID); asynchronous on
+ * stream.
  */
 int gdn_stream_rows(const float* src_pool, float* dst_pool, const int64_t* slots, int32_t n,
                     int64_t row_floats, void* stream);

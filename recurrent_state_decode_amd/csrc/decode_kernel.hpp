@@ -1220,23 +1220,25 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
 
 // The state traffic of a single-token step without its arithmetic
 // (gdn_stream_rows): work unit u = r * chunks + c copies floats
-// [1024 c, 1024 (c + 1)) of pair r's read row to its write row, 128 threads
-// with two 128-bit non-temporal loads and stores each, half a chunk apart --
-// the 4 KiB per workgroup, access hints and XCD order of the decode kernel's
-// V_FIRST single-token shape.
-__global__ __launch_bounds__(128) void stream_rows_kernel(const float* __restrict__ src, float* __restrict__ dst,
-                                                          const int64_t* __restrict__ slots, int64_t row_floats,
-                                                          int32_t chunks, int32_t xcd_shift) {
+// [512 c, 512 (c + 1)) of pair r's read row to its write row, 64 threads with
+// two 128-bit non-temporal loads and stores each, half a chunk apart, in the
+// decode kernels' XCD order.  Of the read-modify-write stream shapes measured
+// over the paged B=256 rows (64 to 256 threads, 2 to 32 KiB per workgroup,
+// plain or non-temporal), this one (2 KiB, 64 threads, non-temporal) moved
+// the bytes fastest.
+__global__ __launch_bounds__(64) void stream_rows_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                         const int64_t* __restrict__ slots, int64_t row_floats,
+                                                         int32_t chunks, int32_t xcd_shift) {
   const int unit = xcd_unit(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x), xcd_shift);
   const int r = unit / chunks;
   const int c = unit - r * chunks;
-  const int64_t off = static_cast<int64_t>(c) * 1024 + 4 * static_cast<int>(threadIdx.x);
+  const int64_t off = static_cast<int64_t>(c) * 512 + 4 * static_cast<int>(threadIdx.x);
   const f32x4* s = reinterpret_cast<const f32x4*>(src + slots[2 * r] * row_floats + off);
   f32x4* d = reinterpret_cast<f32x4*>(dst + slots[2 * r + 1] * row_floats + off);
   const f32x4 a = __builtin_nontemporal_load(s);
-  const f32x4 b = __builtin_nontemporal_load(s + 128);
+  const f32x4 b = __builtin_nontemporal_load(s + 64);
   __builtin_nontemporal_store(a, d);
-  __builtin_nontemporal_store(b, d + 128);
+  __builtin_nontemporal_store(b, d + 64);
 }
 
 // (read row, write row) of every sequence for one decoded token on a CSR

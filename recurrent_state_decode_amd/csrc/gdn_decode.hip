@@ -755,17 +755,17 @@ int64_t gdn_fp8_tile_bytes(int32_t K, int32_t V, int32_t block_v) {
 int gdn_stream_rows(const float* src_pool, float* dst_pool, const int64_t* slots, int32_t n, int64_t row_floats,
                     void* stream) {
   if (!src_pool || !dst_pool || (n > 0 && !slots)) return fail(GDN_ERR_INVALID, "a required pointer is NULL");
-  if (n < 0 || row_floats <= 0 || row_floats % 1024 != 0)
-    return fail(GDN_ERR_INVALID, "n must be >= 0 and row_floats a positive multiple of 1024 (n=%d row_floats=%lld)", n,
+  if (n < 0 || row_floats <= 0 || row_floats % 512 != 0)
+    return fail(GDN_ERR_INVALID, "n must be >= 0 and row_floats a positive multiple of 512 (n=%d row_floats=%lld)", n,
                 (long long)row_floats);
   if (n == 0) {
     g_last_error.clear();
     return GDN_OK;
   }
-  const int64_t chunks = row_floats / 1024;
+  const int64_t chunks = row_floats / 512;
   const int64_t units = chunks * n;
   if (units > 0x7fffffffLL) return fail(GDN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)units);
-  hipLaunchKernelGGL(gdn::stream_rows_kernel, dim3(static_cast<uint32_t>(units)), dim3(128), 0,
+  hipLaunchKernelGGL(gdn::stream_rows_kernel, dim3(static_cast<uint32_t>(units)), dim3(64), 0,
                      static_cast<hipStream_t>(stream), src_pool, dst_pool, slots, row_floats,
                      static_cast<int32_t>(chunks), 6);
   const hipError_t err = hipGetLastError();

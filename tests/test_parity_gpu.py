@@ -423,6 +423,46 @@ def test_codec_decisions_exact_on_the_half_code_grid(layout):
     _report(f"codec_exact/{layout}", rep)
 
 
+@pytest.mark.parametrize("layout", ["K_FIRST", "V_FIRST"])
+def test_codec_tiny_groups_use_the_amax_floor(layout):
+    """A (key row, 32 values) group whose rotated amax is below 2^-100 is rounded as if its amax were
+    2^-100 (the kernel's floor, so that 127 / amax stays finite): with alpha = 1 and beta = 0 the stored
+    state is (rint(127 z / 2^-100) H) (2^-100 / 127) / 32 for z = x H, up to float32 rounding.  The groups
+    here have amax|z| = 127 2^-107, so the floored codes are 128 times coarser than the unfloored ones
+    and the two models differ by far more than the tolerance; an all-zero group stays zero."""
+    from oracle import hadamard as ohad
+    B, HV, K, V = 2, 2, 128, 128
+    w = wl.gdn_pooled(B, 1, HV, K, V, lengths=[1] * B, num_slots=B, state_layout=layout, seed=53,
+                      io_dtype=torch.float32, qdq="int8_hadamard32", block_v=64)
+    w.inputs["a"] = torch.full((B, HV), -float("inf"))     # alpha = 1
+    w.inputs["b"] = torch.zeros((B, HV))                   # beta = b = 0 (probability mode)
+    w.options["beta_mode"] = "probability"
+    rng = np.random.default_rng(54)
+    Hm = ohad.hadamard_matrix()
+    G = V // 32
+    k = -107.0
+    z = (rng.integers(-126, 127, (B, HV, K, G, 32)) + rng.choice([0.0, 0.5, -0.25], (B, HV, K, G, 32))) * 2.0 ** k
+    z[..., 0] = 127 * 2.0 ** k                            # amax|z| = 127 2^-107 in every group
+    z[1, 0, 7, 2, :] = 0.0                                # one all-zero group
+    x = (z @ Hm) / 32
+    assert np.array_equal(x.astype(np.float32).astype(np.float64), x)          # exact float32 inputs
+    floor = 2.0 ** -100
+    expect = (np.rint(127 * z / floor) @ Hm) * (floor / 127) / 32             # floored rounding
+    unfloored = (np.rint(127 * z / (127 * 2.0 ** k)) @ Hm) * 2.0 ** k / 32    # the same rule without it
+    expect, unfloored = expect.reshape(B, HV, K, V), unfloored.reshape(B, HV, K, V)
+    tiles = x.reshape(B, HV, K, V)
+    tiles = tiles if layout == "K_FIRST" else np.swapaxes(tiles, -1, -2)
+    pool = torch.from_numpy(np.ascontiguousarray(tiles).astype(np.float32)).cuda()
+    P.gpu_call(w, pool, P.device_inputs(w))
+    torch.cuda.synchronize()
+    got = pool.cpu().numpy().astype(np.float64)
+    got = got if layout == "K_FIRST" else np.swapaxes(got, -1, -2)
+    tol = 1e-5 * np.abs(expect).max()
+    assert np.abs(got - expect).max() <= tol, np.abs(got - expect).max() / tol
+    assert np.abs(unfloored - expect).max() > 100 * tol
+    assert not got[1, 0, 7, 64:96].any()
+
+
 @pytest.mark.parametrize("layout", ["V_FIRST", "K_FIRST"])
 @pytest.mark.parametrize("kind", ["gdn", "kda"])
 def test_codec_paged_varlen(layout, kind):
