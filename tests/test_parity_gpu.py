@@ -568,6 +568,23 @@ def test_kda_prefill_strong_decay():
     _report("kda_prefill_strong_decay", rep)
 
 
+@pytest.mark.parametrize("qdq", [None, "fp8_e4m3_tile", "int8_hadamard32"])
+@pytest.mark.parametrize("layout", ["K_FIRST", "V_FIRST"])
+def test_kda_decode_strong_decay(qdq, layout):
+    """Half of the key channels decay by about exp(-190) per token (far below float32's range, so those
+    rows of the registers underflow to zero within a token) while the other half decay normally: the
+    per-channel decay acts on the state's key rows directly, with no per-row scale to overflow."""
+    extra = dict(qdq=qdq, block_v=64) if qdq else {}
+    w = wl.kda_pooled(6, 2, 4, 128, 128, lengths=[4, 1, 9, 2, 3, 12], num_slots=8, state_layout=layout,
+                      io_dtype=torch.float32, out_dtype=torch.float32, seed=70, **extra)
+    g = w.inputs["raw_gate"].clone()
+    g[..., :64] = 12.0                                  # softplus ~ 12, times exp(a_log) = 16
+    w.inputs["raw_gate"] = g
+    w.inputs["a_log"] = torch.full_like(w.inputs["a_log"], float(np.log(16.0)))
+    rep, _, _ = P.run_and_check(w)
+    _report(f"kda_decode_strong_decay/{qdq}/{layout}", rep)
+
+
 # ---------------------------------------------------------------- packed int8_hadamard32 pools (codes + scales)
 
 CODEC = dict(qdq="int8_hadamard32", block_v=64)
