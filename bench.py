@@ -67,7 +67,7 @@ def algorithmic_bytes(w, storage="f32"):
     """State read+write for every (sequence, head) with a non-empty suffix, plus per-token I/O.
 
     A packed int8_hadamard32 pool moves K V code bytes and K V / 32 float32 scales per tile, a packed
-    fp8 pool K V code bytes and V / block_v float32 scales (padded to 16 bytes), instead of K V float32
+    fp8 pool K V code bytes and V / block_v float32 scales (the tile padded to whole 128-byte lines), instead of K V float32
     states."""
     import numpy as np
     import torch
@@ -80,7 +80,7 @@ def algorithmic_bytes(w, storage="f32"):
     if storage == "i8h32":
         tile = w.K * w.V + 4 * w.K * (w.V // 32)
     elif storage == "fp8":
-        tile = w.K * w.V + 16 * ((4 * (w.V // w.options.get("block_v", 64)) + 15) // 16)
+        tile = 128 * ((w.K * w.V + 4 * (w.V // w.options.get("block_v", 64)) + 127) // 128)
     else:
         tile = w.K * w.V * 4
     state = 2 * active * w.HV * tile

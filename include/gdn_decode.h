@@ -139,7 +139,8 @@ enum gdn_readout { GDN_READOUT_WORKING = 0, GDN_READOUT_STORED = 1 };
  * gdn_fp8_tile_bytes(K, V, block_v) bytes: the K V OCP E4M3 bytes in the
  * pool's state_layout order (K_FIRST [K][V], V_FIRST [V][K]), then the
  * V / block_v float32 tile scales amax/448 (scale 0 for an all-zero tile),
- * zero-padded to a multiple of 16 bytes; element x = e4m3(byte) * scale of
+ * the tile zero-padded to whole 128-byte lines (so that no two tiles share
+ * a cache line); element x = e4m3(byte) * scale of
  * its [K, block_v] tile.  Requires qdq = GDN_QDQ_FP8_E4M3_TILE (else
  * GDN_ERR_INVALID); results equal those of GDN_STORAGE_F32 with the fp8
  * tiles up to float32 rounding, with about 4x fewer pool bytes. */
@@ -388,7 +389,7 @@ int gdn_checked_build(void);
 int64_t gdn_packed_tile_bytes(int32_t K, int32_t V);
 
 /* Bytes of one (row, value head) tile of a GDN_STORAGE_FP8_TILE pool:
- * K V + 4 (V / block_v) rounded up to a multiple of 16; -1 if block_v does
+ * K V + 4 (V / block_v) rounded up to a multiple of 128; -1 if block_v does
  * not divide V or a size is not positive. */
 int64_t gdn_fp8_tile_bytes(int32_t K, int32_t V, int32_t block_v);
 

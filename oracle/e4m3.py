@@ -188,8 +188,9 @@ def tile_decode(codes, scales, block_v=64):
 
 
 def fp8_tile_bytes(K, V, block_v=64):
-    """Bytes of one packed (row, head) tile: K V codes, then V / block_v float32 scales padded to 16 bytes."""
-    return K * V + 16 * ((4 * (V // block_v) + 15) // 16)
+    """Bytes of one packed (row, head) tile: K V codes, then V / block_v float32 scales, the tile zero-padded to
+    whole 128-byte lines."""
+    return 128 * ((K * V + 4 * (V // block_v) + 127) // 128)
 
 
 def pack_fp8_tiles(codes, scales, state_layout="K_FIRST", block_v=64):

@@ -443,7 +443,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   constexpr bool HAD = QDQ == kQdqHad || PACKED;
   // FP8P: each (row, head) tile of the pool is its K V e4m3 bytes in the pool
   // layout's order, then its V / VB float32 tile scales (amax / 448; VB is
-  // the fp8 tile width) padded to 16 bytes.  The registers of the fp8 path
+  // the fp8 tile width), the tile rounded up to whole 128-byte lines.  The registers of the fp8 path
   // hold grid values with the tile scale in cs, so bytes load and store as
   // they are.
   constexpr bool FP8P = QDQ == kQdqTilePacked;
@@ -668,7 +668,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
 
   const int64_t tile_elems = static_cast<int64_t>(K) * p.V;
   const int64_t tile_bytes = PACKED ? static_cast<int64_t>(K) * p.V + 4 * static_cast<int64_t>(K) * (p.V / 32)
-                                     : static_cast<int64_t>(K) * p.V + 16 * ((4 * p.nvb + 15) / 16);
+                                     : 128 * ((static_cast<int64_t>(K) * p.V + 4 * p.nvb + 127) / 128);
   auto tile_base = [&](int64_t row) -> float* {
     if constexpr (PACKED || FP8P)
       return reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(p.pool) + (row * p.HV + h) * tile_bytes);

@@ -749,7 +749,7 @@ int64_t gdn_packed_tile_bytes(int32_t K, int32_t V) {
 
 int64_t gdn_fp8_tile_bytes(int32_t K, int32_t V, int32_t block_v) {
   if (K <= 0 || V <= 0 || block_v <= 0 || V % block_v != 0) return -1;
-  return static_cast<int64_t>(K) * V + 16 * ((4 * static_cast<int64_t>(V / block_v) + 15) / 16);
+  return 128 * ((static_cast<int64_t>(K) * V + 4 * static_cast<int64_t>(V / block_v) + 127) / 128);
 }
 
 int gdn_stream_rows(const float* src_pool, float* dst_pool, const int64_t* slots, int32_t n, int64_t row_floats,

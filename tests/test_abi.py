@@ -121,10 +121,10 @@ def test_packed_storage_argument_errors():
 def test_fp8_tile_bytes():
     from oracle import e4m3
     lib = rsd.load_library()
-    assert rsd.fp8_tile_bytes(128, 128) == 128 * 128 + 16 == 16400               # two scales, padded to 16
+    assert rsd.fp8_tile_bytes(128, 128) == 128 * 128 + 128 == 16512              # two scales, padded to a line
     for K, V, bv in ((128, 128, 64), (128, 256, 64), (16, 48, 16), (128, 64, 64), (16, 320, 16)):
         assert lib.gdn_fp8_tile_bytes(K, V, bv) == e4m3.fp8_tile_bytes(K, V, bv)
-        assert lib.gdn_fp8_tile_bytes(K, V, bv) % 16 == 0
+        assert lib.gdn_fp8_tile_bytes(K, V, bv) % 128 == 0
     assert lib.gdn_fp8_tile_bytes(128, 100, 64) == -1
     assert lib.gdn_fp8_tile_bytes(128, 128, 0) == -1
     with pytest.raises(ValueError):

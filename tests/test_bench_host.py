@@ -20,7 +20,7 @@ def test_headline_algorithmic_bytes():
 def test_packed_algorithmic_bytes():
     w = wl.paged_gdn_b256()
     w.options.update(qdq="fp8_e4m3_tile", block_v=64)
-    assert bench.algorithmic_bytes(w, "fp8")[0] == 2 * 256 * 32 * (128 * 128 + 16)
+    assert bench.algorithmic_bytes(w, "fp8")[0] == 2 * 256 * 32 * (128 * 128 + 128)
     w.options.update(qdq="int8_hadamard32")
     assert bench.algorithmic_bytes(w, "i8h32")[0] == 2 * 256 * 32 * (128 * 128 + 4 * 128 * 4)
 

@@ -176,7 +176,7 @@ def test_fp8_pack_layout_and_round_trip(layout):
     codes = rng.integers(0, 256, (2, 3, K, V)).astype(np.uint8)
     scales = rng.uniform(0, 1, (2, 3, 2))
     t = e4m3.pack_fp8_tiles(codes, scales, layout)
-    assert t.shape == (2, 3, e4m3.fp8_tile_bytes(K, V)) == (2, 3, K * V + 16)
+    assert t.shape == (2, 3, e4m3.fp8_tile_bytes(K, V)) == (2, 3, K * V + 128)   # whole 128-byte lines
     # element (k, v) at byte k V + v (K_FIRST) or v K + k (V_FIRST); then the float32 scales; zero padding
     k, v = 3, 77
     pos = k * V + v if layout == "K_FIRST" else v * K + k
