@@ -196,3 +196,20 @@ def test_prefill_argument_errors():
     assert kcall(page_size=24) == bnd.GDN_ERR_UNSUPPORTED
     assert kcall(V=64) == bnd.GDN_ERR_UNSUPPORTED
     assert kcall(opt=bnd._options(index_dtype=bnd.GDN_I64, gate_mode=1)) == bnd.GDN_ERR_UNSUPPORTED
+
+
+@no_gpu
+def test_stream_rows_argument_errors():
+    lib = rsd.load_library()
+    assert lib.gdn_stream_rows(None, FAKE, FAKE, 1, 512, None) == bnd.GDN_ERR_INVALID
+    assert lib.gdn_stream_rows(FAKE, None, FAKE, 1, 512, None) == bnd.GDN_ERR_INVALID
+    assert lib.gdn_stream_rows(FAKE, FAKE, None, 1, 512, None) == bnd.GDN_ERR_INVALID
+    assert lib.gdn_stream_rows(FAKE, FAKE, FAKE, -1, 512, None) == bnd.GDN_ERR_INVALID
+    assert lib.gdn_stream_rows(FAKE, FAKE, FAKE, 1, 0, None) == bnd.GDN_ERR_INVALID
+    assert lib.gdn_stream_rows(FAKE, FAKE, FAKE, 1, 768, None) == bnd.GDN_ERR_INVALID
+    assert "multiple of 512" in lib.gdn_last_error().decode()
+    # no pairs: nothing to launch, no slots needed
+    assert lib.gdn_stream_rows(FAKE, FAKE, None, 0, 512, None) == bnd.GDN_OK
+    # more than 2^31 - 1 workgroups (one per 512 floats of every pair) is refused before any launch
+    assert lib.gdn_stream_rows(FAKE, FAKE, FAKE, 1 << 30, 512 * 4, None) == bnd.GDN_ERR_UNSUPPORTED
+    assert "too large" in lib.gdn_last_error().decode()
