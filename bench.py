@@ -363,15 +363,24 @@ _CPU = {}
 
 COUNTERS = ("VALUBusy", "VALUUtilization", "OccupancyPercent", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
             "SQ_WAVES")
+# the matrix-core set, for the kernels that run MFMA (the chunked prefill): cycles the MFMA pipe of each
+# SIMD is busy, MFMA instructions issued, and the same clock and wave counts
+COUNTERS_MFMA = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_WAVES",
+                 "GRBM_GUI_ACTIVE")
+SIMDS = 1024        # 256 CUs x 4 SIMDs
+XCDS = 8
 
 
-def summarize_counters(run_dir, command):
+def summarize_counters(run_dir, sel):
     """profiles/counters_<workload>.txt from one rocprofv3 run with --pmc COUNTERS and --kernel-trace.
 
     Per dispatch of the kernel the bench times (medians over its dispatches): VALUBusy (percent of the
     active time some VALU instruction issues), VALUUtilization (active lanes), OccupancyPercent (resident
     waves against 32 per CU), VALU and LDS instructions per wave, and the shader clock the kernel ran at,
-    GRBM_GUI_ACTIVE cycles over the dispatch's duration."""
+    GRBM_GUI_ACTIVE cycles over the dispatch's duration.  A run with --pmc COUNTERS_MFMA instead writes
+    profiles/counters_mfma_<workload>.txt: MFMA instructions per wave, the cycles the matrix pipe is
+    busy per instruction, and the fraction of the kernel's cycles each SIMD's pipe is busy
+    (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE / XCDS cycles x SIMDS)."""
     import csv
     import statistics
 
@@ -394,18 +403,31 @@ def summarize_counters(run_dir, command):
     med = {k: statistics.median(v.values()) for k, v in per.items()}
     waves = med.get("SQ_WAVES", 0) or 1
     clocks = [per["GRBM_GUI_ACTIVE"][d] / dur[d] for d in per.get("GRBM_GUI_ACTIVE", {}) if d in dur and dur[d] > 0]
-    lines = [f"# rocprofv3 activity counters: {name}", "", "Command (from the repository root):", "",
-             "    " + command, "",
-             f"kernel: {kern}", f"source_hash: {bench_line['roofline']['source_hash']}",
-             f"dispatches: {len(dur)}; kernel duration median {statistics.median(dur.values()):.1f} us" if dur else
-             "dispatches: 0",
-             *(f"{k}: {v}" for k, v in meta.items()),
-             *(f"{k} (median per dispatch): {med[k]:.4g}" for k in COUNTERS if k in med),
-             f"VALU instructions per wave: {med.get('SQ_INSTS_VALU', 0) / waves:.1f}",
-             f"LDS instructions per wave: {med.get('SQ_INSTS_LDS', 0) / waves:.1f}",
-             f"GRBM_GUI_ACTIVE per us of the dispatch (median): {statistics.median(clocks):.0f}" if clocks else
-             "GRBM_GUI_ACTIVE per us: n/a"]
-    path = os.path.join(ROOT, "profiles", f"counters_{name}.txt")
+    mfma = "SQ_VALU_MFMA_BUSY_CYCLES" in med
+    command = (f"rocprofv3 --pmc {' '.join(COUNTERS_MFMA if mfma else COUNTERS)} --kernel-trace -d {run_dir} -o c "
+               f"--output-format csv -- python3 bench.py{sel} --steps 10 --warmup 1 --no-cpu-baseline > {run_dir}.json")
+    head = [f"# rocprofv3 {'matrix-core' if mfma else 'activity'} counters: {name}", "",
+            "Command (from the repository root):", "", "    " + command, "",
+            f"kernel: {kern}", f"source_hash: {bench_line['roofline']['source_hash']}",
+            f"dispatches: {len(dur)}; kernel duration median {statistics.median(dur.values()):.1f} us" if dur else
+            "dispatches: 0",
+            *(f"{k}: {v}" for k, v in meta.items()),
+            *(f"{k} (median per dispatch): {med[k]:.4g}" for k in (COUNTERS_MFMA if mfma else COUNTERS) if k in med)]
+    clock_line = (f"GRBM_GUI_ACTIVE per us of the dispatch (median): {statistics.median(clocks):.0f}" if clocks else
+                  "GRBM_GUI_ACTIVE per us: n/a")
+    if mfma:
+        n_mfma = med.get("SQ_INSTS_MFMA", 0)
+        busy = med["SQ_VALU_MFMA_BUSY_CYCLES"]
+        cycles = med.get("GRBM_GUI_ACTIVE", 0) / XCDS
+        lines = head + [f"MFMA instructions per wave: {n_mfma / waves:.1f}",
+                        f"MFMA pipe busy cycles per MFMA instruction: {busy / n_mfma:.2f}" if n_mfma else
+                        "MFMA pipe busy cycles per MFMA instruction: n/a",
+                        f"MFMA pipe busy fraction per SIMD: {busy / (cycles * SIMDS):.3f}" if cycles else
+                        "MFMA pipe busy fraction per SIMD: n/a", clock_line]
+    else:
+        lines = head + [f"VALU instructions per wave: {med.get('SQ_INSTS_VALU', 0) / waves:.1f}",
+                        f"LDS instructions per wave: {med.get('SQ_INSTS_LDS', 0) / waves:.1f}", clock_line]
+    path = os.path.join(ROOT, "profiles", f"counters_{'mfma_' if mfma else ''}{name}.txt")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -498,8 +520,8 @@ def main():
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 output directories (no GPU needed)")
     ap.add_argument("--summarize-counters", metavar="RUN_DIR",
-                    help="write profiles/counters_<workload>.txt from a rocprofv3 --pmc run of COUNTERS with "
-                         "--kernel-trace (no GPU needed)")
+                    help="write profiles/counters_<workload>.txt (or counters_mfma_<workload>.txt) from a "
+                         "rocprofv3 --pmc run of COUNTERS (or COUNTERS_MFMA) with --kernel-trace (no GPU needed)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a plain 1 GiB -> 1 GiB copy 3 times (a kernel of known traffic for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -527,9 +549,7 @@ def main():
         sel += f" --qdq {args.qdq}" if args.qdq else ""
         sel += " --token-path" if args.token_path else ""
         sel += f" --storage {args.storage}" if args.storage != "f32" else ""
-        d = args.summarize_counters
-        summarize_counters(d, f"rocprofv3 --pmc {' '.join(COUNTERS)} --kernel-trace -d {d} -o c --output-format csv "
-                              f"-- python3 bench.py{sel} --steps 10 --warmup 1 --no-cpu-baseline > {d}.json")
+        summarize_counters(args.summarize_counters, sel)
         return
 
     if args.gpus != 1:

@@ -82,3 +82,50 @@ def test_clock_sampler_reads_the_marked_level(tmp_path):
         time.sleep(0.02)
     s = c.summary()["sclk_mhz"]
     assert s["min"] == s["max"] == 2103 and s["samples"] >= 2
+
+
+def _counter_run(tmp_path, counters, workload="paged_gdn_prefill_b16_t1024_hv32_k128_ps16"):
+    """A fake rocprofv3 counter run directory: two dispatches of the timed kernel and one of another."""
+    import json
+    d = tmp_path / "run"
+    d.mkdir()
+    kern = "gdn::prefill_kernel<2, 4, false, true, gdn::bf16_t>(gdn::PrefillParams)"
+    with open(str(d) + ".json", "w") as f:
+        f.write(json.dumps({"config": {"workload": workload},
+                            "roofline": {"kernel": "gdn::prefill_kernel", "source_hash": "abc"}}) + "\n")
+    with open(d / "c_kernel_trace.csv", "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        f.write(f'1,"{kern}",1000,901000\n2,"{kern}",2000000,2900000\n3,"other",0,10\n')
+    with open(d / "c_counter_collection.csv", "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for did in (1, 2):
+            for name, val in counters.items():
+                f.write(f'{did},"{kern}",{name},{val}\n')
+        f.write('3,"other",SQ_WAVES,5\n')
+    return str(d)
+
+
+def test_counter_summaries(tmp_path, monkeypatch):
+    """The matrix-core summary: busy cycles per MFMA instruction and the busy fraction per SIMD from the
+    clock counter (GRBM_GUI_ACTIVE sums the 8 XCDs); the activity summary keeps its own file name."""
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    cycles = 2_000_000                                   # per XCD
+    run = _counter_run(tmp_path, {"SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * cycles * bench.SIMDS, "SQ_INSTS_MFMA": 32000,
+                                  "SQ_INSTS_VALU_MFMA_MOPS_F32": 1, "SQ_WAVES": 2048,
+                                  "GRBM_GUI_ACTIVE": cycles * bench.XCDS})
+    bench.summarize_counters(run, " --workload paged_gdn_prefill_b16_t1024")
+    text = (tmp_path / "profiles" / "counters_mfma_paged_gdn_prefill_b16_t1024_hv32_k128_ps16.txt").read_text()
+    assert "MFMA instructions per wave: 15.6" in text
+    assert f"MFMA pipe busy cycles per MFMA instruction: {0.5 * cycles * bench.SIMDS / 32000:.2f}" in text
+    assert "MFMA pipe busy fraction per SIMD: 0.500" in text
+    assert "dispatches: 2; kernel duration median 900.0 us" in text
+    assert "--pmc " + " ".join(bench.COUNTERS_MFMA) in text
+
+    import shutil
+    shutil.rmtree(run)
+    run = _counter_run(tmp_path, {"VALUBusy": 40, "SQ_INSTS_VALU": 4096, "SQ_WAVES": 2048,
+                                  "GRBM_GUI_ACTIVE": cycles * bench.XCDS})
+    bench.summarize_counters(run, "")
+    text = (tmp_path / "profiles" / "counters_paged_gdn_prefill_b16_t1024_hv32_k128_ps16.txt").read_text()
+    assert "VALU instructions per wave: 2.0" in text and "--pmc " + " ".join(bench.COUNTERS) in text
