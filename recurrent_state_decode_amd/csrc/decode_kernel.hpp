@@ -150,6 +150,9 @@ __device__ __forceinline__ void load_raw_n(const TIn* p, int64_t i, Raw<TIn, N>&
     const uint2 v = *reinterpret_cast<const uint2*>(p + i);
     r.w[0] = v.x;
     r.w[1] = v.y;
+  } else if constexpr (sizeof(TIn) == 2 && N == 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p + i);
+    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
   } else if constexpr (sizeof(TIn) == 4 && N == 1) {
     r.w[0] = reinterpret_cast<const uint32_t*>(p)[i];
   } else if constexpr (sizeof(TIn) == 4 && N == 2) {

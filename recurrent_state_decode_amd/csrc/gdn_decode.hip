@@ -8,6 +8,7 @@
 // validates them (host_checks.hpp) before it launches anything.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -616,10 +617,25 @@ int prefill_call(bool kda, const void* q, const void* k, const void* v, const vo
   if (units > 0x7fffffffLL) return fail(GDN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)units);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(static_cast<uint32_t>(units)), block(NW * 64);
+  // prefill_ws_kernel: one workgroup per (sequence, pair of value heads,
+  // V-block); the units of one key head's pairs stay on one XCD
+  gdn::PrefillParams pw = p;
+  constexpr int NH = gdn::kWsHeads;
+  const int64_t units_ws = static_cast<int64_t>(B) * ((HV + NH - 1) / NH) * p.nvb;
+  if (units_ws > 0x7fffffffLL) return fail(GDN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)units_ws);
+  pw.xcd_shift = 0;
+  while ((1 << pw.xcd_shift) < std::max(1, p.gqa / NH) * p.nvb && pw.xcd_shift < 6) ++pw.xcd_shift;
+  const dim3 grid_ws(static_cast<uint32_t>(units_ws));
   auto go = [&](auto kda_c, auto vf_c, auto io_c) {
     constexpr bool KDA = decltype(kda_c)::value, VF = decltype(vf_c)::value;
     using TIn = typename decltype(io_c)::type;
-    hipLaunchKernelGGL((gdn::prefill_kernel<VT, NW, KDA, VF, TIn>), grid, block, 0, s, p);
+    // GDN with 16-bit inputs: prefill_ws_kernel (producer and consumer waves,
+    // two value heads per workgroup); KDA, whose A' and P are formed pair by
+    // pair on the VALU, and 32-bit inputs keep the four-wave kernel
+    if constexpr (KDA || sizeof(TIn) != 2)
+      hipLaunchKernelGGL((gdn::prefill_kernel<VT, NW, KDA, VF, TIn>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((gdn::prefill_ws_kernel<VF, TIn>), grid_ws, dim3(gdn::kWsHeads * 6 * 64), 0, s, pw);
   };
   using F = std::false_type;
   using Tr = std::true_type;

@@ -502,4 +502,500 @@ void prefill_kernel(const PrefillParams p) {
   store_state(wrow);
 }
 
+// Warp-specialised GDN prefill (same math and result as prefill_kernel).
+// A workgroup takes one sequence, one 128-column V-block and two value heads
+// (2 hp and 2 hp + 1): twelve waves, six per head.  Of a head's six, four
+// consumer waves keep S in MFMA accumulators and do only the products that
+// involve S -- K S0 and Q S0, U = T diag(beta) (V - diag(exp G) K S0),
+// O = diag(exp G) Q S0 + P U, the S update and the stores -- while two
+// producer waves prepare the next chunk: one normalises and gates q and k,
+// forms A' and P on MFMA and solves for T in registers, the other stages v.
+// They leave q_hat, k_hat, v, g, T diag(beta) and P in the LDS buffer of
+// that chunk's parity.  Nothing the producers do depends on S, so a chunk's
+// serial path is its products with S, and one barrier per chunk hands the
+// buffers over (the consumers of chunk j read buffer j & 1 while the
+// producers write buffer (j + 1) & 1).  The producers keep later chunks'
+// raw inputs in flight across that barrier; they issue no global stores,
+// so waiting for those loads never waits for a store.
+// Two heads per workgroup because one workgroup per CU is what fits: at
+// three waves per SIMD (168 registers), twelve waves of one workgroup sit
+// three to a SIMD, while two six-wave workgroups need a placement the
+// dispatcher does not find (measured: one resident per CU).  Both heads
+// have the same sequence, so the same chunks and the same barriers; a head
+// index past HV (odd HV) only joins the barriers.
+constexpr int kWsHeads = 2;   // value heads per workgroup of prefill_ws_kernel
+
+template <bool VF, typename TIn>
+__global__ __launch_bounds__(kWsHeads * 384) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void prefill_ws_kernel(const PrefillParams p) {
+  constexpr int K = 128, C = kChunk, VT = 2, VBLK = 128;
+  constexpr int LDK = K + 4;       // padded LDS rows
+  constexpr int LDC = C + 1;
+  constexpr int PW = 4;            // the first producer wave (waves 4 and 5)
+  constexpr int NH = kWsHeads;
+  // (16-bit inputs only: 32-bit ones double the producers' raw registers,
+  // which then spill inside the chunk loop; those calls take prefill_kernel)
+  static_assert(sizeof(TIn) == 2, "prefill_ws_kernel takes 16-bit inputs");
+
+  // per head of the pair, then per chunk parity
+  __shared__ __align__(16) float s_q2[NH][2][C][LDK];   // q_hat (scaled)
+  __shared__ __align__(16) float s_k2[NH][3][C][LDK];   // by chunk % 3 (see the consumers)   // k_hat
+  __shared__ __align__(16) float s_v2[NH][2][C][LDK];   // v of this V-block
+  __shared__ float s_g2[NH][2][C];                      // g = log alpha per slot
+  __shared__ float s_tb2[NH][2][C][LDC];                // T diag(beta)
+  __shared__ float s_p2[NH][2][C][LDC];                 // P (lower, diagonal included)
+  __shared__ __align__(16) float s_a2[NH][C][C + 4];    // q / k producer only: A' for its solve
+  __shared__ float s_bp2[NH][C];                        // q / k producer only: beta per slot
+
+  const TIn* __restrict__ gq = static_cast<const TIn*>(p.q);
+  const TIn* __restrict__ gk = static_cast<const TIn*>(p.k);
+  const TIn* __restrict__ gv = static_cast<const TIn*>(p.v);
+  const TIn* __restrict__ gg = static_cast<const TIn*>(p.gate);
+  const TIn* __restrict__ gb = static_cast<const TIn*>(p.beta);
+
+  const int tid = threadIdx.x;
+  const int half = tid / (6 * 64);  // head of the pair
+  const int w = (tid >> 6) - 6 * half;   // wave inside the head's six
+  const int lane = tid & 63;
+  const int n16 = lane & 15;       // MFMA row / column inside a tile
+  const int g4 = lane >> 4;        // MFMA k group
+
+  const int unit = xcd_unit(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x), p.xcd_shift);
+  const int q1 = unit / p.nvb;
+  const int vb = unit - q1 * p.nvb;
+  const int pairs = (p.HV + NH - 1) / NH;
+  const int bs = q1 / pairs;
+  const int h = NH * (q1 - bs * pairs) + half;
+  const bool head_ok = h < p.HV;
+  const int hk = min(h, p.HV - 1) / p.gqa;
+
+  float (&s_q)[2][C][LDK] = s_q2[half];
+  float (&s_k)[3][C][LDK] = s_k2[half];
+  float (&s_v)[2][C][LDK] = s_v2[half];
+  float (&s_g)[2][C] = s_g2[half];
+  float (&s_tb)[2][C][LDC] = s_tb2[half];
+  float (&s_p)[2][C][LDC] = s_p2[half];
+  float (&s_a)[C][C + 4] = s_a2[half];
+  float (&s_bp)[C] = s_bp2[half];
+
+  const int t0 = p.cu_seqlens[bs];
+  const int t1 = p.cu_seqlens[bs + 1];
+  if (t1 <= t0) return;            // empty suffix: no read, no write (uniform per workgroup)
+
+  const int64_t pg_start = load_index(p.page_indptr, bs, p.idx64);
+  const int64_t pg_end = load_index(p.page_indptr, bs + 1, p.idx64);
+  const int lpl = static_cast<int>(load_index(p.last_page_len, bs, p.idx64));
+  const int pos_last = static_cast<int>(pg_end - pg_start - 1) * p.page_size + lpl;
+  const int pos0 = pos_last - (t1 - t0) + 1;
+  const int jfirst = (pos0 - 1) / C;
+  const int jlast = (pos_last - 1) / C;
+  if (!head_ok) {                  // no second head (odd HV): the barriers only
+    for (int j = jfirst; j <= jlast; ++j) __syncthreads();
+    return;
+  }
+
+  // gate prefix of a chunk: inclusive scan of g over the 16 lanes of each
+  // row (row_shr:n with bound_ctrl, so the first n lanes add 0); Gc is G of
+  // slot n16, Gr[r] G of slot 4 g4 + r
+  auto gate_prefix = [&](int buf, float (&Gr)[4], float& Gc) {
+    Gc = s_g[buf][n16];
+    Gc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(Gc), 0x111, 0xF, 0xF, true));
+    Gc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(Gc), 0x112, 0xF, 0xF, true));
+    Gc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(Gc), 0x114, 0xF, 0xF, true));
+    Gc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(Gc), 0x118, 0xF, 0xF, true));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Gr[r] = __shfl(Gc, 4 * g4 + r);
+  };
+
+  if (w >= PW) {
+    // ================= producers =================
+    // Raw inputs of one chunk: wave 4 loads every slot's q and k pieces and
+    // slot (lane % 16)'s gate and beta, wave 5 every slot's v pieces.  Every
+    // load is issued, slots outside the suffix reading the suffix's nearest
+    // token (a valid row; staging turns such slots into identity tokens), so
+    // each chunk issues the same loads and the waits before staging count
+    // exactly.
+    // 16-byte pieces: a token's row of K elements spans LPT lanes, one load
+    // instruction covers TPI tokens (16-bit inputs: 16 lanes, 4 tokens), so a
+    // chunk is NI instructions per tensor -- few enough that two chunks in
+    // flight stay within what a wave's load counter holds (63; past it, issue
+    // stalls until older loads return)
+    constexpr int EW = 16 / static_cast<int>(sizeof(TIn));
+    constexpr int LPT = K / EW;
+    constexpr int TPI = 64 / LPT;
+    constexpr int NI = C / TPI;
+    constexpr int LB = __builtin_ctz(LPT);
+    static_assert(K % EW == 0 && 64 % LPT == 0 && C % TPI == 0 && VBLK == K, "piece layout");
+    const int tl = lane / LPT;       // this lane's token inside an instruction's TPI
+    const int el = lane % LPT;       // its piece of the row
+    struct RawQK {
+      Raw<TIn, EW> q[NI], k[NI];
+      Raw<TIn, 1> a, b;
+    };
+    struct RawV {
+      Raw<TIn, EW> v[NI];
+    };
+    auto in_suffix = [&](int pos) { return pos >= pos0 && pos <= pos_last; };
+    auto token_of = [&](int pos) -> int64_t { return t0 + min(max(pos - pos0, 0), t1 - t0 - 1); };
+    auto load_qk = [&](RawQK& R, int cpos) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int64_t tk = token_of(cpos + TPI * i + tl);
+        load_raw_n<EW>(gq, (tk * p.HK + hk) * K + EW * el, R.q[i]);
+        load_raw_n<EW>(gk, (tk * p.HK + hk) * K + EW * el, R.k[i]);
+      }
+      const int64_t tg = token_of(cpos + n16);
+      load_raw_n<1>(gg, tg * p.HV + h, R.a);
+      load_raw_n<1>(gb, tg * p.HV + h, R.b);
+    };
+    auto load_v = [&](RawV& R, int cpos) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        load_raw_n<EW>(gv, (token_of(cpos + TPI * i + tl) * p.HV + h) * p.V + vb * VBLK + EW * el, R.v[i]);
+    };
+    // EW floats to LDS row t at piece el (16-byte stores)
+    auto put = [&](float* row, const float (&x)[EW]) {
+#pragma unroll
+      for (int f = 0; f < EW / 4; ++f)
+        *reinterpret_cast<float4*>(row + EW * el + 4 * f) = make_float4(x[4 * f], x[4 * f + 1], x[4 * f + 2], x[4 * f + 3]);
+    };
+    auto stage_v = [&](const RawV& R, int cpos, int buf) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int t = TPI * i + tl;
+        const bool ok = in_suffix(cpos + t);
+        float xv[EW];
+        decode_raw(R.v[i], xv);
+#pragma unroll
+        for (int e = 0; e < EW; ++e) xv[e] = ok ? xv[e] : 0.0f;
+        put(&s_v[buf][t][0], xv);
+      }
+    };
+    // normalise, gate and stage q and k of a chunk (slots outside the
+    // suffix: identity tokens)
+    // the head's gate parameters, once, through the scalar cache: a vector
+    // load here, waited for inside the chunk loop, would also wait for the
+    // next chunks' input loads issued before it (the counter retires loads
+    // in order)
+    const float rate = exp_hw(((ConstF32)p.a_log)[h]);
+    const float dtb = ((ConstF32)p.dt_bias)[h];
+    auto stage_qk = [&](const RawQK& R, int cpos, int buf) {
+      const int kb = ((cpos - 1) / C) % 3;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int t = TPI * i + tl;
+        const bool ok = in_suffix(cpos + t);
+        float xq[EW], xk[EW];
+        decode_raw(R.q[i], xq);
+        decode_raw(R.k[i], xk);
+        float sq = 0.0f, sk = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EW; ++e) {
+          xq[e] = ok ? xq[e] : 0.0f;
+          xk[e] = ok ? xk[e] : 0.0f;
+          sq = fmaf(xq[e], xq[e], sq);
+          sk = fmaf(xk[e], xk[e], sk);
+        }
+        float iq = p.scale, ik = 1.0f;
+        if (p.l2norm) {              // sums over the LPT lanes of this token's row
+          iq = p.scale * rsqrtf(lane_reduce<0, LB>(sq) + kL2Eps);
+          ik = rsqrtf(lane_reduce<0, LB>(sk) + kL2Eps);
+        }
+#pragma unroll
+        for (int e = 0; e < EW; ++e) {
+          xq[e] *= iq;
+          xk[e] *= ik;
+        }
+        put(&s_q[buf][t][0], xq);
+        put(&s_k[kb][t][0], xk);
+      }
+      if (lane < C) {
+        float gt = 0.0f, bt = 0.0f;
+        if (in_suffix(cpos + lane)) {
+          float xa[1], xb[1];
+          decode_raw(R.a, xa);
+          decode_raw(R.b, xb);
+          gt = -rate * softplus_f(xa[0] + dtb);
+          bt = p.beta_prob ? xb[0] : sigmoid_f(xb[0]);
+        }
+        s_g[buf][lane] = gt;
+        s_bp[lane] = bt;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // the staged chunk is read by other lanes
+      __builtin_amdgcn_wave_barrier();
+    };
+    // A', P and T of the chunk staged in buf (k_hat in its chunk % 3 buffer)
+    auto prepare = [&](int cpos, int buf) {
+      const int kb = ((cpos - 1) / C) % 3;
+      float Gr[4], Gc;
+      gate_prefix(buf, Gr, Gc);
+      f32x4 accA = {0.0f, 0.0f, 0.0f, 0.0f}, accP = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c4 = 0; c4 < K / 4; ++c4) {
+        const float kk = s_k[kb][n16][4 * c4 + g4];
+        accA = mfma_16x16x4(kk, kk, accA);
+        accP = mfma_16x16x4(s_q[buf][n16][4 * c4 + g4], kk, accP);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 4 * g4 + r, s = n16;
+        const float d = exp_hw(fminf(Gr[r] - Gc, 0.0f));
+        s_a[t][s] = (s < t) ? s_bp[t] * d * accA[r] : 0.0f;
+        s_p[buf][t][s] = (s <= t) ? d * accP[r] : 0.0f;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // A' is read by every lane
+      __builtin_amdgcn_wave_barrier();
+      // row n16 of T = (I + A')^-1: from T (I + A') = I with A' strictly
+      // lower, T[i][s] = [i == s] - sum_{u > s} T[i][u] A'[u][s], taken from
+      // the last column back (row u of A' read as an LDS broadcast).  (row
+      // is n16 made opaque here: hoisted out of the chunk loop, the 16
+      // identity entries would be spilled to scratch, and each scratch
+      // reload waits for every vector load in flight.)
+      int row = n16;
+      asm volatile("" : "+v"(row));
+      float trow[C], acc[C];
+#pragma unroll
+      for (int s = 0; s < C; ++s) acc[s] = 0.0f;
+#pragma unroll
+      for (int u = C - 1; u >= 0; --u) {
+        trow[u] = ((u == row) ? 1.0f : 0.0f) - acc[u];
+#pragma unroll
+        for (int s = 0; s < u; ++s) acc[s] = fmaf(trow[u], s_a[u][s], acc[s]);
+      }
+      if (g4 == 0) {
+#pragma unroll
+        for (int s = 0; s < C; ++s) s_tb[buf][n16][s] = trow[s] * s_bp[s];
+      }
+    };
+
+    // The chunk loop of a producer: the same barriers as the consumers'
+    // loop, one per chunk; before barrier j the buffers of chunk j are
+    // complete.  Iteration j stages chunk j + 1 from the registers, issues
+    // chunk j + 2's loads into them, then (the q / k wave) forms A', P and T
+    // of chunk j + 1: the loads fly during that work, the barrier and the
+    // next iteration's start, and when staging waits for them nothing
+    // younger is in flight.
+    auto produce = [&](auto& R, auto load, auto stage, auto prep) {
+      const int c0 = jfirst * C + 1;
+      load(R, c0);
+      stage(R, c0, jfirst & 1);
+      load(R, c0 + C);
+      prep(c0, jfirst & 1);
+      for (int j = jfirst; j <= jlast; ++j) {
+        __syncthreads();           // chunk j's buffers complete; buffers (j + 1) & 1 free
+        if (j < jlast) {
+          stage(R, (j + 1) * C + 1, (j + 1) & 1);
+          load(R, (j + 2) * C + 1);
+          prep((j + 1) * C + 1, (j + 1) & 1);
+        }
+      }
+    };
+    if (w == PW) {
+      RawQK R;
+      produce(R, load_qk, stage_qk, prepare);
+    } else {
+      RawV R;
+      produce(R, load_v, stage_v, [](int, int) {});
+    }
+    return;
+  }
+
+  // ================= consumers =================
+  const int64_t rrow = load_index(p.page_indices, pg_start + max(pos0 - 2, 0) / p.page_size, p.idx64);
+  const int64_t wrow = load_index(p.page_indices, pg_end - 1, p.idx64);
+  const int64_t tile_elems = static_cast<int64_t>(K) * p.V;
+  const int vcol = vb * VBLK + 16 * VT * w;   // first value column of this wave
+  const int cpp = p.page_size / C;
+  int to_page_end = (cpp - 1) - jfirst % cpp;   // chunks until one ends a page
+  int64_t page_slot = pg_start + jfirst / cpp;  // table entry of that page
+
+  // S[ct][vt] element r = S[16 ct + 4 g4 + r][vcol + 16 vt + n16]
+  f32x4 S[8][VT];
+  const int lane_base = VF ? (vcol + n16) * K + 4 * g4 : 4 * g4 * p.V + vcol + n16;
+  auto state_off = [&](int ct, int vt, int r) -> int {
+    return VF ? lane_base + 16 * vt * K + 16 * ct + r : lane_base + (16 * ct + r) * p.V + 16 * vt;
+  };
+  {
+    const float* src = p.pool + (rrow * p.HV + h) * tile_elems;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) {
+        if constexpr (VF) {
+          S[ct][vt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + state_off(ct, vt, 0)));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float* rowp = src + static_cast<uint32_t>((16 * ct + r) * p.V + 16 * vt);
+            S[ct][vt][r] = __builtin_nontemporal_load(rowp + static_cast<uint32_t>(lane_base));
+          }
+        }
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);   // the state tile (see kWaitVmem0)
+  // key rows 16 ct .. 16 ct + 15 of this wave's columns of S to a pool row
+  auto store_rows = [&](int64_t row, int ct) {
+    float* dst = p.pool + (row * p.HV + h) * tile_elems;
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt) {
+      if constexpr (VF) {
+        *reinterpret_cast<f32x4*>(dst + state_off(ct, vt, 0)) = S[ct][vt];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float* rowp = dst + static_cast<uint32_t>((16 * ct + r) * p.V + 16 * vt);
+          rowp[static_cast<uint32_t>(lane_base)] = S[ct][vt][r];
+        }
+      }
+    }
+  };
+  auto store_state = [&](int64_t row) {
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) store_rows(row, ct);
+  };
+  // A page that a chunk fills receives the state after that chunk.  The
+  // registers keep that state until the next chunk's update, so the store
+  // is issued during the next chunk's K S0 / Q S0 products, 16 key rows
+  // between their matrix instructions, where it drains while they run
+  // instead of in one burst at the chunk's end.
+  bool store_pending = false;
+  int64_t pending_row = 0;
+
+  // ---- S_C = exp(G_C) S0 + sum_s exp(G_C - G_s) k_s u_s^T for chunk jj
+  auto update = [&](int jj, const f32x4 (&Uc)[VT], float eC, const float (&dk)[4]) {
+    const int kb = jj % 3;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      float ka[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ka[r] = dk[r] * s_k[kb][4 * g4 + r][16 * ct + n16];
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) {
+        f32x4 acc = S[ct][vt] * eC;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc = mfma_16x16x4(ka[r], Uc[vt][r], acc);
+        S[ct][vt] = acc;
+      }
+    }
+  };
+  // Head 1 of the pair runs its update one step later: the update of chunk
+  // j opens iteration j + 1, before that chunk's K S0 / Q S0.  On each SIMD
+  // the two heads' consumers then sit in different phases, so one's
+  // latency-bound U / O overlaps the other's matrix products instead of
+  // coinciding with them.  (k_hat is kept three chunks deep for this.)
+  const bool late = half == 1;
+  f32x4 Ul[VT];
+  float eCl = 0.0f, dkl[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  bool page_l = false;
+  int64_t row_l = 0;
+
+  for (int j = jfirst; j <= jlast; ++j) {
+    const int cpos = j * C + 1;              // position of slot 0
+    const bool page_end = to_page_end == 0 && cpos + C - 1 < pos_last;
+    const int64_t page_row = page_end ? load_index_uniform(p.page_indices, page_slot, p.idx64) : 0;
+    if (to_page_end == 0) {
+      to_page_end = cpp;
+      ++page_slot;
+    }
+    --to_page_end;
+    __syncthreads();                         // the producers have finished chunk j's buffers
+    if (late && j > jfirst) {
+      update(j - 1, Ul, eCl, dkl);
+      store_pending = page_l;                // that chunk's page, during this chunk's products
+      pending_row = row_l;
+    }
+    const int buf = j & 1;
+    const int kb = j % 3;
+    float Gr[4], Gc;
+    gate_prefix(buf, Gr, Gc);
+    const float GC = __shfl(Gc, C - 1);      // G of the last slot
+
+    // ---- KS = K S0 and QS = Q S0 for this wave's columns
+    f32x4 KS[VT], O[VT];
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt) {
+      KS[vt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      O[vt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      if (store_pending) store_rows(pending_row, ct);   // the previous chunk's page
+      const float4 kv = *reinterpret_cast<const float4*>(&s_k[kb][n16][16 * ct + 4 * g4]);
+      const float4 qv = *reinterpret_cast<const float4*>(&s_q[buf][n16][16 * ct + 4 * g4]);
+      const float kr[4] = {kv.x, kv.y, kv.z, kv.w};
+      const float qr[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          KS[vt] = mfma_16x16x4(kr[r], S[ct][vt][r], KS[vt]);
+          O[vt] = mfma_16x16x4(qr[r], S[ct][vt][r], O[vt]);
+        }
+    }
+    store_pending = false;
+
+    // ---- U = T diag(beta) (V - diag(exp G) K S0)
+    float eG[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) eG[r] = exp_hw(Gr[r]);
+    f32x4 U[VT];
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float R = s_v[buf][4 * g4 + r][16 * VT * w + 16 * vt + n16] - eG[r] * KS[vt][r];
+        acc = mfma_16x16x4(s_tb[buf][n16][4 * g4 + r], R, acc);
+      }
+      U[vt] = acc;
+    }
+
+    // ---- O = diag(exp G) Q S0 + P U
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) O[vt][r] *= eG[r];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float pa = s_p[buf][n16][4 * g4 + r];
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) O[vt] = mfma_16x16x4(pa, U[vt][r], O[vt]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pos = cpos + 4 * g4 + r;
+      if (pos >= pos0 && pos <= pos_last) {
+        const int64_t t = t0 + (pos - pos0);
+        const int64_t oi = (t * p.HV + h) * p.V + vcol + n16;
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt) {
+          if (p.out_bf16) static_cast<uint16_t*>(p.out)[oi + 16 * vt] = to_bf16_bits(O[vt][r]);
+          else static_cast<float*>(p.out)[oi + 16 * vt] = O[vt][r];
+        }
+      }
+    }
+
+    const float eC = exp_hw(GC);
+    float dk[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dk[r] = exp_hw(fminf(GC - Gr[r], 0.0f));
+    if (!late) {
+      update(j, U, eC, dk);
+      store_pending = page_end;              // stored during the next chunk (page_end implies that chunk exists)
+      pending_row = page_row;
+    } else {
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) Ul[vt] = U[vt];
+      eCl = eC;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dkl[r] = dk[r];
+      page_l = page_end;
+      row_l = page_row;
+    }
+  }
+  if (late) update(jlast, Ul, eCl, dkl);    // (the last chunk fills no page of the suffix's interior)
+
+  store_state(wrow);
+}
+
 }  // namespace gdn

@@ -1,8 +1,9 @@
 """Resource use of the compiled kernels (CPU only: hipcc cross-compiles for gfx950).
 
 No decode kernel may use scratch (private) memory: a per-token stack round trip is a memory
-wait on every token (it cost 4-11 % when a select chain was compiled that way).  The chunked
-prefill may spill a few registers outside its chunk loop but no more than 64 bytes.
+wait on every token (it cost 4-11 % when a select chain was compiled that way).  The four-wave
+chunked prefill may spill a few registers outside its chunk loop but no more than 64 bytes; the
+producer / consumer prefill uses none.
 """
 import os
 import re
@@ -44,6 +45,15 @@ def test_decode_kernels_use_no_scratch(kernel_sets):
 
 
 def test_prefill_spills_stay_small(kernel_sets):
+    # the four-wave kernel: KDA (both I/O types and layouts) and GDN with 32-bit inputs
     pre = {k: v for k, v in kernel_sets.items() if "prefill_kernel" in k}
-    assert len(pre) == 8, sorted(pre)
+    assert len(pre) == 6, sorted(pre)
     assert max(pre.values()) <= 64, pre
+
+
+def test_split_prefill_uses_no_scratch(kernel_sets):
+    """The producer / consumer GDN prefill (16-bit inputs, both layouts) keeps its chunk loop free of scratch: a
+    reload there would wait for the next chunks' input loads in flight (the counter retires loads in order)."""
+    ws = {k: v for k, v in kernel_sets.items() if "prefill_ws_kernel" in k}
+    assert len(ws) == 2, sorted(ws)
+    assert not any(ws.values()), ws
