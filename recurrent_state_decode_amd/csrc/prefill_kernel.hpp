@@ -541,11 +541,11 @@ void prefill_ws_kernel(const PrefillParams p) {
   __shared__ __align__(16) float s_q2[NH][2][C][LDK];   // q_hat (scaled)
   __shared__ __align__(16) float s_k2[NH][3][C][LDK];   // by chunk % 3 (see the consumers)   // k_hat
   __shared__ __align__(16) float s_v2[NH][2][C][LDK];   // v of this V-block
-  __shared__ float s_g2[NH][2][C];                      // g = log alpha per slot
+  __shared__ float s_g2[NH][3][C];                      // g = log alpha per slot, by chunk % 3
   __shared__ float s_tb2[NH][2][C][LDC];                // T diag(beta)
   __shared__ float s_p2[NH][2][C][LDC];                 // P (lower, diagonal included)
   __shared__ __align__(16) float s_a2[NH][C][C + 4];    // q / k producer only: A' for its solve
-  __shared__ float s_bp2[NH][C];                        // q / k producer only: beta per slot
+  __shared__ float s_bp2[NH][3][C];                     // beta per slot, by chunk % 3 (producers only)
 
   const TIn* __restrict__ gq = static_cast<const TIn*>(p.q);
   const TIn* __restrict__ gk = static_cast<const TIn*>(p.k);
@@ -572,11 +572,11 @@ void prefill_ws_kernel(const PrefillParams p) {
   float (&s_q)[2][C][LDK] = s_q2[half];
   float (&s_k)[3][C][LDK] = s_k2[half];
   float (&s_v)[2][C][LDK] = s_v2[half];
-  float (&s_g)[2][C] = s_g2[half];
+  float (&s_g)[3][C] = s_g2[half];
   float (&s_tb)[2][C][LDC] = s_tb2[half];
   float (&s_p)[2][C][LDC] = s_p2[half];
   float (&s_a)[C][C + 4] = s_a2[half];
-  float (&s_bp)[C] = s_bp2[half];
+  float (&s_bp)[3][C] = s_bp2[half];
 
   const int t0 = p.cu_seqlens[bs];
   const int t1 = p.cu_seqlens[bs + 1];
@@ -590,15 +590,15 @@ void prefill_ws_kernel(const PrefillParams p) {
   const int jfirst = (pos0 - 1) / C;
   const int jlast = (pos_last - 1) / C;
   if (!head_ok) {                  // no second head (odd HV): the barriers only
-    for (int j = jfirst; j <= jlast; ++j) __syncthreads();
+    for (int j = jfirst - 1; j <= jlast; ++j) __syncthreads();
     return;
   }
 
-  // gate prefix of a chunk: inclusive scan of g over the 16 lanes of each
+  // gate prefix of the chunk whose g is in buffer gbuf: inclusive scan of g over the 16 lanes of each
   // row (row_shr:n with bound_ctrl, so the first n lanes add 0); Gc is G of
   // slot n16, Gr[r] G of slot 4 g4 + r
-  auto gate_prefix = [&](int buf, float (&Gr)[4], float& Gc) {
-    Gc = s_g[buf][n16];
+  auto gate_prefix = [&](int gbuf, float (&Gr)[4], float& Gc) {
+    Gc = s_g[gbuf][n16];
     Gc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(Gc), 0x111, 0xF, 0xF, true));
     Gc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(Gc), 0x112, 0xF, 0xF, true));
     Gc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(Gc), 0x114, 0xF, 0xF, true));
@@ -609,17 +609,17 @@ void prefill_ws_kernel(const PrefillParams p) {
 
   if (w >= PW) {
     // ================= producers =================
-    // Raw inputs of one chunk: wave 4 loads every slot's q and k pieces and
-    // slot (lane % 16)'s gate and beta, wave 5 every slot's v pieces.  Every
-    // load is issued, slots outside the suffix reading the suffix's nearest
-    // token (a valid row; staging turns such slots into identity tokens), so
-    // each chunk issues the same loads and the waits before staging count
-    // exactly.
+    // Raw inputs: the q / k wave (4) loads every slot's q and k pieces of a
+    // chunk; the v wave (5) every slot's v pieces of a chunk and slot (lane
+    // % 16)'s gate and beta of the chunk after it, and stages those one chunk
+    // earlier than the q / k wave needs them (g and beta are kept three
+    // chunks deep).  Every load is issued, slots outside the suffix reading
+    // the suffix's nearest token (a valid row; staging turns such slots into
+    // identity tokens), so each chunk issues the same loads and the waits
+    // before staging count exactly.
     // 16-byte pieces: a token's row of K elements spans LPT lanes, one load
-    // instruction covers TPI tokens (16-bit inputs: 16 lanes, 4 tokens), so a
-    // chunk is NI instructions per tensor -- few enough that two chunks in
-    // flight stay within what a wave's load counter holds (63; past it, issue
-    // stalls until older loads return)
+    // instruction covers TPI tokens (16 lanes, 4 tokens), so a chunk is NI
+    // instructions per tensor.
     constexpr int EW = 16 / static_cast<int>(sizeof(TIn));
     constexpr int LPT = K / EW;
     constexpr int TPI = 64 / LPT;
@@ -630,28 +630,32 @@ void prefill_ws_kernel(const PrefillParams p) {
     const int el = lane % LPT;       // its piece of the row
     struct RawQK {
       Raw<TIn, EW> q[NI], k[NI];
-      Raw<TIn, 1> a, b;
     };
     struct RawV {
-      Raw<TIn, EW> v[NI];
+      Raw<TIn, EW> v[NI];            // chunk c
+      Raw<TIn, 1> a, b;              // chunk c + 1
     };
     auto in_suffix = [&](int pos) { return pos >= pos0 && pos <= pos_last; };
     auto token_of = [&](int pos) -> int64_t { return t0 + min(max(pos - pos0, 0), t1 - t0 - 1); };
-    auto load_qk = [&](RawQK& R, int cpos) {
+    auto cpos_of = [](int c) { return c * C + 1; };
+    auto load_qk = [&](RawQK& R, int c) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int64_t tk = token_of(cpos + TPI * i + tl);
+        const int64_t tk = token_of(cpos_of(c) + TPI * i + tl);
         load_raw_n<EW>(gq, (tk * p.HK + hk) * K + EW * el, R.q[i]);
         load_raw_n<EW>(gk, (tk * p.HK + hk) * K + EW * el, R.k[i]);
       }
-      const int64_t tg = token_of(cpos + n16);
-      load_raw_n<1>(gg, tg * p.HV + h, R.a);
-      load_raw_n<1>(gb, tg * p.HV + h, R.b);
     };
-    auto load_v = [&](RawV& R, int cpos) {
+    auto load_gb = [&](Raw<TIn, 1>& a, Raw<TIn, 1>& b, int c) {
+      const int64_t tg = token_of(cpos_of(c) + n16);
+      load_raw_n<1>(gg, tg * p.HV + h, a);
+      load_raw_n<1>(gb, tg * p.HV + h, b);
+    };
+    auto load_v = [&](RawV& R, int c) {
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        load_raw_n<EW>(gv, (token_of(cpos + TPI * i + tl) * p.HV + h) * p.V + vb * VBLK + EW * el, R.v[i]);
+        load_raw_n<EW>(gv, (token_of(cpos_of(c) + TPI * i + tl) * p.HV + h) * p.V + vb * VBLK + EW * el, R.v[i]);
+      load_gb(R.a, R.b, c + 1);
     };
     // EW floats to LDS row t at piece el (16-byte stores)
     auto put = [&](float* row, const float (&x)[EW]) {
@@ -659,32 +663,48 @@ void prefill_ws_kernel(const PrefillParams p) {
       for (int f = 0; f < EW / 4; ++f)
         *reinterpret_cast<float4*>(row + EW * el + 4 * f) = make_float4(x[4 * f], x[4 * f + 1], x[4 * f + 2], x[4 * f + 3]);
     };
-    auto stage_v = [&](const RawV& R, int cpos, int buf) {
+    // the head's gate parameters, once, through the scalar cache: a vector
+    // load here, waited for inside the chunk loop, would also wait for the
+    // later chunks' input loads issued before it (the counter retires loads
+    // in order)
+    const float rate = exp_hw(((ConstF32)p.a_log)[h]);
+    const float dtb = ((ConstF32)p.dt_bias)[h];
+    // gate and beta of chunk c (slots outside the suffix: g = 0, beta = 0)
+    auto stage_gb = [&](const Raw<TIn, 1>& a, const Raw<TIn, 1>& b, int c) {
+      if (lane < C) {
+        float gt = 0.0f, bt = 0.0f;
+        if (in_suffix(cpos_of(c) + lane)) {
+          float xa[1], xb[1];
+          decode_raw(a, xa);
+          decode_raw(b, xb);
+          gt = -rate * softplus_f(xa[0] + dtb);
+          bt = p.beta_prob ? xb[0] : sigmoid_f(xb[0]);
+        }
+        s_g[c % 3][lane] = gt;
+        s_bp[c % 3][lane] = bt;
+      }
+    };
+    // v of chunk c, gate and beta of chunk c + 1
+    auto stage_v = [&](const RawV& R, int c) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int t = TPI * i + tl;
-        const bool ok = in_suffix(cpos + t);
+        const bool ok = in_suffix(cpos_of(c) + t);
         float xv[EW];
         decode_raw(R.v[i], xv);
 #pragma unroll
         for (int e = 0; e < EW; ++e) xv[e] = ok ? xv[e] : 0.0f;
-        put(&s_v[buf][t][0], xv);
+        put(&s_v[c & 1][t][0], xv);
       }
+      stage_gb(R.a, R.b, c + 1);
     };
-    // normalise, gate and stage q and k of a chunk (slots outside the
-    // suffix: identity tokens)
-    // the head's gate parameters, once, through the scalar cache: a vector
-    // load here, waited for inside the chunk loop, would also wait for the
-    // next chunks' input loads issued before it (the counter retires loads
-    // in order)
-    const float rate = exp_hw(((ConstF32)p.a_log)[h]);
-    const float dtb = ((ConstF32)p.dt_bias)[h];
-    auto stage_qk = [&](const RawQK& R, int cpos, int buf) {
-      const int kb = ((cpos - 1) / C) % 3;
+    // normalise and stage q and k of chunk c (slots outside the suffix:
+    // identity tokens)
+    auto stage_qk = [&](const RawQK& R, int c) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int t = TPI * i + tl;
-        const bool ok = in_suffix(cpos + t);
+        const bool ok = in_suffix(cpos_of(c) + t);
         float xq[EW], xk[EW];
         decode_raw(R.q[i], xq);
         decode_raw(R.k[i], xk);
@@ -706,29 +726,18 @@ void prefill_ws_kernel(const PrefillParams p) {
           xq[e] *= iq;
           xk[e] *= ik;
         }
-        put(&s_q[buf][t][0], xq);
-        put(&s_k[kb][t][0], xk);
-      }
-      if (lane < C) {
-        float gt = 0.0f, bt = 0.0f;
-        if (in_suffix(cpos + lane)) {
-          float xa[1], xb[1];
-          decode_raw(R.a, xa);
-          decode_raw(R.b, xb);
-          gt = -rate * softplus_f(xa[0] + dtb);
-          bt = p.beta_prob ? xb[0] : sigmoid_f(xb[0]);
-        }
-        s_g[buf][lane] = gt;
-        s_bp[lane] = bt;
+        put(&s_q[c & 1][t][0], xq);
+        put(&s_k[c % 3][t][0], xk);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // the staged chunk is read by other lanes
       __builtin_amdgcn_wave_barrier();
     };
-    // A', P and T of the chunk staged in buf (k_hat in its chunk % 3 buffer)
-    auto prepare = [&](int cpos, int buf) {
-      const int kb = ((cpos - 1) / C) % 3;
+    // A', P and T of chunk c (its q_hat in buffer c & 1, k_hat, g and beta in
+    // buffer c % 3)
+    auto prepare = [&](int c) {
+      const int buf = c & 1, kb = c % 3;
       float Gr[4], Gc;
-      gate_prefix(buf, Gr, Gc);
+      gate_prefix(kb, Gr, Gc);
       f32x4 accA = {0.0f, 0.0f, 0.0f, 0.0f}, accP = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int c4 = 0; c4 < K / 4; ++c4) {
@@ -740,7 +749,7 @@ void prefill_ws_kernel(const PrefillParams p) {
       for (int r = 0; r < 4; ++r) {
         const int t = 4 * g4 + r, s = n16;
         const float d = exp_hw(fminf(Gr[r] - Gc, 0.0f));
-        s_a[t][s] = (s < t) ? s_bp[t] * d * accA[r] : 0.0f;
+        s_a[t][s] = (s < t) ? s_bp[kb][t] * d * accA[r] : 0.0f;
         s_p[buf][t][s] = (s <= t) ? d * accP[r] : 0.0f;
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // A' is read by every lane
@@ -764,38 +773,60 @@ void prefill_ws_kernel(const PrefillParams p) {
       }
       if (g4 == 0) {
 #pragma unroll
-        for (int s = 0; s < C; ++s) s_tb[buf][n16][s] = trow[s] * s_bp[s];
+        for (int s = 0; s < C; ++s) s_tb[buf][n16][s] = trow[s] * s_bp[kb][s];
       }
     };
 
-    // The chunk loop of a producer: the same barriers as the consumers'
-    // loop, one per chunk; before barrier j the buffers of chunk j are
-    // complete.  Iteration j stages chunk j + 1 from the registers, issues
-    // chunk j + 2's loads into them, then (the q / k wave) forms A', P and T
-    // of chunk j + 1: the loads fly during that work, the barrier and the
-    // next iteration's start, and when staging waits for them nothing
-    // younger is in flight.
-    auto produce = [&](auto& R, auto load, auto stage, auto prep) {
-      const int c0 = jfirst * C + 1;
-      load(R, c0);
-      stage(R, c0, jfirst & 1);
-      load(R, c0 + C);
-      prep(c0, jfirst & 1);
-      for (int j = jfirst; j <= jlast; ++j) {
-        __syncthreads();           // chunk j's buffers complete; buffers (j + 1) & 1 free
-        if (j < jlast) {
-          stage(R, (j + 1) * C + 1, (j + 1) & 1);
-          load(R, (j + 2) * C + 1);
-          prep((j + 1) * C + 1, (j + 1) & 1);
-        }
-      }
-    };
+    // The chunk loop of a producer: one barrier before the loop (the q / k
+    // wave's first prepare needs the v wave's first gates), then the
+    // consumers' barriers, one per chunk; before barrier j the buffers of
+    // chunk j are complete.  Two register sets, each refilled right after it
+    // is staged, so a chunk's loads are issued two chunks ahead (they queue
+    // behind the consumers' page stores in the CU's memory pipeline): every
+    // iteration issues the same loads, and waiting for the set it stages
+    // leaves the other set's loads in flight.
     if (w == PW) {
-      RawQK R;
-      produce(R, load_qk, stage_qk, prepare);
+      const int c0 = jfirst;
+      RawQK RA, RB;
+      load_qk(RA, c0);
+      load_qk(RB, c0 + 1);
+      stage_qk(RA, c0);
+      load_qk(RA, c0 + 2);
+      __syncthreads();             // the first gates are staged
+      prepare(c0);
+      for (int j = jfirst;; j += 2) {
+        __syncthreads();           // chunk j's buffers complete; the next ones free
+        if (j < jlast) stage_qk(RB, j + 1);
+        load_qk(RB, j + 3);
+        if (j < jlast) prepare(j + 1);
+        if (j + 1 > jlast) break;
+        __syncthreads();           // chunk j + 1's buffers complete
+        if (j + 1 < jlast) stage_qk(RA, j + 2);
+        load_qk(RA, j + 4);
+        if (j + 1 < jlast) prepare(j + 2);
+        if (j + 2 > jlast) break;
+      }
     } else {
-      RawV R;
-      produce(R, load_v, stage_v, [](int, int) {});
+      const int c0 = jfirst;
+      Raw<TIn, 1> a0, b0;
+      RawV RA, RB;
+      load_gb(a0, b0, c0);
+      load_v(RA, c0);
+      load_v(RB, c0 + 1);
+      stage_gb(a0, b0, c0);
+      stage_v(RA, c0);
+      load_v(RA, c0 + 2);
+      __syncthreads();             // the first gates are staged
+      for (int j = jfirst;; j += 2) {
+        __syncthreads();
+        if (j < jlast) stage_v(RB, j + 1);
+        load_v(RB, j + 3);
+        if (j + 1 > jlast) break;
+        __syncthreads();
+        if (j + 1 < jlast) stage_v(RA, j + 2);
+        load_v(RA, j + 4);
+        if (j + 2 > jlast) break;
+      }
     }
     return;
   }
@@ -833,6 +864,7 @@ void prefill_ws_kernel(const PrefillParams p) {
       }
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmem0);   // the state tile (see kWaitVmem0)
+  __syncthreads();                           // the producers' first barrier
   // key rows 16 ct .. 16 ct + 15 of this wave's columns of S to a pool row
   auto store_rows = [&](int64_t row, int ct) {
     float* dst = p.pool + (row * p.HV + h) * tile_elems;
@@ -907,7 +939,7 @@ void prefill_ws_kernel(const PrefillParams p) {
     const int buf = j & 1;
     const int kb = j % 3;
     float Gr[4], Gc;
-    gate_prefix(buf, Gr, Gc);
+    gate_prefix(kb, Gr, Gc);
     const float GC = __shfl(Gc, C - 1);      // G of the last slot
 
     // ---- KS = K S0 and QS = Q S0 for this wave's columns

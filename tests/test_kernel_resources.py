@@ -3,7 +3,7 @@
 No decode kernel may use scratch (private) memory: a per-token stack round trip is a memory
 wait on every token (it cost 4-11 % when a select chain was compiled that way).  The four-wave
 chunked prefill may spill a few registers outside its chunk loop but no more than 64 bytes; the
-producer / consumer prefill uses none.
+producer / consumer prefill at most 8 bytes, before its chunk loops.
 """
 import os
 import re
@@ -51,9 +51,11 @@ def test_prefill_spills_stay_small(kernel_sets):
     assert max(pre.values()) <= 64, pre
 
 
-def test_split_prefill_uses_no_scratch(kernel_sets):
-    """The producer / consumer GDN prefill (16-bit inputs, both layouts) keeps its chunk loop free of scratch: a
-    reload there would wait for the next chunks' input loads in flight (the counter retires loads in order)."""
+def test_split_prefill_spills_at_most_a_register_pair(kernel_sets):
+    """The producer / consumer GDN prefill (16-bit inputs, both layouts) spills at most a register or two, once,
+    before its chunk loops (the K_FIRST build: one value of a producer's prologue).  More would put reloads in
+    the loop, where each one waits for the later chunks' input loads in flight (the counter retires loads in
+    order)."""
     ws = {k: v for k, v in kernel_sets.items() if "prefill_ws_kernel" in k}
     assert len(ws) == 2, sorted(ws)
-    assert not any(ws.values()), ws
+    assert max(ws.values()) <= 8, ws
