@@ -247,7 +247,19 @@ def stream_reference(torch, rsd, w, pool, d, flush, steps, warmup, stream, state
 
 
 def kernel_name(w):
-    return "gdn::prefill_kernel" if w.chunked else "gdn::decode_kernel"
+    """The kernel a workload's step launches (as rocprofv3 names it, without template arguments): GDN chunked
+    prefill with 16-bit inputs runs the producer / consumer kernel, other chunked prefills the four-wave one."""
+    if not w.chunked:
+        return "gdn::decode_kernel"
+    if w.kind.startswith("gdn") and w.io_dtype.itemsize == 2:
+        return "gdn::prefill_ws_kernel"
+    return "gdn::prefill_kernel"
+
+
+def is_kernel(name, kern):
+    """Whether a rocprofv3 kernel name is `kern` itself (template arguments or parameters follow), not a longer
+    name that begins with it."""
+    return re.search(re.escape(kern) + r"[<(]", name) is not None
 
 
 def traffic_path(workload_name):
@@ -294,7 +306,7 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir, commands):
     kern = bench_kt["roofline"]["kernel"]
     # kernel trace: per-dispatch durations of the decode kernel, warm-up dispatches dropped
     trace = [r for f in _csvs(kt_dir, "kernel_trace.csv") for r in csv.DictReader(open(f))]
-    dec = sorted((r for r in trace if kern in r["Kernel_Name"]), key=lambda r: int(r["Start_Timestamp"]))
+    dec = sorted((r for r in trace if is_kernel(r["Kernel_Name"], kern)), key=lambda r: int(r["Start_Timestamp"]))
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in dec]
     timed = durs[bench_kt["warmup"]:]
     stats = [r for f in _csvs(kt_dir, "kernel_stats.csv") for r in csv.DictReader(open(f))]
@@ -314,7 +326,7 @@ def summarize_profiles(kt_dir, fetch_dir, write_dir, commands):
 
     def counter(d, cname):
         rows = [r for f in _csvs(d, "counter_collection.csv") for r in csv.DictReader(open(f))]
-        dec_v = [float(r["Counter_Value"]) for r in rows if kern in r["Kernel_Name"] and r["Counter_Name"] == cname]
+        dec_v = [float(r["Counter_Value"]) for r in rows if is_kernel(r["Kernel_Name"], kern) and r["Counter_Name"] == cname]
         big = [r for r in rows if r["Counter_Name"] == cname and "copyBuffer" in r["Kernel_Name"]]
         big = [float(r["Counter_Value"]) for r in big if int(r["Grid_Size"]) >= 65536]
         return statistics.median(dec_v), statistics.median(big), len(dec_v)
@@ -391,11 +403,11 @@ def summarize_counters(run_dir, sel):
     rows = [r for f in _csvs(run_dir, "counter_collection.csv") for r in csv.DictReader(open(f))]
     trace = [r for f in _csvs(run_dir, "kernel_trace.csv") for r in csv.DictReader(open(f))]
     dur = {r["Dispatch_Id"]: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-           for r in trace if kern in r["Kernel_Name"]}
+           for r in trace if is_kernel(r["Kernel_Name"], kern)}
     per = {}
     meta = {}
     for r in rows:
-        if kern not in r["Kernel_Name"]:
+        if not is_kernel(r["Kernel_Name"], kern):
             continue
         per.setdefault(r["Counter_Name"], {})[r["Dispatch_Id"]] = float(r["Counter_Value"])
         meta = {k: r.get(k) for k in ("VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "LDS_Block_Size",
