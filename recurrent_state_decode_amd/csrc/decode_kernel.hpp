@@ -476,6 +476,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   __shared__ float s_sc[TC][4];                    // alpha (GDN), beta, q_hat . k_hat
   __shared__ __align__(16) float s_red[AV ? 1 : 2][AV ? 1 : NW][2][VB];
   __shared__ float s_max[2][NW];
+  __shared__ __align__(16) float s_wv[Cfg::KF_RS ? VB : 4];   // K_FIRST, 64 columns: u / c' per column
   // V_FIRST pool with the codec: the tile passes through LDS between the
   // pool's [V][K] rows and the [K][V] register arrangement (row stride K + 1
   // keeps both directions free of bank conflicts)
@@ -1151,27 +1152,74 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
           for (int e = 0; e < EV; ++e) S[s][e] *= al[slot(s, e)];
       }
 
-      float r[NO], pp[NO];
-      reduce_pass(kh, qh, r, pp);
+      float wv[NO];
+      if constexpr (Cfg::KF_RS) {
+        // the waves' partial sums go to LDS reduce-scattered (one (kind,
+        // column) pair per lane and value); wave 0 then finishes each column
+        // once, one lane per column (VB == 64), and hands the write
+        // coefficients u / c' to every wave through LDS
+        float r[4], pp[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          r[e] = kh[0] * S[0][e];
+          pp[e] = qh[0] * S[0][e];
+        }
+#pragma unroll
+        for (int s = 1; s < NS; ++s)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            r[e] = fmaf(kh[s], S[s][e], r[e]);
+            pp[e] = fmaf(qh[s], S[s][e], pp[e]);
+          }
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = rs_halves32(r[e], pp[e]);   // lanes < 32: r_e, else p_e
+        const int kind = lane >> 5, par = (lane >> 4) & 1;
+        s_red[red_buf][w][kind][4 * lr + par] = rs_rows16(x[0], x[1]);
+        s_red[red_buf][w][kind][4 * lr + par + 2] = rs_rows16(x[2], x[3]);
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(w) == 0) {
+          float rj = s_red[red_buf][0][0][lane], pj = s_red[red_buf][0][1][lane];
+#pragma unroll
+          for (int ww = 1; ww < NW; ++ww) {
+            rj += s_red[red_buf][ww][0][lane];
+            pj += s_red[red_buf][ww][1][lane];
+          }
+          const float uj = beta * (s_v[tt][lane] - cn * rj);
+          s_wv[lane] = uj * icn;
+          if (!stored) {
+            float oj = fmaf(qk, uj, cn * pj);
+            if constexpr (HAD) oj = wht32_lanes(oj, lane) * 0.03125f;   // o back to the original basis
+            store_out1(out_row + lane, oj);
+          }
+        }
+        __syncthreads();
+        const float4 wx = *reinterpret_cast<const float4*>(&s_wv[4 * lr]);
+        wv[0] = wx.x; wv[1] = wx.y; wv[2] = wx.z; wv[3] = wx.w;
+        red_buf ^= 1;
+      } else {
+        float r[NO], pp[NO];
+        reduce_pass(kh, qh, r, pp);
 
-      float u[NO], o[NO], wv[NO];
+        float u[NO], o[NO];
 #pragma unroll
-      for (int j = 0; j < NO; ++j) {
-        const int col = AV ? row_idx(j) : 4 * lr + j;
-        u[j] = beta * (s_v[tt][col] - cn * r[j]);
-        o[j] = fmaf(qk, u[j], cn * pp[j]);
-        wv[j] = u[j] * icn;
-      }
-      if constexpr (!HAD) {
-        if (!stored) store_outputs(out_row, o);
-      } else if (!stored && __builtin_amdgcn_readfirstlane(w) == 0) {   // o back to the original basis (wave 0 stores it)
-        float ow[1][NO];
+        for (int j = 0; j < NO; ++j) {
+          const int col = AV ? row_idx(j) : 4 * lr + j;
+          u[j] = beta * (s_v[tt][col] - cn * r[j]);
+          o[j] = fmaf(qk, u[j], cn * pp[j]);
+          wv[j] = u[j] * icn;
+        }
+        if constexpr (!HAD) {
+          if (!stored) store_outputs(out_row, o);
+        } else if (!stored && __builtin_amdgcn_readfirstlane(w) == 0) {   // o back to the original basis (wave 0 stores it)
+          float ow[1][NO];
 #pragma unroll
-        for (int j = 0; j < NO; ++j) ow[0][j] = o[j];
-        wht32(ow, sg1, sg2, sg4);
+          for (int j = 0; j < NO; ++j) ow[0][j] = o[j];
+          wht32(ow, sg1, sg2, sg4);
 #pragma unroll
-        for (int j = 0; j < NO; ++j) o[j] = ow[0][j] * 0.03125f;
-        store_outputs(out_row, o);
+          for (int j = 0; j < NO; ++j) o[j] = ow[0][j] * 0.03125f;
+          store_outputs(out_row, o);
+        }
       }
 
       // S_reg += k_hat (x) wv
