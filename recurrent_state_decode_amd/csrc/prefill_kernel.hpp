@@ -539,7 +539,7 @@ void prefill_ws_kernel(const PrefillParams p) {
 
   // per head of the pair, then per chunk parity
   __shared__ __align__(16) float s_q2[NH][2][C][LDK];   // q_hat (scaled)
-  __shared__ __align__(16) float s_k2[NH][3][C][LDK];   // by chunk % 3 (see the consumers)   // k_hat
+  __shared__ __align__(16) float s_k2[NH][4][C][LDK];   // k_hat by chunk % 4 (see the producers and the consumers)
   __shared__ __align__(16) float s_v2[NH][2][C][LDK];   // v of this V-block
   __shared__ float s_g2[NH][3][C];                      // g = log alpha per slot, by chunk % 3
   __shared__ float s_tb2[NH][2][C][LDC];                // T diag(beta)
@@ -570,7 +570,7 @@ void prefill_ws_kernel(const PrefillParams p) {
   const int hk = min(h, p.HV - 1) / p.gqa;
 
   float (&s_q)[2][C][LDK] = s_q2[half];
-  float (&s_k)[3][C][LDK] = s_k2[half];
+  float (&s_k)[4][C][LDK] = s_k2[half];
   float (&s_v)[2][C][LDK] = s_v2[half];
   float (&s_g)[3][C] = s_g2[half];
   float (&s_tb)[2][C][LDC] = s_tb2[half];
@@ -628,8 +628,8 @@ void prefill_ws_kernel(const PrefillParams p) {
     static_assert(K % EW == 0 && 64 % LPT == 0 && C % TPI == 0 && VBLK == K, "piece layout");
     const int tl = lane / LPT;       // this lane's token inside an instruction's TPI
     const int el = lane % LPT;       // its piece of the row
-    struct RawQK {
-      Raw<TIn, EW> q[NI], k[NI];
+    struct RawX {                    // one chunk of q or of k
+      Raw<TIn, EW> x[NI];
     };
     struct RawV {
       Raw<TIn, EW> v[NI];            // chunk c
@@ -638,12 +638,11 @@ void prefill_ws_kernel(const PrefillParams p) {
     auto in_suffix = [&](int pos) { return pos >= pos0 && pos <= pos_last; };
     auto token_of = [&](int pos) -> int64_t { return t0 + min(max(pos - pos0, 0), t1 - t0 - 1); };
     auto cpos_of = [](int c) { return c * C + 1; };
-    auto load_qk = [&](RawQK& R, int c) {
+    auto load_x = [&](const TIn* __restrict__ g, RawX& R, int c) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int64_t tk = token_of(cpos_of(c) + TPI * i + tl);
-        load_raw_n<EW>(gq, (tk * p.HK + hk) * K + EW * el, R.q[i]);
-        load_raw_n<EW>(gk, (tk * p.HK + hk) * K + EW * el, R.k[i]);
+        load_raw_n<EW>(g, (tk * p.HK + hk) * K + EW * el, R.x[i]);
       }
     };
     auto load_gb = [&](Raw<TIn, 1>& a, Raw<TIn, 1>& b, int c) {
@@ -698,50 +697,41 @@ void prefill_ws_kernel(const PrefillParams p) {
       }
       stage_gb(R.a, R.b, c + 1);
     };
-    // normalise and stage q and k of chunk c (slots outside the suffix:
+    // normalise and stage q (scale > 0: q_hat scaled, into buffer c & 1) or
+    // k (scale 0: into buffer c % 4) of chunk c (slots outside the suffix:
     // identity tokens)
-    auto stage_qk = [&](const RawQK& R, int c) {
+    auto stage_x = [&](const RawX& R, int c, bool is_q) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int t = TPI * i + tl;
         const bool ok = in_suffix(cpos_of(c) + t);
-        float xq[EW], xk[EW];
-        decode_raw(R.q[i], xq);
-        decode_raw(R.k[i], xk);
-        float sq = 0.0f, sk = 0.0f;
+        float x[EW];
+        decode_raw(R.x[i], x);
+        float sx = 0.0f;
 #pragma unroll
         for (int e = 0; e < EW; ++e) {
-          xq[e] = ok ? xq[e] : 0.0f;
-          xk[e] = ok ? xk[e] : 0.0f;
-          sq = fmaf(xq[e], xq[e], sq);
-          sk = fmaf(xk[e], xk[e], sk);
+          x[e] = ok ? x[e] : 0.0f;
+          sx = fmaf(x[e], x[e], sx);
         }
-        float iq = p.scale, ik = 1.0f;
-        if (p.l2norm) {              // sums over the LPT lanes of this token's row
-          iq = p.scale * rsqrtf(lane_reduce<0, LB>(sq) + kL2Eps);
-          ik = rsqrtf(lane_reduce<0, LB>(sk) + kL2Eps);
-        }
+        float ix = is_q ? p.scale : 1.0f;
+        if (p.l2norm) ix *= rsqrtf(lane_reduce<0, LB>(sx) + kL2Eps);   // sum over the LPT lanes of this token's row
 #pragma unroll
-        for (int e = 0; e < EW; ++e) {
-          xq[e] *= iq;
-          xk[e] *= ik;
-        }
-        put(&s_q[c & 1][t][0], xq);
-        put(&s_k[c % 3][t][0], xk);
+        for (int e = 0; e < EW; ++e) x[e] *= ix;
+        put(is_q ? &s_q[c & 1][t][0] : &s_k[c % 4][t][0], x);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // the staged chunk is read by other lanes
       __builtin_amdgcn_wave_barrier();
     };
-    // A', P and T of chunk c (its q_hat in buffer c & 1, k_hat, g and beta in
-    // buffer c % 3)
+    // A', P and T of chunk c (its q_hat in buffer c & 1, k_hat in buffer
+    // c % 4, g and beta in buffer c % 3)
     auto prepare = [&](int c) {
-      const int buf = c & 1, kb = c % 3;
+      const int buf = c & 1, kb = c % 3, k4 = c % 4;
       float Gr[4], Gc;
       gate_prefix(kb, Gr, Gc);
       f32x4 accA = {0.0f, 0.0f, 0.0f, 0.0f}, accP = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int c4 = 0; c4 < K / 4; ++c4) {
-        const float kk = s_k[kb][n16][4 * c4 + g4];
+        const float kk = s_k[k4][n16][4 * c4 + g4];
         accA = mfma_16x16x4(kk, kk, accA);
         accP = mfma_16x16x4(s_q[buf][n16][4 * c4 + g4], kk, accP);
       }
@@ -778,31 +768,36 @@ void prefill_ws_kernel(const PrefillParams p) {
     };
 
     // The chunk loop of a producer: one barrier before the loop (the q / k
-    // wave's first prepare needs the v wave's first gates), then the
-    // consumers' barriers, one per chunk; before barrier j the buffers of
-    // chunk j are complete.  Two register sets, each refilled right after it
-    // is staged, so a chunk's loads are issued two chunks ahead (they queue
-    // behind the consumers' page stores in the CU's memory pipeline): every
-    // iteration issues the same loads, and waiting for the set it stages
-    // leaves the other set's loads in flight.
+    // wave's first prepare needs the v wave's first gates and k_hat), then
+    // the consumers' barriers, one per chunk; before barrier j the buffers of
+    // chunk j are complete.  The q / k wave stages q_hat one chunk ahead and
+    // prepares A', P and T; the v wave stages v one chunk ahead and k_hat two
+    // chunks ahead (barrier j closes the staging of k_hat for chunk j + 2,
+    // which the q / k wave reads after barrier j + 1), so that the
+    // normalisation work is split between the two producer waves, which sit
+    // on different SIMDs.  Two register sets per tensor, each refilled right
+    // after it is staged, so a chunk's loads are issued two chunks ahead
+    // (they queue behind the consumers' page stores in the CU's memory
+    // pipeline): every iteration issues the same loads, and waiting for the
+    // set it stages leaves the other set's loads in flight.
     if (w == PW) {
       const int c0 = jfirst;
-      RawQK RA, RB;
-      load_qk(RA, c0);
-      load_qk(RB, c0 + 1);
-      stage_qk(RA, c0);
-      load_qk(RA, c0 + 2);
-      __syncthreads();             // the first gates are staged
+      RawX QA, QB;
+      load_x(gq, QA, c0);
+      load_x(gq, QB, c0 + 1);
+      stage_x(QA, c0, true);
+      load_x(gq, QA, c0 + 2);
+      __syncthreads();             // the first gates and k_hat are staged
       prepare(c0);
       for (int j = jfirst;; j += 2) {
         __syncthreads();           // chunk j's buffers complete; the next ones free
-        if (j < jlast) stage_qk(RB, j + 1);
-        load_qk(RB, j + 3);
+        if (j < jlast) stage_x(QB, j + 1, true);
+        load_x(gq, QB, j + 3);
         if (j < jlast) prepare(j + 1);
         if (j + 1 > jlast) break;
         __syncthreads();           // chunk j + 1's buffers complete
-        if (j + 1 < jlast) stage_qk(RA, j + 2);
-        load_qk(RA, j + 4);
+        if (j + 1 < jlast) stage_x(QA, j + 2, true);
+        load_x(gq, QA, j + 4);
         if (j + 1 < jlast) prepare(j + 2);
         if (j + 2 > jlast) break;
       }
@@ -810,21 +805,32 @@ void prefill_ws_kernel(const PrefillParams p) {
       const int c0 = jfirst;
       Raw<TIn, 1> a0, b0;
       RawV RA, RB;
+      RawX KA, KB;
       load_gb(a0, b0, c0);
       load_v(RA, c0);
       load_v(RB, c0 + 1);
+      load_x(gk, KA, c0);
+      load_x(gk, KB, c0 + 1);
       stage_gb(a0, b0, c0);
       stage_v(RA, c0);
       load_v(RA, c0 + 2);
-      __syncthreads();             // the first gates are staged
+      stage_x(KA, c0, false);
+      load_x(gk, KA, c0 + 2);
+      __syncthreads();             // the first gates and k_hat are staged
+      if (c0 < jlast) stage_x(KB, c0 + 1, false);
+      load_x(gk, KB, c0 + 3);
       for (int j = jfirst;; j += 2) {
         __syncthreads();
         if (j < jlast) stage_v(RB, j + 1);
         load_v(RB, j + 3);
+        if (j + 2 <= jlast) stage_x(KA, j + 2, false);
+        load_x(gk, KA, j + 4);
         if (j + 1 > jlast) break;
         __syncthreads();
         if (j + 1 < jlast) stage_v(RA, j + 2);
         load_v(RA, j + 4);
+        if (j + 3 <= jlast) stage_x(KB, j + 3, false);
+        load_x(gk, KB, j + 5);
         if (j + 2 > jlast) break;
       }
     }
@@ -895,12 +901,12 @@ void prefill_ws_kernel(const PrefillParams p) {
 
   // ---- S_C = exp(G_C) S0 + sum_s exp(G_C - G_s) k_s u_s^T for chunk jj
   auto update = [&](int jj, const f32x4 (&Uc)[VT], float eC, const float (&dk)[4]) {
-    const int kb = jj % 3;
+    const int k4 = jj % 4;
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       float ka[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ka[r] = dk[r] * s_k[kb][4 * g4 + r][16 * ct + n16];
+      for (int r = 0; r < 4; ++r) ka[r] = dk[r] * s_k[k4][4 * g4 + r][16 * ct + n16];
 #pragma unroll
       for (int vt = 0; vt < VT; ++vt) {
         f32x4 acc = S[ct][vt] * eC;
@@ -914,7 +920,7 @@ void prefill_ws_kernel(const PrefillParams p) {
   // j opens iteration j + 1, before that chunk's K S0 / Q S0.  On each SIMD
   // the two heads' consumers then sit in different phases, so one's
   // latency-bound U / O overlaps the other's matrix products instead of
-  // coinciding with them.  (k_hat is kept three chunks deep for this.)
+  // coinciding with them.  (k_hat is kept one chunk longer for this.)
   const bool late = half == 1;
   f32x4 Ul[VT];
   float eCl = 0.0f, dkl[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -952,7 +958,7 @@ void prefill_ws_kernel(const PrefillParams p) {
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       if (store_pending) store_rows(pending_row, ct);   // the previous chunk's page
-      const float4 kv = *reinterpret_cast<const float4*>(&s_k[kb][n16][16 * ct + 4 * g4]);
+      const float4 kv = *reinterpret_cast<const float4*>(&s_k[j % 4][n16][16 * ct + 4 * g4]);
       const float4 qv = *reinterpret_cast<const float4*>(&s_q[buf][n16][16 * ct + 4 * g4]);
       const float kr[4] = {kv.x, kv.y, kv.z, kv.w};
       const float qr[4] = {qv.x, qv.y, qv.z, qv.w};
