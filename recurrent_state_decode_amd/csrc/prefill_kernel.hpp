@@ -839,7 +839,6 @@ void prefill_ws_kernel(const PrefillParams p) {
 
   // ================= consumers =================
   const int64_t rrow = load_index(p.page_indices, pg_start + max(pos0 - 2, 0) / p.page_size, p.idx64);
-  const int64_t wrow = load_index(p.page_indices, pg_end - 1, p.idx64);
   const int64_t tile_elems = static_cast<int64_t>(K) * p.V;
   const int vcol = vb * VBLK + 16 * VT * w;   // first value column of this wave
   const int cpp = p.page_size / C;
@@ -887,9 +886,41 @@ void prefill_ws_kernel(const PrefillParams p) {
       }
     }
   };
-  auto store_state = [&](int64_t row) {
+  // V_FIRST: key tiles c0 and c0 + 1 (c0 even) as whole 128-byte lines.
+  // A lane holds 4 consecutive keys of one value column, so a tile's store
+  // writes 64-byte half lines (keys 16 c0 .. 16 c0 + 15 of a column over
+  // four lanes).  Rotating tile c0 + 1 by 8 lanes within each 16-lane row
+  // (R) gives every lane of columns n < 8 the other half of a column whose
+  // first half a lane of column n + 8 holds, and vice versa: X = (n < 8 ?
+  // tile c0 : R) covers columns 0..7 of the 16, keys 16 c0 .. 16 c0 + 31,
+  // eight lanes to a line; Y = (n < 8 ? R : tile c0) covers columns 8..15.
+  auto store_pair = [&](int64_t row, int c0) {
+    float* dst = p.pool + (row * p.HV + h) * tile_elems;
+    const bool lo = n16 < 8;
+    const int cx = vcol + (n16 & 7);
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) store_rows(row, ct);
+    for (int vt = 0; vt < VT; ++vt) {
+      f32x4 R, X, Y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        R[e] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(S[c0 + 1][vt][e]), 0x128, 0xF, 0xF, false));
+        X[e] = lo ? S[c0][vt][e] : R[e];
+        Y[e] = lo ? R[e] : S[c0][vt][e];
+      }
+      const int kx = 16 * c0 + (lo ? 0 : 16) + 4 * g4;
+      const int ky = 16 * c0 + (lo ? 16 : 0) + 4 * g4;
+      *reinterpret_cast<f32x4*>(dst + (cx + 16 * vt) * K + kx) = X;
+      *reinterpret_cast<f32x4*>(dst + (cx + 16 * vt + 8) * K + ky) = Y;
+    }
+  };
+  auto store_state = [&](int64_t row) {
+    if constexpr (VF) {
+#pragma unroll
+      for (int ct = 0; ct < 8; ct += 2) store_pair(row, ct);
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) store_rows(row, ct);
+    }
   };
   // A page that a chunk fills receives the state after that chunk.  The
   // registers keep that state until the next chunk's update, so the store
@@ -957,7 +988,13 @@ void prefill_ws_kernel(const PrefillParams p) {
     }
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
-      if (store_pending) store_rows(pending_row, ct);   // the previous chunk's page
+      if (store_pending) {                   // the previous chunk's page
+        if constexpr (VF) {
+          if (ct & 1) store_pair(pending_row, ct - 1);
+        } else {
+          store_rows(pending_row, ct);
+        }
+      }
       const float4 kv = *reinterpret_cast<const float4*>(&s_k[j % 4][n16][16 * ct + 4 * g4]);
       const float4 qv = *reinterpret_cast<const float4*>(&s_q[buf][n16][16 * ct + 4 * g4]);
       const float kr[4] = {kv.x, kv.y, kv.z, kv.w};
@@ -1033,7 +1070,9 @@ void prefill_ws_kernel(const PrefillParams p) {
   }
   if (late) update(jlast, Ul, eCl, dkl);    // (the last chunk fills no page of the suffix's interior)
 
-  store_state(wrow);
+  // the last page's row, read here through the scalar cache (kept from the
+  // start it would occupy registers through the chunk loop)
+  store_state(load_index_uniform(p.page_indices, pg_end - 1, p.idx64));
 }
 
 }  // namespace gdn
