@@ -133,10 +133,43 @@ struct HeadCfg {
 };
 constexpr HeadCfg kHeads[] = {{16, 16}, {128, 64}};
 
+// LDS reserved per workgroup (static plus dynamic shared memory the kernel
+// never touches) for shapes whose state stream moves faster with fewer
+// workgroups resident per CU (160 KiB of LDS per CU).  Measured with
+// interleaved timing rounds:
+//   paged GDN, one token, V_FIRST 8-column blocks:   12 288 bytes (13 per CU
+//       instead of the 14 the registers allow): B=256 173.3 -> 171.0 us
+//   paged KDA, one token, V_FIRST 16-column blocks:  20 992 bytes (7 instead
+//       of 10): B=256 182.4 -> 173.8 us
+//   pooled KDA, several tokens, V_FIRST 64-column blocks: 41 472 bytes (3
+//       instead of 4): B=128 x 1..8 tokens 107.4 -> 105.5 us
+// 0: no reservation.
+template <int VB, int NT, bool VF, bool KDA, int QDQ, int ADDR>
+constexpr int kLdsPerWorkgroup =
+    (QDQ != gdn::kQdqNone || !VF) ? 0
+    : (VB == 8 && NT == 128 && !KDA && ADDR == gdn::kPaged1)  ? 12288
+    : (VB == 16 && NT == 128 && KDA && ADDR == gdn::kPaged1)  ? 20992
+    : (VB == 64 && NT == 256 && KDA && ADDR == gdn::kPooled)  ? 41472
+                                                             : 0;
+
 template <int K, int VB, int NT, bool VF, bool KDA, int QDQ, int ADDR, typename TIn>
 hipError_t launch_one(const gdn::Params& p, int64_t units, hipStream_t stream) {
-  hipLaunchKernelGGL((gdn::decode_kernel<K, VB, NT, VF, KDA, QDQ, ADDR, TIn>), dim3(static_cast<uint32_t>(units)),
-                     dim3(NT), 0, stream, p);
+  auto kernel = gdn::decode_kernel<K, VB, NT, VF, KDA, QDQ, ADDR, TIn>;
+  size_t pad = 0;
+  if constexpr (kLdsPerWorkgroup<VB, NT, VF, KDA, QDQ, ADDR> > 0) {
+    static size_t cached = 0;      // (the kernel's static LDS does not change at run time)
+    static bool known = false;
+    if (!known) {
+      hipFuncAttributes a{};
+      if (hipFuncGetAttributes(&a, reinterpret_cast<const void*>(kernel)) == hipSuccess) {
+        const size_t want = kLdsPerWorkgroup<VB, NT, VF, KDA, QDQ, ADDR>;
+        cached = a.sharedSizeBytes < want ? want - a.sharedSizeBytes : 0;
+      }
+      known = true;
+    }
+    pad = cached;
+  }
+  hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(units)), dim3(NT), pad, stream, p);
   return hipGetLastError();
 }
 
