@@ -913,13 +913,37 @@ void prefill_ws_kernel(const PrefillParams p) {
       *reinterpret_cast<f32x4*>(dst + (cx + 16 * vt + 8) * K + ky) = Y;
     }
   };
+  // K_FIRST: key tile ct as whole 128-byte lines.  A lane holds one value
+  // of a key row; the wave's 32 columns of a row (128 bytes) are split over
+  // its two value tiles, 16 lanes each.  Swapping tile 1 between the lanes
+  // of neighbouring 16-lane rows (v_permlane16_swap) gives each store the
+  // full 32 columns of two key rows: X holds rows 4 g + r for even g, Y for
+  // odd g.
+  auto store_rows_kf = [&](int64_t row, int ct) {
+    static_assert(VT == 2, "two value tiles make a line");
+    float* dst = p.pool + (row * p.HV + h) * tile_elems;
+    const bool even = (g4 & 1) == 0;
+    const int lane_kx = 4 * (g4 & ~1) * p.V + vcol + 16 * (g4 & 1) + n16;
+    const int lane_ky = 4 * (g4 | 1) * p.V + vcol + 16 * (1 - (g4 & 1)) + n16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float a = S[ct][0][r], b = S[ct][1][r];
+      const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(b), __float_as_uint(b), false, false);
+      const float pb = __uint_as_float(even ? pr[1] : pr[0]);   // tile 1 of the lane 16 apart
+      const float x = even ? a : pb, y = even ? pb : a;
+      // uniform row pointer + 32-bit lane offset, as store_rows
+      float* rowp = dst + static_cast<uint32_t>((16 * ct + r) * p.V);
+      rowp[static_cast<uint32_t>(lane_kx)] = x;
+      rowp[static_cast<uint32_t>(lane_ky)] = y;
+    }
+  };
   auto store_state = [&](int64_t row) {
     if constexpr (VF) {
 #pragma unroll
       for (int ct = 0; ct < 8; ct += 2) store_pair(row, ct);
     } else {
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) store_rows(row, ct);
+      for (int ct = 0; ct < 8; ++ct) store_rows_kf(row, ct);
     }
   };
   // A page that a chunk fills receives the state after that chunk.  The
@@ -992,7 +1016,7 @@ void prefill_ws_kernel(const PrefillParams p) {
         if constexpr (VF) {
           if (ct & 1) store_pair(pending_row, ct - 1);
         } else {
-          store_rows(pending_row, ct);
+          store_rows_kf(pending_row, ct);
         }
       }
       const float4 kv = *reinterpret_cast<const float4*>(&s_k[j % 4][n16][16 * ct + 4 * g4]);
