@@ -138,11 +138,14 @@ constexpr HeadCfg kHeads[] = {{16, 16}, {128, 64}};
 // workgroups resident per CU (160 KiB of LDS per CU).  Measured with
 // interleaved timing rounds:
 //   paged GDN, one token, V_FIRST 8-column blocks:   12 288 bytes (13 per CU
-//       instead of the 14 the registers allow): B=256 173.3 -> 171.0 us
+//       instead of the 14 the registers allow): B=256 174.7 -> 172.4 us
 //   paged KDA, one token, V_FIRST 16-column blocks:  20 992 bytes (7 instead
-//       of 10): B=256 182.4 -> 173.8 us
+//       of 10): B=256 179.4 -> 174.5 us
 //   pooled KDA, several tokens, V_FIRST 64-column blocks: 41 472 bytes (3
-//       instead of 4): B=128 x 1..8 tokens 107.4 -> 105.5 us
+//       instead of 4): B=128 x 1..8 tokens 104.6 -> 103.0 us
+// Fewer are slower again (paged GDN at 9 per CU 180 us), and the other
+// shapes measured flat.  (hipFuncGetAttributes gives the static part; the
+// reservation is the same on every device, so one cached value serves all.)
 // 0: no reservation.
 template <int VB, int NT, bool VF, bool KDA, int QDQ, int ADDR>
 constexpr int kLdsPerWorkgroup =

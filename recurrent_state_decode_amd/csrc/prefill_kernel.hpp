@@ -697,8 +697,8 @@ void prefill_ws_kernel(const PrefillParams p) {
       }
       stage_gb(R.a, R.b, c + 1);
     };
-    // normalise and stage q (scale > 0: q_hat scaled, into buffer c & 1) or
-    // k (scale 0: into buffer c % 4) of chunk c (slots outside the suffix:
+    // normalise and stage q (is_q: q_hat times the scale, into buffer c & 1)
+    // or k (k_hat, into buffer c % 4) of chunk c (slots outside the suffix:
     // identity tokens)
     auto stage_x = [&](const RawX& R, int c, bool is_q) {
 #pragma unroll
