@@ -101,6 +101,7 @@ void prefill_kernel(const PrefillParams p) {
   __shared__ float s_p[C][LDC];                 // P (lower, diagonal included)
   __shared__ float s_t[NW][C][LDC];             // T = (I + A')^-1, one copy per wave
   __shared__ float s_g[C], s_b[C];
+  __shared__ __align__(16) float s_o[NW][C][32];  // one chunk's output rows, per wave
   // KDA: per-channel gates.  s_G holds g, then G (in place); s_kg / s_qg =
   // k / q times exp(G); s_kd = exp(G_C - G) k; s_eC = exp(G_C) per channel
   constexpr int KC = KDA ? C : 1, KK = KDA ? LDK : 1;
@@ -442,16 +443,34 @@ void prefill_kernel(const PrefillParams p) {
 #pragma unroll
       for (int vt = 0; vt < VT; ++vt) O[vt] = mfma_16x16x4(pa, U[vt][r], O[vt]);
     }
+    // ---- the output rows, through this wave's LDS block (as in
+    // prefill_ws_kernel: one 16-byte store per lane instead of 8 scattered
+    // ones; 16 VT columns per wave, VT == 2)
+    {
+      static_assert(VT == 2, "a lane stores 8 of the wave's 32 columns");
+      float (&so)[C][16 * VT] = s_o[w];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int pos = cpos + 4 * g4 + r;
+      for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) so[4 * g4 + r][16 * vt + n16] = O[vt][r];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // read back by other lanes of this wave
+      __builtin_amdgcn_wave_barrier();
+      const int ts = lane >> 2, piece = lane & 3;   // token slot, 8-column piece
+      const float4 a = *reinterpret_cast<const float4*>(&so[ts][8 * piece]);
+      const float4 b = *reinterpret_cast<const float4*>(&so[ts][8 * piece + 4]);
+      const int pos = cpos + ts;
       if (pos >= pos0 && pos <= pos_last) {
-        const int64_t t = t0 + (pos - pos0);
-        const int64_t oi = (t * p.HV + h) * p.V + vcol + n16;
-#pragma unroll
-        for (int vt = 0; vt < VT; ++vt) {
-          if (p.out_bf16) static_cast<uint16_t*>(p.out)[oi + 16 * vt] = to_bf16_bits(O[vt][r]);
-          else static_cast<float*>(p.out)[oi + 16 * vt] = O[vt][r];
+        const int64_t oi = ((t0 + (pos - pos0)) * p.HV + h) * p.V + vcol + 8 * piece;
+        if (p.out_bf16) {
+          uint4 pk;
+          pk.x = to_bf16_bits(a.x) | (static_cast<uint32_t>(to_bf16_bits(a.y)) << 16);
+          pk.y = to_bf16_bits(a.z) | (static_cast<uint32_t>(to_bf16_bits(a.w)) << 16);
+          pk.z = to_bf16_bits(b.x) | (static_cast<uint32_t>(to_bf16_bits(b.y)) << 16);
+          pk.w = to_bf16_bits(b.z) | (static_cast<uint32_t>(to_bf16_bits(b.w)) << 16);
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + oi) = pk;
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(p.out) + oi) = a;
+          *reinterpret_cast<float4*>(static_cast<float*>(p.out) + oi + 4) = b;
         }
       }
     }
