@@ -476,6 +476,12 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   __shared__ float s_sc[TC][4];                    // alpha (GDN), beta, q_hat . k_hat
   __shared__ __align__(16) float s_red[AV ? 1 : 2][AV ? 1 : NW][2][VB];
   __shared__ float s_max[2][NW];
+  // V_FIRST rows with several tokens: a chunk's outputs are collected here
+  // and written once per chunk, 8 values per lane, instead of one value per
+  // row lane and token (kPaged1 calls have one token)
+  constexpr bool OUT_LDS = AV && ADDR != kPaged1;
+  static_assert(!OUT_LDS || VB % 8 == 0, "8-value output pieces");
+  __shared__ __align__(16) float s_o[OUT_LDS ? TC : 1][OUT_LDS ? VB : 8];
   __shared__ __align__(16) float s_wv[Cfg::KF_RS ? VB : 4];   // K_FIRST, 64 columns: u / c' per column
   // V_FIRST pool with the codec: the tile passes through LDS between the
   // pool's [V][K] rows and the [K][V] register arrangement (row stride K + 1
@@ -987,7 +993,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
     }
   };
 
-  auto store_outputs = [&](int64_t out_row, const float (&o)[NO]) {
+  const bool staged = OUT_LDS && t1 - t0 > 1;   // uniform per workgroup
+  auto store_outputs = [&](int tt, int64_t out_row, const float (&o)[NO]) {
     if constexpr (!AV) {
       if (w == 0 && rg == 0) store_out4(out_row + 4 * lr, o);
     } else {
@@ -999,7 +1006,31 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
         my_o = (lr == s) ? o[s] : my_o;
         asm volatile("" : "+v"(my_o));
       }
-      if (lr < NS) store_out1(out_row + row_idx(lr), my_o);
+      if (lr < NS) {
+        if (OUT_LDS && staged) s_o[tt][row_idx(lr)] = my_o;
+        else store_out1(out_row + row_idx(lr), my_o);
+      }
+    }
+  };
+  // the staged outputs of tokens c0 .. c0 + n - 1 (after a barrier)
+  auto flush_outputs = [&](int c0, int n) {
+    constexpr int PL = OUT_LDS ? VB / 8 : 1;   // lanes per token
+    for (int idx = tid; idx < n * PL; idx += NT) {
+      const int tt = idx / PL, piece = idx - tt * PL;
+      const int64_t oi = (static_cast<int64_t>(c0 + tt) * p.HV + h) * p.V + out_col0 + 8 * piece;
+      const float4 a = *reinterpret_cast<const float4*>(&s_o[tt][8 * piece]);
+      const float4 b = *reinterpret_cast<const float4*>(&s_o[tt][8 * piece + 4]);
+      if (p.out_bf16) {
+        uint4 pk;
+        pk.x = to_bf16_bits(a.x) | (static_cast<uint32_t>(to_bf16_bits(a.y)) << 16);
+        pk.y = to_bf16_bits(a.z) | (static_cast<uint32_t>(to_bf16_bits(a.w)) << 16);
+        pk.z = to_bf16_bits(b.x) | (static_cast<uint32_t>(to_bf16_bits(b.y)) << 16);
+        pk.w = to_bf16_bits(b.z) | (static_cast<uint32_t>(to_bf16_bits(b.w)) << 16);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + oi) = pk;
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + oi) = a;
+        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + oi + 4) = b;
+      }
     }
   };
 
@@ -1210,7 +1241,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
           wv[j] = u[j] * icn;
         }
         if constexpr (!HAD) {
-          if (!stored) store_outputs(out_row, o);
+          if (!stored) store_outputs(tt, out_row, o);
         } else if (!stored && __builtin_amdgcn_readfirstlane(w) == 0) {   // o back to the original basis (wave 0 stores it)
           float ow[1][NO];
 #pragma unroll
@@ -1218,7 +1249,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
           wht32(ow, sg1, sg2, sg4);
 #pragma unroll
           for (int j = 0; j < NO; ++j) o[j] = ow[0][j] * 0.03125f;
-          store_outputs(out_row, o);
+          store_outputs(tt, out_row, o);
         }
       }
 
@@ -1251,7 +1282,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
 #pragma unroll
             for (int j = 0; j < NO; ++j) ps[j] = pw[0][j] * 0.03125f;
           }
-          store_outputs(out_row, ps);
+          store_outputs(tt, out_row, ps);
         }
       }
       if constexpr (ADDR == kPagedVar) {
@@ -1264,9 +1295,22 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
         }
       }
     }
+    if constexpr (OUT_LDS) {
+      if (staged && c0 + TC < t1) {   // more chunks follow: this chunk's outputs now
+        __syncthreads();
+        flush_outputs(c0, n);
+      }
+    }
   }
 
   store_tile(dst);
+  if constexpr (OUT_LDS) {
+    if (staged) {                     // the last chunk's outputs, after the tile's stores are issued
+      __syncthreads();
+      const int cl = t0 + ((t1 - t0 - 1) / TC) * TC;
+      flush_outputs(cl, t1 - cl);
+    }
+  }
 }
 
 // The state traffic of a single-token step without its arithmetic
