@@ -126,6 +126,7 @@ constexpr float kE4M3Max = 448.0f;
 constexpr int kTokensPerChunk = 8;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // bf16 inputs are carried as their 16-bit patterns
 struct bf16_t {
@@ -456,6 +457,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   using Cfg = Tile<K, VB, NT, AV>;
   constexpr int NW = Cfg::NW, LR = Cfg::LR, RPW = Cfg::RPW, NS = Cfg::NS, LB = Cfg::LB;
   constexpr int EV = Cfg::EV, NKEY = Cfg::NKEY;
+  // CONTIG: a packed fp8 V_FIRST tile keeps a row lane's 8 keys contiguous
+  // (8 lr .. 8 lr + 7) instead of two 4-key pieces half a row apart, so that
+  // each row loads and stores as one 8-byte piece per lane: 16 lanes, one
+  // whole 128-byte line (paged GDN B=256: 66.0 -> 62.5 us).  Not for KDA: its
+  // three per-token key arrays then come out of LDS at a 32-byte lane stride
+  // with bank conflicts (75.7 -> 76.2 us)
+  constexpr bool CONTIG = FP8P && AV && !KDA && EV == 8 && K == 8 * LR;
   constexpr int TC = kTokensPerChunk;
   constexpr int TPW = (TC + NW - 1) / NW;          // tokens per wave in a chunk
   constexpr int EPL = (K + 63) / 64;               // q/k/gate elements per lane (contiguous)
@@ -518,7 +526,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
 
   // key index of this thread's key slot m, and the LDS position of key c
   auto key_of = [&](int m) -> int {
-    if constexpr (AV) return (EV == 8 ? (m / 4) * (K / 2) : 0) + 4 * lr + (m % 4);
+    if constexpr (CONTIG) return 8 * lr + m;
+    else if constexpr (AV) return (EV == 8 ? (m / 4) * (K / 2) : 0) + 4 * lr + (m % 4);
     else return m * (NW * RPW) + w * RPW + rg;
   };
   auto lds_pos = [](int c) -> int {
@@ -526,8 +535,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
     else return (c % (NW * RPW)) * NS + c / (NW * RPW);
   };
   // first LDS position of this thread's key slots (they are contiguous in
-  // both layouts, per half row for V_FIRST)
-  const int kbase = AV ? 4 * lr : (w * RPW + rg) * NS;
+  // both layouts, per half row for V_FIRST unless CONTIG)
+  const int kbase = CONTIG ? 8 * lr : AV ? 4 * lr : (w * RPW + rg) * NS;
 
   // ---- which tokens
   int t0, t1;
@@ -708,18 +717,27 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   if constexpr (FP8P) {
     // 4 e4m3 bytes for every 4 floats of the fp32 layout (same element order)
     const unsigned char* sb = reinterpret_cast<const unsigned char*>(src);
+    auto unpack4 = [&](uint32_t c4, float* x) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c4), false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c4), true);
+      x[0] = lo[0];
+      x[1] = lo[1];
+      x[2] = hi[0];
+      x[3] = hi[1];
+    };
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+    for (int s = 0; s < NS; ++s) {
+      if constexpr (CONTIG) {
+        const u32x2 c8 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
+            sb + static_cast<int64_t>(vb * VB + row_idx(s)) * K + 8 * lr));
+        unpack4(c8.x, &S[s][0]);
+        unpack4(c8.y, &S[s][4]);
+      } else {
 #pragma unroll
-      for (int f = 0; f < EV / 4; ++f) {
-        const uint32_t c4 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sb + row_off(s, f)));
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c4), false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c4), true);
-        S[s][4 * f + 0] = lo[0];
-        S[s][4 * f + 1] = lo[1];
-        S[s][4 * f + 2] = hi[0];
-        S[s][4 * f + 3] = hi[1];
+        for (int f = 0; f < EV / 4; ++f)
+          unpack4(__builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sb + row_off(s, f))), &S[s][4 * f]);
       }
+    }
     const float sc = __builtin_nontemporal_load(reinterpret_cast<const float*>(sb + tile_elems) + vb);
     fp8_scale = sc > 0.0f ? sc : 1.0f;   // an all-zero tile stores scale 0
     finish_raw(n0);                // overlaps the tile load
@@ -902,7 +920,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
     if constexpr (AV) {
 #pragma unroll
       for (int f = 0; f < EV / 4; ++f) {
-        const float4 v = *reinterpret_cast<const float4*>(base + f * (K / 2) + kbase);
+        const float4 v = *reinterpret_cast<const float4*>(base + (CONTIG ? 4 * f : f * (K / 2)) + kbase);
         x[4 * f + 0] = v.x; x[4 * f + 1] = v.y; x[4 * f + 2] = v.z; x[4 * f + 3] = v.w;
       }
     } else if constexpr (NS % 4 == 0) {
@@ -1078,15 +1096,23 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
       // tile scale is cs (one value: GDN's single scale, KDA's are equal),
       // 0 for an all-zero tile
       unsigned char* tb = reinterpret_cast<unsigned char*>(row_base);
+      auto pack4 = [&](const float* x) -> uint32_t {
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], __float_as_int(x[0]), false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], pk, true);
+        return static_cast<uint32_t>(pk);
+      };
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
+      for (int s = 0; s < NS; ++s) {
+        if constexpr (CONTIG) {
+          const u32x2 c8{pack4(&S[s][0]), pack4(&S[s][4])};
+          __builtin_nontemporal_store(
+              c8, reinterpret_cast<u32x2*>(tb + static_cast<int64_t>(vb * VB + row_idx(s)) * K + 8 * lr));
+        } else {
 #pragma unroll
-        for (int f = 0; f < EV / 4; ++f) {
-          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(S[s][4 * f + 0], S[s][4 * f + 1], __float_as_int(S[s][4 * f]),
-                                                   false);
-          pk = __builtin_amdgcn_cvt_pk_fp8_f32(S[s][4 * f + 2], S[s][4 * f + 3], pk, true);
-          __builtin_nontemporal_store(static_cast<uint32_t>(pk), reinterpret_cast<uint32_t*>(tb + row_off(s, f)));
+          for (int f = 0; f < EV / 4; ++f)
+            __builtin_nontemporal_store(pack4(&S[s][4 * f]), reinterpret_cast<uint32_t*>(tb + row_off(s, f)));
         }
+      }
       if (tid == 0)
         __builtin_nontemporal_store(tile_nz ? cs : 0.0f, reinterpret_cast<float*>(tb + tile_elems) + vb);
     } else if constexpr (!HAD) {
