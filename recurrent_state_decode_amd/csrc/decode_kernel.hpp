@@ -464,13 +464,15 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Params p) {
   // three per-token key arrays then come out of LDS at a 32-byte lane stride
   // with bank conflicts (75.7 -> 76.2 us)
   constexpr bool CONTIG = FP8P && AV && !KDA && EV == 8 && K == 8 * LR;
-  // Tokens staged per chunk.  A one-token paged call on a packed fp8 pool
-  // stages exactly one: the compiler cannot see that n <= 1 there and would
-  // keep every wave's raw-input registers for a whole chunk live across the
-  // tile load (GDN 156 -> 114 VGPRs, 3 -> 4 waves per SIMD: paged B=256
-  // 64.9 -> 59.8 us; KDA 105 -> 74 VGPRs, 76.4 -> 67.6 us).  The fp32
-  // one-token shapes measured 1-3 % slower that way and keep the chunk.
-  constexpr int TC = (ADDR == kPaged1 && FP8P) ? 1 : kTokensPerChunk;
+  // Tokens staged per chunk.  A one-token paged call on a packed pool stages
+  // exactly one: the compiler cannot see that n <= 1 there and would keep
+  // every wave's raw-input registers for a whole chunk live across the tile
+  // load (paged B=256: fp8 GDN 156 -> 114 VGPRs, 3 -> 4 waves per SIMD,
+  // 64.9 -> 59.8 us; fp8 KDA 105 -> 74 VGPRs, 76.4 -> 67.6 us; the
+  // int8_hadamard32 codec 114 -> 82 VGPRs, 88.2 -> 75.5 us).  On fp32 pools
+  // the one-token shapes measured 1-3 % slower that way, with or without
+  // QDQ, and keep the chunk.
+  constexpr int TC = (ADDR == kPaged1 && (FP8P || PACKED)) ? 1 : kTokensPerChunk;
   constexpr int TPW = (TC + NW - 1) / NW;          // tokens per wave in a chunk
   constexpr int EPL = (K + 63) / 64;               // q/k/gate elements per lane (contiguous)
   constexpr int EL = K / EPL;                      // lanes holding q/k elements
